@@ -1,0 +1,258 @@
+"""Seeded synthetic inputs for block-sparse attention forward.
+
+This module only draws random tensors and random *dense block masks*; it
+holds none of the attention arithmetic, none of the metadata encodings
+(index lists, varlen offsets, 256->128 expansion) and imports neither the
+oracle nor the HIP package.  Both sides consume what it returns.
+
+Every workload follows the shapes the pages measure on:
+
+* block-aligned causal BlockMask at B=2, H=4, S=1024 and a head_dim x block
+  size sweep (runguoli.com "FlashAttention — CuTe Kernels & Block Sparsity",
+  the H200 measurement paragraph of PR #2903);
+* packed variable-length batches (flash-attention PR #2224 "[CuTe,Flex]
+  varlen blocksparsity", PR description);
+* video sparse attention with 4x8x8 = 256-token cubes, partial edge cubes
+  and per-KV-block valid-token counts (FastVideo PR #1354, Summary and the
+  valid-count mask_mod in the review thread).
+
+Random draw order is always Q, K, V (fp32 N(0,1)) and then the metadata.
+Tensors are float32 numpy arrays; callers round them to bf16 (RNE) before
+use and both sides read the same rounded values.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+
+MASK_NONE = 0
+MASK_CAUSAL = 1
+MASK_KV_VALID_COUNT = 2
+
+SWEEP_HEAD_DIMS = (64, 96, 128, 192, 256)
+SWEEP_BLOCKS = ((128, 128), (64, 128), (128, 64), (64, 64), (128, 112))
+
+
+@dataclass
+class BatchedWorkload:
+    """Batched layout: q [B,Sq,H,D], k/v [B,Sk,Hkv,D] (BSHD, fp32).
+
+    full / part are dense block masks [B,H,M,N] (bool), M=ceil(Sq/bq),
+    N=ceil(Sk/bk).  `full` blocks take no element mask; `part` blocks take
+    `mask_mod`.  kv_valid (int32 [N]) is the per-KV-block valid-token count
+    used by MASK_KV_VALID_COUNT.
+    """
+    name: str
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    full: np.ndarray
+    part: np.ndarray
+    block_q: int
+    block_kv: int
+    mask_mod: int
+    scale: float
+    kv_valid: Optional[np.ndarray] = None
+    extra: dict = field(default_factory=dict)
+
+
+@dataclass
+class VarlenWorkload:
+    """Packed varlen layout: q/k/v [total_tokens, H, D] (THD, fp32).
+
+    seqlens_q / seqlens_k: python int lists.  full[b] / part[b] are dense
+    per-sequence block masks [H, M_b, N_b] with sequence-local block ids.
+    """
+    name: str
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    seqlens_q: List[int]
+    seqlens_k: List[int]
+    full: List[np.ndarray]
+    part: List[np.ndarray]
+    block_q: int
+    block_kv: int
+    mask_mod: int
+    scale: float
+
+
+@dataclass
+class VideoWorkload:
+    """Video sparse attention input at cube granularity.
+
+    q/k/v: [1, n_cubes*cube_elems, H, D] fp32, cube-major, real tokens first
+    inside each cube, padding rows zero.  cube_mask: [1, H, n_cubes, n_cubes]
+    bool (per Q cube, its top-k KV cubes).  cube_valid: int32 [n_cubes].
+    The attention runs on Q blocks of `cube_elems` rows and on KV tiles of
+    `kv_tile` rows; the cube->tile expansion is not done here.
+    """
+    name: str
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    cube_mask: np.ndarray
+    cube_valid: np.ndarray
+    cube_elems: int
+    kv_tile: int
+    scale: float
+    grid: tuple
+    cube: tuple
+
+
+def _qkv(rng, shape_q, shape_kv):
+    q = rng.standard_normal(shape_q, dtype=np.float32)
+    k = rng.standard_normal(shape_kv, dtype=np.float32)
+    v = rng.standard_normal(shape_kv, dtype=np.float32)
+    return q, k, v
+
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+def tiny(seed: int = 1001) -> BatchedWorkload:
+    """B=1, H=1, S=256, D=64 fp32; 64x64 blocks; Bernoulli(0.5) blocks with
+    the diagonal forced on; every selected block in the full list."""
+    rng = np.random.default_rng(seed)
+    B, H, S, D, bs = 1, 1, 256, 64, 64
+    q, k, v = _qkv(rng, (B, S, H, D), (B, S, H, D))
+    M = N = S // bs
+    full = rng.random((B, H, M, N)) < 0.5
+    for i in range(M):
+        full[:, :, i, i] = True
+    part = np.zeros_like(full)
+    return BatchedWorkload("tiny", q, k, v, full, part, bs, bs, MASK_NONE,
+                           1.0 / math.sqrt(D))
+
+
+def causal_blocks(B=2, H=4, S=1024, D=128, bs=128, seed: int = 1002) -> BatchedWorkload:
+    """Block-aligned causal mask: blocks strictly below the diagonal are full
+    blocks, diagonal blocks are mask blocks with the causal mask_mod."""
+    rng = np.random.default_rng(seed)
+    q, k, v = _qkv(rng, (B, S, H, D), (B, S, H, D))
+    M = N = _cdiv(S, bs)
+    ii = np.arange(M)[:, None]
+    jj = np.arange(N)[None, :]
+    full = np.broadcast_to(jj < ii, (B, H, M, N)).copy()
+    part = np.broadcast_to(jj == ii, (B, H, M, N)).copy()
+    return BatchedWorkload("causal_blocks", q, k, v, full, part, bs, bs,
+                           MASK_CAUSAL, 1.0 / math.sqrt(D))
+
+
+def _diagonal_blocks(i, bq, bk, Sq, Sk):
+    """KV blocks that hold both a causally visible (c <= r) and a causally
+    hidden (c > r) element for some row r of Q block i."""
+    r0, r1 = i * bq, min((i + 1) * bq, Sq) - 1
+    out = []
+    for j in range(_cdiv(Sk, bk)):
+        c0, c1 = j * bk, min((j + 1) * bk, Sk) - 1
+        if c0 <= r1 and c1 > r0:
+            out.append(j)
+    return out
+
+
+def sparse_sweep(D: int, bq: int, bk: int, B=2, H=16, S=4096,
+                 density: float = 0.25, seed: Optional[int] = None) -> BatchedWorkload:
+    """Per Q block: the causal-diagonal KV blocks as causal mask blocks plus
+    random other KV blocks as full blocks, floor(density*N) blocks in all."""
+    blocks_id = SWEEP_BLOCKS.index((bq, bk)) if (bq, bk) in SWEEP_BLOCKS else 99
+    rng = np.random.default_rng([1003, D, blocks_id] if seed is None else seed)
+    q, k, v = _qkv(rng, (B, S, H, D), (B, S, H, D))
+    M, N = _cdiv(S, bq), _cdiv(S, bk)
+    k_total = int(math.floor(density * N))
+    full = np.zeros((B, H, M, N), bool)
+    part = np.zeros((B, H, M, N), bool)
+    for i in range(M):
+        diag = _diagonal_blocks(i, bq, bk, S, S)
+        others = np.array([j for j in range(N) if j not in diag])
+        n_pick = max(k_total - len(diag), 0)
+        for b in range(B):
+            for h in range(H):
+                pick = rng.choice(others, size=n_pick, replace=False)
+                full[b, h, i, pick] = True
+                part[b, h, i, diag] = True
+    return BatchedWorkload(f"sweep_d{D}_bq{bq}_bk{bk}", q, k, v, full, part, bq, bk,
+                           MASK_CAUSAL, 1.0 / math.sqrt(D))
+
+
+def varlen_packed(n_seq=8, H=16, D=128, bs=128, lo=128, hi=8192, p_below=0.3,
+                  seed: int = 1004) -> VarlenWorkload:
+    """Packed batch of n_seq sequences (seqlen_q = seqlen_k ~ U{lo..hi}).
+    Per sequence and head: diagonal blocks are causal mask blocks, each block
+    strictly below the diagonal is a full block with probability p_below."""
+    rng = np.random.default_rng(seed)
+    seqlens = [int(x) for x in rng.integers(lo, hi + 1, size=n_seq)]
+    total = sum(seqlens)
+    q, k, v = _qkv(rng, (total, H, D), (total, H, D))
+    full, part = [], []
+    for s in seqlens:
+        M = N = _cdiv(s, bs)
+        ii = np.arange(M)[:, None]
+        jj = np.arange(N)[None, :]
+        below = rng.random((H, M, N)) < p_below
+        full.append(below & (jj < ii)[None])
+        part.append(np.broadcast_to((jj == ii)[None], (H, M, N)).copy())
+    return VarlenWorkload("varlen_packed", q, k, v, seqlens, list(seqlens), full, part,
+                          bs, bs, MASK_CAUSAL, 1.0 / math.sqrt(D))
+
+
+def _cube_layout(grid, cube):
+    """Valid-token count of each cube (cube-major order t, h, w) and, for each
+    real token of the grid (t, h, w order), its padded row."""
+    nc = [_cdiv(g, c) for g, c in zip(grid, cube)]
+    ce = cube[0] * cube[1] * cube[2]
+    valid = np.zeros(nc[0] * nc[1] * nc[2], np.int32)
+    cid = 0
+    for a in range(nc[0]):
+        for b in range(nc[1]):
+            for c in range(nc[2]):
+                valid[cid] = (min(cube[0], grid[0] - a * cube[0]) *
+                              min(cube[1], grid[1] - b * cube[1]) *
+                              min(cube[2], grid[2] - c * cube[2]))
+                cid += 1
+    return valid, ce
+
+
+def video(grid=(30, 48, 52), cube=(4, 8, 8), H=24, D=128, kv_tile=128,
+          topk_frac=0.12, seed: int = 1005) -> VideoWorkload:
+    """Video-style sparse attention at cube granularity.
+
+    Tokens sit in a padded cube-major buffer (real tokens first in each cube,
+    padding zero).  Each Q cube selects its top-k KV cubes by the mean-pooled
+    (over real tokens) Q.K score, k = round(topk_frac * n_cubes), ties to the
+    lower cube id.
+    """
+    rng = np.random.default_rng(seed)
+    valid, ce = _cube_layout(grid, cube)
+    n_cubes = len(valid)
+    S = n_cubes * ce
+    q, k, v = _qkv(rng, (1, S, H, D), (1, S, H, D))
+    pad = np.ones(S, bool)
+    for c in range(n_cubes):
+        pad[c * ce: c * ce + valid[c]] = False
+    q[:, pad] = 0.0
+    k[:, pad] = 0.0
+    v[:, pad] = 0.0
+    # selection scores from mean-pooled real tokens (input generation only)
+    qc = q[0].reshape(n_cubes, ce, H, D).astype(np.float64).sum(1) / valid[:, None, None]
+    kc = k[0].reshape(n_cubes, ce, H, D).astype(np.float64).sum(1) / valid[:, None, None]
+    topk = int(round(topk_frac * n_cubes))
+    cube_mask = np.zeros((1, H, n_cubes, n_cubes), bool)
+    cols = np.arange(n_cubes)
+    for h in range(H):
+        sc = qc[:, h, :] @ kc[:, h, :].T
+        for i in range(n_cubes):
+            order = np.lexsort((cols, -sc[i]))  # by score desc, then id asc
+            cube_mask[0, h, i, order[:topk]] = True
+    return VideoWorkload("video", q, k, v, cube_mask, valid, ce, kv_tile,
+                         1.0 / math.sqrt(D), tuple(grid), tuple(cube))
+
+
+def config(n: int, **kw):
+    """The five named workloads: 1 tiny, 2 causal_blocks, 3 sparse_sweep
+    (pass D, bq, bk), 4 varlen_packed, 5 video."""
+    return {1: tiny, 2: causal_blocks, 3: sparse_sweep, 4: varlen_packed, 5: video}[n](**kw)
