@@ -27,7 +27,7 @@ def mask_to_index(mask: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     """
     mask = np.asarray(mask)
     lead, N = mask.shape[:-1], mask.shape[-1]
-    flat = mask.reshape(-1, N)
+    flat = mask.reshape(int(np.prod(lead, dtype=np.int64)), N)
     cnt = np.zeros(flat.shape[0], np.int32)
     idx = np.full((flat.shape[0], N), -1, np.int32)
     for r in range(flat.shape[0]):

@@ -155,3 +155,8 @@ def test_expand_video_cube_counts():
     assert kv.shape == (672,)
     assert sorted(set(kv.tolist())) == [0, 64, 128]
     assert int(kv.sum()) == 74880
+
+
+def test_mask_to_index_zero_width_rows():
+    cnt, idx = oracle.mask_to_index(np.zeros((2, 3, 0), np.uint8))
+    assert cnt.shape == (2, 3) and (cnt == 0).all() and idx.shape == (2, 3, 0)
