@@ -1,0 +1,401 @@
+// C-ABI entry points of libbsa.so: argument checks, the tile-fit rule,
+// launch-parameter assembly and the optional host-side metadata check.
+// No device allocation, no device->host copies on the normal path.
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include <cmath>
+#include <limits>
+#include <vector>
+
+#include "../../include/bsa.h"
+#include "bsa_internal.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_head_dim(int D) { return D == 64 || D == 96 || D == 128 || D == 192 || D == 256; }
+
+// Tile fit (runguoli.com "FlashAttention - CuTe Kernels & Block Sparsity":
+// fit the forward tile to the sparse block instead of rejecting it): the
+// workgroup row count is the largest of 128/64/32 dividing the sparse Q
+// block, and a larger Q block is covered by block_q / tile_m workgroups that
+// share its block-list row.  KV blocks of any size are cut into 64-key
+// sub-tiles inside the kernel.
+int fit_tile_m(int block_q) {
+  if (block_q % 128 == 0) return 128;
+  if (block_q % 64 == 0) return 64;
+  if (block_q % 32 == 0) return 32;
+  return 0;
+}
+
+int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool strides_ok(const int64_t* s, int n, int esize) {
+  for (int i = 0; i < n; ++i)
+    if (s[i] < 0 || (s[i] * esize) % 16 != 0) return false;
+  return true;
+}
+
+bool list_ok(const bsa_block_list& L) {
+  if (L.cnt == nullptr) return true;
+  if (L.idx == nullptr) return false;
+  for (int i = 0; i < 3; ++i)
+    if (L.cnt_stride[i] < 0) return false;
+  for (int i = 0; i < 4; ++i)
+    if (L.idx_stride[i] < 0) return false;
+  return true;
+}
+
+// ---- BSA_FLAG_VALIDATE: copy the lists to the host and check every row.
+bsa_status fetch(const int32_t* dev, int64_t n, std::vector<int32_t>& host, hipStream_t s) {
+  host.assign((size_t)(n > 0 ? n : 0), 0);
+  if (n <= 0) return BSA_OK;
+  if (hipMemcpyAsync(host.data(), dev, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost, s) !=
+      hipSuccess)
+    return BSA_ERR_HIP;
+  return BSA_OK;
+}
+
+// checks one Q-block row given its two (count, row-start) pairs
+bool row_ok(const std::vector<int32_t>* hidx[2], const int64_t cnt[2], const int64_t start[2],
+            const int64_t step[2], int64_t N, std::vector<char>& seen) {
+  seen.assign((size_t)N, 0);
+  for (int l = 0; l < 2; ++l) {
+    if (cnt[l] < 0 || cnt[l] > N) return false;
+    for (int64_t e = 0; e < cnt[l]; ++e) {
+      const int64_t j = (*hidx[l])[(size_t)(start[l] + e * step[l])];
+      if (j < 0 || j >= N || seen[(size_t)j]) return false;
+      seen[(size_t)j] = 1;
+    }
+  }
+  return true;
+}
+
+int64_t span3(const int64_t* st, int64_t d0, int64_t d1, int64_t d2) {
+  return (d0 - 1) * st[0] + (d1 - 1) * st[1] + (d2 - 1) * st[2] + 1;
+}
+
+bsa_status validate_batched(const bsa_block_sparse& bs, int B, int H, int64_t M, int64_t N,
+                            hipStream_t s) {
+  const bsa_block_list* lists[2] = {&bs.mask, &bs.full};
+  std::vector<int32_t> hc[2], hi[2];
+  for (int l = 0; l < 2; ++l) {
+    if (!lists[l]->cnt) continue;
+    const int64_t nc = span3(lists[l]->cnt_stride, B, H, M);
+    const int64_t ni = span3(lists[l]->idx_stride, B, H, M) + (N - 1) * lists[l]->idx_stride[3];
+    bsa_status st = fetch(lists[l]->cnt, nc, hc[l], s);
+    if (st == BSA_OK) st = fetch(lists[l]->idx, N > 0 ? ni : 0, hi[l], s);
+    if (st != BSA_OK) return st;
+  }
+  if (hipStreamSynchronize(s) != hipSuccess) return BSA_ERR_HIP;
+  std::vector<char> seen;
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h)
+      for (int64_t m = 0; m < M; ++m) {
+        int64_t cnt[2] = {0, 0}, start[2] = {0, 0}, step[2] = {0, 0};
+        const std::vector<int32_t>* hidx[2] = {&hi[0], &hi[1]};
+        for (int l = 0; l < 2; ++l) {
+          const bsa_block_list& L = *lists[l];
+          if (!L.cnt) continue;
+          cnt[l] = hc[l][(size_t)(b * L.cnt_stride[0] + h * L.cnt_stride[1] + m * L.cnt_stride[2])];
+          start[l] = b * L.idx_stride[0] + h * L.idx_stride[1] + m * L.idx_stride[2];
+          step[l] = L.idx_stride[3];
+        }
+        if (!row_ok(hidx, cnt, start, step, N, seen)) return BSA_ERR_METADATA;
+      }
+  return BSA_OK;
+}
+
+bsa_status validate_varlen(const bsa_block_sparse& bs, int B, int H, const int32_t* cu_q,
+                           const int32_t* cu_k, const int32_t* cu_m, const int32_t* off,
+                           int32_t total_m, int32_t total_n, hipStream_t s) {
+  std::vector<int32_t> hq, hk, hm, ho;
+  bsa_status st = fetch(cu_q, B + 1, hq, s);
+  if (st == BSA_OK) st = fetch(cu_k, B + 1, hk, s);
+  if (st == BSA_OK) st = fetch(cu_m, B + 1, hm, s);
+  if (st == BSA_OK) st = fetch(off, B + 1, ho, s);
+  const bsa_block_list* lists[2] = {&bs.mask, &bs.full};
+  std::vector<int32_t> hc[2], hi[2];
+  for (int l = 0; l < 2 && st == BSA_OK; ++l) {
+    if (!lists[l]->cnt) continue;
+    const bsa_block_list& L = *lists[l];
+    const int64_t nc = total_m > 0 ? (H - 1) * L.cnt_stride[1] + (total_m - 1) * L.cnt_stride[2] + 1 : 0;
+    const int64_t ni = total_n > 0 ? (H - 1) * L.idx_stride[1] + (total_n - 1) * L.idx_stride[3] + 1 : 0;
+    st = fetch(L.cnt, nc, hc[l], s);
+    if (st == BSA_OK) st = fetch(L.idx, ni, hi[l], s);
+  }
+  if (st != BSA_OK) return st;
+  if (hipStreamSynchronize(s) != hipSuccess) return BSA_ERR_HIP;
+  // the cumulative arrays must be the ones the sequence lengths imply
+  if (hq[0] != 0 || hk[0] != 0 || hm[0] != 0 || ho[0] != 0) return BSA_ERR_METADATA;
+  for (int b = 0; b < B; ++b) {
+    const int64_t sq = hq[b + 1] - hq[b], sk = hk[b + 1] - hk[b];
+    if (sq < 0 || sk < 0) return BSA_ERR_METADATA;
+    const int64_t nm = cdiv64(sq, bs.block_q), nn = cdiv64(sk, bs.block_kv);
+    if (hm[b + 1] - hm[b] != nm || ho[b + 1] - ho[b] != nm * nn) return BSA_ERR_METADATA;
+  }
+  if (hm[B] != total_m || ho[B] != total_n) return BSA_ERR_METADATA;
+  std::vector<char> seen;
+  for (int h = 0; h < H; ++h)
+    for (int b = 0; b < B; ++b) {
+      const int64_t nm = hm[b + 1] - hm[b];
+      const int64_t nn = nm > 0 ? (ho[b + 1] - ho[b]) / nm : 0;
+      for (int64_t m = 0; m < nm; ++m) {
+        int64_t cnt[2] = {0, 0}, start[2] = {0, 0}, step[2] = {0, 0};
+        const std::vector<int32_t>* hidx[2] = {&hi[0], &hi[1]};
+        for (int l = 0; l < 2; ++l) {
+          const bsa_block_list& L = *lists[l];
+          if (!L.cnt) continue;
+          cnt[l] = hc[l][(size_t)(h * L.cnt_stride[1] + (hm[b] + m) * L.cnt_stride[2])];
+          start[l] = h * L.idx_stride[1] + (ho[b] + m * nn) * L.idx_stride[3];
+          step[l] = L.idx_stride[3];
+        }
+        if (!row_ok(hidx, cnt, start, step, nn, seen)) return BSA_ERR_METADATA;
+      }
+    }
+  return BSA_OK;
+}
+
+void copy_lists(bsa::FwdParams& p, const bsa_block_sparse& bs) {
+  p.mcnt = bs.mask.cnt;
+  p.midx = bs.mask.idx;
+  p.fcnt = bs.full.cnt;
+  p.fidx = bs.full.idx;
+  for (int i = 0; i < 3; ++i) {
+    p.mc_s[i] = bs.mask.cnt_stride[i];
+    p.fc_s[i] = bs.full.cnt_stride[i];
+  }
+  for (int i = 0; i < 4; ++i) {
+    p.mi_s[i] = bs.mask.idx_stride[i];
+    p.fi_s[i] = bs.full.idx_stride[i];
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bsa_status_str(bsa_status s) {
+  switch (s) {
+    case BSA_OK: return "ok";
+    case BSA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case BSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case BSA_ERR_MISALIGNED: return "misaligned pointer or stride (16-byte alignment required)";
+    case BSA_ERR_METADATA: return "invalid block-sparse metadata";
+    case BSA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+bsa_status bsa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, bsa_dtype dt,
+                   int32_t B, int32_t H, int32_t H_kv, int32_t Sq, int32_t Sk, int32_t D,
+                   const int64_t q_str[3], const int64_t k_str[3], const int64_t v_str[3],
+                   const int64_t o_str[3], const bsa_block_sparse* bs, bsa_mask_mod mask_mod,
+                   const int32_t* kv_valid, float softmax_scale, uint32_t flags,
+                   hipStream_t stream) {
+  if (B < 0 || H <= 0 || H_kv <= 0 || Sq < 0 || Sk < 0 || H % H_kv != 0)
+    return BSA_ERR_INVALID_ARGUMENT;
+  if (dt != BSA_BF16 && dt != BSA_F32) return BSA_ERR_INVALID_ARGUMENT;
+  if (mask_mod < BSA_MASK_NONE || mask_mod > BSA_MASK_KV_VALID_COUNT) return BSA_ERR_INVALID_ARGUMENT;
+  if (!bs || !q_str || !k_str || !v_str || !o_str) return BSA_ERR_INVALID_ARGUMENT;
+  if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f)) return BSA_ERR_INVALID_ARGUMENT;
+  if (bs->block_q <= 0 || bs->block_kv <= 0) return BSA_ERR_INVALID_ARGUMENT;
+  if (!list_ok(bs->mask) || !list_ok(bs->full)) return BSA_ERR_INVALID_ARGUMENT;
+  if (!supported_head_dim(D)) return BSA_ERR_UNSUPPORTED;
+  const int tile_m = fit_tile_m(bs->block_q);
+  if (tile_m == 0) return BSA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H * Sq == 0) return BSA_OK;  // nothing to write
+  if (!q || !k || !v || !o || !lse) return BSA_ERR_INVALID_ARGUMENT;
+  if (mask_mod == BSA_MASK_KV_VALID_COUNT && !kv_valid && bs->mask.cnt)
+    return BSA_ERR_INVALID_ARGUMENT;
+  const int es = dt == BSA_BF16 ? 2 : 4;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return BSA_ERR_MISALIGNED;
+  if (!strides_ok(q_str, 3, es) || !strides_ok(k_str, 3, es) || !strides_ok(v_str, 3, es) ||
+      !strides_ok(o_str, 3, es))
+    return BSA_ERR_MISALIGNED;
+  const int64_t M = cdiv64(Sq, bs->block_q), N = cdiv64(Sk, bs->block_kv);
+  const int64_t tiles_per_head = cdiv64(Sq, tile_m);
+  const int64_t tiles = (int64_t)B * H * tiles_per_head;
+  if (tiles > std::numeric_limits<int32_t>::max() || N > std::numeric_limits<int32_t>::max() / 2)
+    return BSA_ERR_UNSUPPORTED;
+  if (flags & BSA_FLAG_VALIDATE) {
+    const bsa_status st = validate_batched(*bs, B, H, M, N, stream);
+    if (st != BSA_OK) return st;
+  }
+  bsa::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.q_sb = q_str[0]; p.q_ss = q_str[1]; p.q_sh = q_str[2];
+  p.k_sb = k_str[0]; p.k_ss = k_str[1]; p.k_sh = k_str[2];
+  p.v_sb = v_str[0]; p.v_ss = v_str[1]; p.v_sh = v_str[2];
+  p.o_sb = o_str[0]; p.o_ss = o_str[1]; p.o_sh = o_str[2];
+  copy_lists(p, *bs);
+  p.kv_valid = kv_valid;
+  p.B = B;
+  p.H = H;
+  p.hrep = H / H_kv;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.block_q = bs->block_q;
+  p.block_kv = bs->block_kv;
+  p.qsub = bs->block_q / tile_m;
+  p.kvsub = (int32_t)cdiv64(bs->block_kv, bsa::kKvTile);
+  p.mask_mod = mask_mod;
+  p.varlen = 0;
+  p.tiles_per_head = (int32_t)tiles_per_head;
+  p.lse_ld = Sq;
+  p.num_tiles = (int32_t)tiles;
+  p.c = softmax_scale * kLog2e;
+  const hipError_t e = bsa::launch_fwd(p, D, tile_m, dt == BSA_F32, stream);
+  return e == hipSuccess ? BSA_OK : BSA_ERR_HIP;
+}
+
+bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                          bsa_dtype dt, int32_t B, int32_t H, int32_t H_kv, int32_t D,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          const int32_t* cu_total_m_blocks, const int32_t* block_idx_offsets,
+                          int32_t total_m_blocks, int32_t total_n_blocks, int32_t total_q,
+                          const int64_t q_str[2], const int64_t k_str[2], const int64_t v_str[2],
+                          const int64_t o_str[2], const bsa_block_sparse* bs,
+                          bsa_mask_mod mask_mod, float softmax_scale, uint32_t flags,
+                          hipStream_t stream) {
+  if (B < 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || total_m_blocks < 0 || total_n_blocks < 0 ||
+      total_q < 0)
+    return BSA_ERR_INVALID_ARGUMENT;
+  if (dt != BSA_BF16 && dt != BSA_F32) return BSA_ERR_INVALID_ARGUMENT;
+  if (mask_mod != BSA_MASK_NONE && mask_mod != BSA_MASK_CAUSAL) {
+    if (mask_mod == BSA_MASK_KV_VALID_COUNT) return BSA_ERR_UNSUPPORTED;
+    return BSA_ERR_INVALID_ARGUMENT;
+  }
+  if (!bs || !q_str || !k_str || !v_str || !o_str) return BSA_ERR_INVALID_ARGUMENT;
+  if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f)) return BSA_ERR_INVALID_ARGUMENT;
+  if (bs->block_q <= 0 || bs->block_kv <= 0) return BSA_ERR_INVALID_ARGUMENT;
+  if (!list_ok(bs->mask) || !list_ok(bs->full)) return BSA_ERR_INVALID_ARGUMENT;
+  if (!supported_head_dim(D)) return BSA_ERR_UNSUPPORTED;
+  const int tile_m = fit_tile_m(bs->block_q);
+  if (tile_m == 0) return BSA_ERR_UNSUPPORTED;
+  if (B == 0 || total_m_blocks == 0) return BSA_OK;
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k || !cu_total_m_blocks ||
+      !block_idx_offsets)
+    return BSA_ERR_INVALID_ARGUMENT;
+  const int es = dt == BSA_BF16 ? 2 : 4;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return BSA_ERR_MISALIGNED;
+  if (!strides_ok(q_str, 2, es) || !strides_ok(k_str, 2, es) || !strides_ok(v_str, 2, es) ||
+      !strides_ok(o_str, 2, es))
+    return BSA_ERR_MISALIGNED;
+  const int qsub = bs->block_q / tile_m;
+  const int64_t tiles_per_head = (int64_t)total_m_blocks * qsub;
+  const int64_t tiles = tiles_per_head * H;
+  if (tiles > std::numeric_limits<int32_t>::max()) return BSA_ERR_UNSUPPORTED;
+  if (flags & BSA_FLAG_VALIDATE) {
+    const bsa_status st = validate_varlen(*bs, B, H, cu_seqlens_q, cu_seqlens_k, cu_total_m_blocks,
+                                          block_idx_offsets, total_m_blocks, total_n_blocks, stream);
+    if (st != BSA_OK) return st;
+  }
+  bsa::FwdParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.q_ss = q_str[0]; p.q_sh = q_str[1];
+  p.k_ss = k_str[0]; p.k_sh = k_str[1];
+  p.v_ss = v_str[0]; p.v_sh = v_str[1];
+  p.o_ss = o_str[0]; p.o_sh = o_str[1];
+  copy_lists(p, *bs);
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.cu_m = cu_total_m_blocks;
+  p.blk_off = block_idx_offsets;
+  p.B = B;
+  p.H = H;
+  p.hrep = H / H_kv;
+  p.block_q = bs->block_q;
+  p.block_kv = bs->block_kv;
+  p.qsub = qsub;
+  p.kvsub = (int32_t)cdiv64(bs->block_kv, bsa::kKvTile);
+  p.mask_mod = mask_mod;
+  p.varlen = 1;
+  p.tiles_per_head = (int32_t)tiles_per_head;
+  p.total_m = total_m_blocks;
+  p.total_n = total_n_blocks;
+  p.lse_ld = total_q;
+  p.num_tiles = (int32_t)tiles;
+  p.c = softmax_scale * kLog2e;
+  const hipError_t e = bsa::launch_fwd(p, D, tile_m, dt == BSA_F32, stream);
+  return e == hipSuccess ? BSA_OK : BSA_ERR_HIP;
+}
+
+bsa_status bsa_mask_to_index(const uint8_t* mask, int32_t B, int32_t H, int32_t M, int32_t N,
+                             int32_t* cnt, int32_t* idx, hipStream_t stream) {
+  if (B < 0 || H < 0 || M < 0 || N < 0) return BSA_ERR_INVALID_ARGUMENT;
+  const int64_t rows = (int64_t)B * H * M;
+  if (rows == 0) return BSA_OK;
+  if (!cnt || (N > 0 && (!mask || !idx))) return BSA_ERR_INVALID_ARGUMENT;
+  const hipError_t e = bsa::launch_mask_to_index(mask, rows, N, cnt, idx, stream);
+  return e == hipSuccess ? BSA_OK : BSA_ERR_HIP;
+}
+
+bsa_status bsa_varlen_mask_to_index(const uint8_t* mask, int32_t H, int32_t B,
+                                    const int32_t* cu_total_m_blocks,
+                                    const int32_t* block_idx_offsets, int32_t total_m_blocks,
+                                    int32_t total_n_blocks, int32_t* cnt, int32_t* idx,
+                                    hipStream_t stream) {
+  if (H < 0 || B < 0 || total_m_blocks < 0 || total_n_blocks < 0) return BSA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)H * total_m_blocks == 0 || B == 0) return BSA_OK;
+  if (!cnt || !cu_total_m_blocks || !block_idx_offsets) return BSA_ERR_INVALID_ARGUMENT;
+  if (total_n_blocks > 0 && (!mask || !idx)) return BSA_ERR_INVALID_ARGUMENT;
+  const hipError_t e =
+      bsa::launch_varlen_mask_to_index(mask, H, B, cu_total_m_blocks, block_idx_offsets,
+                                       total_m_blocks, total_n_blocks, cnt, idx, stream);
+  return e == hipSuccess ? BSA_OK : BSA_ERR_HIP;
+}
+
+bsa_status bsa_varlen_offsets(const int32_t* seqlens_q, const int32_t* seqlens_k, int32_t B,
+                              int32_t block_q, int32_t block_kv, int32_t* cu_total_m_blocks,
+                              int32_t* block_idx_offsets, int32_t* total_m_blocks,
+                              int32_t* total_n_blocks) {
+  if (B < 0 || block_q <= 0 || block_kv <= 0) return BSA_ERR_INVALID_ARGUMENT;
+  if (!cu_total_m_blocks || !block_idx_offsets || !total_m_blocks || !total_n_blocks)
+    return BSA_ERR_INVALID_ARGUMENT;
+  if (B > 0 && (!seqlens_q || !seqlens_k)) return BSA_ERR_INVALID_ARGUMENT;
+  int64_t cm = 0, co = 0;
+  cu_total_m_blocks[0] = 0;
+  block_idx_offsets[0] = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (seqlens_q[b] < 0 || seqlens_k[b] < 0) return BSA_ERR_INVALID_ARGUMENT;
+    const int64_t nm = cdiv64(seqlens_q[b], block_q);
+    const int64_t nn = cdiv64(seqlens_k[b], block_kv);
+    cm += nm;
+    co += nm * nn;
+    if (cm > std::numeric_limits<int32_t>::max() || co > std::numeric_limits<int32_t>::max())
+      return BSA_ERR_INVALID_ARGUMENT;
+    cu_total_m_blocks[b + 1] = (int32_t)cm;
+    block_idx_offsets[b + 1] = (int32_t)co;
+  }
+  *total_m_blocks = (int32_t)cm;
+  *total_n_blocks = (int32_t)co;
+  return BSA_OK;
+}
+
+bsa_status bsa_expand_kv_blocks(const uint8_t* block_mask, const int32_t* block_valid, int32_t R,
+                                int32_t NL, int32_t factor, int32_t child, uint8_t* full,
+                                uint8_t* part, int32_t* kv_valid, hipStream_t stream) {
+  if (R < 0 || NL < 0 || factor <= 0 || child <= 0) return BSA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)NL * factor > std::numeric_limits<int32_t>::max()) return BSA_ERR_INVALID_ARGUMENT;
+  if (NL == 0) return BSA_OK;
+  if (!block_valid || !kv_valid) return BSA_ERR_INVALID_ARGUMENT;
+  if (R > 0 && (!block_mask || !full || !part)) return BSA_ERR_INVALID_ARGUMENT;
+  const hipError_t e = bsa::launch_expand_kv_blocks(block_mask, block_valid, R, NL, factor, child,
+                                                    full, part, kv_valid, stream);
+  return e == hipSuccess ? BSA_OK : BSA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Internal launch interface between the C-ABI layer (bsa_api.cpp) and the
+// gfx950 kernels.  Not installed; not part of the ABI.
+#pragma once
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+namespace bsa {
+
+// Keys per KV sub-tile staged through LDS.  A listed KV block of block_kv
+// tokens is processed as ceil(block_kv / kKvTile) sub-tiles.
+constexpr int kKvTile = 64;
+
+// Everything one forward launch needs, in element units of the input dtype.
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  // strides: batched {batch, seq, head}; varlen {-, token, head}
+  int64_t q_sb, q_ss, q_sh;
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  int64_t o_sb, o_ss, o_sh;
+  // block lists (cnt == nullptr: list absent)
+  const int32_t* mcnt;
+  const int32_t* midx;
+  const int32_t* fcnt;
+  const int32_t* fidx;
+  int64_t mc_s[3], mi_s[4], fc_s[3], fi_s[4];
+  const int32_t* kv_valid;
+  // varlen bookkeeping (device, [B+1]); null for batched
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* cu_m;
+  const int32_t* blk_off;
+  int32_t B, H, hrep, Sq, Sk;
+  int32_t block_q, block_kv, qsub, kvsub;
+  int32_t mask_mod, varlen;
+  int32_t tiles_per_head;  // batched: ceil(Sq/TM); varlen: total_m_blocks*qsub
+  int32_t total_m, total_n;  // varlen only
+  int32_t lse_ld;          // batched: Sq; varlen: total_q
+  int32_t num_tiles;       // grid size
+  float c;                 // softmax_scale * log2(e)
+};
+
+// Launch the forward kernel instance for (D, rows per workgroup, dtype).
+// Returns hipSuccess or the launch error; unsupported combinations return
+// hipErrorInvalidValue (the caller checks support first).
+hipError_t launch_fwd(const FwdParams& p, int D, int tile_m, bool f32_in, hipStream_t s);
+
+hipError_t launch_mask_to_index(const uint8_t* mask, int64_t rows, int32_t N,
+                                int32_t* cnt, int32_t* idx, hipStream_t s);
+
+hipError_t launch_varlen_mask_to_index(const uint8_t* mask, int32_t H, int32_t B,
+                                       const int32_t* cu_m, const int32_t* off,
+                                       int32_t total_m, int32_t total_n,
+                                       int32_t* cnt, int32_t* idx, hipStream_t s);
+
+hipError_t launch_expand_kv_blocks(const uint8_t* block_mask, const int32_t* block_valid,
+                                   int32_t R, int32_t NL, int32_t factor, int32_t child,
+                                   uint8_t* full, uint8_t* part, int32_t* kv_valid,
+                                   hipStream_t s);
+
+}  // namespace bsa

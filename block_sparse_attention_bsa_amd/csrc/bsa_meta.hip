@@ -1,0 +1,140 @@
+// Metadata kernels for gfx950: dense block mask -> block lists (batched and
+// packed varlen rows) and the split of logical KV blocks into child tiles.
+//
+// mask -> index follows the conversion "Dense FlashAttention vs Block-Sparse
+// Attention" (section 2) describes: per Q-block row, the selected KV-block
+// ids in descending order, then -1.  One wave compacts one row: lanes take
+// 64 columns at a time from the top, a ballot gives the selected set and
+// the popcount of the lower lanes' bits gives each id its slot, so the
+// result is deterministic and bit-exact.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bsa_internal.h"
+
+namespace bsa {
+namespace {
+
+constexpr int kWavesPerBlock = 4;
+
+__device__ __forceinline__ void compact_row(const uint8_t* __restrict__ mrow, int N,
+                                            int32_t* __restrict__ irow, int32_t* __restrict__ cnt,
+                                            int lane) {
+  int run = 0;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c0 = 0; c0 < N; c0 += 64) {
+    const int col = N - 1 - (c0 + lane);
+    const bool sel = col >= 0 && mrow[col] != 0;
+    const uint64_t bal = __ballot(sel);
+    if (sel) irow[run + __popcll(bal & below)] = col;
+    run += __popcll(bal);
+  }
+  for (int s = run + lane; s < N; s += 64) irow[s] = -1;
+  if (lane == 0) *cnt = run;
+}
+
+__global__ __launch_bounds__(64 * kWavesPerBlock) void mask_to_index_kernel(
+    const uint8_t* __restrict__ mask, int64_t rows, int32_t N, int32_t* __restrict__ cnt,
+    int32_t* __restrict__ idx) {
+  const int64_t row = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  compact_row(mask + row * N, N, idx + row * N, cnt + row, lane);
+}
+
+__global__ __launch_bounds__(64 * kWavesPerBlock) void varlen_mask_to_index_kernel(
+    const uint8_t* __restrict__ mask, int32_t H, int32_t B, const int32_t* __restrict__ cu_m,
+    const int32_t* __restrict__ off, int32_t total_m, int32_t total_n, int32_t* __restrict__ cnt,
+    int32_t* __restrict__ idx) {
+  const int64_t row = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= (int64_t)H * total_m) return;
+  const int h = (int)(row / total_m);
+  const int mg = (int)(row % total_m);
+  int lo = 0, hi = B - 1;  // largest b with cu_m[b] <= mg
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu_m[mid] <= mg)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const int b = lo;
+  const int nm = cu_m[b + 1] - cu_m[b];
+  const int m = mg - cu_m[b];
+  if (nm <= 0 || m < 0 || m >= nm) return;
+  const int64_t span = (int64_t)off[b + 1] - off[b];
+  const int nn = (int)(span / nm);
+  const int64_t start = (int64_t)off[b] + (int64_t)m * nn;
+  if (nn < 0 || start < 0 || start + nn > total_n) return;
+  const int64_t base = (int64_t)h * total_n + start;
+  compact_row(mask + base, nn, idx + base, cnt + (int64_t)h * total_m + mg, lane);
+}
+
+__global__ __launch_bounds__(256) void expand_kv_blocks_kernel(
+    const uint8_t* __restrict__ bm, const int32_t* __restrict__ bv, int32_t R, int32_t NL,
+    int32_t f, int32_t child, uint8_t* __restrict__ full, uint8_t* __restrict__ part,
+    int32_t* __restrict__ kvv) {
+  const int64_t ncols = (int64_t)NL * f;
+  const int64_t n = (int64_t)R * ncols;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < n || x < ncols;
+       x += stride) {
+    if (x < ncols) {
+      const int j = (int)(x / f), s = (int)(x % f);
+      kvv[x] = min(max(bv[j] - s * child, 0), child);
+    }
+    if (x < n) {
+      const int64_t r = x / ncols;
+      const int jc = (int)(x % ncols);
+      const int j = jc / f, s = jc % f;
+      const int sz = min(max(bv[j] - s * child, 0), child);
+      const bool sel = bm[r * NL + j] != 0;
+      full[x] = (sel && sz == child) ? 1 : 0;
+      part[x] = (sel && sz > 0 && sz < child) ? 1 : 0;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mask_to_index(const uint8_t* mask, int64_t rows, int32_t N, int32_t* cnt,
+                                int32_t* idx, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int64_t blocks = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(mask_to_index_kernel, dim3((unsigned)blocks), dim3(64 * kWavesPerBlock), 0,
+                     s, mask, rows, N, cnt, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_varlen_mask_to_index(const uint8_t* mask, int32_t H, int32_t B,
+                                       const int32_t* cu_m, const int32_t* off, int32_t total_m,
+                                       int32_t total_n, int32_t* cnt, int32_t* idx,
+                                       hipStream_t s) {
+  const int64_t rows = (int64_t)H * total_m;
+  if (rows <= 0) return hipSuccess;
+  const int64_t blocks = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(varlen_mask_to_index_kernel, dim3((unsigned)blocks),
+                     dim3(64 * kWavesPerBlock), 0, s, mask, H, B, cu_m, off, total_m, total_n,
+                     cnt, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_expand_kv_blocks(const uint8_t* block_mask, const int32_t* block_valid,
+                                   int32_t R, int32_t NL, int32_t factor, int32_t child,
+                                   uint8_t* full, uint8_t* part, int32_t* kv_valid,
+                                   hipStream_t s) {
+  const int64_t n = (int64_t)R * NL * factor;
+  const int64_t ncols = (int64_t)NL * factor;
+  const int64_t work = n > ncols ? n : ncols;
+  if (work <= 0) return hipSuccess;
+  int64_t blocks = (work + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(expand_kv_blocks_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     block_mask, block_valid, R, NL, factor, child, full, part, kv_valid);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

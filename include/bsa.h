@@ -1,0 +1,198 @@
+/*
+ * bsa.h - block-sparse attention forward for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libbsa.so.  Plain device/host pointers and sizes only.  Every
+ * device buffer is allocated, owned and freed by the caller; the library
+ * keeps no state, allocates no device memory and enqueues all device work on
+ * the caller's stream.  Without BSA_FLAG_VALIDATE no call synchronises.
+ * Errors are returned as bsa_status codes; nothing is thrown across the ABI.
+ *
+ * The problem statement follows these pages:
+ *  - flash-attention PR #2224 "[CuTe,Flex] varlen blocksparsity" (PR
+ *    description and review thread): batched metadata *_block_cnt
+ *    [B,H,num_m_blocks] / *_block_idx [B,H,num_m_blocks,num_n_blocks], the
+ *    packed varlen layout [H,total_m_blocks] / [H,total_n_blocks], the
+ *    cumulative arrays cu_total_m_blocks and block_idx_offsets, the ordered
+ *    (mask_block_cnt, mask_block_idx, full_block_cnt, full_block_idx) tuple
+ *    with the full list optional, and no device->host syncs at launch;
+ *  - FastVideo PR #1354 "VSA-256 fastpath" (review thread): the per-KV-block
+ *    valid-token-count mask_mod, LSE laid out [B,H,S], BSHD/BHSD inputs,
+ *    256-token logical KV blocks run as 128-token tiles;
+ *  - "Dense FlashAttention vs Block-Sparse Attention" (yiliu30.github.io),
+ *    section 2: the boolean block mask becomes a reversed, -1 padded list of
+ *    selected KV-block ids per Q-block row;
+ *  - runguoli.com "FlashAttention - CuTe Kernels & Block Sparsity": forward
+ *    tiles are fitted to the sparse block sizes instead of rejecting them.
+ *
+ * Semantics of one forward call (batch b, head h, row r of Q block
+ * i = r / block_q; KV head = h / (H / H_kv)):
+ *   visible columns C_r = { c < Sk : c / block_kv listed in full[b,h,i] }
+ *                       U { c < Sk : c / block_kv listed in mask[b,h,i] and mask_mod(r,c) }
+ *   O_r = sum_{c in C_r} softmax_c(scale * q_r.k_c) v_c,   LSE_r = ln sum_{c in C_r} exp(scale * q_r.k_c)
+ *   An empty C_r gives O_r = 0 and LSE_r = -inf.
+ * mask_mod applies to mask-list blocks only; columns >= Sk are never
+ * visible; listed ids outside [0, num_n_blocks) are skipped.  A KV block
+ * must not be listed twice for one row (within or across the two lists);
+ * with BSA_FLAG_VALIDATE such metadata is rejected, without it the result
+ * is undefined (memory stays safe).
+ *
+ * Arithmetic: Q/K/V are rounded to bf16 (round-to-nearest-even) if given as
+ * fp32; QK^T and PV run on bf16 MFMA with fp32 accumulation; softmax is
+ * fp32.  O has the input dtype; LSE is fp32 natural log.
+ */
+#ifndef BSA_H_
+#define BSA_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSA_OK = 0,
+  BSA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size or shape */
+  BSA_ERR_UNSUPPORTED = 2,      /* head_dim, block size or dtype without a kernel */
+  BSA_ERR_MISALIGNED = 3,       /* base pointer or stride not 16-byte aligned */
+  BSA_ERR_METADATA = 4,         /* BSA_FLAG_VALIDATE found bad block lists */
+  BSA_ERR_HIP = 5               /* a HIP runtime call or launch failed */
+} bsa_status;
+
+typedef enum {
+  BSA_BF16 = 0, /* Q,K,V,O bfloat16 */
+  BSA_F32 = 1   /* Q,K,V,O float32; inputs rounded to bf16 at load, O written fp32 */
+} bsa_dtype;
+
+typedef enum {
+  BSA_MASK_NONE = 0,           /* mask-list blocks behave like full blocks */
+  BSA_MASK_CAUSAL = 1,         /* keep kv_idx <= q_idx (sequence-local ids in varlen) */
+  BSA_MASK_KV_VALID_COUNT = 2  /* keep (kv_idx % block_kv) < kv_valid[kv_idx / block_kv] */
+} bsa_mask_mod;
+
+/* Copy the block lists to the host, check them (ids in range, no repeats
+ * within or across the two lists of a row, 0 <= cnt <= num_n_blocks),
+ * synchronising the stream.  Debug path. */
+#define BSA_FLAG_VALIDATE 1u
+
+/* One block list (the mask list or the full list).  int32 device arrays.
+ * cnt == NULL means the list is absent (no blocks).
+ * Batched:  cnt[b,h,m]      at cnt + b*cnt_stride[0] + h*cnt_stride[1] + m*cnt_stride[2]
+ *           idx[b,h,m,s]    at idx + b*idx_stride[0] + h*idx_stride[1] + m*idx_stride[2] + s*idx_stride[3]
+ *           (stride 0 broadcasts the metadata over B or H).
+ * Varlen:   cnt[h,mg]       at cnt + h*cnt_stride[1] + mg*cnt_stride[2]      (mg < total_m_blocks)
+ *           idx[h,p]        at idx + h*idx_stride[1] + p*idx_stride[3]       (p < total_n_blocks)
+ *           where row (b, m) of head h starts at p = block_idx_offsets[b] + m*num_n(b);
+ *           cnt_stride[0], idx_stride[0], idx_stride[2] are ignored.
+ * Only the first cnt entries of a row are read; their order is free. */
+typedef struct {
+  const int32_t* cnt;
+  const int32_t* idx;
+  int64_t cnt_stride[3];
+  int64_t idx_stride[4];
+} bsa_block_list;
+
+/* The (mask, full) pair and the sparse block sizes (in tokens).
+ * block_q must be a multiple of 32; block_kv may be any positive size. */
+typedef struct {
+  bsa_block_list mask;
+  bsa_block_list full;
+  int32_t block_q;
+  int32_t block_kv;
+} bsa_block_sparse;
+
+/* Batched forward.
+ *  q [B,Sq,H,D], k/v [B,Sk,H_kv,D], o [B,Sq,H,D]: device, dtype dt; element
+ *    strides x_str = {batch, seq, head}; head_dim stride is 1.  BSHD and
+ *    BHSD tensors are both expressed through these strides.
+ *  lse: device fp32 [B,H,Sq], contiguous.
+ *  D in {64, 96, 128, 192, 256}; H % H_kv == 0; Sq, Sk >= 0.
+ *  bs: block lists, cnt [B,H,ceil(Sq/block_q)], idx [B,H,ceil(Sq/block_q),ceil(Sk/block_kv)].
+ *  kv_valid: device int32 [ceil(Sk/block_kv)] for BSA_MASK_KV_VALID_COUNT, else ignored.
+ *  softmax_scale: applied to q.k before the softmax (and inside LSE).
+ * Requirements: 16-byte aligned base pointers; every stride times the
+ * element size a multiple of 16 bytes.  O and LSE are overwritten for every
+ * row < Sq. */
+bsa_status bsa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   bsa_dtype dt, int32_t B, int32_t H, int32_t H_kv,
+                   int32_t Sq, int32_t Sk, int32_t D,
+                   const int64_t q_str[3], const int64_t k_str[3],
+                   const int64_t v_str[3], const int64_t o_str[3],
+                   const bsa_block_sparse* bs, bsa_mask_mod mask_mod,
+                   const int32_t* kv_valid, float softmax_scale,
+                   uint32_t flags, hipStream_t stream);
+
+/* Packed variable-length forward (flash-attention PR #2224).
+ *  q [Tq,H,D], k/v [Tk,H_kv,D], o [Tq,H,D]: device, strides {token, head}.
+ *  lse: device fp32 [H,Tq] contiguous (Tq = cu_seqlens_q[B]).
+ *  cu_seqlens_q/k: device int32 [B+1], exclusive prefix sums of lengths.
+ *  cu_total_m_blocks, block_idx_offsets: device int32 [B+1], as produced by
+ *    bsa_varlen_offsets (Q-block and packed-slot prefix sums).
+ *  total_m_blocks, total_n_blocks: their last entries, and total_q =
+ *    cu_seqlens_q[B] (the LSE row length), passed from the host so the
+ *    launch needs no device->host copy.
+ *  Block ids in the lists are sequence-local; mask_mod uses sequence-local
+ *  (q_idx, kv_idx).  BSA_MASK_KV_VALID_COUNT is not supported here.
+ * Alignment rules as bsa_fwd. */
+bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                          bsa_dtype dt, int32_t B, int32_t H, int32_t H_kv, int32_t D,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          const int32_t* cu_total_m_blocks, const int32_t* block_idx_offsets,
+                          int32_t total_m_blocks, int32_t total_n_blocks, int32_t total_q,
+                          const int64_t q_str[2], const int64_t k_str[2],
+                          const int64_t v_str[2], const int64_t o_str[2],
+                          const bsa_block_sparse* bs, bsa_mask_mod mask_mod,
+                          float softmax_scale, uint32_t flags, hipStream_t stream);
+
+/* Dense block mask -> block lists ("Dense FlashAttention vs Block-Sparse
+ * Attention", section 2).  mask: device uint8 [B,H,M,N] contiguous (nonzero
+ * = selected).  Writes cnt: device int32 [B,H,M] (number selected) and idx:
+ * device int32 [B,H,M,N] (selected column ids in descending order, then -1).
+ * Bit-exact; deterministic. */
+bsa_status bsa_mask_to_index(const uint8_t* mask, int32_t B, int32_t H, int32_t M, int32_t N,
+                             int32_t* cnt, int32_t* idx, hipStream_t stream);
+
+/* The same conversion for the packed varlen layout.  mask: device uint8
+ * [H,total_n_blocks] laid out like idx (row (b,m) of head h at
+ * block_idx_offsets[b] + m*num_n(b), width num_n(b)).  Writes cnt [H,total_m_blocks]
+ * and idx [H,total_n_blocks] (device int32, contiguous).  num_n(b) is
+ * recovered as (block_idx_offsets[b+1]-block_idx_offsets[b]) /
+ * (cu_total_m_blocks[b+1]-cu_total_m_blocks[b]). */
+bsa_status bsa_varlen_mask_to_index(const uint8_t* mask, int32_t H, int32_t B,
+                                    const int32_t* cu_total_m_blocks,
+                                    const int32_t* block_idx_offsets,
+                                    int32_t total_m_blocks, int32_t total_n_blocks,
+                                    int32_t* cnt, int32_t* idx, hipStream_t stream);
+
+/* Host-only integer bookkeeping of the packed varlen layout (PR #2224):
+ *   num_m(b) = ceil(seqlens_q[b]/block_q), num_n(b) = ceil(seqlens_k[b]/block_kv),
+ *   cu_total_m_blocks = [0, cumsum num_m], block_idx_offsets = [0, cumsum num_m*num_n].
+ * All pointers are host memory; the two outputs have B+1 entries.  Returns
+ * BSA_ERR_INVALID_ARGUMENT on negative lengths, non-positive block sizes or
+ * int32 overflow.  Touches no device. */
+bsa_status bsa_varlen_offsets(const int32_t* seqlens_q, const int32_t* seqlens_k, int32_t B,
+                              int32_t block_q, int32_t block_kv,
+                              int32_t* cu_total_m_blocks, int32_t* block_idx_offsets,
+                              int32_t* total_m_blocks, int32_t* total_n_blocks);
+
+/* Split logical KV blocks into `factor` child tiles of `child` tokens
+ * (FastVideo PR #1354: 256-token blocks run as 128-token tiles).
+ * block_mask: device uint8 [R,NL] (R rows, e.g. B*H*M); block_valid: device
+ * int32 [NL] valid-token counts in [0, factor*child].  Child s of block j
+ * holds clamp(block_valid[j] - s*child, 0, child) tokens.  Writes device
+ * uint8 full [R,NL*factor] (selected and child full), part [R,NL*factor]
+ * (selected and 0 < size < child) and int32 kv_valid [NL*factor].
+ * Counts outside the range are clamped the same way. */
+bsa_status bsa_expand_kv_blocks(const uint8_t* block_mask, const int32_t* block_valid,
+                                int32_t R, int32_t NL, int32_t factor, int32_t child,
+                                uint8_t* full, uint8_t* part, int32_t* kv_valid,
+                                hipStream_t stream);
+
+/* Static string for a status code. */
+const char* bsa_status_str(bsa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H_ */

@@ -1,0 +1,76 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports
+every function include/bsa.h declares, and its pure-host bookkeeping matches
+the oracle bit-exactly."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_bsa_amd as bsa
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "bsa.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:bsa_status|const char\*)\s+(bsa_\w+)\s*\(", src, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert names == sorted(["bsa_fwd", "bsa_varlen_fwd", "bsa_mask_to_index",
+                            "bsa_varlen_mask_to_index", "bsa_varlen_offsets",
+                            "bsa_expand_kv_blocks", "bsa_status_str"])
+    lib = bsa.load_library()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", bsa.library_path()], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\sT\s+(bsa_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_status_strings():
+    assert bsa.bsa_status_str(0) == "ok"
+    assert "misaligned" in bsa.bsa_status_str(3)
+    assert bsa.bsa_status_str(99) == "unknown status"
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_varlen_offsets_match_oracle(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(0, 12))
+    sq = [int(x) for x in rng.integers(0, 20000, B)]
+    sk = [int(x) for x in rng.integers(0, 20000, B)]
+    bq, bk = int(rng.choice([32, 64, 128, 256])), int(rng.choice([16, 48, 64, 112, 128]))
+    assert bsa.bsa_varlen_offsets(sq, sk, bq, bk) == tuple(oracle.varlen_offsets(sq, sk, bq, bk))
+
+
+def test_varlen_offsets_errors():
+    with pytest.raises(ValueError):
+        bsa.bsa_varlen_offsets([5, -1], [5, 5], 64, 64)
+    with pytest.raises(ValueError):
+        bsa.bsa_varlen_offsets([5], [5], 0, 64)
+    with pytest.raises(ValueError):  # int32 overflow of the packed slot count
+        bsa.bsa_varlen_offsets([2 ** 30], [2 ** 30], 32, 32)
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(bsa, "_lib", None)
+    monkeypatch.setattr(bsa, "_LIB_PATH", "/nonexistent/libbsa.so")
+    with pytest.raises(RuntimeError):
+        bsa.load_library()
+
+
+def test_product_never_imports_the_oracle():
+    pkg = os.path.join(ROOT, "block_sparse_attention_bsa_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", text, re.M), f
+                assert "oracle/" not in text, f

@@ -1,0 +1,353 @@
+"""GPU forward vs the fp64 oracle on seeded inputs (parity tests proper).
+
+Small cases are compared element by element over every row; full-size
+workloads are compared on sampled Q blocks that the oracle computes one by
+one.  Tolerances and the bf16 output-rounding allowance: tests/bsa_testlib.py.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_bsa_amd as bsa
+import oracle
+import workloads
+from bsa_testlib import (as_oracle, check_o_lse, lists_on_device, rows_of, run_batched,
+                         sample_q_blocks, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+NONE, CAUSAL, KVV = bsa.MASK_NONE, bsa.MASK_CAUSAL, bsa.MASK_KV_VALID_COUNT
+
+
+def _oracle_batched(w, qkv, q_blocks=None):
+    q, k, v = (as_oracle(t) for t in qkv)
+    return oracle.blocksparse_attention(q, k, v, w.full, w.part, w.block_q, w.block_kv,
+                                        w.mask_mod, w.scale, w.kv_valid, q_blocks=q_blocks)
+
+
+def test_tiny_fp32_input():
+    w = workloads.tiny()
+    o, lse, qkv = run_batched(w, dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert o.dtype == torch.float32
+    # the oracle reads the bf16-rounded inputs the kernel computes on
+    qkv_r = tuple(t.to(torch.bfloat16) for t in qkv)
+    O, L = _oracle_batched(w, qkv_r)
+    check_o_lse(o, lse, O, L, "tiny")
+
+
+def test_causal_blocks_bf16():
+    w = workloads.causal_blocks()
+    o, lse, qkv = run_batched(w)
+    torch.cuda.synchronize()
+    O, L = _oracle_batched(w, qkv)
+    err, lerr = check_o_lse(o, lse, O, L, "causal_blocks")
+    print(f"causal_blocks raw max|dO|={err:.3e} max|dLSE|={lerr:.3e}")
+
+
+@pytest.mark.parametrize("D", workloads.SWEEP_HEAD_DIMS)
+@pytest.mark.parametrize("bq,bk", workloads.SWEEP_BLOCKS)
+def test_sweep_reduced(D, bq, bk):
+    # every head_dim x block-size pair at a reduced, ragged size (S not a
+    # multiple of either block) that still spans several tiles
+    w = workloads.sparse_sweep(D, bq, bk, B=2, H=2, S=700, density=0.4,
+                               seed=[7, D, bq, bk])
+    o, lse, qkv = run_batched(w)
+    torch.cuda.synchronize()
+    O, L = _oracle_batched(w, qkv)
+    check_o_lse(o, lse, O, L, f"sweep D={D} ({bq},{bk})")
+
+
+@pytest.mark.parametrize("D,bq,bk", [(64, 128, 128), (96, 64, 128), (128, 128, 128),
+                                     (192, 64, 64), (256, 128, 112), (128, 128, 64)])
+def test_sweep_full_size_sampled(D, bq, bk):
+    w = workloads.sparse_sweep(D, bq, bk)
+    o, lse, qkv = run_batched(w)
+    torch.cuda.synchronize()
+    B, S, H, _ = w.q.shape
+    picks = sample_q_blocks(B, H, -(-S // bq), 12, seed=D + bq + bk)
+    O, L = _oracle_batched(w, qkv, q_blocks=picks)
+    check_o_lse(o, lse, O, L, f"full sweep D={D} ({bq},{bk})", sel=rows_of(picks, bq, S))
+
+
+def test_varlen_packed_full_size_sampled():
+    w = workloads.varlen_packed()
+    H, bq, bk = w.q.shape[1], w.block_q, w.block_kv
+    cu, off, tm, tn = bsa.bsa_varlen_offsets(w.seqlens_q, w.seqlens_k, bq, bk)
+    assert (cu, off, tm, tn) == tuple(oracle.varlen_offsets(w.seqlens_q, w.seqlens_k, bq, bk))
+    dev = lambda a: torch.tensor(a, dtype=torch.int32, device="cuda")
+    cu_q = dev([0] + list(np.cumsum(w.seqlens_q)))
+    cu_k = dev([0] + list(np.cumsum(w.seqlens_k)))
+    cu_m, offs = dev(cu), dev(off)
+
+    def packed(masks):
+        out = np.zeros((H, tn), np.uint8)
+        for b, m in enumerate(masks):
+            nm, nn = m.shape[1:]
+            for i in range(nm):
+                out[:, off[b] + i * nn: off[b] + (i + 1) * nn] = m[:, i]
+        return torch.from_numpy(out).cuda()
+
+    mlist = bsa.bsa_varlen_mask_to_index(packed(w.part), cu_m, offs, tm, tn)
+    flist = bsa.bsa_varlen_mask_to_index(packed(w.full), cu_m, offs, tm, tn)
+    c_ref, i_ref = oracle.pack_varlen_lists(w.full, w.seqlens_q, w.seqlens_k, bq, bk)
+    np.testing.assert_array_equal(flist[0].cpu().numpy(), c_ref)
+    np.testing.assert_array_equal(flist[1].cpu().numpy(), i_ref)
+    q, k, v = (to_dev(x) for x in (w.q, w.k, w.v))
+    o, lse = bsa.bsa_varlen_fwd(q, k, v, cu_q, cu_k, cu_m, offs, tm, tn, mlist, flist, bq, bk,
+                                w.mask_mod, w.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    picks = []
+    for b, s in enumerate(w.seqlens_q):
+        nm = -(-s // bq)
+        for i in {0, nm - 1, int(rng.integers(nm))}:
+            picks.append((b, int(rng.integers(H)), i))
+    O, L = oracle.varlen_blocksparse_attention(as_oracle(q), as_oracle(k), as_oracle(v),
+                                               w.seqlens_q, w.seqlens_k, w.full, w.part, bq, bk,
+                                               w.mask_mod, w.scale, q_blocks=picks)
+    starts = np.concatenate([[0], np.cumsum(w.seqlens_q)])
+    tok, hh = [], []
+    for (b, h, i) in picks:
+        r = np.arange(starts[b] + i * bq, min(starts[b] + (i + 1) * bq, starts[b + 1]))
+        tok.append(r)
+        hh.append(np.full(r.size, h))
+    tok, hh = np.concatenate(tok), np.concatenate(hh)
+    check_o_lse(o, lse, O, L, "varlen", sel=((tok, hh), (hh, tok)))
+
+
+def test_varlen_small_all_rows_ragged():
+    # several short sequences incl. lengths below one block and an empty one
+    w = workloads.varlen_packed(H=3, D=64, bs=64, seed=21, seqlens=[1, 63, 0, 200, 130, 64])
+    H, bq, bk = 3, 64, 64
+    cu, off, tm, tn = bsa.bsa_varlen_offsets(w.seqlens_q, w.seqlens_k, bq, bk)
+    dev = lambda a: torch.tensor(a, dtype=torch.int32, device="cuda")
+    cu_q = dev([0] + list(np.cumsum(w.seqlens_q)))
+    # lists from the oracle packing here (the GPU packing is checked elsewhere)
+    mlist = tuple(torch.from_numpy(a).cuda() for a in
+                  oracle.pack_varlen_lists(w.part, w.seqlens_q, w.seqlens_k, bq, bk))
+    flist = tuple(torch.from_numpy(a).cuda() for a in
+                  oracle.pack_varlen_lists(w.full, w.seqlens_q, w.seqlens_k, bq, bk))
+    qd, kd, vd = (to_dev(x) for x in (w.q, w.k, w.v))
+    o, lse = bsa.bsa_varlen_fwd(qd, kd, vd, cu_q, cu_q, dev(cu), dev(off), tm, tn, mlist, flist,
+                                bq, bk, CAUSAL, w.scale, validate=True)
+    torch.cuda.synchronize()
+    O, L = oracle.varlen_blocksparse_attention(as_oracle(qd), as_oracle(kd), as_oracle(vd),
+                                               w.seqlens_q, w.seqlens_k, w.full, w.part, bq, bk,
+                                               CAUSAL, w.scale)
+    check_o_lse(o, lse, O, L, "varlen small")
+
+
+def _video_lists(w):
+    """Cube-level map -> 128-token tile lists + per-tile valid counts, on the GPU."""
+    nc = len(w.cube_valid)
+    bm = torch.from_numpy(w.cube_mask.astype(np.uint8)).cuda()
+    f = w.cube_elems // w.kv_tile
+    full, part, kvv = bsa.bsa_expand_kv_blocks(bm, torch.from_numpy(w.cube_valid).cuda(), f,
+                                               w.kv_tile)
+    return bsa.bsa_mask_to_index(part), bsa.bsa_mask_to_index(full), kvv
+
+
+def test_video_reduced_all_rows():
+    w = workloads.video(grid=(6, 10, 12), cube=(2, 8, 8), H=2, D=128, kv_tile=64,
+                        topk_frac=0.3, seed=31)
+    mlist, flist, kvv = _video_lists(w)
+    q, k, v = (to_dev(x) for x in (w.q, w.k, w.v))
+    o, lse = bsa.bsa_fwd(q, k, v, mlist, flist, w.cube_elems, w.kv_tile, KVV, kvv, w.scale,
+                         validate=True)
+    torch.cuda.synchronize()
+    f, p, kv_ref = oracle.expand_kv_blocks(w.cube_mask, w.cube_valid, w.cube_elems // w.kv_tile,
+                                           w.kv_tile)
+    np.testing.assert_array_equal(kvv.cpu().numpy(), kv_ref)
+    O, L = oracle.blocksparse_attention(as_oracle(q), as_oracle(k), as_oracle(v), f, p,
+                                        w.cube_elems, w.kv_tile, KVV, w.scale, kv_valid=kv_ref)
+    check_o_lse(o, lse, O, L, "video reduced")
+
+
+def test_video_full_size_sampled():
+    w = workloads.video()
+    mlist, flist, kvv = _video_lists(w)
+    q, k, v = (to_dev(x) for x in (w.q, w.k, w.v))
+    o, lse = bsa.bsa_fwd(q, k, v, mlist, flist, w.cube_elems, w.kv_tile, KVV, kvv, w.scale)
+    torch.cuda.synchronize()
+    f, p, kv_ref = oracle.expand_kv_blocks(w.cube_mask, w.cube_valid, 2, w.kv_tile)
+    np.testing.assert_array_equal(kvv.cpu().numpy(), kv_ref)
+    S, H = w.q.shape[1], w.q.shape[2]
+    picks = sample_q_blocks(1, H, S // w.cube_elems, 10, seed=5)
+    O, L = oracle.blocksparse_attention(as_oracle(q), as_oracle(k), as_oracle(v), f, p,
+                                        w.cube_elems, w.kv_tile, KVV, w.scale, kv_valid=kv_ref,
+                                        q_blocks=picks)
+    check_o_lse(o, lse, O, L, "video full", sel=rows_of(picks, w.cube_elems, S))
+
+
+# ---------------------------------------------------------------- edge cases
+
+def _small(seed, B=2, S=300, H=4, Hkv=4, D=64, bq=64, bk=64, p_full=0.3, p_part=0.3,
+           mask_mod=CAUSAL, Sk=None):
+    rng = np.random.default_rng(seed)
+    Sk = S if Sk is None else Sk
+    q = rng.standard_normal((B, S, H, D), dtype=np.float32)
+    k = rng.standard_normal((B, Sk, Hkv, D), dtype=np.float32)
+    v = rng.standard_normal((B, Sk, Hkv, D), dtype=np.float32)
+    M, N = -(-S // bq), -(-Sk // bk)
+    u = rng.random((B, H, M, N))
+    full, part = u < p_full, (u >= p_full) & (u < p_full + p_part)
+    kv_valid = rng.integers(0, bk + 1, N).astype(np.int32) if mask_mod == KVV else None
+    return workloads.BatchedWorkload("edge", q, k, v, full, part, bq, bk, mask_mod,
+                                     1 / math.sqrt(D), kv_valid)
+
+
+@pytest.mark.parametrize("case", [
+    dict(bq=32, bk=64), dict(bq=192, bk=80), dict(bq=64, bk=48), dict(bq=128, bk=200),
+    dict(bq=64, bk=16), dict(bq=256, bk=128, S=600), dict(Hkv=2), dict(Hkv=1, D=128),
+    dict(mask_mod=NONE), dict(mask_mod=KVV, bk=128), dict(mask_mod=KVV, bk=112),
+    dict(S=31, bq=32, bk=32), dict(S=1, bq=64, bk=64), dict(Sk=1, bq=64, bk=64),
+    dict(Sk=700, S=100), dict(D=96, bq=64, bk=112, S=333),
+])
+def test_edge_shapes(case):
+    w = _small(seed=hash(tuple(sorted(case.items()))) % 2 ** 32, **case)
+    o, lse, qkv = run_batched(w, validate=True)
+    torch.cuda.synchronize()
+    O, L = _oracle_batched(w, qkv)
+    check_o_lse(o, lse, O, L, f"edge {case}")
+
+
+def test_empty_lists_give_zero_and_neg_inf():
+    w = _small(1, p_full=0.0, p_part=0.0)
+    q, k, v = (to_dev(x) for x in (w.q, w.k, w.v))
+    M, N = w.full.shape[2:]
+    z = torch.zeros((2, 4, M), dtype=torch.int32, device="cuda")
+    idx = torch.full((2, 4, M, N), -1, dtype=torch.int32, device="cuda")
+    o, lse = bsa.bsa_fwd(q, k, v, (z, idx), None, 64, 64, CAUSAL, None, w.scale)
+    o2, lse2 = bsa.bsa_fwd(q, k, v, None, None, 64, 64, CAUSAL, None, w.scale)
+    torch.cuda.synchronize()
+    for a, l in ((o, lse), (o2, lse2)):
+        assert (a == 0).all() and torch.isneginf(l).all()
+
+
+def test_rows_fully_masked_inside_a_tile_stay_finite():
+    # Q block 1 lists only KV block 3 as a causal mask block: every one of its
+    # rows sees nothing (-> 0, -inf) and must not poison anything else
+    w = _small(2, S=256, bq=64, bk=64, p_full=0.0, p_part=0.0)
+    w.part[:, :, 1, 3] = True
+    w.part[:, :, 2, 0] = True
+    w.full[:, :, 2, 2] = True
+    o, lse, qkv = run_batched(w)
+    torch.cuda.synchronize()
+    O, L = _oracle_batched(w, qkv)
+    check_o_lse(o, lse, O, L, "fully masked rows")
+
+
+def test_bhsd_strides_and_broadcast_metadata():
+    w = _small(3, B=2, S=320, H=4, D=128, bq=64, bk=64)
+    # BHSD storage viewed as [B,S,H,D]
+    qb, kb, vb = (to_dev(np.ascontiguousarray(x.transpose(0, 2, 1, 3))) for x in (w.q, w.k, w.v))
+    q, k, v = (t.permute(0, 2, 1, 3) for t in (qb, kb, vb))
+    # one metadata row shared by every (batch, head): broadcast through stride 0
+    full1 = np.broadcast_to(w.full[:1, :1], w.full.shape).copy()
+    part1 = np.broadcast_to(w.part[:1, :1], w.part.shape).copy()
+    fl = lists_on_device(w.full[:1, :1])
+    pl = lists_on_device(w.part[:1, :1])
+    o, lse = bsa.bsa_fwd(q, k, v, pl, fl, 64, 64, CAUSAL, None, w.scale)
+    torch.cuda.synchronize()
+    O, L = oracle.blocksparse_attention(as_oracle(q), as_oracle(k), as_oracle(v), full1, part1,
+                                        64, 64, CAUSAL, w.scale)
+    check_o_lse(o, lse, O, L, "bhsd+broadcast")
+
+
+def test_list_order_and_full_mask_swap():
+    w = _small(4, mask_mod=NONE, D=128, bq=128, bk=64)
+    o1, l1, qkv = run_batched(w)
+    # reversed (ascending) order inside each list
+    mc, mi = lists_on_device(w.part)
+    fc, fi = lists_on_device(w.full)
+
+    def ascend(c, i):
+        i2 = i.clone()
+        N = i.shape[-1]
+        for idx in np.ndindex(*c.shape):
+            n = int(c[idx])
+            i2[idx][:n] = torch.flip(i[idx][:n], [0])
+        return c, i2
+    o2, l2 = bsa.bsa_fwd(*qkv, ascend(mc, mi), ascend(fc, fi), 128, 64, NONE, None, w.scale)
+    # lists swapped: under mask_mod NONE the mask list is a plain list
+    o3, l3 = bsa.bsa_fwd(*qkv, (fc, fi), (mc, mi), 128, 64, NONE, None, w.scale)
+    torch.cuda.synchronize()
+    O, L = _oracle_batched(w, qkv)
+    for o, l, tag in ((o1, l1, "stored"), (o2, l2, "ascending"), (o3, l3, "swapped")):
+        check_o_lse(o, l, O, L, tag)
+
+
+def test_deterministic_bitwise():
+    w = workloads.sparse_sweep(128, 128, 128, B=1, H=4, S=2048, seed=3)
+    o1, l1, qkv = run_batched(w)
+    o2, l2, _ = run_batched(w)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_out_of_range_ids_are_skipped():
+    w = _small(5, mask_mod=NONE)
+    q, k, v = (to_dev(x) for x in (w.q, w.k, w.v))
+    fc, fi = lists_on_device(w.full)
+    N = fi.shape[-1]
+    # append an out-of-range id after the valid ones; cnt+1 stays <= N where possible
+    fi2 = fi.clone()
+    room = fc < N
+    pos = fc.clamp(max=N - 1).long().unsqueeze(-1)
+    keep = fi.gather(3, pos)
+    fi2.scatter_(3, pos, torch.where(room.unsqueeze(-1), torch.full_like(keep, N + 5), keep))
+    fc2 = torch.where(room, fc + 1, fc)
+    o, lse = bsa.bsa_fwd(q, k, v, None, (fc2, fi2), 64, 64, NONE, None, w.scale)
+    torch.cuda.synchronize()
+    w.part[:] = False
+    O, L = _oracle_batched(w, (q, k, v))
+    check_o_lse(o, lse, O, L, "out-of-range skipped")
+    with pytest.raises(ValueError):
+        bsa.bsa_fwd(q, k, v, None, (fc2, fi2), 64, 64, NONE, None, w.scale, validate=True)
+
+
+def test_validate_rejects_repeats_and_overlap():
+    w = _small(6, mask_mod=NONE)
+    q, k, v = (to_dev(x) for x in (w.q, w.k, w.v))
+    fc, fi = lists_on_device(w.full)
+    M, N = fi.shape[2:]
+    dup = fi.clone()
+    dup[0, 0, 0, :2] = 0
+    cnt2 = fc.clone()
+    cnt2[0, 0, 0] = 2
+    with pytest.raises(ValueError):
+        bsa.bsa_fwd(q, k, v, None, (cnt2, dup), 64, 64, NONE, None, w.scale, validate=True)
+    with pytest.raises(ValueError):
+        bsa.bsa_fwd(q, k, v, (fc, fi), (fc, fi), 64, 64, NONE, None, w.scale, validate=True)
+    bad = fc.clone()
+    bad[1, 1, 1] = N + 1
+    with pytest.raises(ValueError):
+        bsa.bsa_fwd(q, k, v, None, (bad, fi), 64, 64, NONE, None, w.scale, validate=True)
+
+
+def test_argument_errors():
+    w = _small(7)
+    q, k, v = (to_dev(x) for x in (w.q, w.k, w.v))
+    fl = lists_on_device(w.full)
+    pad = lambda t: torch.nn.functional.pad(t, (0, 16)).contiguous()
+    with pytest.raises(ValueError) as e:
+        bsa.bsa_fwd(pad(q), pad(k), pad(v), None, fl, 64, 64)
+    assert e.value.status == 2  # head_dim 80: no kernel
+    with pytest.raises(ValueError) as e:
+        bsa.bsa_fwd(q, k, v, None, fl, 48, 64)
+    assert e.value.status == 2  # block_q not a multiple of 32
+    raw = torch.empty(q.numel() + 8, dtype=torch.bfloat16, device="cuda")
+    qm = raw[1:1 + q.numel()].view(q.shape)
+    qm.copy_(q)
+    with pytest.raises(ValueError) as e:
+        bsa.bsa_fwd(qm, k, v, None, fl, 64, 64)
+    assert e.value.status == 3  # misaligned base pointer
+    with pytest.raises(ValueError) as e:
+        bsa.bsa_fwd(q, k, v, None, fl, 64, 64, softmax_scale=-1.0)
+    assert e.value.status == 1
+    with pytest.raises(ValueError) as e:
+        bsa.bsa_fwd(q, k, v, fl, None, 64, 64, mask_mod=KVV, kv_valid=None)
+    assert e.value.status == 1

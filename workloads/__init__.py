@@ -180,12 +180,15 @@ def sparse_sweep(D: int, bq: int, bk: int, B=2, H=16, S=4096,
 
 
 def varlen_packed(n_seq=8, H=16, D=128, bs=128, lo=128, hi=8192, p_below=0.3,
-                  seed: int = 1004) -> VarlenWorkload:
-    """Packed batch of n_seq sequences (seqlen_q = seqlen_k ~ U{lo..hi}).
-    Per sequence and head: diagonal blocks are causal mask blocks, each block
-    strictly below the diagonal is a full block with probability p_below."""
+                  seed: int = 1004, seqlens: Optional[List[int]] = None) -> VarlenWorkload:
+    """Packed batch of n_seq sequences (seqlen_q = seqlen_k ~ U{lo..hi}, or the
+    given lengths).  Per sequence and head: diagonal blocks are causal mask
+    blocks, each block strictly below the diagonal is a full block with
+    probability p_below."""
     rng = np.random.default_rng(seed)
-    seqlens = [int(x) for x in rng.integers(lo, hi + 1, size=n_seq)]
+    if seqlens is None:
+        seqlens = [int(x) for x in rng.integers(lo, hi + 1, size=n_seq)]
+    seqlens = [int(x) for x in seqlens]
     total = sum(seqlens)
     q, k, v = _qkv(rng, (total, H, D), (total, H, D))
     full, part = [], []
