@@ -1,0 +1,240 @@
+"""Benchmark: effective TFLOP/s of the block-sparse attention forward on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload video|sweep128]
+
+One step is the whole hot path over one synthetic batch already resident in
+HBM: split the cube-level KV selection into 128-token tiles
+(bsa_expand_kv_blocks), build the mask and full block lists
+(bsa_mask_to_index, twice) and run the forward (bsa_fwd).
+
+Default workload: video sparse attention, B=1, H=24, 30x48x52 latent grid in
+4x8x8 = 256-token cubes (74880 tokens, 86016 padded rows), head_dim 128,
+bf16, each Q cube attending to its top 40 of 336 KV cubes (11.9% density),
+KV cubes run as 128-token tiles with per-tile valid-token counts.
+
+FLOPs per step count only computed work: 4 * head_dim * sum over listed
+(Q block, KV tile) pairs of (Q rows) x (KV keys the tile holds: its
+valid-token count), i.e. padding keys the kernel skips are not counted.
+
+Prints one JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective TFLOP/s (computed blocks) bf16 block-sparse attn fwd; % MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
+FWD_KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_bsa_amd", "csrc", "bsa_fwd.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "bsa_fwd_video_hbm_traffic.md")
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=["video", "sweep128"], default="video")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="wall-time budget of the oracle sample on the host (0 = skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def _kernel_hash() -> str:
+    with open(FWD_KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic_from_profile():
+    """Per-launch HBM bytes from the committed counter summary, or None if it
+    is missing or was taken on another revision of the forward kernel."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", text)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not h or not b or h.group(1) != _kernel_hash():
+        return None
+    return float(b.group(1))
+
+
+def _video_inputs(torch, np, workloads):
+    w = workloads.video()
+    dev = torch.device("cuda")
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (w.q, w.k, w.v))
+    cube_mask = torch.from_numpy(w.cube_mask.astype(np.uint8)).to(dev)
+    cube_valid = torch.from_numpy(w.cube_valid).to(dev)
+    # computed work: listed (cube, tile) pairs x 256 Q rows x valid keys of the tile
+    f = w.cube_elems // w.kv_tile
+    tile_valid = np.clip(w.cube_valid[:, None] - np.arange(f)[None, :] * w.kv_tile, 0,
+                         w.kv_tile)  # [cubes, f]
+    keys_per_row = (w.cube_mask[0].astype(np.float64) @ tile_valid.sum(1).astype(np.float64))
+    flops = 4.0 * q.shape[-1] * w.cube_elems * float(keys_per_row.sum())
+    density = float(w.cube_mask.mean())
+    cfg = {"workload": "video_sparse_attention", "B": 1, "H": q.shape[2], "tokens": int(
+        w.cube_valid.sum()), "padded_seq": q.shape[1], "head_dim": q.shape[3], "cube": list(w.cube),
+        "grid": list(w.grid), "block_q": w.cube_elems, "kv_tile": w.kv_tile,
+        "kv_cubes_per_q_cube": int(w.cube_mask[0, 0, 0].sum()), "block_density": round(density, 4),
+        "mask_mod": "kv_valid_count", "layout": "BSHD"}
+    state = dict(q=q, k=k, v=v, cube_mask=cube_mask, cube_valid=cube_valid, f=f, w=w)
+    return state, flops, cfg
+
+
+def _video_step(bsa, st, events=None):
+    full, part, kvv = bsa.bsa_expand_kv_blocks(st["cube_mask"], st["cube_valid"], st["f"],
+                                               st["w"].kv_tile)
+    ml = bsa.bsa_mask_to_index(part)
+    fl = bsa.bsa_mask_to_index(full)
+    if events is not None:
+        events[0].record()
+    o, lse = bsa.bsa_fwd(st["q"], st["k"], st["v"], ml, fl, st["w"].cube_elems, st["w"].kv_tile,
+                         bsa.MASK_KV_VALID_COUNT, kvv, st["w"].scale, out=st.get("o"),
+                         lse=st.get("lse"))
+    if events is not None:
+        events[1].record()
+    st["o"], st["lse"] = o, lse
+
+
+def _sweep_inputs(torch, np, workloads):
+    w = workloads.sparse_sweep(128, 128, 128)
+    dev = torch.device("cuda")
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (w.q, w.k, w.v))
+    sel = (w.full | w.part).astype(np.float64)
+    flops = 4.0 * 128 * 128 * 128 * float(sel.sum())
+    cfg = {"workload": "blocksparse_sweep_d128", "B": 2, "H": 16, "seq": 4096, "head_dim": 128,
+           "block_q": 128, "block_kv": 128, "block_density": round(float(sel.mean()), 4),
+           "mask_mod": "causal_diagonal", "layout": "BSHD"}
+    st = dict(q=q, k=k, v=v, w=w, part=torch.from_numpy(w.part.astype(np.uint8)).to(dev),
+              full=torch.from_numpy(w.full.astype(np.uint8)).to(dev))
+    return st, flops, cfg
+
+
+def _sweep_step(bsa, st, events=None):
+    ml = bsa.bsa_mask_to_index(st["part"])
+    fl = bsa.bsa_mask_to_index(st["full"])
+    if events is not None:
+        events[0].record()
+    o, lse = bsa.bsa_fwd(st["q"], st["k"], st["v"], ml, fl, 128, 128, bsa.MASK_CAUSAL, None,
+                         st["w"].scale, out=st.get("o"), lse=st.get("lse"))
+    if events is not None:
+        events[1].record()
+    st["o"], st["lse"] = o, lse
+
+
+def _cpu_baseline(np, st, workload, budget_s):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    w = st["w"]
+    f64 = lambda t: t.float().cpu().double().numpy()
+    q, k, v = f64(st["q"]), f64(st["k"]), f64(st["v"])
+    rng = np.random.default_rng(0)
+    if workload == "video":
+        full, part, kv = oracle.expand_kv_blocks(w.cube_mask, w.cube_valid, st["f"], w.kv_tile)
+        B, H, M = 1, q.shape[2], len(w.cube_valid)
+        bq, bk, mm, kvv = w.cube_elems, w.kv_tile, oracle.MASK_KV_VALID_COUNT, kv
+        row_keys = lambda b, h, i: float((full[b, h, i] * kv).sum() + (part[b, h, i] * kv).sum())
+    else:
+        full, part = w.full, w.part
+        B, H, M = full.shape[:3]
+        bq, bk, mm, kvv = w.block_q, w.block_kv, w.mask_mod, None
+        row_keys = lambda b, h, i: float((full[b, h, i] | part[b, h, i]).sum() * bk)
+    D = q.shape[-1]
+    flops, n, t0 = 0.0, 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        b, h, i = int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(M))
+        oracle.blocksparse_attention(q, k, v, full, part, bq, bk, mm, w.scale, kvv,
+                                     q_blocks=[(b, h, i)])
+        flops += 4.0 * D * bq * row_keys(b, h, i)
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} random Q blocks ({bq} rows each) of the same workload, fp64 numpy, "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: the block-sparse forward here is a "
+              "single-GPU build (see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_bsa_amd as bsa
+    import workloads
+
+    bsa.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.calibrate_copy:
+        n = 1 << 30
+        x = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
+                          "launches": 3}))
+        return
+    make, step = ((_video_inputs, _video_step) if args.workload == "video"
+                  else (_sweep_inputs, _sweep_step))
+    st, flops, cfg = make(torch, np, workloads)
+    for _ in range(args.warmup):
+        step(bsa, st)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(bsa, st, evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+    fwd_ms = [a.elapsed_time(b) for a, b in evs]
+    fwd_avg = sum(fwd_ms) / len(fwd_ms)
+    value = flops / (ms_step * 1e-3) / 1e12
+    achieved = flops / (fwd_avg * 1e-3) / 1e12
+    traffic = _traffic_from_profile() if args.workload == "video" else None
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q/K/V, seeded top-k block selection)",
+        "config": cfg,
+        "pct_of_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "bsa_fwd_kernel<128,4,bf16>",
+                     "kernel_ms": round(fwd_avg, 4), "flops_per_launch": flops},
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = _cpu_baseline(np, st, args.workload, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

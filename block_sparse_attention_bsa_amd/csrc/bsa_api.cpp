@@ -246,7 +246,6 @@ bsa_status bsa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   p.block_q = bs->block_q;
   p.block_kv = bs->block_kv;
   p.qsub = bs->block_q / tile_m;
-  p.kvsub = (int32_t)cdiv64(bs->block_kv, bsa::kKvTile);
   p.mask_mod = mask_mod;
   p.varlen = 0;
   p.tiles_per_head = (int32_t)tiles_per_head;
@@ -320,7 +319,6 @@ bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, 
   p.block_q = bs->block_q;
   p.block_kv = bs->block_kv;
   p.qsub = qsub;
-  p.kvsub = (int32_t)cdiv64(bs->block_kv, bsa::kKvTile);
   p.mask_mod = mask_mod;
   p.varlen = 1;
   p.tiles_per_head = (int32_t)tiles_per_head;

@@ -129,23 +129,27 @@ struct ListWalk {
 };
 
 // One unit of work: sub-tile st of the KV block listed at position g.
+// blen is the number of leading keys of block j that can be visible: the
+// block size, or for a mask-list block under the valid-count mask_mod its
+// valid-token count (sub-tiles past it are never loaded).
 struct Item {
-  int g, st, j, key0, nk, is_mask;
+  int g, st, j, blen, key0, nk, is_mask;
 };
 
 // Step to the next sub-tile that holds at least one key below Sk; entries
 // with ids outside [0, num_n) are skipped.  Returns false at the end.
-__device__ __forceinline__ bool advance(Item& it, ListWalk& L, int lane, int bk, int kvsub,
-                                        int num_n, int Sk) {
-  int g = it.g, st = it.st + 1, j = it.j;
+__device__ __forceinline__ bool advance(Item& it, ListWalk& L, int lane, int bk, int num_n,
+                                        int Sk, int mask_mod, const int32_t* kv_valid) {
+  int g = it.g, st = it.st + 1, j = it.j, blen = it.blen;
   while (true) {
-    if (g >= 0 && st < kvsub) {
+    if (g >= 0 && st * kKvTile < blen) {
       const int key0 = j * bk + st * kKvTile;
-      const int nk = min(min(kKvTile, bk - st * kKvTile), Sk - key0);
+      const int nk = min(min(kKvTile, blen - st * kKvTile), Sk - key0);
       if (nk > 0) {
         it.g = g;
         it.st = st;
         it.j = j;
+        it.blen = blen;
         it.key0 = key0;
         it.nk = nk;
         it.is_mask = g < L.mcnt;
@@ -156,7 +160,11 @@ __device__ __forceinline__ bool advance(Item& it, ListWalk& L, int lane, int bk,
     st = 0;
     if (g >= L.total) return false;
     j = L.entry(g, lane);
-    if (j < 0 || j >= num_n) st = kvsub;
+    blen = bk;
+    if (j < 0 || j >= num_n)
+      blen = 0;
+    else if (mask_mod == 2 && g < L.mcnt)
+      blen = min(bk, kv_valid[j]);
   }
 }
 
@@ -365,10 +373,10 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(const FwdParams p) {
       s1 = mfma32(a1, qf[ks], s1);
     }
     // element mask: accumulator r of lane half h32 holds key
-    // 16*(r/8) + 8*h32 + r%8 (+32 for s1) of the sub-tile
-    if (it.is_mask || it.nk < KT) {
-      const int mm = it.is_mask ? p.mask_mod : 0;
-      const int kvv = (mm == 2) ? p.kv_valid[it.j] - it.st * KT : KT;
+    // 16*(r/8) + 8*h32 + r%8 (+32 for s1) of the sub-tile.  Keys at or past
+    // nk (block end, sequence end, or the valid-token count) are hidden.
+    const bool causal = it.is_mask && p.mask_mod == 1;
+    if (causal || it.nk < KT) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 16 * (r >> 3) + 8 * h32 + (r & 7);
@@ -376,8 +384,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(const FwdParams p) {
         for (int half = 0; half < 2; ++half) {
           const int kk = key + 32 * half;
           bool keep = kk < it.nk;
-          if (mm == 1) keep = keep && (it.key0 + kk <= qrow);
-          if (mm == 2) keep = keep && (kk < kvv);
+          if (causal) keep = keep && (it.key0 + kk <= qrow);
           if (!keep) {
             if (half == 0)
               s0[r] = neg_inf();
@@ -434,15 +441,15 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(const FwdParams p) {
   ListWalk L{mrow, p.mi_s[3], mcnt, frow, p.fi_s[3], mcnt + fcnt, -1000000, -1};
   unsigned char* buf0 = smem;
   unsigned char* buf1 = smem + STAGE;
-  Item cur{-1, 0, 0, 0, 0, 0};
-  bool have = advance(cur, L, lane, p.block_kv, p.kvsub, num_n, Sk_b);
+  Item cur{-1, 0, 0, 0, 0, 0, 0};
+  bool have = advance(cur, L, lane, p.block_kv, num_n, Sk_b, p.mask_mod, p.kv_valid);
   if (have) {
     issue(cur);
     store(buf0, buf0 + KBYTES);
   }
   __syncthreads();
   Item nxt = cur;
-  bool have_nxt = have && advance(nxt, L, lane, p.block_kv, p.kvsub, num_n, Sk_b);
+  bool have_nxt = have && advance(nxt, L, lane, p.block_kv, num_n, Sk_b, p.mask_mod, p.kv_valid);
   int sb = 0;
   while (have) {
     if (have_nxt) issue(nxt);
@@ -453,7 +460,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_kernel(const FwdParams p) {
     __syncthreads();
     cur = nxt;
     have = have_nxt;
-    if (have) have_nxt = advance(nxt, L, lane, p.block_kv, p.kvsub, num_n, Sk_b);
+    if (have) have_nxt = advance(nxt, L, lane, p.block_kv, num_n, Sk_b, p.mask_mod, p.kv_valid);
     sb ^= 1;
   }
 

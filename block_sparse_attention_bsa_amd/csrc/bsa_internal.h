@@ -36,7 +36,7 @@ struct FwdParams {
   const int32_t* cu_m;
   const int32_t* blk_off;
   int32_t B, H, hrep, Sq, Sk;
-  int32_t block_q, block_kv, qsub, kvsub;
+  int32_t block_q, block_kv, qsub;
   int32_t mask_mod, varlen;
   int32_t tiles_per_head;  // batched: ceil(Sq/TM); varlen: total_m_blocks*qsub
   int32_t total_m, total_n;  // varlen only

@@ -336,8 +336,9 @@ def test_argument_errors():
     with pytest.raises(ValueError) as e:
         bsa.bsa_fwd(pad(q), pad(k), pad(v), None, fl, 64, 64)
     assert e.value.status == 2  # head_dim 80: no kernel
+    fl48 = lists_on_device(np.zeros((2, 4, 7, 5), bool))
     with pytest.raises(ValueError) as e:
-        bsa.bsa_fwd(q, k, v, None, fl, 48, 64)
+        bsa.bsa_fwd(q, k, v, None, fl48, 48, 64)
     assert e.value.status == 2  # block_q not a multiple of 32
     raw = torch.empty(q.numel() + 8, dtype=torch.bfloat16, device="cuda")
     qm = raw[1:1 + q.numel()].view(q.shape)
