@@ -40,6 +40,13 @@ bool strides_ok(const int64_t* s, int n, int esize) {
   return true;
 }
 
+// The bf16 kernel addresses one 64-key K/V sub-tile with 32-bit byte
+// offsets from its first row.
+bool subtile_offsets_fit(int64_t k_row_stride, int64_t v_row_stride, int esize) {
+  const int64_t lim = (int64_t)1 << 31;
+  return 64 * k_row_stride * esize < lim && 64 * v_row_stride * esize < lim;
+}
+
 bool list_ok(const bsa_block_list& L) {
   if (L.cnt == nullptr) return true;
   if (L.idx == nullptr) return false;
@@ -217,6 +224,7 @@ bsa_status bsa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   if (!strides_ok(q_str, 3, es) || !strides_ok(k_str, 3, es) || !strides_ok(v_str, 3, es) ||
       !strides_ok(o_str, 3, es))
     return BSA_ERR_MISALIGNED;
+  if (!subtile_offsets_fit(k_str[1], v_str[1], es)) return BSA_ERR_UNSUPPORTED;
   const int64_t M = cdiv64(Sq, bs->block_q), N = cdiv64(Sk, bs->block_kv);
   const int64_t tiles_per_head = cdiv64(Sq, tile_m);
   const int64_t tiles = (int64_t)B * H * tiles_per_head;
@@ -289,6 +297,7 @@ bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, 
   if (!strides_ok(q_str, 2, es) || !strides_ok(k_str, 2, es) || !strides_ok(v_str, 2, es) ||
       !strides_ok(o_str, 2, es))
     return BSA_ERR_MISALIGNED;
+  if (!subtile_offsets_fit(k_str[0], v_str[0], es)) return BSA_ERR_UNSUPPORTED;
   const int qsub = bs->block_q / tile_m;
   const int64_t tiles_per_head = (int64_t)total_m_blocks * qsub;
   const int64_t tiles = tiles_per_head * H;

@@ -1,0 +1,313 @@
+// Device-side pieces shared by the two forward kernels (gfx950, wave64):
+// work-tile decode, the block-list walk, the online-softmax step on the
+// transposed MFMA accumulators, and the epilogue.
+//
+// MFMA layout (v_mfma_f32_32x32x16_bf16).  Each wave owns 32 query rows and
+// computes everything transposed:
+//     S^T[key, q] = K[key, :] . Q[q, :]          (A = K from LDS, B = Q in registers)
+//     O^T[d, q]  += V^T[d, key] . P^T[key, q]    (A = V^T from LDS, B = P^T in registers)
+// so every accumulator register of a lane belongs to the same query
+// (q = lane % 32): the row max needs one exchange between lanes l and l^32
+// per sub-tile, the running sum none until the epilogue, and the O rescale
+// is a per-lane scalar.  Accumulator r of lane half h = lane / 32 holds row
+// 8*(r/4) + 4*h + r%4 of the 32-row block.  The A operand's row i is fetched
+// from key (or head-dim) swap_b23(i) (bits 2 and 3 of i exchanged), so the
+// 16 rows a lane receives are two runs of 8 consecutive keys (head dims):
+// 16*(r/8) + 8*h + r%8.  P^T then feeds the PV MFMA straight from registers
+// and O is written in 16-byte pieces.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bsa_internal.h"
+
+namespace bsa {
+namespace dev {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int kMaskNone = 0, kMaskCausal = 1, kMaskKvValid = 2;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};  // v_cvt_pk_bf16_f32, round to nearest even
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Row permutation of the MFMA A operand: exchange bits 2 and 3.
+__device__ __forceinline__ int swap_b23(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
+
+__device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Workgroups are dispatched round-robin over the 8 XCDs.  Renumber them so
+// that each XCD receives one contiguous range of logical tiles: the Q tiles
+// of one (batch, head) then share that XCD's L2 for their K/V blocks.
+__device__ __forceinline__ int xcd_remap(int bid, int G) {
+  constexpr int kXcd = 8;
+  const int xcd = bid % kXcd, local = bid / kXcd;
+  const int per = G / kXcd, rem = G % kXcd;
+  return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+// What one workgroup works on: rows [q0, q0 + TM) of one (sequence, head)
+// and the block-list row of their sparse Q block.
+struct TileInfo {
+  int h, q0, Sq, Sk, num_n;
+  int64_t qoff, koff, voff, ooff, lse_base;  // element offsets of row 0 / LSE row 0
+  const int32_t* mrow;
+  const int32_t* frow;
+  int mcnt, fcnt;
+};
+
+// Logical tile t -> TileInfo.  Batched: t = ((b*H + h) * tiles_per_head + qt).
+// Varlen (flash-attention PR #2224 layout): t = h * tiles_per_head + tm with
+// tm = Q block * qsub + sub; the sequence is the largest b with
+// cu_total_m_blocks[b] <= Q block (binary search), the list row starts at
+// block_idx_offsets[b] + m * num_n(b).  Returns false when the tile holds no
+// row of its sequence (the whole workgroup then exits).
+template <int TM>
+__device__ __forceinline__ bool decode_tile(const FwdParams& p, int t, TileInfo& ti) {
+  ti.mrow = nullptr;
+  ti.frow = nullptr;
+  ti.mcnt = ti.fcnt = 0;
+  if (!p.varlen) {
+    const int qt = t % p.tiles_per_head;
+    const int bh = t / p.tiles_per_head;
+    const int h = bh % p.H, b = bh / p.H, hk = h / p.hrep;
+    const int i = qt / p.qsub;
+    ti.h = h;
+    ti.q0 = qt * TM;
+    ti.Sq = p.Sq;
+    ti.Sk = p.Sk;
+    ti.num_n = cdiv(p.Sk, p.block_kv);
+    ti.qoff = b * p.q_sb + h * p.q_sh;
+    ti.koff = b * p.k_sb + hk * p.k_sh;
+    ti.voff = b * p.v_sb + hk * p.v_sh;
+    ti.ooff = b * p.o_sb + h * p.o_sh;
+    ti.lse_base = (int64_t)(b * p.H + h) * p.Sq;
+    if (p.mcnt) {
+      ti.mcnt = p.mcnt[b * p.mc_s[0] + h * p.mc_s[1] + i * p.mc_s[2]];
+      ti.mrow = p.midx + b * p.mi_s[0] + h * p.mi_s[1] + i * p.mi_s[2];
+    }
+    if (p.fcnt) {
+      ti.fcnt = p.fcnt[b * p.fc_s[0] + h * p.fc_s[1] + i * p.fc_s[2]];
+      ti.frow = p.fidx + b * p.fi_s[0] + h * p.fi_s[1] + i * p.fi_s[2];
+    }
+  } else {
+    const int tm = t % p.tiles_per_head;
+    const int h = t / p.tiles_per_head;
+    const int mg = tm / p.qsub, sub = tm % p.qsub;
+    int lo = 0, hi = p.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.cu_m[mid] <= mg)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const int b = lo, hk = h / p.hrep;
+    const int m = mg - p.cu_m[b];
+    const int sq0 = p.cu_q[b], sk0 = p.cu_k[b];
+    ti.h = h;
+    ti.Sq = p.cu_q[b + 1] - sq0;
+    ti.Sk = p.cu_k[b + 1] - sk0;
+    ti.num_n = cdiv(ti.Sk, p.block_kv);
+    ti.q0 = m * p.block_q + sub * TM;
+    if (m < 0 || m >= cdiv(ti.Sq, p.block_q) || ti.q0 >= ti.Sq) return false;
+    const int64_t row_p = (int64_t)p.blk_off[b] + (int64_t)m * ti.num_n;
+    if (row_p < 0 || row_p + ti.num_n > p.total_n) return false;  // inconsistent bookkeeping
+    ti.qoff = (int64_t)sq0 * p.q_ss + h * p.q_sh;
+    ti.koff = (int64_t)sk0 * p.k_ss + hk * p.k_sh;
+    ti.voff = (int64_t)sk0 * p.v_ss + hk * p.v_sh;
+    ti.ooff = (int64_t)sq0 * p.o_ss + h * p.o_sh;
+    ti.lse_base = (int64_t)h * p.lse_ld + sq0;
+    if (p.mcnt) {
+      ti.mcnt = p.mcnt[h * p.mc_s[1] + mg * p.mc_s[2]];
+      ti.mrow = p.midx + h * p.mi_s[1] + row_p * p.mi_s[3];
+    }
+    if (p.fcnt) {
+      ti.fcnt = p.fcnt[h * p.fc_s[1] + mg * p.fc_s[2]];
+      ti.frow = p.fidx + h * p.fi_s[1] + row_p * p.fi_s[3];
+    }
+  }
+  ti.mcnt = min(max(ti.mcnt, 0), ti.num_n);
+  ti.fcnt = min(max(ti.fcnt, 0), ti.num_n);
+  return true;
+}
+
+// Concatenated (mask ++ full) block list of one Q-block row.  Entries are
+// fetched 64 at a time, one per lane, together with the number of leading
+// keys of that block that can be visible (the block size; for a mask-list
+// block under the valid-count mask_mod its valid-token count; 0 for ids
+// outside [0, num_n)), and broadcast with readlane.
+struct ListWalk {
+  const int32_t* mrow;
+  int64_t ms;
+  int mcnt;
+  const int32_t* frow;
+  int64_t fs;
+  int total;
+  int bk, num_n, mask_mod;
+  const int32_t* kv_valid;
+  int base;
+  int chunk_j, chunk_len;
+
+  __device__ __forceinline__ void load(int g, int lane) {
+    base = g;
+    const int gg = g + lane;
+    int j = -1;
+    if (gg < mcnt)
+      j = mrow[gg * ms];
+    else if (gg < total)
+      j = frow[(gg - mcnt) * fs];
+    int len = 0;
+    if (gg < total && j >= 0 && j < num_n) {
+      len = bk;
+      if (mask_mod == kMaskKvValid && gg < mcnt) len = min(bk, kv_valid[j]);
+    }
+    chunk_j = j;
+    chunk_len = len;
+  }
+  __device__ __forceinline__ void entry(int g, int lane, int& j, int& len) {
+    if (g < base || g >= base + 64) load(g, lane);
+    j = __builtin_amdgcn_readlane(chunk_j, g - base);
+    len = __builtin_amdgcn_readlane(chunk_len, g - base);
+  }
+};
+
+// One unit of work: sub-tile st (kKvTile keys) of the KV block listed at
+// position g; its keys [key0, key0 + nk) are the ones that can be visible.
+struct Item {
+  int g, st, j, blen, key0, nk, is_mask;
+};
+
+__device__ __forceinline__ bool advance(Item& it, ListWalk& L, int lane, int Sk) {
+  int g = it.g, st = it.st + 1, j = it.j, blen = it.blen;
+  while (true) {
+    if (g >= 0 && st * kKvTile < blen) {
+      const int key0 = j * L.bk + st * kKvTile;
+      const int nk = min(min(kKvTile, blen - st * kKvTile), Sk - key0);
+      if (nk > 0) {
+        it.g = g;
+        it.st = st;
+        it.j = j;
+        it.blen = blen;
+        it.key0 = key0;
+        it.nk = nk;
+        it.is_mask = g < L.mcnt;
+        return true;
+      }
+    }
+    ++g;
+    st = 0;
+    if (g >= L.total) return false;
+    L.entry(g, lane, j, blen);
+  }
+}
+
+// Online-softmax step for one 64-key sub-tile.  s0/s1 hold S^T for keys
+// 0..31 / 32..63 of the sub-tile (raw dot products).  Applies the element
+// mask, updates the running max m (base-2 units of scale*s) and the running
+// sum l (fp32 P), rescales O only when some row's max grew, and returns P
+// rounded to bf16 in pk0/pk1 (pairs of consecutive accumulators).
+template <int DB>
+__device__ __forceinline__ void softmax_step(f32x16_t& s0, f32x16_t& s1, const Item& it,
+                                             bool causal, int qrow, int h32, float c, float& m_run,
+                                             float& l_run, f32x16_t (&oacc)[DB], uint32_t (&pk0)[8],
+                                             uint32_t (&pk1)[8]) {
+  if (causal || it.nk < kKvTile) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = 16 * (r >> 3) + 8 * h32 + (r & 7);
+      bool keep0 = key < it.nk, keep1 = key + 32 < it.nk;
+      if (causal) {
+        keep0 = keep0 && (it.key0 + key <= qrow);
+        keep1 = keep1 && (it.key0 + key + 32 <= qrow);
+      }
+      if (!keep0) s0[r] = neg_inf();
+      if (!keep1) s1[r] = neg_inf();
+    }
+  }
+  float mx = neg_inf();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m_run, mx * c);
+  if (__any(m_new > m_run)) {
+    const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    m_run = m_new;
+  }
+  const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
+  float ls = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float a0 = __builtin_amdgcn_exp2f(fmaf(s0[2 * i], c, -m_use));
+    const float a1 = __builtin_amdgcn_exp2f(fmaf(s0[2 * i + 1], c, -m_use));
+    const float b0 = __builtin_amdgcn_exp2f(fmaf(s1[2 * i], c, -m_use));
+    const float b1 = __builtin_amdgcn_exp2f(fmaf(s1[2 * i + 1], c, -m_use));
+    pk0[i] = pack_bf16x2(a0, a1);
+    pk1[i] = pack_bf16x2(b0, b1);
+    ls += (a0 + a1) + (b0 + b1);
+  }
+  l_run += ls;
+}
+
+// B operand of PV step ps (keys 16*ps .. 16*ps+15): lane half h32 supplies
+// keys 16*ps + 8*h32 .. +7, i.e. accumulators 8*(ps%2) .. +7 of s_{ps/2}.
+__device__ __forceinline__ uint4 p_operand(const uint32_t (&pk0)[8], const uint32_t (&pk1)[8],
+                                           int ps) {
+  const uint32_t* src = (ps < 2) ? pk0 : pk1;
+  const int o = 4 * (ps & 1);
+  return make_uint4(src[o], src[o + 1], src[o + 2], src[o + 3]);
+}
+
+// O = acc / l (0 when l == 0), LSE = ln2 * (m + log2 l) (-inf when l == 0).
+template <int DB, typename T>
+__device__ __forceinline__ void epilogue(const FwdParams& p, const TileInfo& ti, int qrow, int h32,
+                                         float m_run, float l_run, const f32x16_t (&oacc)[DB]) {
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (qrow >= ti.Sq) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  T* op = reinterpret_cast<T*>(p.o) + ti.ooff + (int64_t)qrow * p.o_ss;
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      T* dst = op + db * 32 + 16 * half + 8 * h32;
+      const int r0 = 8 * half;
+      if constexpr (sizeof(T) == 4) {
+        float4* d4 = reinterpret_cast<float4*>(dst);
+        d4[0] = make_float4(oacc[db][r0] * inv, oacc[db][r0 + 1] * inv, oacc[db][r0 + 2] * inv,
+                            oacc[db][r0 + 3] * inv);
+        d4[1] = make_float4(oacc[db][r0 + 4] * inv, oacc[db][r0 + 5] * inv,
+                            oacc[db][r0 + 6] * inv, oacc[db][r0 + 7] * inv);
+      } else {
+        *reinterpret_cast<uint4*>(dst) =
+            make_uint4(pack_bf16x2(oacc[db][r0] * inv, oacc[db][r0 + 1] * inv),
+                       pack_bf16x2(oacc[db][r0 + 2] * inv, oacc[db][r0 + 3] * inv),
+                       pack_bf16x2(oacc[db][r0 + 4] * inv, oacc[db][r0 + 5] * inv),
+                       pack_bf16x2(oacc[db][r0 + 6] * inv, oacc[db][r0 + 7] * inv));
+      }
+    }
+  }
+  if (h32 == 0) p.lse[ti.lse_base + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : neg_inf();
+}
+
+}  // namespace dev
+}  // namespace bsa

@@ -45,10 +45,13 @@ struct FwdParams {
   float c;                 // softmax_scale * log2(e)
 };
 
-// Launch the forward kernel instance for (D, rows per workgroup, dtype).
-// Returns hipSuccess or the launch error; unsupported combinations return
-// hipErrorInvalidValue (the caller checks support first).
+// Launch the forward kernel instance for (D, rows per workgroup, dtype):
+// bf16 inputs use the DMA-pipelined kernel, fp32 inputs the register-staged
+// one (which rounds to bf16 at load).  Returns hipSuccess or the launch
+// error; unsupported combinations return hipErrorInvalidValue (the caller
+// checks support first).
 hipError_t launch_fwd(const FwdParams& p, int D, int tile_m, bool f32_in, hipStream_t s);
+hipError_t launch_fwd_staged(const FwdParams& p, int D, int tile_m, bool f32_in, hipStream_t s);
 
 hipError_t launch_mask_to_index(const uint8_t* mask, int64_t rows, int32_t N,
                                 int32_t* cnt, int32_t* idx, hipStream_t s);
