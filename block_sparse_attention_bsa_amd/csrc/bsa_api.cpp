@@ -21,11 +21,13 @@ bool supported_head_dim(int D) { return D == 64 || D == 96 || D == 128 || D == 1
 
 // Tile fit (runguoli.com "FlashAttention - CuTe Kernels & Block Sparsity":
 // fit the forward tile to the sparse block instead of rejecting it): the
-// workgroup row count is the largest of 128/64/32 dividing the sparse Q
-// block, and a larger Q block is covered by block_q / tile_m workgroups that
-// share its block-list row.  KV blocks of any size are cut into 64-key
-// sub-tiles inside the kernel.
-int fit_tile_m(int block_q) {
+// workgroup row count is the largest of 256/128/64/32 dividing the sparse Q
+// block (256 only for head_dim <= 128 with bf16 inputs, where eight waves of
+// 32 rows fit two per SIMD), and a larger Q block is covered by
+// block_q / tile_m workgroups that share its block-list row.  KV blocks of
+// any size are cut into 64-key sub-tiles inside the kernel.
+int fit_tile_m(int block_q, int D, bool f32_in) {
+  if (block_q % 256 == 0 && D <= 128 && !f32_in) return 256;
   if (block_q % 128 == 0) return 128;
   if (block_q % 64 == 0) return 64;
   if (block_q % 32 == 0) return 32;
@@ -213,7 +215,7 @@ bsa_status bsa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   if (bs->block_q <= 0 || bs->block_kv <= 0) return BSA_ERR_INVALID_ARGUMENT;
   if (!list_ok(bs->mask) || !list_ok(bs->full)) return BSA_ERR_INVALID_ARGUMENT;
   if (!supported_head_dim(D)) return BSA_ERR_UNSUPPORTED;
-  const int tile_m = fit_tile_m(bs->block_q);
+  const int tile_m = fit_tile_m(bs->block_q, D, dt == BSA_F32);
   if (tile_m == 0) return BSA_ERR_UNSUPPORTED;
   if ((int64_t)B * H * Sq == 0) return BSA_OK;  // nothing to write
   if (!q || !k || !v || !o || !lse) return BSA_ERR_INVALID_ARGUMENT;
@@ -286,7 +288,7 @@ bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, 
   if (bs->block_q <= 0 || bs->block_kv <= 0) return BSA_ERR_INVALID_ARGUMENT;
   if (!list_ok(bs->mask) || !list_ok(bs->full)) return BSA_ERR_INVALID_ARGUMENT;
   if (!supported_head_dim(D)) return BSA_ERR_UNSUPPORTED;
-  const int tile_m = fit_tile_m(bs->block_q);
+  const int tile_m = fit_tile_m(bs->block_q, D, dt == BSA_F32);
   if (tile_m == 0) return BSA_ERR_UNSUPPORTED;
   if (B == 0 || total_m_blocks == 0) return BSA_OK;
   if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k || !cu_total_m_blocks ||

@@ -45,16 +45,24 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
 typedef __attribute__((address_space(3))) char lds_char;
 
-// One wave-wide 16-byte-per-lane DMA: lane l's 16 bytes at g land at LDS
-// byte address lds_addr + 16*l.  lds_addr must be wave-uniform (it goes
-// through M0; the s_nop covers the M0-write hazard).
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_addr)
+// One wave-wide 16-byte-per-lane DMA: lane l's 16 bytes at base + off land
+// at LDS byte address lds_addr + 16*l.  base (64-bit) and lds_addr must be
+// wave-uniform: base goes in SGPRs (global "saddr" form, so a precomputed
+// 32-bit lane offset is all the address arithmetic a lane needs), lds_addr
+// in M0 (the s_nop covers the M0-write hazard).
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_addr) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+               "{m0}"(lds_addr)
                : "memory");
 }
 
-// s_waitcnt vmcnt(0): every vector-memory op of this wave, DMA included, done.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N) (expcnt, lgkmcnt left alone): at most N of this wave's
+// vector-memory ops, DMA included, still in flight.  Ops complete in order.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 
 __device__ __forceinline__ uint2 read_tr(const uint4* lds, int byte_off) {
   lds_char* base = (lds_char*)(lds);  // generic -> LDS address space
@@ -73,8 +81,17 @@ struct FwdCfg {
   static constexpr int KSLOTS = kKvTile * RSK;  // = 64 * RSK: RSK DMA blocks of 64 slots
   static constexpr int VSLOTS = kKvTile * RSV;
   static constexpr int STAGE_SLOTS = KSLOTS + VSLOTS;  // K tile, then V tile
-  static constexpr int LDS_BYTES = 2 * STAGE_SLOTS * 16;
-  static constexpr int WAVES_PER_EU = LDS_BYTES <= 80 * 1024 ? 2 : 1;
+  static constexpr int STAGE_BYTES = STAGE_SLOTS * 16;
+  // Up to 4 waves: two stages, so two workgroups share a CU.  8 waves (one
+  // workgroup per CU, two waves per SIMD): three stages when they fit.
+  static constexpr int STAGES = (NW == 8 && 3 * STAGE_BYTES <= 160 * 1024) ? 3 : 2;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int WAVES_PER_EU =
+      NW == 8 ? 2 : (LDS_BYTES <= 80 * 1024 ? 2 : 1);
+  static constexpr int KIPW = (RSK + NW - 1) / NW;  // K DMA instructions per wave per sub-tile
+  static constexpr int VIPW = (RSV + NW - 1) / NW;
+  static constexpr int DMA_PER_ITEM = KIPW + VIPW;
+  static_assert(STAGES == 2 || DMA_PER_ITEM < 64, "vmcnt range");
   static_assert(DC % 2 == 0 && RSV % 16 != 0 && RSV % 4 == 0, "stride rules");
 };
 
@@ -84,7 +101,7 @@ __attribute__((amdgpu_waves_per_eu(FwdCfg<D, NW>::WAVES_PER_EU)))
 void bsa_fwd_kernel(const FwdParams p) {
   using C = FwdCfg<D, NW>;
   constexpr int DS = C::DS, DB = C::DB, DC = C::DC, RSK = C::RSK, RSV = C::RSV;
-  __shared__ uint4 smem[2 * C::STAGE_SLOTS];
+  __shared__ uint4 smem[C::STAGES * C::STAGE_SLOTS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, l32 = lane & 31, h32 = lane >> 5;
@@ -119,28 +136,48 @@ void bsa_fwd_kernel(const FwdParams p) {
   // copy of the row's last chunk, which is never read).  Keys past nk repeat
   // the last visible key (finite data, masked later).  Lane byte offsets
   // within the sub-tile fit in 32 bits (the host bounds the row stride).
-  constexpr int KIPW = (RSK + NW - 1) / NW, VIPW = (RSV + NW - 1) / NW;
+  constexpr int KIPW = C::KIPW, VIPW = C::VIPW, STAGES = C::STAGES;
   const int kss2 = p.k_ss * 2, vss2 = p.v_ss * 2;
+  // lane byte offsets within a full sub-tile, one per DMA instruction
+  uint32_t koff[KIPW], voff[VIPW];
+#pragma unroll
+  for (int ii = 0; ii < KIPW; ++ii) {
+    const int slot = min(ii * NW + w, RSK - 1) * 64 + lane;
+    koff[ii] = (slot / RSK) * kss2 + min(slot % RSK, DC - 1) * 16;
+  }
+#pragma unroll
+  for (int ii = 0; ii < VIPW; ++ii) {
+    const int slot = min(ii * NW + w, RSV - 1) * 64 + lane;
+    voff[ii] = (slot / RSV) * vss2 + min(slot % RSV, DC - 1) * 16;
+  }
   const uint32_t lds_base = (uint32_t)(size_t)((lds_char*)smem);
   auto issue = [&](const Item& it, int stage) {
     const char* kt = reinterpret_cast<const char*>(kp + it.key0 * p.k_ss);
     const char* vt = reinterpret_cast<const char*>(vp + it.key0 * p.v_ss);
     const uint32_t kl = lds_base + stage * C::STAGE_SLOTS * 16;
     const uint32_t vl = kl + C::KSLOTS * 16;
-    const int last = it.nk - 1;
+    if (it.nk == kKvTile) {
 #pragma unroll
-    for (int ii = 0; ii < KIPW; ++ii) {
-      const int blk = min(ii * NW + w, RSK - 1);
-      const int slot = blk * 64 + lane;
-      const int r = slot / RSK, c = min(slot % RSK, DC - 1);
-      dma16(kt + (min(r, last) * kss2 + c * 16), kl + blk * 1024);
-    }
+      for (int ii = 0; ii < KIPW; ++ii) dma16(kt, koff[ii], kl + min(ii * NW + w, RSK - 1) * 1024);
 #pragma unroll
-    for (int ii = 0; ii < VIPW; ++ii) {
-      const int blk = min(ii * NW + w, RSV - 1);
-      const int slot = blk * 64 + lane;
-      const int r = slot / RSV, c = min(slot % RSV, DC - 1);
-      dma16(vt + (min(r, last) * vss2 + c * 16), vl + blk * 1024);
+      for (int ii = 0; ii < VIPW; ++ii) dma16(vt, voff[ii], vl + min(ii * NW + w, RSV - 1) * 1024);
+    } else {
+      // partial sub-tile: keys past nk repeat the last visible key
+      const int last = it.nk - 1;
+#pragma unroll
+      for (int ii = 0; ii < KIPW; ++ii) {
+        const int blk = min(ii * NW + w, RSK - 1);
+        const int slot = blk * 64 + lane;
+        const int r = slot / RSK, c = min(slot % RSK, DC - 1);
+        dma16(kt, min(r, last) * kss2 + c * 16, kl + blk * 1024);
+      }
+#pragma unroll
+      for (int ii = 0; ii < VIPW; ++ii) {
+        const int blk = min(ii * NW + w, RSV - 1);
+        const int slot = blk * 64 + lane;
+        const int r = slot / RSV, c = min(slot % RSV, DC - 1);
+        dma16(vt, min(r, last) * vss2 + c * 16, vl + blk * 1024);
+      }
     }
   };
 
@@ -187,22 +224,56 @@ void bsa_fwd_kernel(const FwdParams p) {
 
   ListWalk L{ti.mrow, p.mi_s[3], ti.mcnt, ti.frow, p.fi_s[3], ti.mcnt + ti.fcnt,
              p.block_kv, ti.num_n, p.mask_mod, p.kv_valid, -1000000, -1, 0};
-  Item cur{-1, 0, 0, 0, 0, 0, 0};
-  if (advance(cur, L, lane, ti.Sk)) {
-    issue(cur, 0);
-    Item nxt = cur;
-    bool have_nxt = advance(nxt, L, lane, ti.Sk);
-    int stage = 0;
-    while (true) {
-      wait_vmem();
-      __syncthreads();  // this stage landed; everyone is done reading the other one
-      if (have_nxt) issue(nxt, stage ^ 1);
-      compute(stage, cur);
-      if (!have_nxt) break;
-      cur = nxt;
-      have_nxt = advance(nxt, L, lane, ti.Sk);
-      stage ^= 1;
+  // STAGES-deep pipeline: up to STAGES-1 sub-tiles in flight ahead of the
+  // one being computed.  The npend issued, not yet computed sub-tiles (p0
+  // oldest, then p1) occupy stages stage, stage+1 (mod STAGES).
+  Item walker{-1, 0, 0, 0, 0, 0, 0};
+  bool more = advance(walker, L, lane, ti.Sk);
+  Item p0 = walker, p1 = walker;
+  int npend = 0;
+  if (more) {
+    issue(walker, 0);
+    p0 = walker;
+    npend = 1;
+    more = advance(walker, L, lane, ti.Sk);
+  }
+  if constexpr (STAGES == 3) {
+    if (more) {
+      issue(walker, 1);
+      p1 = walker;
+      npend = 2;
+      more = advance(walker, L, lane, ti.Sk);
     }
+  }
+  int stage = 0;
+  while (npend > 0) {
+    // the oldest pending sub-tile landed (for this wave), then for all waves;
+    // every wave is also done computing the stage the next DMA overwrites
+    if constexpr (STAGES == 3) {
+      if (npend == 2)
+        wait_vmem<C::DMA_PER_ITEM>();
+      else
+        wait_vmem<0>();
+    } else {
+      wait_vmem<0>();
+    }
+    __syncthreads();
+    const Item cur = p0;
+    if constexpr (STAGES == 3) p0 = p1;
+    if (more) {
+      int ns = stage + npend;
+      if (ns >= STAGES) ns -= STAGES;
+      issue(walker, ns);
+      if (STAGES == 3 && npend == 2)
+        p1 = walker;
+      else
+        p0 = walker;
+      more = advance(walker, L, lane, ti.Sk);
+    } else {
+      --npend;
+    }
+    compute(stage, cur);
+    stage = stage + 1 == STAGES ? 0 : stage + 1;
   }
   epilogue<DB, __bf16>(p, ti, qrow, h32, m_run, l_run, oacc);
 }
@@ -218,6 +289,9 @@ hipError_t launch_one(const FwdParams& p, hipStream_t s) {
 template <int D>
 hipError_t launch_tm(const FwdParams& p, int tile_m, hipStream_t s) {
   switch (tile_m) {
+    case 256:
+      if constexpr (D <= 128) return launch_one<D, 8>(p, s);
+      return hipErrorInvalidValue;
     case 128: return launch_one<D, 4>(p, s);
     case 64: return launch_one<D, 2>(p, s);
     case 32: return launch_one<D, 1>(p, s);

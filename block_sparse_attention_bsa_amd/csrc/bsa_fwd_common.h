@@ -238,9 +238,15 @@ __device__ __forceinline__ void softmax_step(f32x16_t& s0, f32x16_t& s1, const I
       if (!keep1) s1[r] = neg_inf();
     }
   }
-  float mx = neg_inf();
+  // row max: 32 values, a tree of 3-input maxes (v_max3_f32)
+  float t[11];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+  for (int i = 0; i < 5; ++i) t[i] = fmaxf(fmaxf(s0[3 * i], s0[3 * i + 1]), s0[3 * i + 2]);
+#pragma unroll
+  for (int i = 0; i < 5; ++i) t[5 + i] = fmaxf(fmaxf(s1[3 * i], s1[3 * i + 1]), s1[3 * i + 2]);
+  t[10] = fmaxf(s0[15], s1[15]);
+  float mx = fmaxf(fmaxf(fmaxf(fmaxf(t[0], t[1]), t[2]), fmaxf(fmaxf(t[3], t[4]), t[5])),
+                   fmaxf(fmaxf(fmaxf(t[6], t[7]), t[8]), fmaxf(t[9], t[10])));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const float m_new = fmaxf(m_run, mx * c);
   if (__any(m_new > m_run)) {

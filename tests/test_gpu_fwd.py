@@ -205,6 +205,8 @@ def _small(seed, B=2, S=300, H=4, Hkv=4, D=64, bq=64, bk=64, p_full=0.3, p_part=
     dict(mask_mod=NONE), dict(mask_mod=KVV, bk=128), dict(mask_mod=KVV, bk=112),
     dict(S=31, bq=32, bk=32), dict(S=1, bq=64, bk=64), dict(Sk=1, bq=64, bk=64),
     dict(Sk=700, S=100), dict(D=96, bq=64, bk=112, S=333),
+    dict(bq=512, bk=128, S=1100, D=128), dict(bq=256, bk=80, S=700, D=96, mask_mod=NONE),
+    dict(bq=256, bk=64, S=513, D=128, Hkv=2, mask_mod=KVV),
 ])
 def test_edge_shapes(case):
     w = _small(seed=hash(tuple(sorted(case.items()))) % 2 ** 32, **case)
