@@ -219,6 +219,9 @@ def main():
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (fwd_avg * 1e-3) / 1e12
     traffic = _traffic_from_profile() if args.workload == "video" else None
+    # head_dim 128; 256-row workgroups for 256-token Q cubes, 128 rows otherwise
+    kernel_name = "bsa_fwd_kernel<128,8> (256-row workgroup)" if args.workload == "video" \
+        else "bsa_fwd_kernel<128,4> (128-row workgroup)"
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
@@ -228,7 +231,7 @@ def main():
         "pct_of_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": traffic, "kernel": "bsa_fwd_kernel<128,4,bf16>",
+                     "traffic": traffic, "kernel": kernel_name,
                      "kernel_ms": round(fwd_avg, 4), "flops_per_launch": flops},
     }
     if args.cpu_seconds > 0:
