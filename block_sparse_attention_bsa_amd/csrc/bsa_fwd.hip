@@ -303,6 +303,7 @@ hipError_t launch_tm(const FwdParams& p, int tile_m, hipStream_t s) {
 
 hipError_t launch_fwd(const FwdParams& p, int D, int tile_m, bool f32_in, hipStream_t s) {
   if (f32_in) return launch_fwd_staged(p, D, tile_m, true, s);
+  if (tile_m == 256) return launch_fwd_pp(p, D, s);
   switch (D) {
     case 64: return launch_tm<64>(p, tile_m, s);
     case 96: return launch_tm<96>(p, tile_m, s);

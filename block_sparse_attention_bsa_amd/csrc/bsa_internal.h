@@ -52,6 +52,8 @@ struct FwdParams {
 // checks support first).
 hipError_t launch_fwd(const FwdParams& p, int D, int tile_m, bool f32_in, hipStream_t s);
 hipError_t launch_fwd_staged(const FwdParams& p, int D, int tile_m, bool f32_in, hipStream_t s);
+// 256-row ping-pong kernel (bf16, D in {64, 96, 128}).
+hipError_t launch_fwd_pp(const FwdParams& p, int D, hipStream_t s);
 
 hipError_t launch_mask_to_index(const uint8_t* mask, int64_t rows, int32_t N,
                                 int32_t* cnt, int32_t* idx, hipStream_t s);

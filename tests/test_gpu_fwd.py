@@ -354,3 +354,73 @@ def test_argument_errors():
     with pytest.raises(ValueError) as e:
         bsa.bsa_fwd(q, k, v, fl, None, 64, 64, mask_mod=KVV, kv_valid=None)
     assert e.value.status == 1
+
+
+# ------------------------------------------- 256-row workgroups (eight waves)
+
+@pytest.mark.parametrize("D", [64, 96, 128])
+@pytest.mark.parametrize("mask_mod,bk,S,Sk", [
+    (CAUSAL, 64, 700, None), (CAUSAL, 128, 777, None), (CAUSAL, 96, 600, None),
+    (NONE, 200, 530, 900), (KVV, 128, 700, None), (KVV, 80, 513, 431),
+])
+def test_256_row_tiles(D, mask_mod, bk, S, Sk):
+    w = _small(seed=D * 1000 + bk + S, B=2, S=S, H=4, Hkv=2, D=D, bq=256, bk=bk,
+               mask_mod=mask_mod, Sk=Sk)
+    o, lse, qkv = run_batched(w, validate=True)
+    torch.cuda.synchronize()
+    O, L = _oracle_batched(w, qkv)
+    check_o_lse(o, lse, O, L, f"256 rows D={D} mm={mask_mod} bk={bk}")
+
+
+def test_256_row_tiles_long_lists_and_empty_rows():
+    # lists longer than 64 entries (the list is fetched 64 entries at a time),
+    # Q blocks with no entries, rows that see nothing under the causal mask
+    w = _small(seed=99, B=1, S=2300, H=2, Hkv=2, D=128, bq=256, bk=16, p_full=0.5,
+               p_part=0.2)
+    w.full[:, :, 3] = False
+    w.part[:, :, 3] = False
+    w.part[:, :, 5] = False
+    w.full[:, :, 5] = False
+    w.part[:, :, 5, 143] = True  # only a block above the diagonal: every row empty
+    o, lse, qkv = run_batched(w, validate=True)
+    torch.cuda.synchronize()
+    O, L = _oracle_batched(w, qkv)
+    check_o_lse(o, lse, O, L, "256 rows long lists")
+
+
+def test_256_row_varlen():
+    w = workloads.varlen_packed(H=2, D=128, bs=256, seed=41, seqlens=[1, 300, 0, 513, 256, 700])
+    bq = bk = 256
+    cu, off, tm, tn = bsa.bsa_varlen_offsets(w.seqlens_q, w.seqlens_k, bq, bk)
+    dev = lambda a: torch.tensor(a, dtype=torch.int32, device="cuda")
+    cu_q = dev([0] + list(np.cumsum(w.seqlens_q)))
+    mlist = tuple(torch.from_numpy(a).cuda() for a in
+                  oracle.pack_varlen_lists(w.part, w.seqlens_q, w.seqlens_k, bq, bk))
+    flist = tuple(torch.from_numpy(a).cuda() for a in
+                  oracle.pack_varlen_lists(w.full, w.seqlens_q, w.seqlens_k, bq, bk))
+    qd, kd, vd = (to_dev(x) for x in (w.q, w.k, w.v))
+    o, lse = bsa.bsa_varlen_fwd(qd, kd, vd, cu_q, cu_q, dev(cu), dev(off), tm, tn, mlist, flist,
+                                bq, bk, CAUSAL, w.scale, validate=True)
+    torch.cuda.synchronize()
+    O, L = oracle.varlen_blocksparse_attention(as_oracle(qd), as_oracle(kd), as_oracle(vd),
+                                               w.seqlens_q, w.seqlens_k, w.full, w.part, bq, bk,
+                                               CAUSAL, w.scale)
+    check_o_lse(o, lse, O, L, "varlen 256")
+
+
+def test_video_256_cubes_partial_tiles_all_rows():
+    # 4x8x8 cubes on a grid that leaves cubes of 16..256 valid tokens, so KV
+    # tiles end inside a 64-key sub-tile and take the element mask
+    w = workloads.video(grid=(6, 10, 12), cube=(4, 8, 8), H=2, D=128, kv_tile=128,
+                        topk_frac=0.5, seed=32)
+    mlist, flist, kvv = _video_lists(w)
+    q, k, v = (to_dev(x) for x in (w.q, w.k, w.v))
+    o, lse = bsa.bsa_fwd(q, k, v, mlist, flist, w.cube_elems, w.kv_tile, KVV, kvv, w.scale,
+                         validate=True)
+    torch.cuda.synchronize()
+    f, p, kv_ref = oracle.expand_kv_blocks(w.cube_mask, w.cube_valid, w.cube_elems // w.kv_tile,
+                                           w.kv_tile)
+    assert (kv_ref % 64 != 0).any()
+    O, L = oracle.blocksparse_attention(as_oracle(q), as_oracle(k), as_oracle(v), f, p,
+                                        w.cube_elems, w.kv_tile, KVV, w.scale, kv_valid=kv_ref)
+    check_o_lse(o, lse, O, L, "video 256 partial")
