@@ -11,10 +11,11 @@
 // Schedule.  Waves 0-3 (group 0) and 4-7 (group 1) share the four SIMDs,
 // one wave of each group per SIMD.  Per item a wave has an MFMA phase
 // (O += P_j V_j, then S_{j+1} = K_{j+1} Q^T: D/8 + D/8 MFMAs of 32 cycles)
-// and a VALU phase (element mask, row max, lazy rescale, exp, P_{j+1} in
-// bf16, row sum, and the scalar list walk).  Group 1 runs one phase behind
-// group 0 and workgroup barriers separate the phases, so on every SIMD one
-// wave keeps the matrix core busy while the other does its softmax.
+// and a VALU phase (element mask, row max, lazy rescale, exp, P in bf16,
+// row sum).  Between two workgroup barriers group 0 runs its MFMA phase
+// first and group 1 its VALU phase first, so on every SIMD one wave keeps
+// the matrix core busy while the other does its softmax; one barrier per
+// item keeps the K/V ring consistent.
 //
 // K/V staging.  A four-stage LDS ring holds one item per stage; item j+3 is
 // fetched while item j computes.  Each stage is K [64 keys][RSK slots] then
@@ -426,45 +427,47 @@ void bsa_fwd_pp_kernel(const FwdParams p) {
   for (int ks = 0; ks < DS; ++ks)
     asm volatile("" ::"v"(qf[ks].x), "v"(qf[ks].y), "v"(qf[ks].z), "v"(qf[ks].w));
   barrier();  // items 0..2 landed for every wave
+  // Both groups take the scores of item 0; group 0 also its softmax (group 1
+  // takes it at the start of its first interval).
   if (e0) {
     qk_only(0);
-    softmax(t0);
+    if (!g1) softmax(t0);
   }
-  // group 1 starts one phase behind group 0
-  if (g1) barrier();
-  // Items j and j+1 exist inside the loop; the last item's accumulate-only
-  // phase is peeled off below (one MFMA-phase body keeps O in one register
-  // set).  Every wave issues JMAX DMAs per item, items past the end
-  // included, so "all but the newest item landed" is always vmcnt(JMAX).
+  // Interval j: group 0 runs [MFMA phase j, softmax j+1], group 1 runs
+  // [softmax j, MFMA phase j], so on each SIMD one wave's MFMAs overlap the
+  // other's softmax.  One barrier per interval: every wave's part of item
+  // j+2 has landed, and no wave reads item j's stage any more (item j+4
+  // refills it).  Items j and j+1 exist inside the loop; the last item's
+  // accumulate-only phase is peeled off below (one MFMA-phase body keeps O
+  // in one register set).  Every wave issues JMAX DMAs per item, items past
+  // the end included, so "all but the newest item landed" is vmcnt(JMAX).
   int j = 0;
   while (e1) {
+    if (g1) softmax(t0);
     // MFMA phase of item j; item j+3 goes into the stage item j-1 used
     __builtin_amdgcn_s_setprio(1);
     mfma_phase(std::integral_constant<int, NPV + NQK>{}, j & 3, (j + 1) & 3, true, t3,
                (j + 3) & 3);
     __builtin_amdgcn_s_setprio(0);
-    if (g1) wait_vmem<JMAX>();  // item j+2 landed (this wave)
-    barrier();
-    // VALU phase of item j+1, and the walk to item j+4
-    softmax(t1);
+    if (!g1) softmax(t1);
+    // walk to item j+4
+    t0 = t1;
     t1 = t2;
     e1 = e2;
     t2 = t3;
     e2 = e3;
     e3 = e3 && L.next(lane, t3);
     if (!e3) t3.nm = 0;
-    if (!g1) wait_vmem<JMAX>();
+    wait_vmem<JMAX>();  // item j+2 landed (this wave)
     barrier();
     ++j;
   }
   if (e0) {  // item j is the last one: accumulate only
+    if (g1) softmax(t0);
     __builtin_amdgcn_s_setprio(1);
     mfma_phase(std::integral_constant<int, NPV>{}, j & 3, 0, false, t3, 0);
     __builtin_amdgcn_s_setprio(0);
-    barrier();
-    barrier();
   }
-  if (!g1) barrier();  // every wave passes the same number of barriers
   wait_vmem<0>();      // no DMA of this workgroup outlives it
   epilogue<DB, __bf16>(p, ti, qrow, h32, m_run, l_a + l_b, oacc);
 }
