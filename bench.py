@@ -34,8 +34,10 @@ if ROOT not in sys.path:
 
 METRIC = "effective TFLOP/s (computed blocks) bf16 block-sparse attn fwd; % MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
-FWD_KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_bsa_amd", "csrc", "bsa_fwd.hip")
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "bsa_fwd_video_hbm_traffic.md")
+# sources of the forward kernel the video workload launches (256-row workgroups)
+FWD_KERNEL_SRCS = [os.path.join(ROOT, "block_sparse_attention_bsa_amd", "csrc", f)
+                   for f in ("bsa_fwd_pp.hip", "bsa_fwd_common.h")]
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "bsa_fwd_pp_kernel_video_hbm_traffic.md")
 
 
 def _parse():
@@ -46,14 +48,19 @@ def _parse():
     ap.add_argument("--workload", choices=["video", "sweep128"], default="video")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-time budget of the oracle sample on the host (0 = skip)")
+    ap.add_argument("--print-kernel-hash", action="store_true",
+                    help="print the source hash the HBM-traffic summary is keyed on and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
 
 
 def _kernel_hash() -> str:
-    with open(FWD_KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in FWD_KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _traffic_from_profile():
@@ -173,6 +180,9 @@ def _cpu_baseline(np, st, workload, budget_s):
 
 def main():
     args = _parse()
+    if args.print_kernel_hash:
+        print(_kernel_hash())
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: the block-sparse forward here is a "
               "single-GPU build (see DESIGN.md for how it would shard).", file=sys.stderr)
@@ -220,8 +230,8 @@ def main():
     achieved = flops / (fwd_avg * 1e-3) / 1e12
     traffic = _traffic_from_profile() if args.workload == "video" else None
     # head_dim 128; 256-row workgroups for 256-token Q cubes, 128 rows otherwise
-    kernel_name = "bsa_fwd_kernel<128,8> (256-row workgroup)" if args.workload == "video" \
-        else "bsa_fwd_kernel<128,4> (128-row workgroup)"
+    kernel_name = "bsa_fwd_pp_kernel<128> (256-row workgroup, 8 waves)" \
+        if args.workload == "video" else "bsa_fwd_kernel<128,4> (128-row workgroup)"
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
