@@ -356,26 +356,28 @@ def test_argument_errors():
     assert e.value.status == 1
 
 
-# ------------------------------------------- 256-row workgroups (eight waves)
+# ------------------------------------------ 256- and 128-row Q blocks (d <= 128)
 
+@pytest.mark.parametrize("bq", [256, 128])
 @pytest.mark.parametrize("D", [64, 96, 128])
 @pytest.mark.parametrize("mask_mod,bk,S,Sk", [
     (CAUSAL, 64, 700, None), (CAUSAL, 128, 777, None), (CAUSAL, 96, 600, None),
-    (NONE, 200, 530, 900), (KVV, 128, 700, None), (KVV, 80, 513, 431),
+    (NONE, 200, 530, 900), (KVV, 128, 700, None), (KVV, 80, 513, 431), (KVV, 40, 300, None),
 ])
-def test_256_row_tiles(D, mask_mod, bk, S, Sk):
-    w = _small(seed=D * 1000 + bk + S, B=2, S=S, H=4, Hkv=2, D=D, bq=256, bk=bk,
+def test_q_block_256_128(bq, D, mask_mod, bk, S, Sk):
+    w = _small(seed=D * 1000 + bk + S + bq, B=2, S=S, H=4, Hkv=2, D=D, bq=bq, bk=bk,
                mask_mod=mask_mod, Sk=Sk)
     o, lse, qkv = run_batched(w, validate=True)
     torch.cuda.synchronize()
     O, L = _oracle_batched(w, qkv)
-    check_o_lse(o, lse, O, L, f"256 rows D={D} mm={mask_mod} bk={bk}")
+    check_o_lse(o, lse, O, L, f"bq={bq} D={D} mm={mask_mod} bk={bk}")
 
 
-def test_256_row_tiles_long_lists_and_empty_rows():
+@pytest.mark.parametrize("bq", [256, 128])
+def test_q_block_256_128_long_lists_and_empty_rows(bq):
     # lists longer than 64 entries (the list is fetched 64 entries at a time),
     # Q blocks with no entries, rows that see nothing under the causal mask
-    w = _small(seed=99, B=1, S=2300, H=2, Hkv=2, D=128, bq=256, bk=16, p_full=0.5,
+    w = _small(seed=99 + bq, B=1, S=2300, H=2, Hkv=2, D=128, bq=bq, bk=16, p_full=0.5,
                p_part=0.2)
     w.full[:, :, 3] = False
     w.part[:, :, 3] = False
@@ -385,7 +387,7 @@ def test_256_row_tiles_long_lists_and_empty_rows():
     o, lse, qkv = run_batched(w, validate=True)
     torch.cuda.synchronize()
     O, L = _oracle_batched(w, qkv)
-    check_o_lse(o, lse, O, L, "256 rows long lists")
+    check_o_lse(o, lse, O, L, f"bq={bq} long lists")
 
 
 def test_256_row_varlen():
