@@ -32,11 +32,15 @@
 // 12 mod 16 for ds_read_b64_tr_b16) is the same as in the other bf16
 // kernel: no LDS bank conflicts.
 //
-// Softmax.  The running max is only raised when some row's max grows by more
-// than 2^kTau (kTau = 8): below that P = 2^(s*c - m) stays <= 256, exact in
-// fp32 and in bf16's exponent range, and O, l and the LSE are all relative
-// to the same stale m.  The row sum is taken over the fp32 P (so the LSE
-// carries no bf16 rounding); P is rounded to bf16 only for the PV product.
+// Softmax.  The running max m is lazy.  Each item's P = 2^(s*c - m) is
+// taken against the current m first, with the lane's sum over its 32 keys;
+// only if that sum leaves [0, kSumCap] (m stale by more than 16 in log2
+// units, or still -inf before any key of the row was seen) does the wave
+// take the row max, rescale O and l, and redo the item.  So the common item
+// has no max reduction at all, P stays <= 2^16 (far inside fp32 and bf16
+// range), and O, l and the LSE are all relative to the same m.  The row
+// sum is taken over the fp32 P (so the LSE carries no bf16 rounding); P is
+// rounded to bf16 only for the PV product.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -54,7 +58,7 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
 typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr float kTau = 8.f;
+constexpr float kSumCap = 65536.f;
 // Word 3 of a raw (unstrided) buffer descriptor on the gfx9 family: 32-bit
 // data format, no swizzle; accesses at or past num_records return zero.
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
@@ -99,11 +103,17 @@ __device__ __forceinline__ uint2 read_tr(const char* lds, int byte_off) {
   return __builtin_bit_cast(uint2, v);
 }
 
-// max over the two lane halves (lanes l and l ^ 32)
+// max over the two lane halves (lanes l and l ^ 32).  v_permlane32_swap
+// trades the upper half of its first operand for the lower half of its
+// second, so with x in both, one result holds x of the lower half in every
+// lane and the other x of the upper half.  The two results are copied out
+// as scalars before the cast: a __builtin_bit_cast of a vector element
+// reads the vector's first element, whatever the index.
 __device__ __forceinline__ float half_swap_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
-                                                  __builtin_bit_cast(uint32_t, x), false, false);
-  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+  const uint32_t a = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+  const uint32_t lo = r[0], hi = r[1];
+  return fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
 }
 
 // What the pipeline keeps of an item: first key, and the visible-key count
@@ -357,17 +367,40 @@ void bsa_fwd_pp_kernel(const FwdParams p) {
         s1[r] = kr + 32 < t ? s1[r] : neg_inf();
       }
     }
-    float t3[11];
+    // P against the running max, and this lane's sum over its 32 keys.
+    float la = 0.f, lb = 0.f;
+    auto exps = [&](float mu) {
+      la = 0.f;
+      lb = 0.f;
 #pragma unroll
-    for (int i = 0; i < 5; ++i) t3[i] = fmaxf(fmaxf(s0[3 * i], s0[3 * i + 1]), s0[3 * i + 2]);
+      for (int i = 0; i < 8; ++i) {
+        const float a0 = __builtin_amdgcn_exp2f(fmaf(s0[2 * i], c, -mu));
+        const float a1 = __builtin_amdgcn_exp2f(fmaf(s0[2 * i + 1], c, -mu));
+        const float b0 = __builtin_amdgcn_exp2f(fmaf(s1[2 * i], c, -mu));
+        const float b1 = __builtin_amdgcn_exp2f(fmaf(s1[2 * i + 1], c, -mu));
+        pk0[i] = pack_bf16x2(a0, a1);
+        pk1[i] = pack_bf16x2(b0, b1);
+        la += a0 + a1;
+        lb += b0 + b1;
+      }
+    };
+    exps(m_run);
+    // Every P is at most the lane's sum, so a sum within kSumCap (it is
+    // never NaN or inf then) bounds the whole item.  A larger sum means the
+    // running max is stale by more than log2(kSumCap); inf or NaN means no
+    // key of the row has been seen yet (m_run = -inf).  Both are rare: take
+    // the row max, rescale, and redo the item.
+    if (__any(!(la + lb <= kSumCap))) {
+      float t3[11];
 #pragma unroll
-    for (int i = 0; i < 5; ++i) t3[5 + i] = fmaxf(fmaxf(s1[3 * i], s1[3 * i + 1]), s1[3 * i + 2]);
-    t3[10] = fmaxf(s0[15], s1[15]);
-    float mx = fmaxf(fmaxf(fmaxf(fmaxf(t3[0], t3[1]), t3[2]), fmaxf(fmaxf(t3[3], t3[4]), t3[5])),
-                     fmaxf(fmaxf(fmaxf(t3[6], t3[7]), t3[8]), fmaxf(t3[9], t3[10])));
-    mx = half_swap_max(mx);
-    const float m_new = fmaxf(m_run, mx * c);
-    if (__any(m_new > m_run + kTau)) {
+      for (int i = 0; i < 5; ++i) t3[i] = fmaxf(fmaxf(s0[3 * i], s0[3 * i + 1]), s0[3 * i + 2]);
+#pragma unroll
+      for (int i = 0; i < 5; ++i) t3[5 + i] = fmaxf(fmaxf(s1[3 * i], s1[3 * i + 1]), s1[3 * i + 2]);
+      t3[10] = fmaxf(s0[15], s1[15]);
+      float mx = fmaxf(fmaxf(fmaxf(fmaxf(t3[0], t3[1]), t3[2]), fmaxf(fmaxf(t3[3], t3[4]), t3[5])),
+                       fmaxf(fmaxf(fmaxf(t3[6], t3[7]), t3[8]), fmaxf(t3[9], t3[10])));
+      mx = half_swap_max(mx);
+      const float m_new = fmaxf(m_run, mx * c);
       // alpha = 2^(m_run - m_new); rows with nothing visible yet keep O = 0
       const float alpha = m_new == neg_inf() ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_a *= alpha;
@@ -377,19 +410,10 @@ void bsa_fwd_pp_kernel(const FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
       m_run = m_new;
+      exps(m_run == neg_inf() ? 0.f : m_run);
     }
-    const float mu = m_run == neg_inf() ? 0.f : m_run;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float a0 = __builtin_amdgcn_exp2f(fmaf(s0[2 * i], c, -mu));
-      const float a1 = __builtin_amdgcn_exp2f(fmaf(s0[2 * i + 1], c, -mu));
-      const float b0 = __builtin_amdgcn_exp2f(fmaf(s1[2 * i], c, -mu));
-      const float b1 = __builtin_amdgcn_exp2f(fmaf(s1[2 * i + 1], c, -mu));
-      pk0[i] = pack_bf16x2(a0, a1);
-      pk1[i] = pack_bf16x2(b0, b1);
-      l_a += a0 + a1;
-      l_b += b0 + b1;
-    }
+    l_a += la;
+    l_b += lb;
   };
 
   ItemStream L{ti.mrow, ti.frow, p.mi_s[3], p.fi_s[3], ti.mcnt, ti.mcnt + ti.fcnt,
