@@ -23,12 +23,14 @@
 // padding).  The stage is cut into 1 KiB blocks dealt round-robin to the
 // eight waves; each block is one buffer_load_dwordx4 ... lds (64 lanes x 16
 // bytes straight into LDS) from a per-lane offset computed once, issued
-// between two MFMAs of the MFMA phase.  Every wave issues the same number of
-// these per item (a wave with no block left loads nothing into a spare
-// block), so one vmcnt value tracks "all but the newest item landed".  The
-// buffer descriptor of an item spans only its visible keys, so rows past a
-// partial item's key count read as zero: no clamping and no reads past the
-// sequence end.  Read geometry (odd K stride for ds_read_b128, V stride 4 or
+// between two MFMAs of the MFMA phase.  Waves w < NFULLW own JMAX blocks of
+// a stage, the others JMAX - 1, and each ends the interval with a vmcnt
+// wait of its own count: "all but the newest item landed".  The buffer
+// descriptor of an item spans only its visible keys, so rows past a partial
+// item's key count read as zero: no clamping and no reads past the sequence
+// end.  DMAs whose lanes are all out of range cost several times as much as
+// in-range ones, so there are no padding DMAs, and an item past the end of
+// the list reloads the sequence's first keys into a stage nobody reads.  Read geometry (odd K stride for ds_read_b128, V stride 4 or
 // 12 mod 16 for ds_read_b64_tr_b16) is the same as in the other bf16
 // kernel: no LDS bank conflicts.
 //
@@ -193,9 +195,9 @@ struct PPCfg {
   static constexpr int STAGE_SLOTS = 64 * NBLK;
   static constexpr int STAGE_BYTES = STAGE_SLOTS * 16;
   static constexpr int STAGES = 4;
-  static constexpr int SPARE_SLOTS = 64;  // DMA target of waves with no block left
-  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES + SPARE_SLOTS * 16;
-  static constexpr int JMAX = (NBLK + NW - 1) / NW;  // DMA instructions per wave per item
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int JMAX = (NBLK + NW - 1) / NW;      // most DMA instructions of a wave per item
+  static constexpr int NFULLW = NBLK - NW * (JMAX - 1);  // waves w < NFULLW issue JMAX
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
   static_assert(DC % 2 == 0 && RSV % 16 != 0 && RSV % 4 == 0, "stride rules");
 };
@@ -231,8 +233,8 @@ void bsa_fwd_pp_kernel(const FwdParams p) {
 
   // DMA geometry: block b = w + 8*jj of a stage (K blocks first, then V);
   // lane l fills slot 64*b + l, i.e. key slot / RS, chunk slot % RS (a
-  // padding slot repeats the row's last chunk; it is never read).  A block
-  // index past the stage goes to the spare block with an empty descriptor.
+  // padding slot repeats the row's last chunk; it is never read).  Block
+  // w + 8*(JMAX-1) exists only for waves w < NFULLW.
   const uint32_t kss2 = (uint32_t)(p.k_ss * 2), vss2 = (uint32_t)(p.v_ss * 2);
   const uint32_t lds_base = (uint32_t)(size_t)((lds_char*)smem);
   uint32_t doff[JMAX];
@@ -244,23 +246,26 @@ void bsa_fwd_pp_kernel(const FwdParams p) {
     const int slot = (isk ? b : b - C::KBLK) * 64 + lane;
     doff[jj] = (uint32_t)(slot / rs) * (isk ? kss2 : vss2) + (uint32_t)min(slot % rs, DC - 1) * 16u;
   }
-  // descriptors of one item: K, V, and the empty one for the spare block
+  // descriptors of one item: K and V.  An item past the end (nm == 0)
+  // points at the sequence's first keys; its stage is never read.
   struct Rsrc {
-    u32x4_t k, v, z;
+    u32x4_t k, v;
   };
+  const int nk_none = min(kKvTile, ti.Sk);
   auto rsrc_of = [&](const Sub& it) {
+    const uint32_t k0 = it.nm != 0 ? (uint32_t)it.key0 : 0u;
+    const uint32_t nk = it.nm != 0 ? (uint32_t)it.nk() : (uint32_t)nk_none;
     Rsrc r;
-    r.k = make_rsrc(kaddr + (uint64_t)(uint32_t)it.key0 * kss2, (uint32_t)it.nk() * kss2);
-    r.v = make_rsrc(vaddr + (uint64_t)(uint32_t)it.key0 * vss2, (uint32_t)it.nk() * vss2);
-    r.z = make_rsrc(kaddr, 0u);
+    r.k = make_rsrc(kaddr + (uint64_t)k0 * kss2, nk * kss2);
+    r.v = make_rsrc(vaddr + (uint64_t)k0 * vss2, nk * vss2);
     return r;
   };
-  // DMA instruction jj of an item into a stage
+  // DMA instruction jj of an item into a stage (the last jj only for w < NFULLW)
   auto dma_part = [&](const Rsrc& r, int stage, int jj) {
     const int b = w + 8 * jj;
-    const uint32_t dst = b < C::NBLK ? lds_base + (uint32_t)(stage * C::STAGE_BYTES + b * 1024)
-                                     : lds_base + (uint32_t)(C::STAGES * C::STAGE_BYTES);
-    dma16(b < C::KBLK ? r.k : (b < C::NBLK ? r.v : r.z), doff[jj], dst);
+    if (jj == JMAX - 1 && b >= C::NBLK) return;
+    dma16(b < C::KBLK ? r.k : r.v, doff[jj],
+          lds_base + (uint32_t)(stage * C::STAGE_BYTES + b * 1024));
   };
   auto issue = [&](const Sub& it, int stage) {
     const Rsrc r = rsrc_of(it);
@@ -463,8 +468,9 @@ void bsa_fwd_pp_kernel(const FwdParams p) {
   // j+2 has landed, and no wave reads item j's stage any more (item j+4
   // refills it).  Items j and j+1 exist inside the loop; the last item's
   // accumulate-only phase is peeled off below (one MFMA-phase body keeps O
-  // in one register set).  Every wave issues JMAX DMAs per item, items past
-  // the end included, so "all but the newest item landed" is vmcnt(JMAX).
+  // in one register set).  Every wave issues its JMAX or JMAX - 1 DMAs per
+  // item, items past the end included, so "all but the newest item landed"
+  // is vmcnt of that count.
   int j = 0;
   while (e1) {
     if (g1) softmax(t0);
@@ -482,7 +488,10 @@ void bsa_fwd_pp_kernel(const FwdParams p) {
     e2 = e3;
     e3 = e3 && L.next(lane, t3);
     if (!e3) t3.nm = 0;
-    wait_vmem<JMAX>();  // item j+2 landed (this wave)
+    if (w < C::NFULLW)  // item j+2 landed (this wave)
+      wait_vmem<JMAX>();
+    else
+      wait_vmem<JMAX - 1>();
     barrier();
     ++j;
   }
