@@ -19,8 +19,18 @@
 //
 // K/V staging.  A four-stage LDS ring holds one item per stage; item j+3 is
 // fetched while item j computes.  Each stage is K [64 keys][RSK slots] then
-// V [64 keys][RSV slots] of 16 bytes (the slots past D/8 in a row are
-// padding).  The stage is cut into 1 KiB blocks dealt round-robin to the
+// V [64 keys][RSV slots] of 16 bytes.  For D = 64 and 128 the rows are not
+// padded (RS = D/8) and the 16-byte chunk c of key r sits at position
+// c ^ swz(r) of its row, an XOR swizzle that keeps both read patterns free
+// of bank conflicts: K (ds_read_b128, 16 lanes read one chunk of 16 keys)
+// uses swz = r & 15 (D = 128) or (r >> 1) & 7 (D = 64), so the 16 keys
+// land on 16 different 16-byte bank groups; V (ds_read_b64_tr_b16, half a
+// wave reads 64 bytes of each of 4 consecutive keys) uses swz = 4 * (r & 3)
+// (D = 128) or 4 * ((r >> 1) & 1) (D = 64), so the 4 keys fill the 4
+// quarters of the 64 banks.  The swizzle only touches address bits 4-7, so
+// a lane keeps one address per K k-step and per V head-dim block and the
+// DMA lanes fetch their chunks in permuted order.  D = 96 (12 chunks) pads
+// instead: odd K stride, V stride 12 (mod 16).  The stage is cut into 1 KiB blocks dealt round-robin to the
 // eight waves; each block is one buffer_load_dwordx4 ... lds (64 lanes x 16
 // bytes straight into LDS) from a per-lane offset computed once, issued
 // between two MFMAs of the MFMA phase.  Waves w < NFULLW own JMAX blocks of
@@ -181,14 +191,17 @@ struct ItemStream {
   }
 };
 
+constexpr int NW_PP = 8;  // waves per workgroup
+
 template <int D>
 struct PPCfg {
-  static constexpr int NW = 8, TM = 256;
+  static constexpr int NW = NW_PP, TM = 256;
   static constexpr int DS = D / 16;  // QK^T k-steps
   static constexpr int DB = D / 32;  // O^T row blocks
   static constexpr int DC = D / 8;   // 16-byte chunks per row
-  static constexpr int RSK = DC + 1;                                         // odd
-  static constexpr int RSV = (DC % 16 == 4 || DC % 16 == 12) ? DC : DC + 4;  // 4 or 12 mod 16
+  static constexpr bool SWZ = D == 64 || D == 128;  // unpadded, XOR-swizzled rows
+  static constexpr int RSK = SWZ ? DC : DC + 1;     // else odd
+  static constexpr int RSV = SWZ ? DC : (DC % 16 == 4 || DC % 16 == 12) ? DC : DC + 4;  // else 4/12 mod 16
   static constexpr int KBLK = RSK, VBLK = RSV;  // 1 KiB blocks: 64 keys x RS slots / 64 lanes
   static constexpr int NBLK = KBLK + VBLK;
   static constexpr int KSLOTS = 64 * RSK;
@@ -199,7 +212,15 @@ struct PPCfg {
   static constexpr int JMAX = (NBLK + NW - 1) / NW;      // most DMA instructions of a wave per item
   static constexpr int NFULLW = NBLK - NW * (JMAX - 1);  // waves w < NFULLW issue JMAX
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
-  static_assert(DC % 2 == 0 && RSV % 16 != 0 && RSV % 4 == 0, "stride rules");
+  static_assert(DC % 2 == 0 && (SWZ || (RSK % 2 == 1 && RSV % 16 != 0 && RSV % 4 == 0)),
+                "stride rules");
+  // chunk position swizzles of K and V rows (see the header)
+  __device__ __forceinline__ static int kswz(int r) {
+    return D == 128 ? (r & 15) : D == 64 ? ((r >> 1) & 7) : 0;
+  }
+  __device__ __forceinline__ static int vswz(int r) {
+    return D == 128 ? 4 * (r & 3) : D == 64 ? 4 * ((r >> 1) & 1) : 0;
+  }
 };
 
 template <int D>
@@ -232,8 +253,9 @@ void bsa_fwd_pp_kernel(const FwdParams p) {
   float m_run = neg_inf(), l_a = 0.f, l_b = 0.f;
 
   // DMA geometry: block b = w + 8*jj of a stage (K blocks first, then V);
-  // lane l fills slot 64*b + l, i.e. key slot / RS, chunk slot % RS (a
-  // padding slot repeats the row's last chunk; it is never read).  Block
+  // lane l fills slot 64*b + l, i.e. key slot / RS, chunk position slot % RS,
+  // which holds chunk position ^ swz(key) (swizzled rows) or the chunk itself
+  // (padded rows: a padding slot repeats the row's last chunk, never read).  Block
   // w + 8*(JMAX-1) exists only for waves w < NFULLW.
   const uint32_t kss2 = (uint32_t)(p.k_ss * 2), vss2 = (uint32_t)(p.v_ss * 2);
   const uint32_t lds_base = (uint32_t)(size_t)((lds_char*)smem);
@@ -244,7 +266,9 @@ void bsa_fwd_pp_kernel(const FwdParams p) {
     const bool isk = b < C::KBLK;
     const int rs = isk ? RSK : RSV;
     const int slot = (isk ? b : b - C::KBLK) * 64 + lane;
-    doff[jj] = (uint32_t)(slot / rs) * (isk ? kss2 : vss2) + (uint32_t)min(slot % rs, DC - 1) * 16u;
+    const int key = slot / rs, pos = slot % rs;
+    const int chunk = C::SWZ ? pos ^ (isk ? C::kswz(key) : C::vswz(key)) : min(pos, DC - 1);
+    doff[jj] = (uint32_t)key * (isk ? kss2 : vss2) + (uint32_t)chunk * 16u;
   }
   // descriptors of one item: K and V.  An item past the end (nm == 0)
   // points at the sequence's first keys; its stage is never read.
@@ -263,7 +287,7 @@ void bsa_fwd_pp_kernel(const FwdParams p) {
   // DMA instruction jj of an item into a stage (the last jj only for w < NFULLW)
   auto dma_part = [&](const Rsrc& r, int stage, int jj) {
     const int b = w + 8 * jj;
-    if (jj == JMAX - 1 && b >= C::NBLK) return;
+    if (C::NFULLW < NW_PP && jj == JMAX - 1 && b >= C::NBLK) return;
     dma16(b < C::KBLK ? r.k : r.v, doff[jj],
           lds_base + (uint32_t)(stage * C::STAGE_BYTES + b * 1024));
   };
@@ -273,13 +297,25 @@ void bsa_fwd_pp_kernel(const FwdParams p) {
     for (int jj = 0; jj < JMAX; ++jj) dma_part(r, stage, jj);
   };
 
-  // per-lane LDS read geometry
+  // per-lane LDS read geometry.  K: row arow (+32 for the second key half),
+  // chunk 2*ks + h32.  V: key vkey + 16*ps (+4 for the second read), head
+  // dims 32*db + vd .. +3.  Swizzled rows: the k-step and the head-dim block
+  // enter as an XOR on address bits 4-7, so one address per ks (K) and per
+  // db (V); the key offsets added after it leave those bits alone.
   const int arow = swap_b23(l32);
-  const int kbase = (arow * RSK + h32) * 16;  // + kb*32*RSK*16 + ks*32 bytes
+  const int kbase = (arow * RSK + h32) * 16;  // padded rows: + kh*32*RSK*16 + ks*32 bytes
   const int vs = lane & 15, vg = lane >> 4;
   const int vkey = 8 * h32 + (vs >> 2);
   const int vd = 16 * (vg & 1) + 4 * (((vs & 1) << 1) | ((vs >> 1) & 1));
-  const int vbase = (vkey * RSV + (vd >> 3)) * 16 + 8 * ((vd >> 2) & 1);
+  const int vbase = (vkey * RSV + (vd >> 3)) * 16 + 8 * ((vd >> 2) & 1);  // padded: + ps, db offsets
+  int kx[C::SWZ ? DS : 1], vx[C::SWZ ? DB : 1];
+  if constexpr (C::SWZ) {
+#pragma unroll
+    for (int ks = 0; ks < DS; ++ks)
+      kx[ks] = (arow * RSK * 16 + 16 * (h32 ^ C::kswz(arow))) ^ (32 * ks);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) vx[db] = (vbase + 16 * C::vswz(vkey)) ^ (64 * db);
+  }
 
   f32x16_t s0, s1;          // S^T of the item after the one being accumulated
   uint32_t pk0[8], pk1[8];  // P^T (bf16 pairs) of the item being accumulated
@@ -290,15 +326,19 @@ void bsa_fwd_pp_kernel(const FwdParams p) {
   // of K).  Operands are read kWin slots ahead of their MFMA so the LDS
   // latency hides behind the MFMAs in between; the slot order is pinned.
   constexpr int NPV = 4 * DB, NQK = 2 * DS, kWin = 5;
+  // vl: the stage's V tile; kb: its K tile (+ kbase for padded rows)
   auto operand = [&](int i, const char* vl, const char* kb) -> uint4 {
     if (i < NPV) {
       const int ps = i / DB, db = i % DB;
-      const int off = vbase + (16 * ps * RSV + 4 * db) * 16;
+      const int off = C::SWZ ? vx[C::SWZ ? db : 0] + 16 * ps * RSV * 16
+                             : vbase + (16 * ps * RSV + 4 * db) * 16;
       const uint2 t0 = read_tr(vl, off);
       const uint2 t1 = read_tr(vl, off + 4 * RSV * 16);
       return make_uint4(t0.x, t0.y, t1.x, t1.y);
     }
     const int k = i - NPV;
+    if constexpr (C::SWZ)
+      return *reinterpret_cast<const uint4*>(kb + kx[k >> 1] + (k & 1) * 32 * RSK * 16);
     return *reinterpret_cast<const uint4*>(kb + (k & 1) * 32 * RSK * 16 + (k >> 1) * 32);
   };
   auto slot = [&](int i, const uint4& a) {
@@ -320,7 +360,8 @@ void bsa_fwd_pp_kernel(const FwdParams p) {
                         int nstage) {
     constexpr int NS = decltype(ns_tag)::value;
     const char* vl = reinterpret_cast<const char*>(smem + vstage * C::STAGE_SLOTS + C::KSLOTS);
-    const char* kb = reinterpret_cast<const char*>(smem + kstage * C::STAGE_SLOTS) + kbase;
+    const char* kb = reinterpret_cast<const char*>(smem + kstage * C::STAGE_SLOTS) +
+                     (C::SWZ ? 0 : kbase);
     if constexpr (NS > NPV) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -350,7 +391,8 @@ void bsa_fwd_pp_kernel(const FwdParams p) {
       s0[r] = 0.f;
       s1[r] = 0.f;
     }
-    const char* kb = reinterpret_cast<const char*>(smem + kstage * C::STAGE_SLOTS) + kbase;
+    const char* kb = reinterpret_cast<const char*>(smem + kstage * C::STAGE_SLOTS) +
+                     (C::SWZ ? 0 : kbase);
 #pragma unroll
     for (int k = 0; k < NQK; ++k) slot(NPV + k, operand(NPV + k, nullptr, kb));
   };
