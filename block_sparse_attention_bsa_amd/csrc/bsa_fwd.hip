@@ -18,18 +18,23 @@
 // workgroup barrier (every wave's DMA landed, every wave finished reading
 // the stage the next DMA overwrites).
 //
-// LDS layout: both tiles are [64 keys][RS 16-byte slots] with head-dim
-// chunk c of key r at slot r*RS + c; the RS - D/8 slots at the end of a row
-// are padding the DMA skips.  K is read as the S^T MFMA A operand with
-// ds_read_b128: the 16 lanes of a quarter-wave read 16 different keys of one
-// chunk, and an odd K stride puts them on 16 different bank groups.  V stays
-// key-major and is read with ds_read_b64_tr_b16, which transposes 4x4 blocks
-// of b16 inside each group of 16 lanes: source lane s of a group loads 4
-// consecutive head dims of key kb + s/4, and lane i receives head dim d(i)
-// of keys kb..kb+3, exactly the O^T MFMA A-operand layout.  Half a wave then
-// reads 4 keys x 4 chunks, and a V stride of 4 or 12 (mod 16) slots puts
-// those on 16 different bank groups.  Every read address is a per-lane base
-// plus a compile-time offset.
+// LDS layout: both tiles are [64 keys][RS 16-byte slots].  K is read as the
+// S^T MFMA A operand with ds_read_b128: the 16 lanes of a quarter-wave read
+// one chunk of 16 different keys.  V stays key-major and is read with
+// ds_read_b64_tr_b16, which transposes 4x4 blocks of b16 inside each group
+// of 16 lanes: source lane s of a group loads 4 consecutive head dims of key
+// kb + s/4, and lane i receives head dim d(i) of keys kb..kb+3, exactly the
+// O^T MFMA A-operand layout; half a wave then reads 4 keys x 4 chunks.  For
+// head_dim 64, 128 and 256 rows are unpadded (RS = D/8) and chunk c of key r
+// sits at position c ^ swz(r): K uses swz = r & 15 (D >= 128) or
+// (r >> 1) & 7 (D = 64), which puts the 16 keys of a quarter-wave on 16
+// different 16-byte bank groups; V uses swz = 4 * (r & 3) (D >= 128) or
+// 4 * ((r >> 1) & 1) (D = 64), which puts the 4 keys of a half-wave on the 4
+// quarters of the banks.  The k-step and the head-dim block enter the read
+// address as an XOR on bits 4..8, so a lane keeps one address per K k-step
+// and per V head-dim block.  Head_dim 96 and 192 pad instead: chunk c at
+// slot r*RS + c, an odd K stride and a V stride of 4 or 12 (mod 16) slots;
+// every read address is then a per-lane base plus a compile-time offset.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -76,23 +81,32 @@ struct FwdCfg {
   static constexpr int DS = D / 16;  // QK^T k-steps
   static constexpr int DB = D / 32;  // O^T row blocks
   static constexpr int DC = D / 8;   // 16-byte chunks per row
-  static constexpr int RSK = DC + 1;                                    // odd
-  static constexpr int RSV = (DC % 16 == 4 || DC % 16 == 12) ? DC : DC + 4;  // 4 or 12 mod 16
+  // D = 64, 128, 256: unpadded rows, chunk c of key r at position c ^ swz(r)
+  // (the swizzle of the 256-row kernel; D = 256 rows hold 32 chunks and the
+  // same K and V swizzles keep both read patterns free of bank conflicts).
+  // D = 96, 192: padded rows, odd K stride, V stride 4 or 12 (mod 16).
+  static constexpr bool SWZ = D == 64 || D == 128 || D == 256;
+  static constexpr int RSK = SWZ ? DC : DC + 1;
+  static constexpr int RSV = SWZ ? DC : (DC % 16 == 4 || DC % 16 == 12) ? DC : DC + 4;
   static constexpr int KSLOTS = kKvTile * RSK;  // = 64 * RSK: RSK DMA blocks of 64 slots
   static constexpr int VSLOTS = kKvTile * RSV;
   static constexpr int STAGE_SLOTS = KSLOTS + VSLOTS;  // K tile, then V tile
   static constexpr int STAGE_BYTES = STAGE_SLOTS * 16;
-  // Up to 4 waves: two stages, so two workgroups share a CU.  8 waves (one
-  // workgroup per CU, two waves per SIMD): three stages when they fit.
-  static constexpr int STAGES = (NW == 8 && 3 * STAGE_BYTES <= 160 * 1024) ? 3 : 2;
+  // Two stages; two workgroups share a CU when both fit in its LDS.
+  static constexpr int STAGES = 2;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-  static constexpr int WAVES_PER_EU =
-      NW == 8 ? 2 : (LDS_BYTES <= 80 * 1024 ? 2 : 1);
-  static constexpr int KIPW = (RSK + NW - 1) / NW;  // K DMA instructions per wave per sub-tile
+  static constexpr int WAVES_PER_EU = LDS_BYTES <= 80 * 1024 ? 2 : 1;
+  static constexpr int KIPW = (RSK + NW - 1) / NW;  // most K DMA instructions of a wave per sub-tile
   static constexpr int VIPW = (RSV + NW - 1) / NW;
-  static constexpr int DMA_PER_ITEM = KIPW + VIPW;
-  static_assert(STAGES == 2 || DMA_PER_ITEM < 64, "vmcnt range");
-  static_assert(DC % 2 == 0 && RSV % 16 != 0 && RSV % 4 == 0, "stride rules");
+  static_assert(NW <= 4, "256-row tiles run in the ping-pong kernel");
+  static_assert(DC % 2 == 0 && (SWZ || (RSK % 2 == 1 && RSV % 16 != 0 && RSV % 4 == 0)),
+                "stride rules");
+  __device__ __forceinline__ static int kswz(int r) {
+    return D >= 128 ? (r & 15) : D == 64 ? ((r >> 1) & 7) : 0;
+  }
+  __device__ __forceinline__ static int vswz(int r) {
+    return D >= 128 ? 4 * (r & 3) : D == 64 ? 4 * ((r >> 1) & 1) : 0;
+  }
 };
 
 template <int D, int NW>
@@ -129,26 +143,30 @@ void bsa_fwd_kernel(const FwdParams p) {
   float m_run = neg_inf(), l_run = 0.f;
 
   // DMA of one 64-key sub-tile.  The tile's RS blocks of 64 slots are
-  // dealt round-robin to the waves, each wave issuing the same number of
-  // instructions (a wave with nothing left re-issues the last block, which
-  // writes the same bytes again).  Lane l of block blk fills slot
-  // 64*blk + l, i.e. key slot / RS, chunk slot % RS (a padding slot gets a
-  // copy of the row's last chunk, which is never read).  Keys past nk repeat
-  // the last visible key (finite data, masked later).  Lane byte offsets
-  // within the sub-tile fit in 32 bits (the host bounds the row stride).
+  // dealt round-robin to the waves; a wave issues only the blocks that
+  // exist (each sub-tile ends with vmcnt(0), so the counts need not match).
+  // Lane l of block blk fills slot 64*blk + l, i.e. key slot / RS at chunk
+  // position slot % RS, which holds chunk position ^ swz(key) (swizzled
+  // rows) or the chunk itself (padded rows: a padding slot gets a copy of
+  // the row's last chunk, never read).  Keys past nk repeat the last visible
+  // key (finite data, masked later).  Lane byte offsets within the sub-tile
+  // fit in 32 bits (the host bounds the row stride).
   constexpr int KIPW = C::KIPW, VIPW = C::VIPW, STAGES = C::STAGES;
   const int kss2 = p.k_ss * 2, vss2 = p.v_ss * 2;
   // lane byte offsets within a full sub-tile, one per DMA instruction
+  // key row and source chunk of slot `slot` of a K (isk) or V tile
+  auto kchunk = [&](int key, int pos) { return C::SWZ ? pos ^ C::kswz(key) : min(pos, DC - 1); };
+  auto vchunk = [&](int key, int pos) { return C::SWZ ? pos ^ C::vswz(key) : min(pos, DC - 1); };
   uint32_t koff[KIPW], voff[VIPW];
 #pragma unroll
   for (int ii = 0; ii < KIPW; ++ii) {
     const int slot = min(ii * NW + w, RSK - 1) * 64 + lane;
-    koff[ii] = (slot / RSK) * kss2 + min(slot % RSK, DC - 1) * 16;
+    koff[ii] = (slot / RSK) * kss2 + kchunk(slot / RSK, slot % RSK) * 16;
   }
 #pragma unroll
   for (int ii = 0; ii < VIPW; ++ii) {
     const int slot = min(ii * NW + w, RSV - 1) * 64 + lane;
-    voff[ii] = (slot / RSV) * vss2 + min(slot % RSV, DC - 1) * 16;
+    voff[ii] = (slot / RSV) * vss2 + vchunk(slot / RSV, slot % RSV) * 16;
   }
   const uint32_t lds_base = (uint32_t)(size_t)((lds_char*)smem);
   auto issue = [&](const Item& it, int stage) {
@@ -156,27 +174,33 @@ void bsa_fwd_kernel(const FwdParams p) {
     const char* vt = reinterpret_cast<const char*>(vp + it.key0 * p.v_ss);
     const uint32_t kl = lds_base + stage * C::STAGE_SLOTS * 16;
     const uint32_t vl = kl + C::KSLOTS * 16;
+    // block ii*NW + w exists unless it is the last one of a wave and past RS
+    auto kblk = [&](int ii) { return !(RSK % NW != 0 && ii == KIPW - 1 && ii * NW + w >= RSK); };
+    auto vblk = [&](int ii) { return !(RSV % NW != 0 && ii == VIPW - 1 && ii * NW + w >= RSV); };
     if (it.nk == kKvTile) {
 #pragma unroll
-      for (int ii = 0; ii < KIPW; ++ii) dma16(kt, koff[ii], kl + min(ii * NW + w, RSK - 1) * 1024);
+      for (int ii = 0; ii < KIPW; ++ii)
+        if (kblk(ii)) dma16(kt, koff[ii], kl + (ii * NW + w) * 1024);
 #pragma unroll
-      for (int ii = 0; ii < VIPW; ++ii) dma16(vt, voff[ii], vl + min(ii * NW + w, RSV - 1) * 1024);
+      for (int ii = 0; ii < VIPW; ++ii)
+        if (vblk(ii)) dma16(vt, voff[ii], vl + (ii * NW + w) * 1024);
     } else {
-      // partial sub-tile: keys past nk repeat the last visible key
+      // partial sub-tile: keys past nk repeat the last visible key (laid out
+      // with the destination row's swizzle)
       const int last = it.nk - 1;
 #pragma unroll
       for (int ii = 0; ii < KIPW; ++ii) {
-        const int blk = min(ii * NW + w, RSK - 1);
-        const int slot = blk * 64 + lane;
-        const int r = slot / RSK, c = min(slot % RSK, DC - 1);
-        dma16(kt, min(r, last) * kss2 + c * 16, kl + blk * 1024);
+        if (!kblk(ii)) continue;
+        const int slot = (ii * NW + w) * 64 + lane;
+        const int r = slot / RSK;
+        dma16(kt, min(r, last) * kss2 + kchunk(r, slot % RSK) * 16, kl + (ii * NW + w) * 1024);
       }
 #pragma unroll
       for (int ii = 0; ii < VIPW; ++ii) {
-        const int blk = min(ii * NW + w, RSV - 1);
-        const int slot = blk * 64 + lane;
-        const int r = slot / RSV, c = min(slot % RSV, DC - 1);
-        dma16(vt, min(r, last) * vss2 + c * 16, vl + blk * 1024);
+        if (!vblk(ii)) continue;
+        const int slot = (ii * NW + w) * 64 + lane;
+        const int r = slot / RSV;
+        dma16(vt, min(r, last) * vss2 + vchunk(r, slot % RSV) * 16, vl + (ii * NW + w) * 1024);
       }
     }
   };
@@ -188,6 +212,16 @@ void bsa_fwd_kernel(const FwdParams p) {
   const int vkey = 8 * h32 + (vs >> 2);       // + 16*ps + 4*t
   const int vd = 16 * (vg & 1) + 4 * (((vs & 1) << 1) | ((vs >> 1) & 1));  // + 32*db
   const int vbase = (vkey * RSV + (vd >> 3)) * 16 + 8 * ((vd >> 2) & 1);
+  // swizzled rows: the k-step (K) and the head-dim block (V) enter as an XOR
+  // on address bits 4..8; the key offsets added after it leave those alone
+  int kx[C::SWZ ? DS : 1], vx[C::SWZ ? DB : 1];
+  if constexpr (C::SWZ) {
+#pragma unroll
+    for (int ks = 0; ks < DS; ++ks)
+      kx[ks] = (arow * RSK * 16 + 16 * (h32 ^ C::kswz(arow))) ^ (32 * ks);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) vx[db] = (vbase + 16 * C::vswz(vkey)) ^ (64 * db);
+  }
 
   auto compute = [&](int stage, const Item& it) {
     const uint4* kl = smem + stage * C::STAGE_SLOTS;
@@ -198,11 +232,12 @@ void bsa_fwd_kernel(const FwdParams p) {
       s0[r] = 0.f;
       s1[r] = 0.f;
     }
-    const char* kb = reinterpret_cast<const char*>(kl) + kbase;
+    const char* kb = reinterpret_cast<const char*>(kl) + (C::SWZ ? 0 : kbase);
 #pragma unroll
     for (int ks = 0; ks < DS; ++ks) {
-      const uint4 a0 = *reinterpret_cast<const uint4*>(kb + ks * 32);
-      const uint4 a1 = *reinterpret_cast<const uint4*>(kb + 32 * RSK * 16 + ks * 32);
+      const int ko = C::SWZ ? kx[C::SWZ ? ks : 0] : ks * 32;
+      const uint4 a0 = *reinterpret_cast<const uint4*>(kb + ko);
+      const uint4 a1 = *reinterpret_cast<const uint4*>(kb + ko + 32 * RSK * 16);
       s0 = mfma32(a0, qf[ks], s0);
       s1 = mfma32(a1, qf[ks], s1);
     }
@@ -214,7 +249,8 @@ void bsa_fwd_kernel(const FwdParams p) {
       const uint4 bop = p_operand(pk0, pk1, ps);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int off = vbase + (16 * ps * RSV + 4 * db) * 16;
+        const int off = C::SWZ ? vx[C::SWZ ? db : 0] + 16 * ps * RSV * 16
+                               : vbase + (16 * ps * RSV + 4 * db) * 16;
         const uint2 t0 = read_tr(vl, off);
         const uint2 t1 = read_tr(vl, off + 4 * RSV * 16);
         oacc[db] = mfma32(make_uint4(t0.x, t0.y, t1.x, t1.y), bop, oacc[db]);
@@ -224,56 +260,35 @@ void bsa_fwd_kernel(const FwdParams p) {
 
   ListWalk L{ti.mrow, p.mi_s[3], ti.mcnt, ti.frow, p.fi_s[3], ti.mcnt + ti.fcnt,
              p.block_kv, ti.num_n, p.mask_mod, p.kv_valid, -1000000, -1, 0};
-  // STAGES-deep pipeline: up to STAGES-1 sub-tiles in flight ahead of the
-  // one being computed.  The npend issued, not yet computed sub-tiles (p0
-  // oldest, then p1) occupy stages stage, stage+1 (mod STAGES).
+  // Two-stage pipeline: the sub-tile after the one being computed streams
+  // into the other stage.  p0 is the issued, not yet computed sub-tile.
+  static_assert(STAGES == 2, "two stages");
   Item walker{-1, 0, 0, 0, 0, 0, 0};
   bool more = advance(walker, L, lane, ti.Sk);
-  Item p0 = walker, p1 = walker;
-  int npend = 0;
+  Item p0 = walker;
+  bool pending = false;
   if (more) {
     issue(walker, 0);
     p0 = walker;
-    npend = 1;
+    pending = true;
     more = advance(walker, L, lane, ti.Sk);
   }
-  if constexpr (STAGES == 3) {
-    if (more) {
-      issue(walker, 1);
-      p1 = walker;
-      npend = 2;
-      more = advance(walker, L, lane, ti.Sk);
-    }
-  }
   int stage = 0;
-  while (npend > 0) {
-    // the oldest pending sub-tile landed (for this wave), then for all waves;
-    // every wave is also done computing the stage the next DMA overwrites
-    if constexpr (STAGES == 3) {
-      if (npend == 2)
-        wait_vmem<C::DMA_PER_ITEM>();
-      else
-        wait_vmem<0>();
-    } else {
-      wait_vmem<0>();
-    }
+  while (pending) {
+    // the pending sub-tile landed (for this wave), then for all waves; every
+    // wave is also done computing the stage the next DMA overwrites
+    wait_vmem<0>();
     __syncthreads();
     const Item cur = p0;
-    if constexpr (STAGES == 3) p0 = p1;
     if (more) {
-      int ns = stage + npend;
-      if (ns >= STAGES) ns -= STAGES;
-      issue(walker, ns);
-      if (STAGES == 3 && npend == 2)
-        p1 = walker;
-      else
-        p0 = walker;
+      issue(walker, stage ^ 1);
+      p0 = walker;
       more = advance(walker, L, lane, ti.Sk);
     } else {
-      --npend;
+      pending = false;
     }
     compute(stage, cur);
-    stage = stage + 1 == STAGES ? 0 : stage + 1;
+    stage ^= 1;
   }
   epilogue<DB, __bf16>(p, ti, qrow, h32, m_run, l_run, oacc);
 }
@@ -288,10 +303,7 @@ hipError_t launch_one(const FwdParams& p, hipStream_t s) {
 
 template <int D>
 hipError_t launch_tm(const FwdParams& p, int tile_m, hipStream_t s) {
-  switch (tile_m) {
-    case 256:
-      if constexpr (D <= 128) return launch_one<D, 8>(p, s);
-      return hipErrorInvalidValue;
+  switch (tile_m) {  // 256-row tiles run in the ping-pong kernel
     case 128: return launch_one<D, 4>(p, s);
     case 64: return launch_one<D, 2>(p, s);
     case 32: return launch_one<D, 1>(p, s);

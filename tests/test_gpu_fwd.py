@@ -374,6 +374,20 @@ def test_q_block_256_128(bq, D, mask_mod, bk, S, Sk):
     check_o_lse(o, lse, O, L, f"bq={bq} D={D} mm={mask_mod} bk={bk}")
 
 
+@pytest.mark.parametrize("D", [64, 96, 128])
+@pytest.mark.parametrize("mask_mod,S,bk", [(CAUSAL, 300, 128), (NONE, 100, 64), (KVV, 640, 112)])
+def test_q_block_128_odd_tile_count(D, mask_mod, S, bk):
+    # 128-row tiles run two to a workgroup; an odd tile count leaves the last
+    # workgroup with a single tile
+    w = _small(seed=D + S + bk, B=1, S=S, H=1, Hkv=1, D=D, bq=128, bk=bk, mask_mod=mask_mod,
+               p_full=0.4, p_part=0.4)
+    assert (w.full.shape[2] * w.full.shape[1] * w.full.shape[0]) % 2 == 1
+    o, lse, qkv = run_batched(w, validate=True)
+    torch.cuda.synchronize()
+    O, L = _oracle_batched(w, qkv)
+    check_o_lse(o, lse, O, L, f"odd tiles D={D} mm={mask_mod} S={S}")
+
+
 @pytest.mark.parametrize("bq", [256, 128])
 def test_q_block_256_128_long_lists_and_empty_rows(bq):
     # lists longer than 64 entries (the list is fetched 64 entries at a time),
