@@ -17,6 +17,12 @@ FLOPs per step count only computed work: 4 * head_dim * sum over listed
 valid-token count), i.e. padding keys the kernel skips are not counted.
 
 Prints one JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
+
+`--table` instead times the forward alone on every workload of the set (tiny
+fp32, causal blocks, the 25 head_dim x block-size sweep runs, varlen packed,
+video) and prints a markdown table: GPU milliseconds (median of 20 launches,
+HIP events), effective TFLOP/s and % of the bf16 peak, and the oracle's rate
+on a sample of Q blocks of the same workload.
 """
 from __future__ import annotations
 
@@ -52,6 +58,8 @@ def _parse():
                     help="print the source hash the HBM-traffic summary is keyed on and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--table", action="store_true",
+                    help="time the forward on every workload and print a markdown table")
     return ap.parse_args()
 
 
@@ -178,6 +186,159 @@ def _cpu_baseline(np, st, workload, budget_s):
                       f"{dt:.1f} s wall"}
 
 
+def _pairs_flops(full, part, bq, bk, Sq, Sk, D):
+    """4*D*sum over listed (Q block, KV block) pairs of the clipped block area."""
+    import numpy as np
+    M, N = full.shape[-2:]
+    mext = np.minimum(bq, Sq - np.arange(M) * bq).astype(np.float64)
+    next_ = np.minimum(bk, Sk - np.arange(N) * bk).astype(np.float64)
+    sel = (full | part).astype(np.float64)
+    return 4.0 * D * float((sel * mext[:, None] * next_[None, :]).sum())
+
+
+def _time_launches(torch, fn, n=20, warm=3):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return ms[len(ms) // 2]
+
+
+def _oracle_rate(fn_blocks, flops_of, budget_s):
+    """TFLOP/s of the oracle over random Q blocks for about budget_s seconds."""
+    t0, fl = time.perf_counter(), 0.0
+    while time.perf_counter() - t0 < budget_s:
+        fl += flops_of(fn_blocks())
+    return fl / (time.perf_counter() - t0) / 1e12
+
+
+def table(torch, np, bsa, workloads, oracle_s):
+    import oracle
+    f64 = lambda t: t.float().cpu().double().numpy()
+    dev = torch.device("cuda")
+    rows = []
+
+    def batched(name, w, dtype=torch.bfloat16, oracle_budget=oracle_s):
+        q, k, v = (torch.from_numpy(x).to(dtype).to(dev) for x in (w.q, w.k, w.v))
+        lists = [bsa.bsa_mask_to_index(torch.from_numpy(m.astype(np.uint8)).to(dev))
+                 if m.any() else None for m in (w.part, w.full)]
+        kvv = None if w.kv_valid is None else torch.from_numpy(
+            np.asarray(w.kv_valid, np.int32)).to(dev)
+        o, lse = bsa.bsa_fwd(q, k, v, lists[0], lists[1], w.block_q, w.block_kv, w.mask_mod,
+                             kvv, w.scale)
+        ms = _time_launches(torch, lambda: bsa.bsa_fwd(q, k, v, lists[0], lists[1], w.block_q,
+                                                       w.block_kv, w.mask_mod, kvv, w.scale,
+                                                       out=o, lse=lse))
+        B, Sq, H, D = w.q.shape
+        Sk = w.k.shape[1]
+        fl = _pairs_flops(w.full, w.part, w.block_q, w.block_kv, Sq, Sk, D)
+        cpu = None
+        if oracle_budget > 0:
+            qo, ko, vo = (f64(t.to(torch.bfloat16)) for t in (q, k, v))
+            rng = np.random.default_rng(0)
+            M = w.full.shape[2]
+
+            def one():
+                pick = (int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(M)))
+                oracle.blocksparse_attention(qo, ko, vo, w.full, w.part, w.block_q, w.block_kv,
+                                             w.mask_mod, w.scale, w.kv_valid, q_blocks=[pick])
+                return pick
+
+            def fl_of(pick):
+                b, h, i = pick
+                return _pairs_flops(w.full[b:b + 1, h:h + 1, i:i + 1],
+                                    w.part[b:b + 1, h:h + 1, i:i + 1], w.block_q, w.block_kv,
+                                    min(w.block_q, Sq - i * w.block_q), Sk, D)
+            cpu = _oracle_rate(one, fl_of, oracle_budget)
+        rows.append((name, ms, fl, cpu))
+
+    batched("tiny fp32 (B1 H1 S256 d64, 64x64, Bernoulli 0.5)", workloads.tiny(),
+            dtype=torch.float32)
+    batched("causal blocks (B2 H4 S1024 d128, 128x128)", workloads.causal_blocks())
+    for D in workloads.SWEEP_HEAD_DIMS:
+        for bq, bk in workloads.SWEEP_BLOCKS:
+            w = workloads.sparse_sweep(D, bq, bk)
+            batched(f"sweep d{D} ({bq},{bk}) (B2 H16 S4096, 25 %)", w,
+                    oracle_budget=oracle_s if (D, bq, bk) == (128, 128, 128) else 0)
+    # varlen packed
+    w = workloads.varlen_packed()
+    H, bq, bk = w.q.shape[1], w.block_q, w.block_kv
+    cu, off, tm, tn = bsa.bsa_varlen_offsets(w.seqlens_q, w.seqlens_k, bq, bk)
+    dv = lambda a: torch.tensor(a, dtype=torch.int32, device=dev)
+    cu_q, cu_k = dv([0] + list(np.cumsum(w.seqlens_q))), dv([0] + list(np.cumsum(w.seqlens_k)))
+    cu_m, offs = dv(cu), dv(off)
+
+    def packed(masks):
+        out = np.zeros((H, tn), np.uint8)
+        for b, m in enumerate(masks):
+            nm, nn = m.shape[1:]
+            for i in range(nm):
+                out[:, off[b] + i * nn: off[b] + (i + 1) * nn] = m[:, i]
+        return torch.from_numpy(out).to(dev)
+
+    ml = bsa.bsa_varlen_mask_to_index(packed(w.part), cu_m, offs, tm, tn)
+    fl_ = bsa.bsa_varlen_mask_to_index(packed(w.full), cu_m, offs, tm, tn)
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (w.q, w.k, w.v))
+    o, lse = bsa.bsa_varlen_fwd(q, k, v, cu_q, cu_k, cu_m, offs, tm, tn, ml, fl_, bq, bk,
+                                w.mask_mod, w.scale)
+    ms = _time_launches(torch, lambda: bsa.bsa_varlen_fwd(q, k, v, cu_q, cu_k, cu_m, offs, tm, tn,
+                                                          ml, fl_, bq, bk, w.mask_mod, w.scale,
+                                                          out=o, lse=lse))
+    D = w.q.shape[-1]
+    fl = sum(_pairs_flops(fu[None], pa[None], bq, bk, sq, sk, D)
+             for fu, pa, sq, sk in zip(w.full, w.part, w.seqlens_q, w.seqlens_k))
+    cpu = None
+    if oracle_s > 0:
+        qo, ko, vo = (f64(t) for t in (q, k, v))
+        rng = np.random.default_rng(0)
+
+        def one():
+            b = int(rng.integers(len(w.seqlens_q)))
+            i = int(rng.integers(-(-w.seqlens_q[b] // bq)))
+            h = int(rng.integers(H))
+            oracle.varlen_blocksparse_attention(qo, ko, vo, w.seqlens_q, w.seqlens_k, w.full,
+                                                w.part, bq, bk, w.mask_mod, w.scale,
+                                                q_blocks=[(b, h, i)])
+            return b, h, i
+
+        def fl_of(pick):
+            b, h, i = pick
+            sq, sk = w.seqlens_q[b], w.seqlens_k[b]
+            return _pairs_flops(w.full[b][None, h:h + 1, i:i + 1], w.part[b][None, h:h + 1, i:i + 1],
+                                bq, bk, min(bq, sq - i * bq), sk, D)
+        cpu = _oracle_rate(one, fl_of, oracle_s)
+    rows.append((f"varlen packed (8 seqs, {sum(w.seqlens_q)} tokens, H16 d128, 128x128)", ms, fl,
+                 cpu))
+    # video (forward only; the step's metadata kernels add < 1 %)
+    st, flops, _ = _video_inputs(torch, np, workloads)
+    wv = st["w"]
+    full, part, kvv = bsa.bsa_expand_kv_blocks(st["cube_mask"], st["cube_valid"], st["f"],
+                                               wv.kv_tile)
+    mlv, flv = bsa.bsa_mask_to_index(part), bsa.bsa_mask_to_index(full)
+    o, lse = bsa.bsa_fwd(st["q"], st["k"], st["v"], mlv, flv, wv.cube_elems, wv.kv_tile,
+                         bsa.MASK_KV_VALID_COUNT, kvv, wv.scale)
+    ms = _time_launches(torch, lambda: bsa.bsa_fwd(st["q"], st["k"], st["v"], mlv, flv,
+                                                   wv.cube_elems, wv.kv_tile,
+                                                   bsa.MASK_KV_VALID_COUNT, kvv, wv.scale,
+                                                   out=o, lse=lse))
+    cpu = _cpu_baseline(np, st, "video", oracle_s)["value"] if oracle_s > 0 else None
+    rows.append(("video (B1 H24 86016 rows d128, 256x128, 11.9 %)", ms, flops, cpu))
+    print("| Workload | GPU ms | GFLOP | TFLOP/s | % bf16 peak | Oracle TFLOP/s (CPU) |")
+    print("|---|---|---|---|---|---|")
+    for name, ms, fl, cpu in rows:
+        tf = fl / (ms * 1e-3) / 1e12
+        c = "" if cpu is None else f"{cpu:.4f}"
+        print(f"| {name} | {ms:.4f} | {fl / 1e9:.2f} | {tf:.1f} | {100 * tf / PEAK_BF16_TFLOPS:.1f} "
+              f"| {c} |", flush=True)
+
+
 def main():
     args = _parse()
     if args.print_kernel_hash:
@@ -197,6 +358,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.table:
+        table(torch, np, bsa, workloads, args.cpu_seconds / 3.0)
+        return
     if args.calibrate_copy:
         n = 1 << 30
         x = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)

@@ -92,8 +92,11 @@ struct FwdCfg {
   static constexpr int VSLOTS = kKvTile * RSV;
   static constexpr int STAGE_SLOTS = KSLOTS + VSLOTS;  // K tile, then V tile
   static constexpr int STAGE_BYTES = STAGE_SLOTS * 16;
-  // Two stages; two workgroups share a CU when both fit in its LDS.
-  static constexpr int STAGES = 2;
+  // 64- and 32-row tiles at d <= 128: one stage (32 KiB at d = 128), so four
+  // workgroups share a CU and hide each other's fetch and softmax; otherwise
+  // two stages (the next sub-tile streams in while one computes), two
+  // workgroups per CU where they fit.
+  static constexpr int STAGES = (NW <= 2 && D <= 128) ? 1 : 2;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr int WAVES_PER_EU = LDS_BYTES <= 80 * 1024 ? 2 : 1;
   static constexpr int KIPW = (RSK + NW - 1) / NW;  // most K DMA instructions of a wave per sub-tile
@@ -260,9 +263,9 @@ void bsa_fwd_kernel(const FwdParams p) {
 
   ListWalk L{ti.mrow, p.mi_s[3], ti.mcnt, ti.frow, p.fi_s[3], ti.mcnt + ti.fcnt,
              p.block_kv, ti.num_n, p.mask_mod, p.kv_valid, -1000000, -1, 0};
-  // Two-stage pipeline: the sub-tile after the one being computed streams
-  // into the other stage.  p0 is the issued, not yet computed sub-tile.
-  static_assert(STAGES == 2, "two stages");
+  // Two stages: the sub-tile after the one being computed streams into the
+  // other stage.  One stage: the next sub-tile is fetched once every wave is
+  // done with the current one.  p0 is the issued, not yet computed sub-tile.
   Item walker{-1, 0, 0, 0, 0, 0, 0};
   bool more = advance(walker, L, lane, ti.Sk);
   Item p0 = walker;
@@ -274,14 +277,30 @@ void bsa_fwd_kernel(const FwdParams p) {
     more = advance(walker, L, lane, ti.Sk);
   }
   int stage = 0;
-  while (pending) {
+  if constexpr (STAGES == 1) {
+    while (pending) {
+      wait_vmem<0>();
+      __syncthreads();
+      const Item cur = p0;
+      compute(0, cur);
+      if (more) {
+        __syncthreads();  // every wave done with the stage before it is refilled
+        issue(walker, 0);
+        p0 = walker;
+        more = advance(walker, L, lane, ti.Sk);
+      } else {
+        pending = false;
+      }
+    }
+  }
+  while (STAGES == 2 && pending) {
     // the pending sub-tile landed (for this wave), then for all waves; every
     // wave is also done computing the stage the next DMA overwrites
     wait_vmem<0>();
     __syncthreads();
     const Item cur = p0;
     if (more) {
-      issue(walker, stage ^ 1);
+      issue(walker, STAGES == 2 ? stage ^ 1 : 0);
       p0 = walker;
       more = advance(walker, L, lane, ti.Sk);
     } else {
