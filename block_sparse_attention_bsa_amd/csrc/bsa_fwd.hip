@@ -92,11 +92,15 @@ struct FwdCfg {
   static constexpr int VSLOTS = kKvTile * RSV;
   static constexpr int STAGE_SLOTS = KSLOTS + VSLOTS;  // K tile, then V tile
   static constexpr int STAGE_BYTES = STAGE_SLOTS * 16;
-  // 64- and 32-row tiles at d <= 128: one stage (32 KiB at d = 128), so four
-  // workgroups share a CU and hide each other's fetch and softmax; otherwise
-  // two stages (the next sub-tile streams in while one computes), two
-  // workgroups per CU where they fit.
-  static constexpr int STAGES = (NW <= 2 && D <= 128) ? 1 : 2;
+  // One stage (the next sub-tile is fetched once the current one is done)
+  // or two (it streams in while the current one computes), chosen by
+  // measurement on the 25 %-density sweep: 64- and 32-row tiles at d <= 128
+  // take one (32 KiB at d = 128, four workgroups per CU that hide each
+  // other's fetch and softmax: +40 %), 128-row tiles take one at d = 128
+  // (+6 %) and d = 192 (two workgroups per CU instead of one: +17 %) and two
+  // otherwise (d = 64: -2 %, d = 256: -11 % with one).
+  static constexpr int STAGES =
+      ((NW <= 2 && D <= 128) || (NW == 4 && (D == 128 || D == 192))) ? 1 : 2;
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr int WAVES_PER_EU = LDS_BYTES <= 80 * 1024 ? 2 : 1;
   static constexpr int KIPW = (RSK + NW - 1) / NW;  // most K DMA instructions of a wave per sub-tile
