@@ -94,13 +94,20 @@ struct FwdCfg {
   static constexpr int STAGE_BYTES = STAGE_SLOTS * 16;
   // One stage (the next sub-tile is fetched once the current one is done)
   // or two (it streams in while the current one computes), chosen by
-  // measurement on the 25 %-density sweep: 64- and 32-row tiles at d <= 128
-  // take one (32 KiB at d = 128, four workgroups per CU that hide each
-  // other's fetch and softmax: +40 %), 128-row tiles take one at d = 128
-  // (+6 %) and d = 192 (two workgroups per CU instead of one: +17 %) and two
-  // otherwise (d = 64: -2 %, d = 256: -11 % with one).
-  static constexpr int STAGES =
-      ((NW <= 2 && D <= 128) || (NW == 4 && (D == 128 || D == 192))) ? 1 : 2;
+  // measurement on the 25 %-density sweep (TFLOP/s, two stages -> one):
+  //   64/32-row tiles, d <= 128: one (d = 128, (64,128): 400 -> 542; four
+  //     workgroups per CU hide each other's fetch and softmax)
+  //   128-row tiles: one at d = 128 (664 -> 694) and d = 192 (481 -> 552,
+  //     two workgroups per CU instead of one); two at d = 64 (-2 % with one)
+  //     and d = 256 (-11 %)
+  //   64-row tiles: one at d = 256 (201 -> 411), two at d = 192 (268 -> 173
+  //     with one: register spills)
+  static constexpr int stages() {
+    if (D <= 128 && NW <= 2) return 1;
+    if (NW == 4) return (D == 128 || D == 192) ? 1 : 2;
+    return (D == 256 && NW == 2) ? 1 : 2;
+  }
+  static constexpr int STAGES = stages();
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
   static constexpr int WAVES_PER_EU = LDS_BYTES <= 80 * 1024 ? 2 : 1;
   static constexpr int KIPW = (RSK + NW - 1) / NW;  // most K DMA instructions of a wave per sub-tile
