@@ -148,8 +148,33 @@ def _sweep_step(bsa, st, events=None):
     st["o"], st["lse"] = o, lse
 
 
-def _cpu_baseline(np, st, workload, budget_s):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
+class _MaxErr:
+    """Largest |GPU - oracle| over the Q blocks the oracle computed: raw for O
+    and LSE, and for a bf16 O also beyond half a bf16 ulp of the oracle's value
+    (the rounding of the stored output), the quantity the 4e-3 bound is on."""
+
+    def __init__(self):
+        self.n, self.o, self.o_excess, self.lse = 0, 0.0, 0.0, 0.0
+
+    def note(self, o_gpu, lse_gpu, o_ref, lse_ref):
+        import numpy as np
+        self.n += 1
+        err = np.abs(o_gpu.double().cpu().numpy() - o_ref)
+        if o_gpu.dtype.itemsize == 2:
+            a = np.abs(o_ref)
+            ulp = 2.0 ** (np.floor(np.log2(np.where(a > 0, a, 1.0))) - 7)
+            err_x = err - 0.5 * np.where(a > 0, ulp, 0.0)
+        else:
+            err_x = err
+        self.o = max(self.o, float(err.max()))
+        self.o_excess = max(self.o_excess, float(err_x.max()))
+        self.lse = max(self.lse, float(np.abs(lse_gpu.double().cpu().numpy() - lse_ref).max()))
+
+
+def _cpu_baseline(np, st, workload, budget_s, gpu_out=None, err=None):
+    """The oracle, as it stands, on a bounded sample of the same workload.
+    With gpu_out=(O, LSE) and err, the GPU's rows of each sampled block are
+    compared with the oracle's (outside the timed part)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -172,14 +197,18 @@ def _cpu_baseline(np, st, workload, budget_s):
         bq, bk, mm, kvv = w.block_q, w.block_kv, w.mask_mod, None
         row_keys = lambda b, h, i: float((full[b, h, i] | part[b, h, i]).sum() * bk)
     D = q.shape[-1]
-    flops, n, t0 = 0.0, 0, time.perf_counter()
-    while time.perf_counter() - t0 < budget_s:
+    flops, n, dt, Sq = 0.0, 0, 0.0, q.shape[1]
+    while dt < budget_s:
         b, h, i = int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(M))
-        oracle.blocksparse_attention(q, k, v, full, part, bq, bk, mm, w.scale, kvv,
-                                     q_blocks=[(b, h, i)])
+        t0 = time.perf_counter()
+        O, L = oracle.blocksparse_attention(q, k, v, full, part, bq, bk, mm, w.scale, kvv,
+                                            q_blocks=[(b, h, i)])
+        dt += time.perf_counter() - t0
         flops += 4.0 * D * bq * row_keys(b, h, i)
         n += 1
-    dt = time.perf_counter() - t0
+        if gpu_out is not None:
+            r = slice(i * bq, min((i + 1) * bq, Sq))
+            err.note(gpu_out[0][b, r, h], gpu_out[1][b, h, r], O[b, r, h], L[b, h, r])
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{n} random Q blocks ({bq} rows each) of the same workload, fp64 numpy, "
@@ -211,19 +240,34 @@ def _time_launches(torch, fn, n=20, warm=3):
     return ms[len(ms) // 2]
 
 
-def _oracle_rate(fn_blocks, flops_of, budget_s):
-    """TFLOP/s of the oracle over random Q blocks for about budget_s seconds."""
-    t0, fl = time.perf_counter(), 0.0
-    while time.perf_counter() - t0 < budget_s:
-        fl += flops_of(fn_blocks())
-    return fl / (time.perf_counter() - t0) / 1e12
+def _oracle_rate(fn_blocks, flops_of, budget_s, check):
+    """TFLOP/s of the oracle over random Q blocks for about budget_s seconds.
+    fn_blocks() -> (pick, (O, LSE)); check(pick, O, LSE) runs untimed."""
+    dt, fl = 0.0, 0.0
+    while dt < budget_s:
+        t0 = time.perf_counter()
+        pick, (O, L) = fn_blocks()
+        dt += time.perf_counter() - t0
+        fl += flops_of(pick)
+        check(pick, O, L)
+    return fl / dt / 1e12
 
 
 def table(torch, np, bsa, workloads, oracle_s):
     import oracle
     f64 = lambda t: t.float().cpu().double().numpy()
     dev = torch.device("cuda")
-    rows = []
+    print("| Workload | GPU ms | GFLOP | TFLOP/s | % bf16 peak | Oracle TFLOP/s (CPU) "
+          "| Oracle blocks | max abs err O | O err beyond bf16 rounding | max abs err LSE |")
+    print("|---|---|---|---|---|---|---|---|---|---|", flush=True)
+
+    def emit(name, ms, fl, cpu, err):
+        tf = fl / (ms * 1e-3) / 1e12
+        c = "" if cpu is None else f"{cpu:.4f}"
+        e = (" | | | " if err.n == 0 else
+             f"{err.n} | {err.o:.2e} | {err.o_excess:.2e} | {err.lse:.2e}")
+        print(f"| {name} | {ms:.4f} | {fl / 1e9:.2f} | {tf:.1f} "
+              f"| {100 * tf / PEAK_BF16_TFLOPS:.1f} | {c} | {e} |", flush=True)
 
     def batched(name, w, dtype=torch.bfloat16, oracle_budget=oracle_s):
         q, k, v = (torch.from_numpy(x).to(dtype).to(dev) for x in (w.q, w.k, w.v))
@@ -239,7 +283,7 @@ def table(torch, np, bsa, workloads, oracle_s):
         B, Sq, H, D = w.q.shape
         Sk = w.k.shape[1]
         fl = _pairs_flops(w.full, w.part, w.block_q, w.block_kv, Sq, Sk, D)
-        cpu = None
+        cpu, err = None, _MaxErr()
         if oracle_budget > 0:
             qo, ko, vo = (f64(t.to(torch.bfloat16)) for t in (q, k, v))
             rng = np.random.default_rng(0)
@@ -247,17 +291,22 @@ def table(torch, np, bsa, workloads, oracle_s):
 
             def one():
                 pick = (int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(M)))
-                oracle.blocksparse_attention(qo, ko, vo, w.full, w.part, w.block_q, w.block_kv,
-                                             w.mask_mod, w.scale, w.kv_valid, q_blocks=[pick])
-                return pick
+                return pick, oracle.blocksparse_attention(
+                    qo, ko, vo, w.full, w.part, w.block_q, w.block_kv, w.mask_mod, w.scale,
+                    w.kv_valid, q_blocks=[pick])
+
+            def check(pick, O, L):
+                b, h, i = pick
+                r = slice(i * w.block_q, min((i + 1) * w.block_q, Sq))
+                err.note(o[b, r, h], lse[b, h, r], O[b, r, h], L[b, h, r])
 
             def fl_of(pick):
                 b, h, i = pick
                 return _pairs_flops(w.full[b:b + 1, h:h + 1, i:i + 1],
                                     w.part[b:b + 1, h:h + 1, i:i + 1], w.block_q, w.block_kv,
                                     min(w.block_q, Sq - i * w.block_q), Sk, D)
-            cpu = _oracle_rate(one, fl_of, oracle_budget)
-        rows.append((name, ms, fl, cpu))
+            cpu = _oracle_rate(one, fl_of, oracle_budget, check)
+        emit(name, ms, fl, cpu, err)
 
     batched("tiny fp32 (B1 H1 S256 d64, 64x64, Bernoulli 0.5)", workloads.tiny(),
             dtype=torch.float32)
@@ -294,28 +343,33 @@ def table(torch, np, bsa, workloads, oracle_s):
     D = w.q.shape[-1]
     fl = sum(_pairs_flops(fu[None], pa[None], bq, bk, sq, sk, D)
              for fu, pa, sq, sk in zip(w.full, w.part, w.seqlens_q, w.seqlens_k))
-    cpu = None
+    cpu, err = None, _MaxErr()
     if oracle_s > 0:
         qo, ko, vo = (f64(t) for t in (q, k, v))
         rng = np.random.default_rng(0)
+        cq = np.concatenate([[0], np.cumsum(w.seqlens_q)])
 
         def one():
             b = int(rng.integers(len(w.seqlens_q)))
             i = int(rng.integers(-(-w.seqlens_q[b] // bq)))
             h = int(rng.integers(H))
-            oracle.varlen_blocksparse_attention(qo, ko, vo, w.seqlens_q, w.seqlens_k, w.full,
-                                                w.part, bq, bk, w.mask_mod, w.scale,
-                                                q_blocks=[(b, h, i)])
-            return b, h, i
+            return (b, h, i), oracle.varlen_blocksparse_attention(
+                qo, ko, vo, w.seqlens_q, w.seqlens_k, w.full, w.part, bq, bk, w.mask_mod,
+                w.scale, q_blocks=[(b, h, i)])
+
+        def check(pick, O, L):
+            b, h, i = pick
+            r = slice(int(cq[b]) + i * bq, int(cq[b]) + min((i + 1) * bq, w.seqlens_q[b]))
+            err.note(o[r, h], lse[h, r], O[r, h], L[h, r])
 
         def fl_of(pick):
             b, h, i = pick
             sq, sk = w.seqlens_q[b], w.seqlens_k[b]
             return _pairs_flops(w.full[b][None, h:h + 1, i:i + 1], w.part[b][None, h:h + 1, i:i + 1],
                                 bq, bk, min(bq, sq - i * bq), sk, D)
-        cpu = _oracle_rate(one, fl_of, oracle_s)
-    rows.append((f"varlen packed (8 seqs, {sum(w.seqlens_q)} tokens, H16 d128, 128x128)", ms, fl,
-                 cpu))
+        cpu = _oracle_rate(one, fl_of, oracle_s, check)
+    emit(f"varlen packed (8 seqs, {sum(w.seqlens_q)} tokens, H16 d128, 128x128)", ms, fl, cpu,
+         err)
     # video (forward only; the step's metadata kernels add < 1 %)
     st, flops, _ = _video_inputs(torch, np, workloads)
     wv = st["w"]
@@ -328,15 +382,10 @@ def table(torch, np, bsa, workloads, oracle_s):
                                                    wv.cube_elems, wv.kv_tile,
                                                    bsa.MASK_KV_VALID_COUNT, kvv, wv.scale,
                                                    out=o, lse=lse))
-    cpu = _cpu_baseline(np, st, "video", oracle_s)["value"] if oracle_s > 0 else None
-    rows.append(("video (B1 H24 86016 rows d128, 256x128, 11.9 %)", ms, flops, cpu))
-    print("| Workload | GPU ms | GFLOP | TFLOP/s | % bf16 peak | Oracle TFLOP/s (CPU) |")
-    print("|---|---|---|---|---|---|")
-    for name, ms, fl, cpu in rows:
-        tf = fl / (ms * 1e-3) / 1e12
-        c = "" if cpu is None else f"{cpu:.4f}"
-        print(f"| {name} | {ms:.4f} | {fl / 1e9:.2f} | {tf:.1f} | {100 * tf / PEAK_BF16_TFLOPS:.1f} "
-              f"| {c} |", flush=True)
+    err = _MaxErr()
+    cpu = (_cpu_baseline(np, st, "video", oracle_s, gpu_out=(o, lse), err=err)["value"]
+           if oracle_s > 0 else None)
+    emit("video (B1 H24 86016 rows d128, 256x128, 11.9 %)", ms, flops, cpu, err)
 
 
 def main():
