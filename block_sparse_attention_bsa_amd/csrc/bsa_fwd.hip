@@ -10,13 +10,15 @@
 //
 // Each listed KV block is cut into 64-key sub-tiles.  K and V rows go
 // straight from HBM into LDS with 16-byte global_load_lds DMA (no staging
-// registers), two stages, issued one sub-tile ahead: while sub-tile i
-// computes from one stage, sub-tile i+1 streams into the other.  The DMA is
-// issued from inline assembly so the compiler does not conservatively wait
-// for it before every LDS read of the other stage; the kernel orders it
-// itself: each sub-tile starts with vmcnt(0) (this wave's DMA landed) and a
-// workgroup barrier (every wave's DMA landed, every wave finished reading
-// the stage the next DMA overwrites).
+// registers).  With two stages, sub-tile i+1 streams into one stage while
+// sub-tile i computes from the other.  With one stage (chosen where the
+// smaller LDS footprint lets more workgroups share a CU), sub-tile i+1 is
+// fetched once every wave has finished with sub-tile i, and the other
+// workgroups on the CU compute meanwhile.  The DMA is issued from inline
+// assembly so the compiler does not conservatively wait for it before every
+// LDS read; the kernel orders it itself: each sub-tile starts with vmcnt(0)
+// (this wave's DMA landed) and a workgroup barrier (every wave's DMA landed,
+// every wave finished reading the stage the next DMA overwrites).
 //
 // LDS layout: both tiles are [64 keys][RS 16-byte slots].  K is read as the
 // S^T MFMA A operand with ds_read_b128: the 16 lanes of a quarter-wave read
@@ -167,10 +169,10 @@ void bsa_fwd_kernel(const FwdParams p) {
   // fit in 32 bits (the host bounds the row stride).
   constexpr int KIPW = C::KIPW, VIPW = C::VIPW, STAGES = C::STAGES;
   const int kss2 = p.k_ss * 2, vss2 = p.v_ss * 2;
-  // lane byte offsets within a full sub-tile, one per DMA instruction
-  // key row and source chunk of slot `slot` of a K (isk) or V tile
+  // source chunk stored at chunk position pos of key row `key` (K or V tile)
   auto kchunk = [&](int key, int pos) { return C::SWZ ? pos ^ C::kswz(key) : min(pos, DC - 1); };
   auto vchunk = [&](int key, int pos) { return C::SWZ ? pos ^ C::vswz(key) : min(pos, DC - 1); };
+  // lane byte offsets within a full sub-tile, one per DMA instruction
   uint32_t koff[KIPW], voff[VIPW];
 #pragma unroll
   for (int ii = 0; ii < KIPW; ++ii) {
@@ -311,7 +313,7 @@ void bsa_fwd_kernel(const FwdParams p) {
     __syncthreads();
     const Item cur = p0;
     if (more) {
-      issue(walker, STAGES == 2 ? stage ^ 1 : 0);
+      issue(walker, stage ^ 1);
       p0 = walker;
       more = advance(walker, L, lane, ti.Sk);
     } else {
