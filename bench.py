@@ -40,6 +40,7 @@ if ROOT not in sys.path:
 
 METRIC = "effective TFLOP/s (computed blocks) bf16 block-sparse attn fwd; % MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA
+PEAK_SCLK_MHZ = 2400.0     # the clock that peak is quoted at
 # sources of the forward kernel the video workload launches (256-row workgroups)
 FWD_KERNEL_SRCS = [os.path.join(ROOT, "block_sparse_attention_bsa_amd", "csrc", f)
                    for f in ("bsa_fwd_pp.hip", "bsa_fwd_common.h")]
@@ -71,15 +72,15 @@ def _kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def _traffic_from_profile():
-    """Per-launch HBM bytes from the committed counter summary, or None if it
-    is missing or was taken on another revision of the forward kernel."""
+def _from_profile(key):
+    """A per-launch figure from the committed counter summary of the forward
+    kernel, or None if it is missing or was taken on another revision."""
     try:
         text = open(TRAFFIC_SUMMARY).read()
     except OSError:
         return None
     h = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", text)
-    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    b = re.search(re.escape(key) + r":\s*([0-9.eE+]+)", text)
     if not h or not b or h.group(1) != _kernel_hash():
         return None
     return float(b.group(1))
@@ -97,13 +98,18 @@ def _video_inputs(torch, np, workloads):
                          w.kv_tile)  # [cubes, f]
     keys_per_row = (w.cube_mask[0].astype(np.float64) @ tile_valid.sum(1).astype(np.float64))
     flops = 4.0 * q.shape[-1] * w.cube_elems * float(keys_per_row.sum())
+    # the coarser count: every listed tile with a valid key at its full 128 keys
+    full_tiles = (tile_valid > 0).sum(1).astype(np.float64) * w.kv_tile
+    flops_full_tiles = 4.0 * q.shape[-1] * w.cube_elems * float(
+        (w.cube_mask[0].astype(np.float64) @ full_tiles).sum())
     density = float(w.cube_mask.mean())
     cfg = {"workload": "video_sparse_attention", "B": 1, "H": q.shape[2], "tokens": int(
         w.cube_valid.sum()), "padded_seq": q.shape[1], "head_dim": q.shape[3], "cube": list(w.cube),
         "grid": list(w.grid), "block_q": w.cube_elems, "kv_tile": w.kv_tile,
         "kv_cubes_per_q_cube": int(w.cube_mask[0, 0, 0].sum()), "block_density": round(density, 4),
         "mask_mod": "kv_valid_count", "layout": "BSHD"}
-    state = dict(q=q, k=k, v=v, cube_mask=cube_mask, cube_valid=cube_valid, f=f, w=w)
+    state = dict(q=q, k=k, v=v, cube_mask=cube_mask, cube_valid=cube_valid, f=f, w=w,
+                 flops_full_tiles=flops_full_tiles)
     return state, flops, cfg
 
 
@@ -441,7 +447,12 @@ def main():
     fwd_avg = sum(fwd_ms) / len(fwd_ms)
     value = flops / (ms_step * 1e-3) / 1e12
     achieved = flops / (fwd_avg * 1e-3) / 1e12
-    traffic = _traffic_from_profile() if args.workload == "video" else None
+    video = args.workload == "video"
+    traffic = _from_profile("hbm_bytes_per_launch") if video else None
+    # GPU-active cycles per launch (per XCD) from the committed counter run of
+    # this kernel revision: the cycle count does not move with the clock, so
+    # over the live kernel time it gives the shader clock of this run
+    cycles = _from_profile("active_cycles_per_launch_per_xcd") if video else None
     # head_dim 128; 256-row workgroups for 256-token Q cubes, 128 rows otherwise
     kernel_name = "bsa_fwd_pp_kernel<128> (256-row workgroup, 8 waves)" \
         if args.workload == "video" else "bsa_fwd_kernel<128,4> (128-row workgroup)"
@@ -455,8 +466,17 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": kernel_name,
-                     "kernel_ms": round(fwd_avg, 4), "flops_per_launch": flops},
+                     "kernel_ms": round(fwd_avg, 4), "flops_per_launch": flops,
+                     # achieved against the peak scaled to the clock of this run
+                     "measured_sclk_mhz": None, "frac_at_measured_clock": None},
     }
+    if cycles:
+        sclk = cycles / (fwd_avg * 1e-3) / 1e6
+        out["roofline"]["measured_sclk_mhz"] = round(sclk, 1)
+        out["roofline"]["frac_at_measured_clock"] = round(
+            achieved / (PEAK_BF16_TFLOPS * sclk / PEAK_SCLK_MHZ), 4)
+    if video:
+        out["flops_full_tiles_per_launch"] = st["flops_full_tiles"]
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = _cpu_baseline(np, st, args.workload, args.cpu_seconds)
     print(json.dumps(out), flush=True)
