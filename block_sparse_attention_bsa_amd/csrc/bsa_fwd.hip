@@ -97,21 +97,27 @@ struct FwdCfg {
   // One stage (the next sub-tile is fetched once the current one is done)
   // or two (it streams in while the current one computes), chosen by
   // measurement on the 25 %-density sweep (TFLOP/s, two stages -> one):
-  //   64/32-row tiles, d <= 128: one (d = 128, (64,128): 400 -> 542; four
-  //     workgroups per CU hide each other's fetch and softmax)
   //   128-row tiles: one at d = 128 (664 -> 694) and d = 192 (481 -> 552,
   //     two workgroups per CU instead of one); two at d = 64 (-2 % with one)
   //     and d = 256 (-11 %)
-  //   64-row tiles: one at d = 256 (201 -> 411), two at d = 192 (268 -> 173
-  //     with one: register spills)
+  //   64-row tiles: one (d = 128, (64,128): 400 -> 542, four workgroups per
+  //     CU hide each other's fetch and softmax; d = 192: 273 -> 436-481 and
+  //     d = 256: 201 -> 411, two workgroups per CU instead of one)
+  //   32-row tiles: one at d <= 128, two above
   static constexpr int stages() {
-    if (D <= 128 && NW <= 2) return 1;
     if (NW == 4) return (D == 128 || D == 192) ? 1 : 2;
-    return (D == 256 && NW == 2) ? 1 : 2;
+    if (NW == 2) return 1;
+    return D <= 128 ? 1 : 2;
   }
   static constexpr int STAGES = stages();
   static constexpr int LDS_BYTES = STAGES * STAGE_BYTES;
-  static constexpr int WAVES_PER_EU = LDS_BYTES <= 80 * 1024 ? 2 : 1;
+  // Register budget: 256 per wave (two waves per SIMD) when the LDS lets
+  // eight or more waves share a CU, else 512.  A 64-row tile at d = 192 or
+  // 256 fits two workgroups (four waves) per CU: one wave per SIMD, so the
+  // larger budget costs no occupancy and removes the spills.
+  static constexpr int WGS_PER_CU_BY_LDS = (160 * 1024) / LDS_BYTES;
+  static constexpr int WAVES_PER_EU =
+      NW == 1 ? (LDS_BYTES <= 80 * 1024 ? 2 : 1) : (WGS_PER_CU_BY_LDS * NW >= 8 ? 2 : 1);
   static constexpr int KIPW = (RSK + NW - 1) / NW;  // most K DMA instructions of a wave per sub-tile
   static constexpr int VIPW = (RSV + NW - 1) / NW;
   static_assert(NW <= 4, "256-row tiles run in the ping-pong kernel");
