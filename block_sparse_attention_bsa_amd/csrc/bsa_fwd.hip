@@ -120,6 +120,15 @@ struct FwdCfg {
       NW == 1 ? (LDS_BYTES <= 80 * 1024 ? 2 : 1) : (WGS_PER_CU_BY_LDS * NW >= 8 ? 2 : 1);
   static constexpr int KIPW = (RSK + NW - 1) / NW;  // most K DMA instructions of a wave per sub-tile
   static constexpr int VIPW = (RSV + NW - 1) / NW;
+  // Swizzled rows: DMA block ii of a wave covers keys (ii*NW + w) * 64/RS ..,
+  // so its lane offsets repeat every KP (VP) blocks up to a wave-uniform key
+  // step (the K swizzle has a period of 16 keys, the V swizzle of 4), and
+  // only KP (VP) offsets per lane are kept.  Padded rows keep one per block.
+  static constexpr int gcd(int a, int b) { return b == 0 ? a : gcd(b, a % b); }
+  static constexpr int KSTEP = SWZ ? NW * 64 / RSK : 0;  // keys between blocks ii and ii+1
+  static constexpr int VSTEP = SWZ ? NW * 64 / RSV : 0;
+  static constexpr int KP = SWZ ? 16 / gcd(16, KSTEP) : KIPW;
+  static constexpr int VP = SWZ ? 4 / gcd(4, VSTEP) : VIPW;
   static_assert(NW <= 4, "256-row tiles run in the ping-pong kernel");
   static_assert(DC % 2 == 0 && (SWZ || (RSK % 2 == 1 && RSV % 16 != 0 && RSV % 4 == 0)),
                 "stride rules");
@@ -178,15 +187,17 @@ void bsa_fwd_kernel(const FwdParams p) {
   // source chunk stored at chunk position pos of key row `key` (K or V tile)
   auto kchunk = [&](int key, int pos) { return C::SWZ ? pos ^ C::kswz(key) : min(pos, DC - 1); };
   auto vchunk = [&](int key, int pos) { return C::SWZ ? pos ^ C::vswz(key) : min(pos, DC - 1); };
-  // lane byte offsets within a full sub-tile, one per DMA instruction
-  uint32_t koff[KIPW], voff[VIPW];
+  // lane byte offsets within a full sub-tile for the first KP (VP) DMA
+  // blocks of this wave; block ii uses entry ii % KP and a key step
+  constexpr int KP = C::KP < KIPW ? C::KP : KIPW, VP = C::VP < VIPW ? C::VP : VIPW;
+  uint32_t koff[KP], voff[VP];
 #pragma unroll
-  for (int ii = 0; ii < KIPW; ++ii) {
+  for (int ii = 0; ii < KP; ++ii) {
     const int slot = min(ii * NW + w, RSK - 1) * 64 + lane;
     koff[ii] = (slot / RSK) * kss2 + kchunk(slot / RSK, slot % RSK) * 16;
   }
 #pragma unroll
-  for (int ii = 0; ii < VIPW; ++ii) {
+  for (int ii = 0; ii < VP; ++ii) {
     const int slot = min(ii * NW + w, RSV - 1) * 64 + lane;
     voff[ii] = (slot / RSV) * vss2 + vchunk(slot / RSV, slot % RSV) * 16;
   }
@@ -202,10 +213,12 @@ void bsa_fwd_kernel(const FwdParams p) {
     if (it.nk == kKvTile) {
 #pragma unroll
       for (int ii = 0; ii < KIPW; ++ii)
-        if (kblk(ii)) dma16(kt, koff[ii], kl + (ii * NW + w) * 1024);
+        if (kblk(ii))
+          dma16(kt + (ii / KP) * (KP * C::KSTEP) * kss2, koff[ii % KP], kl + (ii * NW + w) * 1024);
 #pragma unroll
       for (int ii = 0; ii < VIPW; ++ii)
-        if (vblk(ii)) dma16(vt, voff[ii], vl + (ii * NW + w) * 1024);
+        if (vblk(ii))
+          dma16(vt + (ii / VP) * (VP * C::VSTEP) * vss2, voff[ii % VP], vl + (ii * NW + w) * 1024);
     } else {
       // partial sub-tile: keys past nk repeat the last visible key (laid out
       // with the destination row's swizzle)
