@@ -189,7 +189,24 @@ void bsa_fwd_kernel(const FwdParams p) {
   auto vchunk = [&](int key, int pos) { return C::SWZ ? pos ^ C::vswz(key) : min(pos, DC - 1); };
   // lane byte offsets within a full sub-tile for the first KP (VP) DMA
   // blocks of this wave; block ii uses entry ii % KP and a key step
-  constexpr int KP = C::KP < KIPW ? C::KP : KIPW, VP = C::VP < VIPW ? C::VP : VIPW;
+  // Padded rows with many DMA blocks under the 256-register budget (d = 192,
+  // 128-row tiles) compute the offsets when they issue (a few VALU per DMA)
+  // rather than keep one register per block, which spilled.
+  constexpr bool OTF = !C::SWZ && C::WAVES_PER_EU == 2 && D >= 192;
+  constexpr int KP = OTF ? 1 : C::KP < KIPW ? C::KP : KIPW;
+  constexpr int VP = OTF ? 1 : C::VP < VIPW ? C::VP : VIPW;
+  auto kofs = [&](int ii) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // computed at the DMA, not hoisted into a live register
+    const int slot = min(ii * NW + w, RSK - 1) * 64 + ln;
+    return (uint32_t)((slot / RSK) * kss2 + kchunk(slot / RSK, slot % RSK) * 16);
+  };
+  auto vofs = [&](int ii) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int slot = min(ii * NW + w, RSV - 1) * 64 + ln;
+    return (uint32_t)((slot / RSV) * vss2 + vchunk(slot / RSV, slot % RSV) * 16);
+  };
   uint32_t koff[KP], voff[VP];
 #pragma unroll
   for (int ii = 0; ii < KP; ++ii) {
@@ -214,11 +231,13 @@ void bsa_fwd_kernel(const FwdParams p) {
 #pragma unroll
       for (int ii = 0; ii < KIPW; ++ii)
         if (kblk(ii))
-          dma16(kt + (ii / KP) * (KP * C::KSTEP) * kss2, koff[ii % KP], kl + (ii * NW + w) * 1024);
+          dma16(kt + (ii / KP) * (KP * C::KSTEP) * kss2, OTF ? kofs(ii) : koff[ii % KP],
+                kl + (ii * NW + w) * 1024);
 #pragma unroll
       for (int ii = 0; ii < VIPW; ++ii)
         if (vblk(ii))
-          dma16(vt + (ii / VP) * (VP * C::VSTEP) * vss2, voff[ii % VP], vl + (ii * NW + w) * 1024);
+          dma16(vt + (ii / VP) * (VP * C::VSTEP) * vss2, OTF ? vofs(ii) : voff[ii % VP],
+                vl + (ii * NW + w) * 1024);
     } else {
       // partial sub-tile: keys past nk repeat the last visible key (laid out
       // with the destination row's swizzle)
@@ -267,29 +286,48 @@ void bsa_fwd_kernel(const FwdParams p) {
       s0[r] = 0.f;
       s1[r] = 0.f;
     }
+    // Both products read their LDS operands one step ahead of the MFMAs that
+    // use them and no further (sched_barrier): left to itself the compiler
+    // hoists every read of the loop, and the registers that takes spill at
+    // d = 192 and cost occupancy elsewhere.
     const char* kb = reinterpret_cast<const char*>(kl) + (C::SWZ ? 0 : kbase);
+    auto kld = [&](int ks, int half) {
+      const int ko = C::SWZ ? kx[C::SWZ ? ks : 0] : ks * 32;
+      return *reinterpret_cast<const uint4*>(kb + ko + half * 32 * RSK * 16);
+    };
+    uint4 n0 = kld(0, 0), n1 = kld(0, 1);
 #pragma unroll
     for (int ks = 0; ks < DS; ++ks) {
-      const int ko = C::SWZ ? kx[C::SWZ ? ks : 0] : ks * 32;
-      const uint4 a0 = *reinterpret_cast<const uint4*>(kb + ko);
-      const uint4 a1 = *reinterpret_cast<const uint4*>(kb + ko + 32 * RSK * 16);
+      const uint4 a0 = n0, a1 = n1;
+      if (ks + 1 < DS) {
+        n0 = kld(ks + 1, 0);
+        n1 = kld(ks + 1, 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       s0 = mfma32(a0, qf[ks], s0);
       s1 = mfma32(a1, qf[ks], s1);
+      __builtin_amdgcn_sched_barrier(0);
     }
     uint32_t pk0[8], pk1[8];
     softmax_step<DB>(s0, s1, it, it.is_mask && p.mask_mod == kMaskCausal, qrow, h32, p.c, m_run,
                      l_run, oacc, pk0, pk1);
+    // PV step i: keys 16*(i / DB) .., head dims 32*(i % DB) ..
+    auto vld = [&](int i) {
+      const int ps = i / DB, db = i % DB;
+      const int off = C::SWZ ? vx[C::SWZ ? db : 0] + 16 * ps * RSV * 16
+                             : vbase + (16 * ps * RSV + 4 * db) * 16;
+      const uint2 t0 = read_tr(vl, off);
+      const uint2 t1 = read_tr(vl, off + 4 * RSV * 16);
+      return make_uint4(t0.x, t0.y, t1.x, t1.y);
+    };
+    uint4 nv = vld(0);
 #pragma unroll
-    for (int ps = 0; ps < 4; ++ps) {
-      const uint4 bop = p_operand(pk0, pk1, ps);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int off = C::SWZ ? vx[C::SWZ ? db : 0] + 16 * ps * RSV * 16
-                               : vbase + (16 * ps * RSV + 4 * db) * 16;
-        const uint2 t0 = read_tr(vl, off);
-        const uint2 t1 = read_tr(vl, off + 4 * RSV * 16);
-        oacc[db] = mfma32(make_uint4(t0.x, t0.y, t1.x, t1.y), bop, oacc[db]);
-      }
+    for (int i = 0; i < 4 * DB; ++i) {
+      const uint4 a = nv;
+      if (i + 1 < 4 * DB) nv = vld(i + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      oacc[i % DB] = mfma32(a, p_operand(pk0, pk1, i / DB), oacc[i % DB]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
