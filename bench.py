@@ -231,13 +231,18 @@ def _pairs_flops(full, part, bq, bk, Sq, Sk, D):
     return 4.0 * D * float((sel * mext[:, None] * next_[None, :]).sum())
 
 
-def _time_launches(torch, fn, n=20, warm=3):
+def _time_launches(torch, fn, n=20, warm=3, flush=None):
+    """Median of n launches, each between its own pair of HIP events.  With
+    flush (a device buffer), the buffer is overwritten before every launch,
+    outside the events, so no input is left in L2 or the MALL ("cold")."""
     for _ in range(warm):
         fn()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n)]
-    for a, b in ev:
+    for i, (a, b) in enumerate(ev):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
         a.record()
         fn()
         b.record()
@@ -388,10 +393,18 @@ def table(torch, np, bsa, workloads, oracle_s):
                                                    wv.cube_elems, wv.kv_tile,
                                                    bsa.MASK_KV_VALID_COUNT, kvv, wv.scale,
                                                    out=o, lse=lse))
+    # cold: a 1 GiB buffer (four times the 256 MB MALL) written before each launch
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    ms_cold = _time_launches(torch, lambda: bsa.bsa_fwd(st["q"], st["k"], st["v"], mlv, flv,
+                                                        wv.cube_elems, wv.kv_tile,
+                                                        bsa.MASK_KV_VALID_COUNT, kvv, wv.scale,
+                                                        out=o, lse=lse), n=10, flush=flush)
+    del flush
     err = _MaxErr()
     cpu = (_cpu_baseline(np, st, "video", oracle_s, gpu_out=(o, lse), err=err)["value"]
            if oracle_s > 0 else None)
     emit("video (B1 H24 86016 rows d128, 256x128, 11.9 %)", ms, flops, cpu, err)
+    emit("video, cold (1 GiB written before each launch)", ms_cold, flops, None, _MaxErr())
 
 
 def main():
