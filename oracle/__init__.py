@@ -8,8 +8,9 @@ Every function here is pinned by CPU tests (tests/test_oracle_*.py) against
 page examples, closed forms, brute force and library routines; none is
 "parity unpinned".
 """
-from .attention import (MASK_CAUSAL, MASK_KV_VALID_COUNT, MASK_NONE,  # noqa: F401
-                        blocksparse_attention, dense_attention, expand_element_mask,
-                        mask_mod_keep, softmax_weights, varlen_blocksparse_attention)
+from .attention import (MASK_CAUSAL, MASK_KV_VALID_COUNT, MASK_LOCAL, MASK_NONE,  # noqa: F401
+                        block_sparsity, blocksparse_attention, dense_attention,
+                        expand_element_mask, mask_mod_keep, softmax_weights,
+                        varlen_blocksparse_attention)
 from .metadata import (cdiv, expand_kv_blocks, index_to_mask, mask_to_index,  # noqa: F401
                        pack_varlen_lists, varlen_offsets)

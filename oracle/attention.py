@@ -34,16 +34,22 @@ from .metadata import cdiv, varlen_offsets
 MASK_NONE = 0
 MASK_CAUSAL = 1
 MASK_KV_VALID_COUNT = 2
+MASK_LOCAL = 3
 
 
 def mask_mod_keep(mask_mod: int, rows: np.ndarray, cols: np.ndarray,
-                  block_kv: int, kv_valid: Optional[np.ndarray]) -> np.ndarray:
+                  block_kv: int, kv_valid: Optional[np.ndarray],
+                  window: Optional[Tuple[int, int]] = None) -> np.ndarray:
     """Element mask of a mask-list block, keep[r, c] for the given absolute
     (sequence-local) row and column ids.
 
     causal: keep c <= r (q_idx >= kv_idx).  kv valid count (FastVideo PR
     #1354 review: kv_blk = n // block, kv_off = n % block, valid =
-    kv_sizes[kv_blk]): keep kv_off < valid.
+    kv_sizes[kv_blk]): keep kv_off < valid.  local ("Dense FlashAttention vs
+    Block-Sparse Attention", section 6: the causal/local range a selected
+    block must fall in), window = (left, right) in tokens: keep
+    r - left <= c <= r + right; a negative bound is unbounded, so (-1, 0) is
+    causal and (-1, -1) keeps everything.
     """
     rows = np.asarray(rows)
     cols = np.asarray(cols)
@@ -56,7 +62,42 @@ def mask_mod_keep(mask_mod: int, rows: np.ndarray, cols: np.ndarray,
             raise ValueError("kv valid-count mask needs kv_valid")
         keep = (cols % block_kv) < np.asarray(kv_valid)[cols // block_kv]
         return np.broadcast_to(keep[None, :], (rows.size, cols.size)).copy()
+    if mask_mod == MASK_LOCAL:
+        if window is None:
+            raise ValueError("local mask needs window=(left, right)")
+        left, right = window
+        d = rows[:, None].astype(np.int64) - cols[None, :].astype(np.int64)  # r - c
+        keep = np.ones(d.shape, bool)
+        if left >= 0:
+            keep &= d <= left
+        if right >= 0:
+            keep &= -d <= right
+        return keep
     raise ValueError(f"unknown mask_mod {mask_mod}")
+
+
+def block_sparsity(mask_mod: int, Sq: int, Sk: int, block_q: int, block_kv: int,
+                   window: Optional[Tuple[int, int]] = None,
+                   kv_valid: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Classify every (Q block m, KV block n) of an Sq x Sk problem under an
+    element mask_mod, the way flash-attention's compute_block_sparsity turns a
+    mask_mod into block-sparse tensors (PR #2224 description and review):
+    full[m, n] = 1 when every element of the block (clipped to Sq x Sk) is
+    kept, part[m, n] = 1 when some but not all are, both 0 when none is.
+    Element by element over each block; returns uint8 [M, N] masks."""
+    M, N = cdiv(Sq, block_q), cdiv(Sk, block_kv)
+    full = np.zeros((M, N), np.uint8)
+    part = np.zeros((M, N), np.uint8)
+    for m in range(M):
+        rows = np.arange(m * block_q, min((m + 1) * block_q, Sq))
+        for n in range(N):
+            cols = np.arange(n * block_kv, min((n + 1) * block_kv, Sk))
+            keep = mask_mod_keep(mask_mod, rows, cols, block_kv, kv_valid, window)
+            if keep.all():
+                full[m, n] = 1
+            elif keep.any():
+                part[m, n] = 1
+    return full, part
 
 
 def _softmax_rows(S: np.ndarray, V: np.ndarray):
@@ -80,7 +121,7 @@ def _softmax_rows(S: np.ndarray, V: np.ndarray):
 
 
 def _q_block(q, k, v, b, h, i, full_row, part_row, bq, bk, Sq, Sk, mask_mod,
-             kv_valid, scale, Hkv, H, want_weights=False):
+             kv_valid, scale, Hkv, H, want_weights=False, window=None):
     """One (b, h, Q block i): gather the listed KV blocks, mask, softmax."""
     hk = h * Hkv // H
     r0, r1 = i * bq, min((i + 1) * bq, Sq)
@@ -98,7 +139,7 @@ def _q_block(q, k, v, b, h, i, full_row, part_row, bq, bk, Sq, Sk, mask_mod,
         if full_row[j]:
             keep = np.ones((rows.size, cols.size), bool)
         else:
-            keep = mask_mod_keep(mask_mod, rows, cols, bk, kv_valid)
+            keep = mask_mod_keep(mask_mod, rows, cols, bk, kv_valid, window)
         cols_parts.append(cols)
         keep_parts.append(keep)
     if cols_parts:
@@ -119,7 +160,8 @@ def blocksparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                           full: np.ndarray, part: np.ndarray, block_q: int,
                           block_kv: int, mask_mod: int, scale: float,
                           kv_valid: Optional[np.ndarray] = None,
-                          q_blocks: Optional[Iterable[Tuple[int, int, int]]] = None):
+                          q_blocks: Optional[Iterable[Tuple[int, int, int]]] = None,
+                          window: Optional[Tuple[int, int]] = None):
     """Batched block-sparse attention forward in float64.
 
     q [B,Sq,H,D], k/v [B,Sk,Hkv,D]; full/part dense block masks [B,H,M,N]
@@ -145,14 +187,14 @@ def blocksparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     for (b, h, i) in q_blocks:
         rows, o, lse = _q_block(q, k, v, b, h, i, full[b, h, i], part[b, h, i],
                                 block_q, block_kv, Sq, Sk, mask_mod, kv_valid,
-                                scale, Hkv, H)
+                                scale, Hkv, H, window=window)
         O[b, rows, h, :] = o
         LSE[b, h, rows] = lse
     return O, LSE
 
 
 def softmax_weights(q, k, v, full, part, block_q, block_kv, mask_mod, scale,
-                    b, h, i, kv_valid=None):
+                    b, h, i, kv_valid=None, window=None):
     """Row softmax weights of one Q block over its gathered columns (for the
     sum-to-one invariant).  Returns (rows, cols, W)."""
     q = np.asarray(q, np.float64)
@@ -162,13 +204,14 @@ def softmax_weights(q, k, v, full, part, block_q, block_kv, mask_mod, scale,
     _, Sk, Hkv, _ = k.shape
     rows, _, _, W, C = _q_block(q, k, v, b, h, i, full[b, h, i], part[b, h, i],
                                 block_q, block_kv, Sq, Sk, mask_mod, kv_valid,
-                                scale, Hkv, H, want_weights=True)
+                                scale, Hkv, H, want_weights=True, window=window)
     return rows, C, W
 
 
 def expand_element_mask(full: np.ndarray, part: np.ndarray, block_q: int,
                         block_kv: int, Sq: int, Sk: int, mask_mod: int,
-                        kv_valid: Optional[np.ndarray] = None) -> np.ndarray:
+                        kv_valid: Optional[np.ndarray] = None,
+                        window: Optional[Tuple[int, int]] = None) -> np.ndarray:
     """Block masks -> dense element mask [B,H,Sq,Sk], element by element with
     plain Python loops (tiny inputs only)."""
     B, H = full.shape[:2]
@@ -187,6 +230,10 @@ def expand_element_mask(full: np.ndarray, part: np.ndarray, block_q: int,
                             out[b, h, r, c] = c <= r
                         elif mask_mod == MASK_KV_VALID_COUNT:
                             out[b, h, r, c] = (c % block_kv) < kv_valid[j]
+                        elif mask_mod == MASK_LOCAL:
+                            left, right = window
+                            out[b, h, r, c] = ((left < 0 or r - c <= left) and
+                                               (right < 0 or c - r <= right))
     return out
 
 
@@ -217,7 +264,8 @@ def varlen_blocksparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                                  full: List[np.ndarray], part: List[np.ndarray],
                                  block_q: int, block_kv: int, mask_mod: int,
                                  scale: float, kv_valid=None,
-                                 q_blocks: Optional[Iterable[Tuple[int, int, int]]] = None):
+                                 q_blocks: Optional[Iterable[Tuple[int, int, int]]] = None,
+                                 window: Optional[Tuple[int, int]] = None):
     """Packed varlen forward (PR #2224): each sequence b is an independent
     batch-1 problem with sequence-local row/column ids.  q [Tq,H,D],
     k/v [Tk,Hkv,D]; full[b]/part[b] dense per-sequence block masks [H,M_b,N_b].
@@ -245,7 +293,8 @@ def varlen_blocksparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
         vb = v[None, ck[b]:ck[b + 1]]
         o, lse = blocksparse_attention(qb, kb, vb, full[b][None], part[b][None],
                                        block_q, block_kv, mask_mod, scale, kv_valid,
-                                       q_blocks=None if sel is None else sel[b])
+                                       q_blocks=None if sel is None else sel[b],
+                                       window=window)
         O[cq[b]:cq[b + 1]] = o[0]
         LSE[:, cq[b]:cq[b + 1]] = lse[0]
     return O, LSE
