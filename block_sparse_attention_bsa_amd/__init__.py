@@ -16,14 +16,16 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 __all__ = [
-    "MASK_NONE", "MASK_CAUSAL", "MASK_KV_VALID_COUNT", "BsaError",
+    "MASK_NONE", "MASK_CAUSAL", "MASK_KV_VALID_COUNT", "MASK_LOCAL", "BsaError",
     "bsa_fwd", "bsa_varlen_fwd", "bsa_mask_to_index", "bsa_varlen_mask_to_index",
-    "bsa_varlen_offsets", "bsa_expand_kv_blocks", "bsa_status_str", "library_path", "load_library",
+    "bsa_varlen_offsets", "bsa_expand_kv_blocks", "bsa_block_sparsity", "bsa_status_str",
+    "library_path", "load_library",
 ]
 
 MASK_NONE = 0
 MASK_CAUSAL = 1
 MASK_KV_VALID_COUNT = 2
+MASK_LOCAL = 3
 FLAG_VALIDATE = 1
 
 BSA_OK = 0
@@ -58,7 +60,16 @@ class _BlockList(ctypes.Structure):
 
 class _BlockSparse(ctypes.Structure):
     _fields_ = [("mask", _BlockList), ("full", _BlockList),
-                ("block_q", ctypes.c_int32), ("block_kv", ctypes.c_int32)]
+                ("block_q", ctypes.c_int32), ("block_kv", ctypes.c_int32),
+                ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32)]
+
+
+def _window(mask_mod: int, window) -> Tuple[int, int]:
+    if mask_mod != MASK_LOCAL:
+        return -1, -1
+    if window is None or len(window) != 2:
+        raise ValueError("MASK_LOCAL needs window=(left, right) (a negative bound is unbounded)")
+    return int(window[0]), int(window[1])
 
 
 def library_path() -> str:
@@ -87,10 +98,11 @@ def load_library():
     I32P = ctypes.POINTER(ctypes.c_int32)
     lib.bsa_varlen_offsets.argtypes = [I32P, I32P, I32, I32, I32, I32P, I32P, I32P, I32P]
     lib.bsa_expand_kv_blocks.argtypes = [P, P, I32, I32, I32, I32, P, P, P, P]
+    lib.bsa_block_sparsity.argtypes = [ctypes.c_int, I32, I32, P, I32, I32, I32, I32, P, P, P]
     lib.bsa_status_str.argtypes = [ctypes.c_int]
     lib.bsa_status_str.restype = ctypes.c_char_p
     for fn in ("bsa_fwd", "bsa_varlen_fwd", "bsa_mask_to_index", "bsa_varlen_mask_to_index",
-               "bsa_varlen_offsets", "bsa_expand_kv_blocks"):
+               "bsa_varlen_offsets", "bsa_expand_kv_blocks", "bsa_block_sparsity"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -169,14 +181,15 @@ def bsa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             block_q: int, block_kv: int, mask_mod: int = MASK_NONE,
             kv_valid: Optional[torch.Tensor] = None, softmax_scale: Optional[float] = None,
             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-            validate: bool = False):
+            validate: bool = False, window: Optional[Tuple[int, int]] = None):
     """Batched block-sparse attention forward.
 
     q [B,Sq,H,D], k/v [B,Sk,Hkv,D] (bf16 or fp32, head_dim contiguous, any
     other strides, e.g. BSHD or a BHSD tensor permuted to this view).
     mask_list / full_list: (cnt int32 [B|1,H|1,M], idx int32 [B|1,H|1,M,N])
     with M = ceil(Sq/block_q), N = ceil(Sk/block_kv); a size-1 batch or head
-    dimension broadcasts.  Returns (O [B,Sq,H,D], LSE float32 [B,H,Sq]).
+    dimension broadcasts.  window=(left, right): the bounds of MASK_LOCAL.
+    Returns (O [B,Sq,H,D], LSE float32 [B,H,Sq]).
     """
     lib = load_library()
     for n, t in (("q", q), ("k", k), ("v", v)):
@@ -207,7 +220,8 @@ def bsa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         if not kv_valid.is_contiguous() or kv_valid.numel() < N:
             raise ValueError(f"kv_valid must be a contiguous int32 tensor with {N} entries")
     bs = _BlockSparse(_block_list(mask_list, True, (B, H, M, N)),
-                      _block_list(full_list, True, (B, H, M, N)), int(block_q), int(block_kv))
+                      _block_list(full_list, True, (B, H, M, N)), int(block_q), int(block_kv),
+                      *_window(mask_mod, window))
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     st = lib.bsa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _DTYPES[q.dtype],
                      B, H, Hkv, Sq, Sk, D,
@@ -229,7 +243,8 @@ def bsa_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    full_list: Optional[Tuple[torch.Tensor, torch.Tensor]],
                    block_q: int, block_kv: int, mask_mod: int = MASK_NONE,
                    softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                   lse: Optional[torch.Tensor] = None, validate: bool = False):
+                   lse: Optional[torch.Tensor] = None, validate: bool = False,
+                   window: Optional[Tuple[int, int]] = None):
     """Packed varlen forward.  q [Tq,H,D], k/v [Tk,Hkv,D]; lists (cnt int32
     [H,total_m_blocks], idx int32 [H,total_n_blocks]); cu arrays int32 [B+1]
     on the device; the two totals are host ints.  Returns (O [Tq,H,D],
@@ -268,7 +283,7 @@ def bsa_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise ValueError("totals must be non-negative")
     shp = (H, int(total_m_blocks), int(total_n_blocks))
     bs = _BlockSparse(_block_list(mask_list, False, shp), _block_list(full_list, False, shp),
-                      int(block_q), int(block_kv))
+                      int(block_q), int(block_kv), *_window(mask_mod, window))
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     st = lib.bsa_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _DTYPES[q.dtype],
                             B, H, Hkv, D, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
@@ -365,3 +380,30 @@ def bsa_expand_kv_blocks(block_mask: torch.Tensor, block_valid: torch.Tensor, fa
                                   _stream(block_mask))
     _check("bsa_expand_kv_blocks", st)
     return full, part, kvv
+
+
+def bsa_block_sparsity(mask_mod: int, Sq: int, Sk: int, block_q: int, block_kv: int,
+                       window: Optional[Tuple[int, int]] = None,
+                       kv_valid: Optional[torch.Tensor] = None,
+                       device: Optional[torch.device] = None):
+    """Classify the (Q block, KV block) grid of an Sq x Sk problem under an
+    element mask_mod: returns (full, part) uint8 [ceil(Sq/block_q),
+    ceil(Sk/block_kv)] on the device (1 = every / some but not every element
+    kept).  bsa_mask_to_index turns them into the full and mask lists."""
+    lib = load_library()
+    if block_q <= 0 or block_kv <= 0 or Sq < 0 or Sk < 0:
+        raise ValueError("sizes must be non-negative and block sizes positive")
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    if kv_valid is not None:
+        _dev("kv_valid", kv_valid, torch.int32)
+        dev = kv_valid.device
+    M, N = -(-Sq // block_q), -(-Sk // block_kv)
+    full = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    part = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    wl, wr = _window(mask_mod, window)
+    with torch.cuda.device(dev):
+        st = lib.bsa_block_sparsity(int(mask_mod), wl, wr, _ptr(kv_valid), int(Sq), int(Sk),
+                                    int(block_q), int(block_kv), _ptr(full), _ptr(part),
+                                    _stream(full))
+    _check("bsa_block_sparsity", st)
+    return full, part

@@ -26,8 +26,9 @@ bool supported_head_dim(int D) { return D == 64 || D == 96 || D == 128 || D == 1
 // 32 rows fit two per SIMD), and a larger Q block is covered by
 // block_q / tile_m workgroups that share its block-list row.  KV blocks of
 // any size are cut into 64-key sub-tiles inside the kernel.
-int fit_tile_m(int block_q, int D, bool f32_in) {
-  if (block_q % 256 == 0 && D <= 128 && !f32_in) return 256;
+int fit_tile_m(int block_q, int D, bool f32_in, int mask_mod) {
+  // the 256-row kernel knows the causal and valid-count masks only
+  if (block_q % 256 == 0 && D <= 128 && !f32_in && mask_mod != BSA_MASK_LOCAL) return 256;
   if (block_q % 128 == 0) return 128;
   if (block_q % 64 == 0) return 64;
   if (block_q % 32 == 0) return 32;
@@ -209,13 +210,13 @@ bsa_status bsa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   if (B < 0 || H <= 0 || H_kv <= 0 || Sq < 0 || Sk < 0 || H % H_kv != 0)
     return BSA_ERR_INVALID_ARGUMENT;
   if (dt != BSA_BF16 && dt != BSA_F32) return BSA_ERR_INVALID_ARGUMENT;
-  if (mask_mod < BSA_MASK_NONE || mask_mod > BSA_MASK_KV_VALID_COUNT) return BSA_ERR_INVALID_ARGUMENT;
+  if (mask_mod < BSA_MASK_NONE || mask_mod > BSA_MASK_LOCAL) return BSA_ERR_INVALID_ARGUMENT;
   if (!bs || !q_str || !k_str || !v_str || !o_str) return BSA_ERR_INVALID_ARGUMENT;
   if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f)) return BSA_ERR_INVALID_ARGUMENT;
   if (bs->block_q <= 0 || bs->block_kv <= 0) return BSA_ERR_INVALID_ARGUMENT;
   if (!list_ok(bs->mask) || !list_ok(bs->full)) return BSA_ERR_INVALID_ARGUMENT;
   if (!supported_head_dim(D)) return BSA_ERR_UNSUPPORTED;
-  const int tile_m = fit_tile_m(bs->block_q, D, dt == BSA_F32);
+  const int tile_m = fit_tile_m(bs->block_q, D, dt == BSA_F32, mask_mod);
   if (tile_m == 0) return BSA_ERR_UNSUPPORTED;
   if ((int64_t)B * H * Sq == 0) return BSA_OK;  // nothing to write
   if (!q || !k || !v || !o || !lse) return BSA_ERR_INVALID_ARGUMENT;
@@ -257,6 +258,8 @@ bsa_status bsa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   p.block_kv = bs->block_kv;
   p.qsub = bs->block_q / tile_m;
   p.mask_mod = mask_mod;
+  p.win_left = bs->window_left;
+  p.win_right = bs->window_right;
   p.varlen = 0;
   p.tiles_per_head = (int32_t)tiles_per_head;
   p.lse_ld = Sq;
@@ -279,7 +282,7 @@ bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, 
       total_q < 0)
     return BSA_ERR_INVALID_ARGUMENT;
   if (dt != BSA_BF16 && dt != BSA_F32) return BSA_ERR_INVALID_ARGUMENT;
-  if (mask_mod != BSA_MASK_NONE && mask_mod != BSA_MASK_CAUSAL) {
+  if (mask_mod != BSA_MASK_NONE && mask_mod != BSA_MASK_CAUSAL && mask_mod != BSA_MASK_LOCAL) {
     if (mask_mod == BSA_MASK_KV_VALID_COUNT) return BSA_ERR_UNSUPPORTED;
     return BSA_ERR_INVALID_ARGUMENT;
   }
@@ -288,7 +291,7 @@ bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, 
   if (bs->block_q <= 0 || bs->block_kv <= 0) return BSA_ERR_INVALID_ARGUMENT;
   if (!list_ok(bs->mask) || !list_ok(bs->full)) return BSA_ERR_INVALID_ARGUMENT;
   if (!supported_head_dim(D)) return BSA_ERR_UNSUPPORTED;
-  const int tile_m = fit_tile_m(bs->block_q, D, dt == BSA_F32);
+  const int tile_m = fit_tile_m(bs->block_q, D, dt == BSA_F32, mask_mod);
   if (tile_m == 0) return BSA_ERR_UNSUPPORTED;
   if (B == 0 || total_m_blocks == 0) return BSA_OK;
   if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k || !cu_total_m_blocks ||
@@ -331,6 +334,8 @@ bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, 
   p.block_kv = bs->block_kv;
   p.qsub = qsub;
   p.mask_mod = mask_mod;
+  p.win_left = bs->window_left;
+  p.win_right = bs->window_right;
   p.varlen = 1;
   p.tiles_per_head = (int32_t)tiles_per_head;
   p.total_m = total_m_blocks;
@@ -339,6 +344,22 @@ bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, 
   p.num_tiles = (int32_t)tiles;
   p.c = softmax_scale * kLog2e;
   const hipError_t e = bsa::launch_fwd(p, D, tile_m, dt == BSA_F32, stream);
+  return e == hipSuccess ? BSA_OK : BSA_ERR_HIP;
+}
+
+bsa_status bsa_block_sparsity(bsa_mask_mod mask_mod, int32_t window_left, int32_t window_right,
+                              const int32_t* kv_valid, int32_t Sq, int32_t Sk, int32_t block_q,
+                              int32_t block_kv, uint8_t* full, uint8_t* part,
+                              hipStream_t stream) {
+  if (mask_mod < BSA_MASK_NONE || mask_mod > BSA_MASK_LOCAL) return BSA_ERR_INVALID_ARGUMENT;
+  if (Sq < 0 || Sk < 0 || block_q <= 0 || block_kv <= 0) return BSA_ERR_INVALID_ARGUMENT;
+  const int64_t M = cdiv64(Sq, block_q), N = cdiv64(Sk, block_kv);
+  if (M * N == 0) return BSA_OK;
+  if (M * N > std::numeric_limits<int32_t>::max()) return BSA_ERR_UNSUPPORTED;
+  if (!full || !part) return BSA_ERR_INVALID_ARGUMENT;
+  if (mask_mod == BSA_MASK_KV_VALID_COUNT && !kv_valid) return BSA_ERR_INVALID_ARGUMENT;
+  const hipError_t e = bsa::launch_block_sparsity(mask_mod, window_left, window_right, kv_valid, Sq,
+                                                  Sk, block_q, block_kv, full, part, stream);
   return e == hipSuccess ? BSA_OK : BSA_ERR_HIP;
 }
 

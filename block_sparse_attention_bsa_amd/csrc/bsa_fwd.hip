@@ -140,7 +140,9 @@ struct FwdCfg {
   }
 };
 
-template <int D, int NW>
+// LOCAL: the local mask_mod's key range on mask-list sub-tiles (a separate
+// instance, so the others keep the plain causal test).
+template <int D, int NW, bool LOCAL>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(FwdCfg<D, NW>::WAVES_PER_EU)))
 void bsa_fwd_kernel(const FwdParams p) {
@@ -277,6 +279,10 @@ void bsa_fwd_kernel(const FwdParams p) {
     for (int db = 0; db < DB; ++db) vx[db] = (vbase + 16 * C::vswz(vkey)) ^ (64 * db);
   }
 
+  // element mask of mask-list sub-tiles (causal or local): this row's kept keys
+  const bool list_masked = LOCAL || p.mask_mod == kMaskCausal;
+  int mlo = 0, mhi = qrow;
+  if constexpr (LOCAL) row_key_range(kMaskLocal, p.win_left, p.win_right, qrow, mlo, mhi);
   auto compute = [&](int stage, const Item& it) {
     const uint4* kl = smem + stage * C::STAGE_SLOTS;
     const uint4* vl = kl + C::KSLOTS;
@@ -309,7 +315,7 @@ void bsa_fwd_kernel(const FwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     uint32_t pk0[8], pk1[8];
-    softmax_step<DB>(s0, s1, it, it.is_mask && p.mask_mod == kMaskCausal, qrow, h32, p.c, m_run,
+    softmax_step<DB, LOCAL>(s0, s1, it, it.is_mask && list_masked, mlo, mhi, h32, p.c, m_run,
                      l_run, oacc, pk0, pk1);
     // PV step i: keys 16*(i / DB) .., head dims 32*(i % DB) ..
     auto vld = [&](int i) {
@@ -386,8 +392,10 @@ template <int D, int NW>
 hipError_t launch_one(const FwdParams& p, hipStream_t s) {
   FwdParams copy = p;
   void* args[] = {&copy};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW>),
-                         dim3(p.num_tiles), dim3(NW * 64), args, 0, s);
+  const void* k = p.mask_mod == kMaskLocal
+                      ? reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, true>)
+                      : reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, false>);
+  return hipLaunchKernel(k, dim3(p.num_tiles), dim3(NW * 64), args, 0, s);
 }
 
 template <int D>

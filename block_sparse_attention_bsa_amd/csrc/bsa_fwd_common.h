@@ -30,7 +30,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr int kMaskNone = 0, kMaskCausal = 1, kMaskKvValid = 2;
+constexpr int kMaskNone = 0, kMaskCausal = 1, kMaskKvValid = 2, kMaskLocal = 3;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
@@ -220,19 +220,28 @@ __device__ __forceinline__ bool advance(Item& it, ListWalk& L, int lane, int Sk)
 // mask, updates the running max m (base-2 units of scale*s) and the running
 // sum l (fp32 P), rescales O only when some row's max grew, and returns P
 // rounded to bf16 in pk0/pk1 (pairs of consecutive accumulators).
-template <int DB>
+// masked: a mask-list sub-tile under the causal (RANGE false) or local
+// (RANGE true) mask_mod; its kept keys of this lane's row are key <= mhi
+// (causal: mhi = qrow) or mlo <= key <= mhi (local, absolute ids;
+// row_key_range gives them).  The valid-count mask is already in it.nk.
+template <int DB, bool RANGE = false>
 __device__ __forceinline__ void softmax_step(f32x16_t& s0, f32x16_t& s1, const Item& it,
-                                             bool causal, int qrow, int h32, float c, float& m_run,
-                                             float& l_run, f32x16_t (&oacc)[DB], uint32_t (&pk0)[8],
-                                             uint32_t (&pk1)[8]) {
-  if (causal || it.nk < kKvTile) {
+                                             bool masked, int mlo, int mhi, int h32, float c,
+                                             float& m_run, float& l_run, f32x16_t (&oacc)[DB],
+                                             uint32_t (&pk0)[8], uint32_t (&pk1)[8]) {
+  if (masked || it.nk < kKvTile) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = 16 * (r >> 3) + 8 * h32 + (r & 7);
       bool keep0 = key < it.nk, keep1 = key + 32 < it.nk;
-      if (causal) {
-        keep0 = keep0 && (it.key0 + key <= qrow);
-        keep1 = keep1 && (it.key0 + key + 32 <= qrow);
+      if (masked) {
+        const int c0 = it.key0 + key, c1 = c0 + 32;
+        keep0 = keep0 && c0 <= mhi;
+        keep1 = keep1 && c1 <= mhi;
+        if constexpr (RANGE) {
+          keep0 = keep0 && c0 >= mlo;
+          keep1 = keep1 && c1 >= mlo;
+        }
       }
       if (!keep0) s0[r] = neg_inf();
       if (!keep1) s1[r] = neg_inf();
@@ -272,6 +281,21 @@ __device__ __forceinline__ void softmax_step(f32x16_t& s0, f32x16_t& s1, const I
     ls += (a0 + a1) + (b0 + b1);
   }
   l_run += ls;
+}
+
+// Keys [lo, hi] of row qrow that the causal (kMaskCausal: key <= qrow) or
+// local (kMaskLocal: qrow - wl <= key <= qrow + wr, a negative bound
+// unbounded) mask_mod keeps; [0, INT_MAX] for the others.
+__device__ __forceinline__ void row_key_range(int mask_mod, int wl, int wr, int qrow, int& lo,
+                                              int& hi) {
+  lo = 0;
+  hi = 0x7fffffff;
+  if (mask_mod == kMaskCausal) {
+    hi = qrow;
+  } else if (mask_mod == kMaskLocal) {
+    if (wl >= 0) lo = qrow - wl;
+    if (wr >= 0) hi = qrow + min(wr, 0x7fffffff - qrow);
+  }
 }
 
 // B operand of PV step ps (keys 16*ps .. 16*ps+15): lane half h32 supplies

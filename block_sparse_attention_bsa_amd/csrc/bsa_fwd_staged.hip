@@ -152,6 +152,10 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_staged_kernel(const FwdParams
   };
 
   const int arow = swap_b23(l32);
+  // element mask of mask-list sub-tiles (causal or local): this row's kept keys
+  const bool list_masked = p.mask_mod == kMaskCausal || p.mask_mod == kMaskLocal;
+  int mlo, mhi;
+  row_key_range(p.mask_mod, p.win_left, p.win_right, qrow, mlo, mhi);
   auto compute = [&](const unsigned char* Kb, const unsigned char* Vb, const Item& it) {
     f32x16_t s0, s1;
 #pragma unroll
@@ -168,7 +172,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_staged_kernel(const FwdParams
       s1 = mfma32(a1, qf[ks], s1);
     }
     uint32_t pk0[8], pk1[8];
-    softmax_step<DB>(s0, s1, it, it.is_mask && p.mask_mod == kMaskCausal, qrow, h32, p.c, m_run,
+    softmax_step<DB, true>(s0, s1, it, it.is_mask && list_masked, mlo, mhi, h32, p.c, m_run,
                      l_run, oacc, pk0, pk1);
 #pragma unroll
     for (int ps = 0; ps < 4; ++ps) {

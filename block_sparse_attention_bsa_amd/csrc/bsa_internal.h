@@ -43,6 +43,7 @@ struct FwdParams {
   int32_t lse_ld;          // batched: Sq; varlen: total_q
   int32_t num_tiles;       // grid size
   float c;                 // softmax_scale * log2(e)
+  int32_t win_left, win_right;  // local mask_mod bounds (negative = unbounded)
 };
 
 // Launch the forward kernel instance for (D, rows per workgroup, dtype):
@@ -62,6 +63,10 @@ hipError_t launch_varlen_mask_to_index(const uint8_t* mask, int32_t H, int32_t B
                                        const int32_t* cu_m, const int32_t* off,
                                        int32_t total_m, int32_t total_n,
                                        int32_t* cnt, int32_t* idx, hipStream_t s);
+
+hipError_t launch_block_sparsity(int32_t mask_mod, int32_t win_left, int32_t win_right,
+                                 const int32_t* kv_valid, int32_t Sq, int32_t Sk, int32_t block_q,
+                                 int32_t block_kv, uint8_t* full, uint8_t* part, hipStream_t s);
 
 hipError_t launch_expand_kv_blocks(const uint8_t* block_mask, const int32_t* block_valid,
                                    int32_t R, int32_t NL, int32_t factor, int32_t child,

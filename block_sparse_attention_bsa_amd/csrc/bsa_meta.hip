@@ -1,5 +1,6 @@
 // Metadata kernels for gfx950: dense block mask -> block lists (batched and
-// packed varlen rows) and the split of logical KV blocks into child tiles.
+// packed varlen rows), the split of logical KV blocks into child tiles, and
+// the full / partial classification of blocks under an element mask_mod.
 //
 // mask -> index follows the conversion "Dense FlashAttention vs Block-Sparse
 // Attention" (section 2) describes: per Q-block row, the selected KV-block
@@ -96,7 +97,57 @@ __global__ __launch_bounds__(256) void expand_kv_blocks_kernel(
   }
 }
 
+// Full / partial / empty class of block (m, n) under an element mask_mod
+// (the role of flash-attention's compute_block_sparsity).  Causal and local
+// masks keep a cell by the difference d = row - col alone: causal keeps
+// d >= 0, local keeps -wr <= d <= wl (a negative bound is unbounded).  Over
+// the block's rows [r0, r1) and columns [c0, c1) the differences are every
+// integer in [r0 - (c1 - 1), (r1 - 1) - c0], so the block is full when that
+// range lies inside the kept one and empty when the two do not meet.  The
+// valid-count mask keeps the first kv_valid[n] columns of KV block n.
+__global__ __launch_bounds__(256) void block_sparsity_kernel(
+    int32_t mm, int32_t wl, int32_t wr, const int32_t* __restrict__ kv_valid, int32_t Sq,
+    int32_t Sk, int32_t bq, int32_t bk, int32_t M, int32_t N, uint8_t* __restrict__ full,
+    uint8_t* __restrict__ part) {
+  const int64_t n_all = (int64_t)M * N;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; x < n_all; x += stride) {
+    const int m = (int)(x / N), n = (int)(x % N);
+    const int64_t r0 = (int64_t)m * bq, r1 = min((int64_t)(m + 1) * bq, (int64_t)Sq);
+    const int64_t c0 = (int64_t)n * bk, c1 = min((int64_t)(n + 1) * bk, (int64_t)Sk);
+    bool all = true, any = true;
+    if (mm == 1 || mm == 3) {
+      const int64_t dmin = r0 - (c1 - 1), dmax = (r1 - 1) - c0;
+      // kept differences [lo, hi]
+      const int64_t lo = mm == 1 ? 0 : (wr < 0 ? INT64_MIN / 2 : -(int64_t)wr);
+      const int64_t hi = mm == 1 ? INT64_MAX / 2 : (wl < 0 ? INT64_MAX / 2 : (int64_t)wl);
+      all = dmin >= lo && dmax <= hi;
+      any = dmax >= lo && dmin <= hi;
+    } else if (mm == 2) {
+      const int64_t v = kv_valid[n];
+      all = v >= c1 - c0;
+      any = v > 0;
+    }
+    full[x] = all ? 1 : 0;
+    part[x] = (any && !all) ? 1 : 0;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_block_sparsity(int32_t mask_mod, int32_t win_left, int32_t win_right,
+                                 const int32_t* kv_valid, int32_t Sq, int32_t Sk, int32_t block_q,
+                                 int32_t block_kv, uint8_t* full, uint8_t* part, hipStream_t s) {
+  const int32_t M = (int32_t)(((int64_t)Sq + block_q - 1) / block_q);
+  const int32_t N = (int32_t)(((int64_t)Sk + block_kv - 1) / block_kv);
+  const int64_t work = (int64_t)M * N;
+  if (work <= 0) return hipSuccess;
+  int64_t blocks = (work + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(block_sparsity_kernel, dim3((unsigned)blocks), dim3(256), 0, s, mask_mod,
+                     win_left, win_right, kv_valid, Sq, Sk, block_q, block_kv, M, N, full, part);
+  return hipGetLastError();
+}
 
 hipError_t launch_mask_to_index(const uint8_t* mask, int64_t rows, int32_t N, int32_t* cnt,
                                 int32_t* idx, hipStream_t s) {

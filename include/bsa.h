@@ -67,7 +67,11 @@ typedef enum {
 typedef enum {
   BSA_MASK_NONE = 0,           /* mask-list blocks behave like full blocks */
   BSA_MASK_CAUSAL = 1,         /* keep kv_idx <= q_idx (sequence-local ids in varlen) */
-  BSA_MASK_KV_VALID_COUNT = 2  /* keep (kv_idx % block_kv) < kv_valid[kv_idx / block_kv] */
+  BSA_MASK_KV_VALID_COUNT = 2, /* keep (kv_idx % block_kv) < kv_valid[kv_idx / block_kv] */
+  BSA_MASK_LOCAL = 3           /* keep q_idx - window_left <= kv_idx <= q_idx + window_right
+                                  (sequence-local ids in varlen); a negative bound is unbounded,
+                                  so (-1, 0) is causal.  The causal/local range of "Dense
+                                  FlashAttention vs Block-Sparse Attention", section 6. */
 } bsa_mask_mod;
 
 /* Copy the block lists to the host, check them (ids in range, no repeats
@@ -93,12 +97,16 @@ typedef struct {
 } bsa_block_list;
 
 /* The (mask, full) pair and the sparse block sizes (in tokens).
- * block_q must be a multiple of 32; block_kv may be any positive size. */
+ * block_q must be a multiple of 32; block_kv may be any positive size.
+ * window_left / window_right: the bounds of BSA_MASK_LOCAL (ignored by the
+ * other mask_mods). */
 typedef struct {
   bsa_block_list mask;
   bsa_block_list full;
   int32_t block_q;
   int32_t block_kv;
+  int32_t window_left;
+  int32_t window_right;
 } bsa_block_sparse;
 
 /* Batched forward.
@@ -187,6 +195,25 @@ bsa_status bsa_expand_kv_blocks(const uint8_t* block_mask, const int32_t* block_
                                 int32_t R, int32_t NL, int32_t factor, int32_t child,
                                 uint8_t* full, uint8_t* part, int32_t* kv_valid,
                                 hipStream_t stream);
+
+/* Block classification of an element mask_mod, the role of flash-attention's
+ * compute_block_sparsity (PR #2224 description and review thread): for Q block
+ * m (rows [m*block_q, min((m+1)*block_q, Sq))) and KV block n (columns
+ * [n*block_kv, min((n+1)*block_kv, Sk))) writes
+ *   full[m,n] = 1 if mask_mod keeps every element of the block,
+ *   part[m,n] = 1 if it keeps some but not all,
+ *   both 0    if it keeps none,
+ * as device uint8 [ceil(Sq/block_q), ceil(Sk/block_kv)] row-major masks.
+ * With bsa_mask_to_index they become the full and mask lists whose forward
+ * equals dense attention under the element mask (mask_mod applied to the
+ * mask list).  mask_mod: BSA_MASK_NONE (every block full), BSA_MASK_CAUSAL,
+ * BSA_MASK_LOCAL (window_left, window_right as in bsa_block_sparse) or
+ * BSA_MASK_KV_VALID_COUNT (kv_valid: device int32 [ceil(Sk/block_kv)], else
+ * ignored).  Sq, Sk >= 0, block sizes > 0.  Bit-exact; no synchronisation. */
+bsa_status bsa_block_sparsity(bsa_mask_mod mask_mod, int32_t window_left, int32_t window_right,
+                              const int32_t* kv_valid, int32_t Sq, int32_t Sk, int32_t block_q,
+                              int32_t block_kv, uint8_t* full, uint8_t* part,
+                              hipStream_t stream);
 
 /* Static string for a status code. */
 const char* bsa_status_str(bsa_status s);
