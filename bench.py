@@ -327,6 +327,49 @@ def table(torch, np, bsa, workloads, oracle_s):
             w = workloads.sparse_sweep(D, bq, bk)
             batched(f"sweep d{D} ({bq},{bk}) (B2 H16 S4096, 25 %)", w,
                     oracle_budget=oracle_s if (D, bq, bk) == (128, 128, 128) else 0)
+    # sliding window: lists from the GPU classifier of the local mask_mod
+    w = workloads.sliding_window()
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (w.q, w.k, w.v))
+    B, S, H, D = w.q.shape
+    full_c, part_c = bsa.bsa_block_sparsity(bsa.MASK_LOCAL, S, S, w.block_q, w.block_kv,
+                                            window=w.window, device=dev)
+    M, N = full_c.shape
+    fl_w = bsa.bsa_mask_to_index(full_c.reshape(1, 1, M, N).contiguous())
+    ml_w = bsa.bsa_mask_to_index(part_c.reshape(1, 1, M, N).contiguous())
+    run_w = lambda **kw: bsa.bsa_fwd(q, k, v, ml_w, fl_w, w.block_q, w.block_kv, bsa.MASK_LOCAL,
+                                     None, w.scale, window=w.window, **kw)
+    o, lse = run_w()
+    ms = _time_launches(torch, lambda: run_w(out=o, lse=lse))
+    fc, pc = full_c.cpu().numpy().astype(bool), part_c.cpu().numpy().astype(bool)
+    fl = _pairs_flops(np.broadcast_to(fc, (B, H, M, N)), np.broadcast_to(pc, (B, H, M, N)),
+                      w.block_q, w.block_kv, S, S, D)
+    cpu, err = None, _MaxErr()
+    if oracle_s > 0:
+        qo, ko, vo = (f64(t) for t in (q, k, v))
+        of, op_ = oracle.block_sparsity(oracle.MASK_LOCAL, S, S, w.block_q, w.block_kv,
+                                        window=w.window)
+        ofb = np.broadcast_to(of.astype(bool), (B, H, M, N))
+        opb = np.broadcast_to(op_.astype(bool), (B, H, M, N))
+        rng = np.random.default_rng(0)
+
+        def one():
+            pick = (int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(M)))
+            return pick, oracle.blocksparse_attention(qo, ko, vo, ofb, opb, w.block_q, w.block_kv,
+                                                      oracle.MASK_LOCAL, w.scale,
+                                                      q_blocks=[pick], window=w.window)
+
+        def check(pick, O, L):
+            b, h, i = pick
+            r = slice(i * w.block_q, min((i + 1) * w.block_q, S))
+            err.note(o[b, r, h], lse[b, h, r], O[b, r, h], L[b, h, r])
+
+        def fl_of(pick):
+            b, h, i = pick
+            return _pairs_flops(ofb[b:b + 1, h:h + 1, i:i + 1], opb[b:b + 1, h:h + 1, i:i + 1],
+                                w.block_q, w.block_kv, min(w.block_q, S - i * w.block_q), S, D)
+        cpu = _oracle_rate(one, fl_of, oracle_s, check)
+    emit(f"sliding window (B{B} H{H} S{S} d{D}, window {w.window[0]} back, 128x128, "
+         f"{100 * fl / (4.0 * D * B * H * S * S):.1f} %)", ms, fl, cpu, err)
     # varlen packed
     w = workloads.varlen_packed()
     H, bq, bk = w.q.shape[1], w.block_q, w.block_kv

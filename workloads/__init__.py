@@ -81,6 +81,22 @@ class VarlenWorkload:
 
 
 @dataclass
+class WindowWorkload:
+    """Sliding-window attention input: q/k/v [B,S,H,D] (BSHD, fp32) and the
+    local mask_mod's (left, right) window.  No block masks: the lists come
+    from classifying the window (bsa_block_sparsity on the GPU side,
+    oracle.block_sparsity on the CPU side)."""
+    name: str
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    block_q: int
+    block_kv: int
+    window: tuple
+    scale: float
+
+
+@dataclass
 class VideoWorkload:
     """Video sparse attention input at cube granularity.
 
@@ -201,6 +217,18 @@ def varlen_packed(n_seq=8, H=16, D=128, bs=128, lo=128, hi=8192, p_below=0.3,
         part.append(np.broadcast_to((jj == ii)[None], (H, M, N)).copy())
     return VarlenWorkload("varlen_packed", q, k, v, seqlens, list(seqlens), full, part,
                           bs, bs, MASK_CAUSAL, 1.0 / math.sqrt(D))
+
+
+def sliding_window(B=2, H=16, S=8192, D=128, bs=128, window=(1024, 0),
+                   seed: int = 1006) -> WindowWorkload:
+    """Causal sliding window of `window[0]` keys back (the causal/local range
+    of "Dense FlashAttention vs Block-Sparse Attention", section 6) at the
+    sweep's batch, head and head_dim scale: 1024 of 8192 keys per row is
+    about 12.5 % density, below the 25 % of the sweep."""
+    rng = np.random.default_rng(seed)
+    q, k, v = _qkv(rng, (B, S, H, D), (B, S, H, D))
+    return WindowWorkload(f"sliding_window_w{window[0]}_{window[1]}", q, k, v, bs, bs,
+                          tuple(window), 1.0 / math.sqrt(D))
 
 
 def _cube_layout(grid, cube):
