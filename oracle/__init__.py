@@ -12,5 +12,6 @@ from .attention import (MASK_CAUSAL, MASK_KV_VALID_COUNT, MASK_LOCAL, MASK_NONE,
                         block_sparsity, blocksparse_attention, dense_attention,
                         expand_element_mask, mask_mod_keep, softmax_weights,
                         varlen_blocksparse_attention)
-from .metadata import (cdiv, expand_kv_blocks, index_to_mask, mask_to_index,  # noqa: F401
+from .metadata import (bitmask_to_index, bitmask_to_mask, cdiv,  # noqa: F401
+                       expand_kv_blocks, index_to_mask, mask_to_index,
                        pack_varlen_lists, varlen_offsets)

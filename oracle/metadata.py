@@ -1,5 +1,5 @@
-"""Metadata oracle: block-mask -> index lists, varlen offsets, KV-block
-expansion.  Pure integer work, plain Python/numpy, bit-exact by definition.
+"""Metadata oracle: block-mask -> index lists, packed bitmaps, varlen
+offsets, KV-block expansion.  Pure integer work, plain Python/numpy, bit-exact by definition.
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import this
 module; only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline
@@ -35,6 +35,41 @@ def mask_to_index(mask: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
         cnt[r] = len(sel)
         idx[r, :len(sel)] = sel
     return cnt.reshape(lead), idx.reshape(lead + (N,))
+
+
+def bitmask_to_mask(words: np.ndarray, N: int, H: int | None = None) -> np.ndarray:
+    """Packed UInt32 block bitmap -> boolean block mask.
+
+    Follows the bitmap input of the PrimTS page ("proxy-compensated
+    block-sparse attention", flashinfer pull request 4872: the description's
+    bitmask paragraph and the test commit's notes): one row of 32-bit words
+    per (batch, KV head, Q block),
+    each bit selecting one KV block; bits at or beyond N in the final word
+    are padding and are ignored.  Reading taken for the bit order, which the
+    pages leave open: bit j (value 2**j) of word w selects KV block 32*w + j.
+
+    words: integer array [B, Hkv, M, W] with W = ceil(N/32), any integer
+    dtype holding the 32-bit pattern.  H: number of Q heads (a multiple of
+    Hkv, default Hkv); Q head h reads the row of KV head h // (H // Hkv).
+    Returns bool [B, H, M, N].
+    """
+    w = np.asarray(words).astype(np.int64) & 0xFFFFFFFF
+    B, Hkv, M, W = w.shape
+    if W != cdiv(N, 32):
+        raise ValueError(f"{W} words per row for {N} blocks")
+    H = Hkv if H is None else H
+    if Hkv == 0 or H % Hkv:
+        raise ValueError("H must be a multiple of Hkv")
+    n = np.arange(N)
+    bits = ((w[..., n // 32] >> (n % 32)) & 1).astype(bool)  # [B, Hkv, M, N]
+    group = H // Hkv
+    return bits[:, np.arange(H) // group]
+
+
+def bitmask_to_index(words: np.ndarray, N: int, H: int | None = None):
+    """Packed bitmap -> the (cnt, idx) block lists of mask_to_index: the
+    bitmap and index formats describe the same selection."""
+    return mask_to_index(bitmask_to_mask(words, N, H))
 
 
 def index_to_mask(cnt: np.ndarray, idx: np.ndarray, N: int) -> np.ndarray:
