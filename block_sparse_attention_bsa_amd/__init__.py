@@ -17,7 +17,8 @@ import torch
 
 __all__ = [
     "MASK_NONE", "MASK_CAUSAL", "MASK_KV_VALID_COUNT", "MASK_LOCAL", "BsaError",
-    "bsa_fwd", "bsa_varlen_fwd", "bsa_mask_to_index", "bsa_varlen_mask_to_index",
+    "bsa_fwd", "bsa_varlen_fwd", "bsa_mask_to_index", "bsa_bitmask_to_index",
+    "bsa_varlen_mask_to_index",
     "bsa_varlen_offsets", "bsa_expand_kv_blocks", "bsa_block_sparsity", "bsa_status_str",
     "library_path", "load_library",
 ]
@@ -94,6 +95,7 @@ def load_library():
                                    P, P, P, P, I32, I32, I32, I64P, I64P, I64P, I64P, BS,
                                    ctypes.c_int, F32, U32, P]
     lib.bsa_mask_to_index.argtypes = [P, I32, I32, I32, I32, P, P, P]
+    lib.bsa_bitmask_to_index.argtypes = [P, I32, I32, I32, I32, I32, P, P, P]
     lib.bsa_varlen_mask_to_index.argtypes = [P, I32, I32, P, P, I32, I32, P, P, P]
     I32P = ctypes.POINTER(ctypes.c_int32)
     lib.bsa_varlen_offsets.argtypes = [I32P, I32P, I32, I32, I32, I32P, I32P, I32P, I32P]
@@ -315,6 +317,36 @@ def bsa_mask_to_index(mask: torch.Tensor, cnt: Optional[torch.Tensor] = None,
         raise ValueError("cnt/idx must be contiguous [B,H,M] / [B,H,M,N] int32 tensors")
     st = lib.bsa_mask_to_index(_ptr(mask), B, H, M, N, _ptr(cnt), _ptr(idx), _stream(mask))
     _check("bsa_mask_to_index", st)
+    return cnt, idx
+
+
+def bsa_bitmask_to_index(words: torch.Tensor, N: int, H: Optional[int] = None,
+                         cnt: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None):
+    """Packed UInt32 block bitmap [B,Hkv,M,ceil(N/32)] (int32 or uint32,
+    contiguous, device; bit j of word w selects KV block 32*w+j, padding bits
+    past N ignored) -> (cnt int32 [B,H,M], idx int32 [B,H,M,N]) in the format
+    of bsa_mask_to_index.  Q head h reads KV head h // (H // Hkv); H defaults
+    to Hkv."""
+    lib = load_library()
+    if not isinstance(words, torch.Tensor) or words.dtype not in (torch.int32, torch.uint32) \
+            or not words.is_cuda or words.dim() != 4 or not words.is_contiguous():
+        raise ValueError("words must be a contiguous int32/uint32 [B,Hkv,M,W] device tensor")
+    B, Hkv, M, W = words.shape
+    H = Hkv if H is None else int(H)
+    if N < 0 or W != (N + 31) // 32:
+        raise ValueError(f"{W} words per row for N={N} blocks (need {(N + 31) // 32})")
+    if Hkv == 0 or H % Hkv:
+        raise ValueError(f"H={H} must be a positive multiple of Hkv={Hkv}")
+    if cnt is None:
+        cnt = torch.empty((B, H, M), dtype=torch.int32, device=words.device)
+    if idx is None:
+        idx = torch.empty((B, H, M, N), dtype=torch.int32, device=words.device)
+    if not cnt.is_contiguous() or not idx.is_contiguous() or tuple(idx.shape) != (B, H, M, N) \
+            or tuple(cnt.shape) != (B, H, M):
+        raise ValueError("cnt/idx must be contiguous [B,H,M] / [B,H,M,N] int32 tensors")
+    st = lib.bsa_bitmask_to_index(_ptr(words), B, Hkv, H, M, N, _ptr(cnt), _ptr(idx),
+                                  _stream(words))
+    _check("bsa_bitmask_to_index", st)
     return cnt, idx
 
 

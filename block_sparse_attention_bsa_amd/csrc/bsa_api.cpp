@@ -373,6 +373,18 @@ bsa_status bsa_mask_to_index(const uint8_t* mask, int32_t B, int32_t H, int32_t 
   return e == hipSuccess ? BSA_OK : BSA_ERR_HIP;
 }
 
+bsa_status bsa_bitmask_to_index(const uint32_t* words, int32_t B, int32_t Hkv, int32_t H,
+                                int32_t M, int32_t N, int32_t* cnt, int32_t* idx,
+                                hipStream_t stream) {
+  if (B < 0 || Hkv < 0 || H < 0 || M < 0 || N < 0) return BSA_ERR_INVALID_ARGUMENT;
+  if (H > 0 && (Hkv == 0 || H % Hkv != 0)) return BSA_ERR_INVALID_ARGUMENT;
+  const int64_t rows = (int64_t)B * H * M;
+  if (rows == 0) return BSA_OK;
+  if (!cnt || (N > 0 && (!words || !idx))) return BSA_ERR_INVALID_ARGUMENT;
+  const hipError_t e = bsa::launch_bitmask_to_index(words, B, Hkv, H, M, N, cnt, idx, stream);
+  return e == hipSuccess ? BSA_OK : BSA_ERR_HIP;
+}
+
 bsa_status bsa_varlen_mask_to_index(const uint8_t* mask, int32_t H, int32_t B,
                                     const int32_t* cu_total_m_blocks,
                                     const int32_t* block_idx_offsets, int32_t total_m_blocks,

@@ -56,6 +56,8 @@ hipError_t launch_fwd_staged(const FwdParams& p, int D, int tile_m, bool f32_in,
 // 256-row ping-pong kernel (bf16, D in {64, 96, 128}).
 hipError_t launch_fwd_pp(const FwdParams& p, int D, hipStream_t s);
 
+hipError_t launch_bitmask_to_index(const uint32_t* words, int32_t B, int32_t Hkv, int32_t H,
+                                  int32_t M, int32_t N, int32_t* cnt, int32_t* idx, hipStream_t s);
 hipError_t launch_mask_to_index(const uint8_t* mask, int64_t rows, int32_t N,
                                 int32_t* cnt, int32_t* idx, hipStream_t s);
 

@@ -1,5 +1,5 @@
-// Metadata kernels for gfx950: dense block mask -> block lists (batched and
-// packed varlen rows), the split of logical KV blocks into child tiles, and
+// Metadata kernels for gfx950: dense block mask or packed bitmap -> block
+// lists (batched and packed varlen rows), the split of logical KV blocks into child tiles, and
 // the full / partial classification of blocks under an element mask_mod.
 //
 // mask -> index follows the conversion "Dense FlashAttention vs Block-Sparse
@@ -18,20 +18,45 @@ namespace {
 
 constexpr int kWavesPerBlock = 4;
 
-__device__ __forceinline__ void compact_row(const uint8_t* __restrict__ mrow, int N,
-                                            int32_t* __restrict__ irow, int32_t* __restrict__ cnt,
-                                            int lane) {
+// sel(col) says whether KV block col of the row is selected.
+template <class Sel>
+__device__ __forceinline__ void compact_row_by(Sel sel_of, int N, int32_t* __restrict__ irow,
+                                               int32_t* __restrict__ cnt, int lane) {
   int run = 0;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int c0 = 0; c0 < N; c0 += 64) {
     const int col = N - 1 - (c0 + lane);
-    const bool sel = col >= 0 && mrow[col] != 0;
+    const bool sel = col >= 0 && sel_of(col);
     const uint64_t bal = __ballot(sel);
     if (sel) irow[run + __popcll(bal & below)] = col;
     run += __popcll(bal);
   }
   for (int s = run + lane; s < N; s += 64) irow[s] = -1;
   if (lane == 0) *cnt = run;
+}
+
+__device__ __forceinline__ void compact_row(const uint8_t* __restrict__ mrow, int N,
+                                            int32_t* __restrict__ irow, int32_t* __restrict__ cnt,
+                                            int lane) {
+  compact_row_by([&](int col) { return mrow[col] != 0; }, N, irow, cnt, lane);
+}
+
+// Packed bitmap rows [B, Hkv, M, W] (W = ceil(N/32)): bit j of word w selects
+// KV block 32*w + j; bits at or past N are never tested.  Q head h of the
+// output reads KV head h / group.
+__global__ __launch_bounds__(64 * kWavesPerBlock) void bitmask_to_index_kernel(
+    const uint32_t* __restrict__ words, int64_t rows, int32_t H, int32_t group, int32_t M,
+    int32_t N, int32_t W, int32_t* __restrict__ cnt, int32_t* __restrict__ idx) {
+  const int64_t row = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int64_t bh = row / M;
+  const int32_t m = (int32_t)(row - bh * M);
+  const int64_t b = bh / H;
+  const int32_t h = (int32_t)(bh - b * H);
+  const uint32_t* __restrict__ wrow = words + ((b * (H / group) + h / group) * M + m) * W;
+  compact_row_by([&](int col) { return ((wrow[col >> 5] >> (col & 31)) & 1u) != 0; }, N,
+                 idx + row * N, cnt + row, lane);
 }
 
 __global__ __launch_bounds__(64 * kWavesPerBlock) void mask_to_index_kernel(
@@ -156,6 +181,18 @@ hipError_t launch_mask_to_index(const uint8_t* mask, int64_t rows, int32_t N, in
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(mask_to_index_kernel, dim3((unsigned)blocks), dim3(64 * kWavesPerBlock), 0,
                      s, mask, rows, N, cnt, idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_bitmask_to_index(const uint32_t* words, int32_t B, int32_t Hkv, int32_t H,
+                                  int32_t M, int32_t N, int32_t* cnt, int32_t* idx,
+                                  hipStream_t s) {
+  const int64_t rows = (int64_t)B * H * M;
+  if (rows <= 0) return hipSuccess;
+  const int64_t blocks = (rows + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bitmask_to_index_kernel, dim3((unsigned)blocks), dim3(64 * kWavesPerBlock),
+                     0, s, words, rows, H, H / Hkv, M, N, (N + 31) / 32, cnt, idx);
   return hipGetLastError();
 }
 

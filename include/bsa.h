@@ -160,6 +160,23 @@ bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, 
 bsa_status bsa_mask_to_index(const uint8_t* mask, int32_t B, int32_t H, int32_t M, int32_t N,
                              int32_t* cnt, int32_t* idx, hipStream_t stream);
 
+/* Packed UInt32 block bitmap -> block lists (the bitmap input of the PrimTS
+ * page, "proxy-compensated block-sparse attention", flashinfer pull request
+ * 4872: description and test notes).  words: device uint32 [B,Hkv,M,W]
+ * contiguous, W = ceil(N/32), one row per (batch, KV head, Q block); bit j
+ * (value 1<<j) of word w selects KV block 32*w+j, and bits at or past N in
+ * the final word are padding and ignored.  Q head h (H a multiple of Hkv)
+ * takes the row of KV head h/(H/Hkv).  Writes cnt: device int32 [B,H,M] and
+ * idx: device int32 [B,H,M,N] in the format of bsa_mask_to_index, so a
+ * forward over these lists equals one over the lists of the same selection
+ * given as a dense mask, bit for bit.  N == 0 writes cnt only and reads no
+ * words.  Caller owns every buffer.  Returns BSA_ERR_INVALID_ARGUMENT for
+ * negative sizes, H not a multiple of Hkv, or a missing pointer; BSA_ERR_HIP
+ * if the launch fails.  Bit-exact; deterministic. */
+bsa_status bsa_bitmask_to_index(const uint32_t* words, int32_t B, int32_t Hkv, int32_t H,
+                                int32_t M, int32_t N, int32_t* cnt, int32_t* idx,
+                                hipStream_t stream);
+
 /* The same conversion for the packed varlen layout.  mask: device uint8
  * [H,total_n_blocks] laid out like idx (row (b,m) of head h at
  * block_idx_offsets[b] + m*num_n(b), width num_n(b)).  Writes cnt [H,total_m_blocks]

@@ -24,7 +24,8 @@ def test_library_exports_every_declared_symbol():
     names = _declared()
     assert names == sorted(["bsa_fwd", "bsa_varlen_fwd", "bsa_mask_to_index",
                             "bsa_varlen_mask_to_index", "bsa_varlen_offsets",
-                            "bsa_expand_kv_blocks", "bsa_block_sparsity", "bsa_status_str"])
+                            "bsa_expand_kv_blocks", "bsa_block_sparsity", "bsa_bitmask_to_index",
+                            "bsa_status_str"])
     lib = bsa.load_library()
     for n in names:
         assert hasattr(lib, n), n
