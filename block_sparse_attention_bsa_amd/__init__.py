@@ -62,7 +62,9 @@ class _BlockList(ctypes.Structure):
 class _BlockSparse(ctypes.Structure):
     _fields_ = [("mask", _BlockList), ("full", _BlockList),
                 ("block_q", ctypes.c_int32), ("block_kv", ctypes.c_int32),
-                ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32)]
+                ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
+                ("proxy_k", ctypes.c_void_p), ("proxy_v", ctypes.c_void_p),
+                ("proxy_k_str", ctypes.c_int64 * 3), ("proxy_v_str", ctypes.c_int64 * 3)]
 
 
 def _window(mask_mod: int, window) -> Tuple[int, int]:
@@ -183,7 +185,8 @@ def bsa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             block_q: int, block_kv: int, mask_mod: int = MASK_NONE,
             kv_valid: Optional[torch.Tensor] = None, softmax_scale: Optional[float] = None,
             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-            validate: bool = False, window: Optional[Tuple[int, int]] = None):
+            validate: bool = False, window: Optional[Tuple[int, int]] = None,
+            proxy: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
     """Batched block-sparse attention forward.
 
     q [B,Sq,H,D], k/v [B,Sk,Hkv,D] (bf16 or fp32, head_dim contiguous, any
@@ -191,6 +194,9 @@ def bsa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     mask_list / full_list: (cnt int32 [B|1,H|1,M], idx int32 [B|1,H|1,M,N])
     with M = ceil(Sq/block_q), N = ceil(Sk/block_kv); a size-1 batch or head
     dimension broadcasts.  window=(left, right): the bounds of MASK_LOCAL.
+    proxy=(k_mean, v_sum): bf16 [B,N,Hkv,D] block summaries for the
+    proxy-compensated route (MASK_NONE only): every block a row does not list
+    enters its softmax once, weighted by the block's token count.
     Returns (O [B,Sq,H,D], LSE float32 [B,H,Sq]).
     """
     lib = load_library()
@@ -224,6 +230,15 @@ def bsa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     bs = _BlockSparse(_block_list(mask_list, True, (B, H, M, N)),
                       _block_list(full_list, True, (B, H, M, N)), int(block_q), int(block_kv),
                       *_window(mask_mod, window))
+    if proxy is not None:
+        for n, t in zip(("proxy k_mean", "proxy v_sum"), proxy):
+            _dev(n, t, q.dtype)
+            if tuple(t.shape) != (B, N, Hkv, D) or t.stride(-1) != 1:
+                raise ValueError(f"{n} must be [B,N,Hkv,D]={(B, N, Hkv, D)} with a contiguous "
+                                 "last dimension")
+        bs.proxy_k, bs.proxy_v = proxy[0].data_ptr(), proxy[1].data_ptr()
+        bs.proxy_k_str = (ctypes.c_int64 * 3)(*proxy[0].stride()[:3])
+        bs.proxy_v_str = (ctypes.c_int64 * 3)(*proxy[1].stride()[:3])
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     st = lib.bsa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _DTYPES[q.dtype],
                      B, H, Hkv, Sq, Sk, D,

@@ -216,7 +216,12 @@ bsa_status bsa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   if (bs->block_q <= 0 || bs->block_kv <= 0) return BSA_ERR_INVALID_ARGUMENT;
   if (!list_ok(bs->mask) || !list_ok(bs->full)) return BSA_ERR_INVALID_ARGUMENT;
   if (!supported_head_dim(D)) return BSA_ERR_UNSUPPORTED;
-  const int tile_m = fit_tile_m(bs->block_q, D, dt == BSA_F32, mask_mod);
+  // proxy-compensated route: the staged bf16 kernel, 128-row tiles at most
+  const bool proxy = bs->proxy_k != nullptr || bs->proxy_v != nullptr;
+  if (proxy && (!bs->proxy_k || !bs->proxy_v)) return BSA_ERR_INVALID_ARGUMENT;
+  if (proxy && (mask_mod != BSA_MASK_NONE || dt != BSA_BF16)) return BSA_ERR_UNSUPPORTED;
+  int tile_m = fit_tile_m(bs->block_q, D, dt == BSA_F32, mask_mod);
+  if (proxy && tile_m == 256) tile_m = 128;
   if (tile_m == 0) return BSA_ERR_UNSUPPORTED;
   if ((int64_t)B * H * Sq == 0) return BSA_OK;  // nothing to write
   if (!q || !k || !v || !o || !lse) return BSA_ERR_INVALID_ARGUMENT;
@@ -229,6 +234,14 @@ bsa_status bsa_fwd(const void* q, const void* k, const void* v, void* o, float* 
     return BSA_ERR_MISALIGNED;
   if (!subtile_offsets_fit(k_str[1], v_str[1], es)) return BSA_ERR_UNSUPPORTED;
   const int64_t M = cdiv64(Sq, bs->block_q), N = cdiv64(Sk, bs->block_kv);
+  if (proxy) {
+    if (N > bsa::kProxyMaxBlocks) return BSA_ERR_UNSUPPORTED;
+    if (!aligned16(bs->proxy_k) || !aligned16(bs->proxy_v) || !strides_ok(bs->proxy_k_str, 3, es) ||
+        !strides_ok(bs->proxy_v_str, 3, es))
+      return BSA_ERR_MISALIGNED;
+    if (!subtile_offsets_fit(bs->proxy_k_str[1], bs->proxy_v_str[1], es))
+      return BSA_ERR_UNSUPPORTED;
+  }
   const int64_t tiles_per_head = cdiv64(Sq, tile_m);
   const int64_t tiles = (int64_t)B * H * tiles_per_head;
   if (tiles > std::numeric_limits<int32_t>::max() || N > std::numeric_limits<int32_t>::max() / 2)
@@ -265,7 +278,14 @@ bsa_status bsa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   p.lse_ld = Sq;
   p.num_tiles = (int32_t)tiles;
   p.c = softmax_scale * kLog2e;
-  const hipError_t e = bsa::launch_fwd(p, D, tile_m, dt == BSA_F32, stream);
+  if (proxy) {
+    p.ksum = bs->proxy_k;
+    p.vsum = bs->proxy_v;
+    p.ks_sb = bs->proxy_k_str[0]; p.ks_ss = bs->proxy_k_str[1]; p.ks_sh = bs->proxy_k_str[2];
+    p.vs_sb = bs->proxy_v_str[0]; p.vs_ss = bs->proxy_v_str[1]; p.vs_sh = bs->proxy_v_str[2];
+  }
+  const hipError_t e = proxy ? bsa::launch_fwd_proxy(p, D, tile_m, stream)
+                             : bsa::launch_fwd(p, D, tile_m, dt == BSA_F32, stream);
   return e == hipSuccess ? BSA_OK : BSA_ERR_HIP;
 }
 
@@ -278,6 +298,7 @@ bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, 
                           const int64_t o_str[2], const bsa_block_sparse* bs,
                           bsa_mask_mod mask_mod, float softmax_scale, uint32_t flags,
                           hipStream_t stream) {
+  if (bs && (bs->proxy_k || bs->proxy_v)) return BSA_ERR_UNSUPPORTED;  // batched only
   if (B < 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || total_m_blocks < 0 || total_n_blocks < 0 ||
       total_q < 0)
     return BSA_ERR_INVALID_ARGUMENT;

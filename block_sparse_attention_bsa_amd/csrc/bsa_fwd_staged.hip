@@ -6,6 +6,15 @@
 // and converted while the current one computes, then written to the other
 // LDS stage, K row-major and V transposed (V^T[d][key]) so both MFMA A
 // operands are 16-byte LDS reads.
+//
+// The PROXY instance adds the proxy-compensated route of the PrimTS page
+// ("proxy-compensated block-sparse attention", flashinfer pull request 4872):
+// after the listed blocks, the same pipeline walks the caller's block
+// summaries 64 at a time as if they were keys (mean K as the key, summed V
+// as the value).  An LDS bitmap of the Q block's listed blocks masks the
+// summaries of blocks that are attended exactly, chunks whose blocks are all
+// listed are skipped, and the row sum counts each summary at its block's
+// token mass, so the result is one softmax over exact keys and proxies.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,7 +49,59 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-template <int D, int NW, bool F32IN>
+// softmax_step for a chunk of summaries: keys n0 .. n0+nk-1 (n0 = it.key0,
+// a multiple of 64); bit k of ex0 / ex1 set means summary n0+k / n0+32+k is
+// a listed block (no proxy).  The row sum adds mass(n) * p, where mass(n) is
+// wfull for every block but the last (n == tail_n), whose mass is wtail; the
+// PV product takes p as is.
+template <int DB>
+__device__ __forceinline__ void proxy_softmax_step(f32x16_t& s0, f32x16_t& s1, const Item& it,
+                                                   uint32_t ex0, uint32_t ex1, float wfull,
+                                                   int tail_n, float wtail, int h32, float c,
+                                                   float& m_run, float& l_run,
+                                                   f32x16_t (&oacc)[DB], uint32_t (&pk0)[8],
+                                                   uint32_t (&pk1)[8]) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = 16 * (r >> 3) + 8 * h32 + (r & 7);
+    if (!(key < it.nk && ((ex0 >> key) & 1u) == 0)) s0[r] = neg_inf();
+    if (!(key + 32 < it.nk && ((ex1 >> key) & 1u) == 0)) s1[r] = neg_inf();
+  }
+  float mx = neg_inf();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(m_run, mx * c);
+  if (__any(m_new > m_run)) {
+    const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    m_run = m_new;
+  }
+  const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
+  const int tk = tail_n - it.key0;  // chunk-local key of the last block (may be outside)
+  float ls = 0.f, lt = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int k0 = 16 * (i >> 2) + 8 * h32 + ((2 * i) & 7);  // key of element 2i of s0
+    const float a0 = __builtin_amdgcn_exp2f(fmaf(s0[2 * i], c, -m_use));
+    const float a1 = __builtin_amdgcn_exp2f(fmaf(s0[2 * i + 1], c, -m_use));
+    const float b0 = __builtin_amdgcn_exp2f(fmaf(s1[2 * i], c, -m_use));
+    const float b1 = __builtin_amdgcn_exp2f(fmaf(s1[2 * i + 1], c, -m_use));
+    pk0[i] = pack_bf16x2(a0, a1);
+    pk1[i] = pack_bf16x2(b0, b1);
+    ls += (a0 + a1) + (b0 + b1);
+    lt += (k0 == tk ? a0 : 0.f) + (k0 + 1 == tk ? a1 : 0.f) + (k0 + 32 == tk ? b0 : 0.f) +
+          (k0 + 33 == tk ? b1 : 0.f);
+  }
+  l_run += fmaf(wtail - wfull, lt, wfull * ls);
+}
+
+template <int D, int NW, bool F32IN, bool PROXY>
 __global__ __launch_bounds__(NW * 64) void bsa_fwd_staged_kernel(const FwdParams p) {
   using T = typename std::conditional<F32IN, float, __bf16>::type;
   constexpr int NT = NW * 64;
@@ -60,15 +121,38 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_staged_kernel(const FwdParams
   static_assert(D % 32 == 0, "head_dim must be a multiple of 32");
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+  // listed blocks of this Q block (+1 word: a chunk's second word may lie past the last)
+  __shared__ uint32_t xbits[PROXY ? kProxyMaxBlocks / 32 + 1 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, h32 = lane >> 5;
 
   TileInfo ti;
-  if (!decode_tile<TM>(p, xcd_remap(blockIdx.x, p.num_tiles), ti)) return;
+  const int tix = xcd_remap(blockIdx.x, p.num_tiles);
+  if (!decode_tile<TM>(p, tix, ti)) return;
   const T* qp = reinterpret_cast<const T*>(p.q) + ti.qoff;
   const T* kp = reinterpret_cast<const T*>(p.k) + ti.koff;
   const T* vp = reinterpret_cast<const T*>(p.v) + ti.voff;
+  const T* ksp = nullptr;
+  const T* vsp = nullptr;
+  if constexpr (PROXY) {  // batched only: tile = ((b*H + h) * tiles_per_head + qt)
+    const int bh = tix / p.tiles_per_head;
+    const int b = bh / p.H, hk = (bh % p.H) / p.hrep;
+    ksp = reinterpret_cast<const T*>(p.ksum) + b * p.ks_sb + hk * p.ks_sh;
+    vsp = reinterpret_cast<const T*>(p.vsum) + b * p.vs_sb + hk * p.vs_sh;
+    const int nwords = (ti.num_n + 31) / 32 + 1;
+    for (int i = tid; i < nwords; i += NT) xbits[i] = 0u;
+    __syncthreads();
+    for (int e = tid; e < ti.mcnt; e += NT) {
+      const int j = ti.mrow[(int64_t)e * p.mi_s[3]];
+      if ((unsigned)j < (unsigned)ti.num_n) atomicOr(&xbits[j >> 5], 1u << (j & 31));
+    }
+    for (int e = tid; e < ti.fcnt; e += NT) {
+      const int j = ti.frow[(int64_t)e * p.fi_s[3]];
+      if ((unsigned)j < (unsigned)ti.num_n) atomicOr(&xbits[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+  }
 
   const int qrow = ti.q0 + 32 * w + l32;
   uint4 qf[DS];
@@ -91,13 +175,18 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_staged_kernel(const FwdParams
   Chunk<F32IN> kst[KC];
   Chunk<F32IN> vst[VB][4];
   auto issue = [&](const Item& it) {
+    const bool px = PROXY && it.is_mask == 2;
+    const T* kb = px ? ksp : kp;
+    const T* vb_ = px ? vsp : vp;
+    const int64_t kss = px ? p.ks_ss : p.k_ss;
+    const int64_t vss = px ? p.vs_ss : p.v_ss;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
       const int ci = tid + c * NT;
       if (KCH % NT == 0 || ci < KCH) {
         const int row = ci / DC, col = ci % DC;
         if (row < it.nk)
-          kst[c].load(kp + (int64_t)(it.key0 + row) * p.k_ss + col * 8);
+          kst[c].load(kb + (int64_t)(it.key0 + row) * kss + col * 8);
         else
           kst[c].zero();
       }
@@ -111,7 +200,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_staged_kernel(const FwdParams
         for (int rr = 0; rr < 4; ++rr) {
           const int key = kg * 4 + rr;
           if (key < it.nk)
-            vst[vb][rr].load(vp + (int64_t)(it.key0 + key) * p.v_ss + dc * 8);
+            vst[vb][rr].load(vb_ + (int64_t)(it.key0 + key) * vss + dc * 8);
           else
             vst[vb][rr].zero();
         }
@@ -172,8 +261,16 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_staged_kernel(const FwdParams
       s1 = mfma32(a1, qf[ks], s1);
     }
     uint32_t pk0[8], pk1[8];
-    softmax_step<DB, true>(s0, s1, it, it.is_mask && list_masked, mlo, mhi, h32, p.c, m_run,
-                     l_run, oacc, pk0, pk1);
+    if (PROXY && it.is_mask == 2) {
+      const int n0 = it.key0;
+      proxy_softmax_step<DB>(s0, s1, it, xbits[n0 >> 5], xbits[(n0 >> 5) + 1],
+                             (float)p.block_kv, ti.num_n - 1,
+                             (float)(ti.Sk - (ti.num_n - 1) * p.block_kv), h32, p.c, m_run,
+                             l_run, oacc, pk0, pk1);
+    } else {
+      softmax_step<DB, true>(s0, s1, it, it.is_mask && list_masked, mlo, mhi, h32, p.c, m_run,
+                             l_run, oacc, pk0, pk1);
+    }
 #pragma unroll
     for (int ps = 0; ps < 4; ++ps) {
       const uint4 bop = p_operand(pk0, pk1, ps);
@@ -190,15 +287,39 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_staged_kernel(const FwdParams
              p.block_kv, ti.num_n, p.mask_mod, p.kv_valid, -1000000, -1, 0};
   unsigned char* buf0 = smem;
   unsigned char* buf1 = smem + STAGE;
+  // listed blocks first, then (PROXY) the chunks of summaries with an unlisted block
+  bool in_proxy = false;
+  int pn = 0;
+  auto step = [&](Item& it) -> bool {
+    if (!in_proxy) {
+      if (advance(it, L, lane, ti.Sk)) return true;
+      in_proxy = true;
+    }
+    if constexpr (PROXY) {
+      while (pn < ti.num_n) {
+        const int n0 = pn;
+        pn += kKvTile;
+        const int nk = min(kKvTile, ti.num_n - n0);
+        const uint64_t live = nk >= 64 ? ~0ull : ((1ull << nk) - 1);
+        const uint64_t ex = (uint64_t)xbits[n0 >> 5] | ((uint64_t)xbits[(n0 >> 5) + 1] << 32);
+        if ((~ex & live) == 0) continue;  // every block of the chunk is listed
+        it.key0 = n0;
+        it.nk = nk;
+        it.is_mask = 2;
+        return true;
+      }
+    }
+    return false;
+  };
   Item cur{-1, 0, 0, 0, 0, 0, 0};
-  bool have = advance(cur, L, lane, ti.Sk);
+  bool have = step(cur);
   if (have) {
     issue(cur);
     store(buf0, buf0 + KBYTES);
   }
   __syncthreads();
   Item nxt = cur;
-  bool have_nxt = have && advance(nxt, L, lane, ti.Sk);
+  bool have_nxt = have && step(nxt);
   int sb = 0;
   while (have) {
     if (have_nxt) issue(nxt);
@@ -209,38 +330,39 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_staged_kernel(const FwdParams
     __syncthreads();
     cur = nxt;
     have = have_nxt;
-    if (have) have_nxt = advance(nxt, L, lane, ti.Sk);
+    if (have) have_nxt = step(nxt);
     sb ^= 1;
   }
   epilogue<DB, T>(p, ti, qrow, h32, m_run, l_run, oacc);
 }
 
-template <int D, int NW, bool F32>
+template <int D, int NW, bool F32, bool PROXY>
 hipError_t launch_one(const FwdParams& p, hipStream_t s) {
   FwdParams copy = p;
   void* args[] = {&copy};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&bsa_fwd_staged_kernel<D, NW, F32>),
-                         dim3(p.num_tiles), dim3(NW * 64), args, 0, s);
+  return hipLaunchKernel(
+      reinterpret_cast<const void*>(&bsa_fwd_staged_kernel<D, NW, F32, PROXY>),
+      dim3(p.num_tiles), dim3(NW * 64), args, 0, s);
 }
 
-template <int D, bool F32>
+template <int D, bool F32, bool PROXY>
 hipError_t launch_tm(const FwdParams& p, int tile_m, hipStream_t s) {
   switch (tile_m) {
-    case 128: return launch_one<D, 4, F32>(p, s);
-    case 64: return launch_one<D, 2, F32>(p, s);
-    case 32: return launch_one<D, 1, F32>(p, s);
+    case 128: return launch_one<D, 4, F32, PROXY>(p, s);
+    case 64: return launch_one<D, 2, F32, PROXY>(p, s);
+    case 32: return launch_one<D, 1, F32, PROXY>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <bool F32>
+template <bool F32, bool PROXY>
 hipError_t launch_d(const FwdParams& p, int D, int tile_m, hipStream_t s) {
   switch (D) {
-    case 64: return launch_tm<64, F32>(p, tile_m, s);
-    case 96: return launch_tm<96, F32>(p, tile_m, s);
-    case 128: return launch_tm<128, F32>(p, tile_m, s);
-    case 192: return launch_tm<192, F32>(p, tile_m, s);
-    case 256: return launch_tm<256, F32>(p, tile_m, s);
+    case 64: return launch_tm<64, F32, PROXY>(p, tile_m, s);
+    case 96: return launch_tm<96, F32, PROXY>(p, tile_m, s);
+    case 128: return launch_tm<128, F32, PROXY>(p, tile_m, s);
+    case 192: return launch_tm<192, F32, PROXY>(p, tile_m, s);
+    case 256: return launch_tm<256, F32, PROXY>(p, tile_m, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -248,7 +370,11 @@ hipError_t launch_d(const FwdParams& p, int D, int tile_m, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_staged(const FwdParams& p, int D, int tile_m, bool f32_in, hipStream_t s) {
-  return f32_in ? launch_d<true>(p, D, tile_m, s) : launch_d<false>(p, D, tile_m, s);
+  return f32_in ? launch_d<true, false>(p, D, tile_m, s) : launch_d<false, false>(p, D, tile_m, s);
+}
+
+hipError_t launch_fwd_proxy(const FwdParams& p, int D, int tile_m, hipStream_t s) {
+  return launch_d<false, true>(p, D, tile_m, s);
 }
 
 }  // namespace bsa

@@ -10,6 +10,7 @@ namespace bsa {
 // Keys per KV sub-tile staged through LDS.  A listed KV block of block_kv
 // tokens is processed as ceil(block_kv / kKvTile) sub-tiles.
 constexpr int kKvTile = 64;
+constexpr int kProxyMaxBlocks = 16384;  // semantic KV blocks per row with proxies (LDS bitmap)
 
 // Everything one forward launch needs, in element units of the input dtype.
 struct FwdParams {
@@ -44,6 +45,11 @@ struct FwdParams {
   int32_t num_tiles;       // grid size
   float c;                 // softmax_scale * log2(e)
   int32_t win_left, win_right;  // local mask_mod bounds (negative = unbounded)
+  // proxy-compensated route: mean-K / summed-V block summaries [B, N, H_kv, D]
+  const void* ksum;
+  const void* vsum;
+  int64_t ks_sb, ks_ss, ks_sh;
+  int64_t vs_sb, vs_ss, vs_sh;
 };
 
 // Launch the forward kernel instance for (D, rows per workgroup, dtype):
@@ -53,6 +59,8 @@ struct FwdParams {
 // checks support first).
 hipError_t launch_fwd(const FwdParams& p, int D, int tile_m, bool f32_in, hipStream_t s);
 hipError_t launch_fwd_staged(const FwdParams& p, int D, int tile_m, bool f32_in, hipStream_t s);
+// bf16 staged kernel with the proxy-compensated route (batched, no element mask)
+hipError_t launch_fwd_proxy(const FwdParams& p, int D, int tile_m, hipStream_t s);
 // 256-row ping-pong kernel (bf16, D in {64, 96, 128}).
 hipError_t launch_fwd_pp(const FwdParams& p, int D, hipStream_t s);
 

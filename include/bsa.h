@@ -99,7 +99,23 @@ typedef struct {
 /* The (mask, full) pair and the sparse block sizes (in tokens).
  * block_q must be a multiple of 32; block_kv may be any positive size.
  * window_left / window_right: the bounds of BSA_MASK_LOCAL (ignored by the
- * other mask_mods). */
+ * other mask_mods).
+ *
+ * proxy_k / proxy_v: optional summaries for the proxy-compensated route (the
+ * PrimTS page, "proxy-compensated block-sparse attention", flashinfer pull
+ * request 4872: description, proxy paragraph).  Both NULL: plain block-sparse
+ * attention.  Both set: every KV block n that a Q-block row does not list
+ * (in either list) enters that row's softmax once, with score
+ * softmax_scale * q.proxy_k[n], value proxy_v[n], and weight c_n in the
+ * denominator, where c_n = min(block_kv, Sk - n*block_kv) is its token count:
+ *   O = (sum_exact e^s v + sum_omitted e^sbar Vsum) / (sum_exact e^s + sum_omitted c e^sbar),
+ *   LSE = log of that denominator.
+ * proxy_k holds the mean key and proxy_v the summed value of each block
+ * (device, dtype dt = BSA_BF16, [B, N, H_kv, D] with N = ceil(Sk/block_kv),
+ * element strides proxy_*_str = {batch, block, head}, head_dim stride 1,
+ * 16-byte aligned like K and V).  Requires BSA_MASK_NONE, the batched
+ * forward and N <= 16384; otherwise BSA_ERR_UNSUPPORTED.  A row whose blocks
+ * are all listed has no proxy term. */
 typedef struct {
   bsa_block_list mask;
   bsa_block_list full;
@@ -107,6 +123,10 @@ typedef struct {
   int32_t block_kv;
   int32_t window_left;
   int32_t window_right;
+  const void* proxy_k;
+  const void* proxy_v;
+  int64_t proxy_k_str[3];
+  int64_t proxy_v_str[3];
 } bsa_block_sparse;
 
 /* Batched forward.

@@ -1,0 +1,113 @@
+"""GPU: the proxy-compensated route (bsa_fwd with proxy=(k_mean, v_sum))
+against oracle.proxy_attention on the same bf16 inputs and summaries."""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_bsa_amd as bsa
+import oracle
+from bsa_testlib import as_oracle, check_o_lse, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed, B, Sq, Sk, H, Hkv, D, bq, bk, density, listed_rows=None):
+    rng = np.random.default_rng(seed)
+    q, k, v = (to_dev(rng.standard_normal(s, dtype=np.float32))
+               for s in ((B, Sq, H, D), (B, Sk, Hkv, D), (B, Sk, Hkv, D)))
+    M, N = -(-Sq // bq), -(-Sk // bk)
+    sel = rng.random((B, H, M, N)) < density
+    if listed_rows is not None:
+        for (b, h, i), val in listed_rows.items():
+            sel[b, h, i] = val
+    split = rng.random((B, H, M, N)) < 0.5
+    full, part = sel & split, sel & ~split
+    kbar, vsum = oracle.block_summaries(as_oracle(k), as_oracle(v), bk)
+    ks, vs = (torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).cuda() for x in (kbar, vsum))
+    return q, k, v, full, part, ks, vs
+
+
+def _lists(m):
+    return bsa.bsa_mask_to_index(torch.from_numpy(np.ascontiguousarray(m, np.uint8)).cuda())
+
+
+def _run(q, k, v, full, part, ks, vs, bq, bk, q_blocks=None):
+    D = q.shape[-1]
+    scale = 1 / math.sqrt(D)
+    o, lse = bsa.bsa_fwd(q, k, v, _lists(part) if part.any() else None,
+                         _lists(full) if full.any() else None, bq, bk, bsa.MASK_NONE, None,
+                         scale, validate=True, proxy=(ks, vs))
+    torch.cuda.synchronize()
+    O, L = oracle.proxy_attention(as_oracle(q), as_oracle(k), as_oracle(v), full, part,
+                                  as_oracle(ks), as_oracle(vs), bq, bk, scale, q_blocks=q_blocks)
+    return o, lse, O, L
+
+
+@pytest.mark.parametrize("case", [
+    dict(Sq=300, Sk=700, D=128, bq=128, bk=128, density=0.3),
+    dict(Sq=256, Sk=1000, D=64, bq=64, bk=64, density=0.4),
+    dict(Sq=200, Sk=4033, D=128, bq=64, bk=16, density=0.1),     # 253 blocks: 4 chunks, tail of 1
+    dict(Sq=256, Sk=5000, D=96, bq=32, bk=48, density=0.2),
+    dict(Sq=130, Sk=900, D=192, bq=128, bk=64, density=0.25),
+    dict(Sq=100, Sk=777, D=256, bq=64, bk=64, density=0.25),
+    dict(Sq=512, Sk=16000, D=128, bq=256, bk=16, density=0.05),  # 1000 blocks, 256-row Q blocks
+])
+def test_proxy_matches_oracle(case):
+    seed = zlib.crc32(repr(sorted(case.items())).encode())
+    B, H, Hkv = 2, 4, 2
+    listed = {(0, 0, 0): True, (0, 1, 0): False}  # one row all listed, one with no listed block
+    q, k, v, full, part, ks, vs = _case(seed, B, H=H, Hkv=Hkv, listed_rows=listed, **case)
+    o, lse, O, L = _run(q, k, v, full, part, ks, vs, case["bq"], case["bk"])
+    check_o_lse(o, lse, O, L, f"proxy {case}")
+
+
+def test_all_listed_rows_ignore_the_summaries():
+    q, k, v, full, part, ks, vs = _case(11, 1, 256, 640, 2, 1, 128, 128, 128, 1.0)
+    a = bsa.bsa_fwd(q, k, v, _lists(part), _lists(full), 128, 128, bsa.MASK_NONE, None, 0.1,
+                    proxy=(ks, vs))
+    b = bsa.bsa_fwd(q, k, v, _lists(part), _lists(full), 128, 128, bsa.MASK_NONE, None, 0.1,
+                    proxy=(torch.randn_like(ks), torch.randn_like(vs)))
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_pages_workload_sampled():
+    """B1 Sq=Sk=32760 H12 d128, 64x64 blocks, 84 of 512 blocks listed per row
+    (the proxy workload of the PrimTS page), sampled Q blocks against the oracle."""
+    B, S, H, D, bq, bk, per_row = 1, 32760, 12, 128, 64, 64, 84
+    rng = np.random.default_rng(1007)
+    q, k, v = (to_dev(rng.standard_normal((B, S, H, D), dtype=np.float32)) for _ in range(3))
+    M = N = -(-S // 64)
+    sel = np.zeros((B, H, M, N), bool)
+    for h in range(H):
+        for i in range(M):
+            sel[0, h, i, rng.choice(N, per_row, replace=False)] = True
+    full, part = sel, np.zeros_like(sel)
+    kk = k.float().cpu().numpy().astype(np.float64)
+    vv = v.float().cpu().numpy().astype(np.float64)
+    kbar, vsum = oracle.block_summaries(kk, vv, bk)
+    ks, vs = (torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).cuda() for x in (kbar, vsum))
+    blocks = [(0, int(h), int(i)) for h, i in zip(rng.integers(0, H, 12), rng.integers(0, M, 12))]
+    blocks.append((0, 0, M - 1))  # the ragged last Q block
+    o, lse, O, L = _run(q, k, v, full, part, ks, vs, bq, bk, q_blocks=blocks)
+    rows = np.concatenate([np.arange(i * bq, min((i + 1) * bq, S)) for _, _, i in blocks])
+    heads = np.concatenate([np.full(min((i + 1) * bq, S) - i * bq, h) for _, h, i in blocks])
+    zero = np.zeros_like(rows)
+    check_o_lse(o, lse, O, L, "proxy pages workload (sampled)",
+                sel=((zero, rows, heads), (zero, heads, rows)))
+
+
+def test_proxy_rejects_what_it_does_not_cover():
+    q, k, v, full, part, ks, vs = _case(12, 1, 128, 256, 2, 2, 64, 64, 64, 0.5)
+    with pytest.raises(bsa.BsaError):
+        bsa.bsa_fwd(q, k, v, None, _lists(full), 64, 64, bsa.MASK_CAUSAL, None, 0.1,
+                    proxy=(ks, vs))
+    with pytest.raises(bsa.BsaError):
+        bsa.bsa_fwd(q.float(), k.float(), v.float(), None, _lists(full), 64, 64, bsa.MASK_NONE,
+                    None, 0.1, proxy=(ks.float(), vs.float()))
+    with pytest.raises(ValueError):
+        bsa.bsa_fwd(q, k, v, None, _lists(full), 64, 64, bsa.MASK_NONE, None, 0.1,
+                    proxy=(ks[:, :-1], vs))
