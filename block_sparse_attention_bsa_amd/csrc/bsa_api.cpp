@@ -284,8 +284,10 @@ bsa_status bsa_fwd(const void* q, const void* k, const void* v, void* o, float* 
     p.ks_sb = bs->proxy_k_str[0]; p.ks_ss = bs->proxy_k_str[1]; p.ks_sh = bs->proxy_k_str[2];
     p.vs_sb = bs->proxy_v_str[0]; p.vs_ss = bs->proxy_v_str[1]; p.vs_sh = bs->proxy_v_str[2];
   }
-  const hipError_t e = proxy ? bsa::launch_fwd_proxy(p, D, tile_m, stream)
-                             : bsa::launch_fwd(p, D, tile_m, dt == BSA_F32, stream);
+  // the DMA kernel reuses K's and V's row offsets for the summaries
+  const bool proxy_dma = proxy && bs->proxy_k_str[1] == k_str[1] && bs->proxy_v_str[1] == v_str[1];
+  const hipError_t e = proxy && !proxy_dma ? bsa::launch_fwd_proxy_staged(p, D, tile_m, stream)
+                                           : bsa::launch_fwd(p, D, tile_m, dt == BSA_F32, stream);
   return e == hipSuccess ? BSA_OK : BSA_ERR_HIP;
 }
 

@@ -41,6 +41,7 @@
 #include <stdint.h>
 
 #include "bsa_fwd_common.h"
+#include "bsa_fwd_proxy.h"
 
 namespace bsa {
 namespace {
@@ -142,23 +143,36 @@ struct FwdCfg {
 
 // LOCAL: the local mask_mod's key range on mask-list sub-tiles (a separate
 // instance, so the others keep the plain causal test).
-template <int D, int NW, bool LOCAL>
+template <int D, int NW, bool LOCAL, bool PROXY>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(FwdCfg<D, NW>::WAVES_PER_EU)))
 void bsa_fwd_kernel(const FwdParams p) {
   using C = FwdCfg<D, NW>;
   constexpr int DS = C::DS, DB = C::DB, DC = C::DC, RSK = C::RSK, RSV = C::RSV;
   __shared__ uint4 smem[C::STAGES * C::STAGE_SLOTS];
+  __shared__ uint32_t xbits[PROXY ? kProxyBitmapWords : 1];  // listed blocks (proxy route)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, l32 = lane & 31, h32 = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
 
   TileInfo ti;
-  if (!decode_tile<C::TM>(p, xcd_remap(blockIdx.x, p.num_tiles), ti)) return;
+  const int tix = xcd_remap(blockIdx.x, p.num_tiles);
+  if (!decode_tile<C::TM>(p, tix, ti)) return;
   const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + ti.qoff;
   const __bf16* kp = reinterpret_cast<const __bf16*>(p.k) + ti.koff;
   const __bf16* vp = reinterpret_cast<const __bf16*>(p.v) + ti.voff;
+  // proxy route (batched; summaries share K's and V's row strides, so the DMA
+  // lane offsets below serve both)
+  const __bf16* ksp = nullptr;
+  const __bf16* vsp = nullptr;
+  if constexpr (PROXY) {
+    const int bh = tix / p.tiles_per_head;
+    const int b = bh / p.H, hk = (bh % p.H) / p.hrep;
+    ksp = reinterpret_cast<const __bf16*>(p.ksum) + b * p.ks_sb + hk * p.ks_sh;
+    vsp = reinterpret_cast<const __bf16*>(p.vsum) + b * p.vs_sb + hk * p.vs_sh;
+    build_listed_bitmap(xbits, p, ti, tid, NW * 64);
+  }
 
   // Q fragments (S^T MFMA B operand): Q[qrow][16*ks + 8*h32 .. +7]
   const int qrow = ti.q0 + 32 * w + l32;
@@ -222,8 +236,12 @@ void bsa_fwd_kernel(const FwdParams p) {
   }
   const uint32_t lds_base = (uint32_t)(size_t)((lds_char*)smem);
   auto issue = [&](const Item& it, int stage) {
-    const char* kt = reinterpret_cast<const char*>(kp + it.key0 * p.k_ss);
-    const char* vt = reinterpret_cast<const char*>(vp + it.key0 * p.v_ss);
+    // the item is wave-uniform; the proxy instance says so explicitly, since
+    // the chunk walk's LDS reads hide it from the compiler (DMA bases are SGPRs)
+    const bool px = PROXY && __builtin_amdgcn_readfirstlane(it.is_mask) == 2;
+    const int key0 = PROXY ? __builtin_amdgcn_readfirstlane(it.key0) : it.key0;
+    const char* kt = reinterpret_cast<const char*>((px ? ksp : kp) + key0 * p.k_ss);
+    const char* vt = reinterpret_cast<const char*>((px ? vsp : vp) + key0 * p.v_ss);
     const uint32_t kl = lds_base + stage * C::STAGE_SLOTS * 16;
     const uint32_t vl = kl + C::KSLOTS * 16;
     // block ii*NW + w exists unless it is the last one of a wave and past RS
@@ -315,8 +333,12 @@ void bsa_fwd_kernel(const FwdParams p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     uint32_t pk0[8], pk1[8];
-    softmax_step<DB, LOCAL>(s0, s1, it, it.is_mask && list_masked, mlo, mhi, h32, p.c, m_run,
-                     l_run, oacc, pk0, pk1);
+    if constexpr (PROXY)
+      softmax_step_any<DB>(s0, s1, it, xbits, p.block_kv, ti.num_n, ti.Sk, h32, p.c, m_run,
+                           l_run, oacc, pk0, pk1);
+    else
+      softmax_step<DB, LOCAL>(s0, s1, it, it.is_mask && list_masked, mlo, mhi, h32, p.c, m_run,
+                              l_run, oacc, pk0, pk1);
     // PV step i: keys 16*(i / DB) .., head dims 32*(i % DB) ..
     auto vld = [&](int i) {
       const int ps = i / DB, db = i % DB;
@@ -342,15 +364,26 @@ void bsa_fwd_kernel(const FwdParams p) {
   // Two stages: the sub-tile after the one being computed streams into the
   // other stage.  One stage: the next sub-tile is fetched once every wave is
   // done with the current one.  p0 is the issued, not yet computed sub-tile.
+  // listed blocks, then (PROXY) the chunks of summaries holding an unlisted block
+  bool in_proxy = false;
+  int pn = 0;
+  auto step = [&](Item& it) -> bool {
+    if (!in_proxy) {
+      if (advance(it, L, lane, ti.Sk)) return true;
+      in_proxy = true;
+    }
+    if constexpr (PROXY) return next_proxy_chunk(xbits, ti.num_n, pn, it);
+    return false;
+  };
   Item walker{-1, 0, 0, 0, 0, 0, 0};
-  bool more = advance(walker, L, lane, ti.Sk);
+  bool more = step(walker);
   Item p0 = walker;
   bool pending = false;
   if (more) {
     issue(walker, 0);
     p0 = walker;
     pending = true;
-    more = advance(walker, L, lane, ti.Sk);
+    more = step(walker);
   }
   int stage = 0;
   if constexpr (STAGES == 1) {
@@ -363,7 +396,7 @@ void bsa_fwd_kernel(const FwdParams p) {
         __syncthreads();  // every wave done with the stage before it is refilled
         issue(walker, 0);
         p0 = walker;
-        more = advance(walker, L, lane, ti.Sk);
+        more = step(walker);
       } else {
         pending = false;
       }
@@ -378,7 +411,7 @@ void bsa_fwd_kernel(const FwdParams p) {
     if (more) {
       issue(walker, stage ^ 1);
       p0 = walker;
-      more = advance(walker, L, lane, ti.Sk);
+      more = step(walker);
     } else {
       pending = false;
     }
@@ -392,9 +425,10 @@ template <int D, int NW>
 hipError_t launch_one(const FwdParams& p, hipStream_t s) {
   FwdParams copy = p;
   void* args[] = {&copy};
-  const void* k = p.mask_mod == kMaskLocal
-                      ? reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, true>)
-                      : reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, false>);
+  const void* k = p.ksum ? reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, false, true>)
+                  : p.mask_mod == kMaskLocal
+                      ? reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, true, false>)
+                      : reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, false, false>);
   return hipLaunchKernel(k, dim3(p.num_tiles), dim3(NW * 64), args, 0, s);
 }
 

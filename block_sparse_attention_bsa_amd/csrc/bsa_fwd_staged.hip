@@ -21,6 +21,7 @@
 #include <type_traits>
 
 #include "bsa_fwd_common.h"
+#include "bsa_fwd_proxy.h"
 
 namespace bsa {
 namespace {
@@ -49,58 +50,6 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// softmax_step for a chunk of summaries: keys n0 .. n0+nk-1 (n0 = it.key0,
-// a multiple of 64); bit k of ex0 / ex1 set means summary n0+k / n0+32+k is
-// a listed block (no proxy).  The row sum adds mass(n) * p, where mass(n) is
-// wfull for every block but the last (n == tail_n), whose mass is wtail; the
-// PV product takes p as is.
-template <int DB>
-__device__ __forceinline__ void proxy_softmax_step(f32x16_t& s0, f32x16_t& s1, const Item& it,
-                                                   uint32_t ex0, uint32_t ex1, float wfull,
-                                                   int tail_n, float wtail, int h32, float c,
-                                                   float& m_run, float& l_run,
-                                                   f32x16_t (&oacc)[DB], uint32_t (&pk0)[8],
-                                                   uint32_t (&pk1)[8]) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int key = 16 * (r >> 3) + 8 * h32 + (r & 7);
-    if (!(key < it.nk && ((ex0 >> key) & 1u) == 0)) s0[r] = neg_inf();
-    if (!(key + 32 < it.nk && ((ex1 >> key) & 1u) == 0)) s1[r] = neg_inf();
-  }
-  float mx = neg_inf();
-#pragma unroll
-  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(m_run, mx * c);
-  if (__any(m_new > m_run)) {
-    const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    l_run *= alpha;
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-    m_run = m_new;
-  }
-  const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
-  const int tk = tail_n - it.key0;  // chunk-local key of the last block (may be outside)
-  float ls = 0.f, lt = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int k0 = 16 * (i >> 2) + 8 * h32 + ((2 * i) & 7);  // key of element 2i of s0
-    const float a0 = __builtin_amdgcn_exp2f(fmaf(s0[2 * i], c, -m_use));
-    const float a1 = __builtin_amdgcn_exp2f(fmaf(s0[2 * i + 1], c, -m_use));
-    const float b0 = __builtin_amdgcn_exp2f(fmaf(s1[2 * i], c, -m_use));
-    const float b1 = __builtin_amdgcn_exp2f(fmaf(s1[2 * i + 1], c, -m_use));
-    pk0[i] = pack_bf16x2(a0, a1);
-    pk1[i] = pack_bf16x2(b0, b1);
-    ls += (a0 + a1) + (b0 + b1);
-    lt += (k0 == tk ? a0 : 0.f) + (k0 + 1 == tk ? a1 : 0.f) + (k0 + 32 == tk ? b0 : 0.f) +
-          (k0 + 33 == tk ? b1 : 0.f);
-  }
-  l_run += fmaf(wtail - wfull, lt, wfull * ls);
-}
-
 template <int D, int NW, bool F32IN, bool PROXY>
 __global__ __launch_bounds__(NW * 64) void bsa_fwd_staged_kernel(const FwdParams p) {
   using T = typename std::conditional<F32IN, float, __bf16>::type;
@@ -122,7 +71,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_staged_kernel(const FwdParams
 
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
   // listed blocks of this Q block (+1 word: a chunk's second word may lie past the last)
-  __shared__ uint32_t xbits[PROXY ? kProxyMaxBlocks / 32 + 1 : 1];
+  __shared__ uint32_t xbits[PROXY ? kProxyBitmapWords : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, l32 = lane & 31, h32 = lane >> 5;
@@ -140,18 +89,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_staged_kernel(const FwdParams
     const int b = bh / p.H, hk = (bh % p.H) / p.hrep;
     ksp = reinterpret_cast<const T*>(p.ksum) + b * p.ks_sb + hk * p.ks_sh;
     vsp = reinterpret_cast<const T*>(p.vsum) + b * p.vs_sb + hk * p.vs_sh;
-    const int nwords = (ti.num_n + 31) / 32 + 1;
-    for (int i = tid; i < nwords; i += NT) xbits[i] = 0u;
-    __syncthreads();
-    for (int e = tid; e < ti.mcnt; e += NT) {
-      const int j = ti.mrow[(int64_t)e * p.mi_s[3]];
-      if ((unsigned)j < (unsigned)ti.num_n) atomicOr(&xbits[j >> 5], 1u << (j & 31));
-    }
-    for (int e = tid; e < ti.fcnt; e += NT) {
-      const int j = ti.frow[(int64_t)e * p.fi_s[3]];
-      if ((unsigned)j < (unsigned)ti.num_n) atomicOr(&xbits[j >> 5], 1u << (j & 31));
-    }
-    __syncthreads();
+    build_listed_bitmap(xbits, p, ti, tid, NT);
   }
 
   const int qrow = ti.q0 + 32 * w + l32;
@@ -261,12 +199,9 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_staged_kernel(const FwdParams
       s1 = mfma32(a1, qf[ks], s1);
     }
     uint32_t pk0[8], pk1[8];
-    if (PROXY && it.is_mask == 2) {
-      const int n0 = it.key0;
-      proxy_softmax_step<DB>(s0, s1, it, xbits[n0 >> 5], xbits[(n0 >> 5) + 1],
-                             (float)p.block_kv, ti.num_n - 1,
-                             (float)(ti.Sk - (ti.num_n - 1) * p.block_kv), h32, p.c, m_run,
-                             l_run, oacc, pk0, pk1);
+    if constexpr (PROXY) {
+      softmax_step_any<DB>(s0, s1, it, xbits, p.block_kv, ti.num_n, ti.Sk, h32, p.c, m_run,
+                           l_run, oacc, pk0, pk1);
     } else {
       softmax_step<DB, true>(s0, s1, it, it.is_mask && list_masked, mlo, mhi, h32, p.c, m_run,
                              l_run, oacc, pk0, pk1);
@@ -295,20 +230,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_staged_kernel(const FwdParams
       if (advance(it, L, lane, ti.Sk)) return true;
       in_proxy = true;
     }
-    if constexpr (PROXY) {
-      while (pn < ti.num_n) {
-        const int n0 = pn;
-        pn += kKvTile;
-        const int nk = min(kKvTile, ti.num_n - n0);
-        const uint64_t live = nk >= 64 ? ~0ull : ((1ull << nk) - 1);
-        const uint64_t ex = (uint64_t)xbits[n0 >> 5] | ((uint64_t)xbits[(n0 >> 5) + 1] << 32);
-        if ((~ex & live) == 0) continue;  // every block of the chunk is listed
-        it.key0 = n0;
-        it.nk = nk;
-        it.is_mask = 2;
-        return true;
-      }
-    }
+    if constexpr (PROXY) return next_proxy_chunk(xbits, ti.num_n, pn, it);
     return false;
   };
   Item cur{-1, 0, 0, 0, 0, 0, 0};
@@ -373,7 +295,7 @@ hipError_t launch_fwd_staged(const FwdParams& p, int D, int tile_m, bool f32_in,
   return f32_in ? launch_d<true, false>(p, D, tile_m, s) : launch_d<false, false>(p, D, tile_m, s);
 }
 
-hipError_t launch_fwd_proxy(const FwdParams& p, int D, int tile_m, hipStream_t s) {
+hipError_t launch_fwd_proxy_staged(const FwdParams& p, int D, int tile_m, hipStream_t s) {
   return launch_d<false, true>(p, D, tile_m, s);
 }
 

@@ -59,8 +59,10 @@ struct FwdParams {
 // checks support first).
 hipError_t launch_fwd(const FwdParams& p, int D, int tile_m, bool f32_in, hipStream_t s);
 hipError_t launch_fwd_staged(const FwdParams& p, int D, int tile_m, bool f32_in, hipStream_t s);
-// bf16 staged kernel with the proxy-compensated route (batched, no element mask)
-hipError_t launch_fwd_proxy(const FwdParams& p, int D, int tile_m, hipStream_t s);
+// bf16 staged kernel with the proxy-compensated route (batched, no element
+// mask, any summary strides); launch_fwd takes the route itself (p.ksum set)
+// when the summaries share K's and V's row strides.
+hipError_t launch_fwd_proxy_staged(const FwdParams& p, int D, int tile_m, hipStream_t s);
 // 256-row ping-pong kernel (bf16, D in {64, 96, 128}).
 hipError_t launch_fwd_pp(const FwdParams& p, int D, hipStream_t s);
 

@@ -64,14 +64,30 @@ def test_proxy_matches_oracle(case):
     check_o_lse(o, lse, O, L, f"proxy {case}")
 
 
-def test_all_listed_rows_ignore_the_summaries():
-    q, k, v, full, part, ks, vs = _case(11, 1, 256, 640, 2, 1, 128, 128, 128, 1.0)
-    a = bsa.bsa_fwd(q, k, v, _lists(part), _lists(full), 128, 128, bsa.MASK_NONE, None, 0.1,
-                    proxy=(ks, vs))
-    b = bsa.bsa_fwd(q, k, v, _lists(part), _lists(full), 128, 128, bsa.MASK_NONE, None, 0.1,
+@pytest.mark.parametrize("bq,bk", [(128, 128), (64, 64)])
+def test_all_listed_rows_equal_the_plain_forward_bit_for_bit(bq, bk):
+    """Summaries of listed blocks never enter, and exact blocks take the
+    plain kernel's arithmetic."""
+    q, k, v, full, part, ks, vs = _case(11, 1, 256, 640, 2, 1, 128, bq, bk, 1.0)
+    a = bsa.bsa_fwd(q, k, v, _lists(part), _lists(full), bq, bk, bsa.MASK_NONE, None, 0.1,
                     proxy=(torch.randn_like(ks), torch.randn_like(vs)))
+    b = bsa.bsa_fwd(q, k, v, _lists(part), _lists(full), bq, bk, bsa.MASK_NONE, None, 0.1)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("D,bq,bk", [(128, 128, 64), (64, 64, 48)])
+def test_summaries_in_another_layout(D, bq, bk):
+    """Summaries whose row stride differs from K's and V's take the
+    register-staged kernel; both layouts match the oracle."""
+    q, k, v, full, part, ks, vs = _case(13, 2, 300, 900, 4, 2, D, bq, bk, 0.3)
+    ks2 = ks.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)  # [B,N,Hkv,D], row stride D
+    vs2 = vs.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    assert ks2.stride(1) != k.stride(1)
+    o, lse, O, L = _run(q, k, v, full, part, ks2, vs2, bq, bk)
+    check_o_lse(o, lse, O, L, f"proxy, summaries [B,Hkv,N,D] d{D}")
+    o1, l1, _, _ = _run(q, k, v, full, part, ks, vs, bq, bk)
+    check_o_lse(o1, l1, O, L, f"proxy, summaries [B,N,Hkv,D] d{D}")
 
 
 def test_pages_workload_sampled():

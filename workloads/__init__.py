@@ -231,6 +231,24 @@ def sliding_window(B=2, H=16, S=8192, D=128, bs=128, window=(1024, 0),
                           tuple(window), 1.0 / math.sqrt(D))
 
 
+def proxy_routes(B=1, S=32760, H=12, D=128, bs=64, per_row=84,
+                 seed: int = 1007) -> BatchedWorkload:
+    """The proxy-route workload of the PrimTS page (its proxy-overhead table):
+    B1, 32760 tokens, 12 heads, d128, 64x64 blocks, 84 of the 512 KV blocks
+    listed per Q-block row (16.4 %), drawn uniformly per (head, Q block), no
+    element mask.  The last KV block holds 56 tokens."""
+    rng = np.random.default_rng(seed)
+    q, k, v = _qkv(rng, (B, S, H, D), (B, S, H, D))
+    M = N = _cdiv(S, bs)
+    full = np.zeros((B, H, M, N), bool)
+    for b in range(B):
+        for h in range(H):
+            for i in range(M):
+                full[b, h, i, rng.choice(N, per_row, replace=False)] = True
+    return BatchedWorkload(f"proxy_routes_{per_row}of{N}", q, k, v, full, np.zeros_like(full),
+                           bs, bs, MASK_NONE, 1.0 / math.sqrt(D))
+
+
 def _cube_layout(grid, cube):
     """Valid-token count of each cube (cube-major order t, h, w) and, for each
     real token of the grid (t, h, w order), its padded row."""
