@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "MASK_NONE", "MASK_CAUSAL", "MASK_KV_VALID_COUNT", "MASK_LOCAL", "BsaError",
-    "bsa_fwd", "bsa_varlen_fwd", "bsa_mask_to_index", "bsa_bitmask_to_index",
+    "bsa_fwd", "bsa_varlen_fwd", "bsa_mask_to_index", "bsa_bitmask_to_index", "bsa_kv_major_lists",
     "bsa_varlen_mask_to_index",
     "bsa_varlen_offsets", "bsa_expand_kv_blocks", "bsa_block_sparsity", "bsa_status_str",
     "library_path", "load_library",
@@ -97,6 +97,7 @@ def load_library():
                                    P, P, P, P, I32, I32, I32, I64P, I64P, I64P, I64P, BS,
                                    ctypes.c_int, F32, U32, P]
     lib.bsa_mask_to_index.argtypes = [P, I32, I32, I32, I32, P, P, P]
+    lib.bsa_kv_major_lists.argtypes = [P, P, I32, I32, I32, I32, P, P, P, P]
     lib.bsa_bitmask_to_index.argtypes = [P, I32, I32, I32, I32, I32, P, P, P]
     lib.bsa_varlen_mask_to_index.argtypes = [P, I32, I32, P, P, I32, I32, P, P, P]
     I32P = ctypes.POINTER(ctypes.c_int32)
@@ -333,6 +334,28 @@ def bsa_mask_to_index(mask: torch.Tensor, cnt: Optional[torch.Tensor] = None,
     st = lib.bsa_mask_to_index(_ptr(mask), B, H, M, N, _ptr(cnt), _ptr(idx), _stream(mask))
     _check("bsa_mask_to_index", st)
     return cnt, idx
+
+
+def bsa_kv_major_lists(lists: Tuple[torch.Tensor, torch.Tensor]):
+    """Block lists (cnt int32 [B,H,M], idx int32 [B,H,M,N], contiguous, as
+    bsa_mask_to_index writes them) -> KV-major lists (cnt_t int32 [B,H,N],
+    idx_t int32 [B,H,N,M]): per KV block, the Q blocks that list it, in
+    descending order, then -1."""
+    lib = load_library()
+    cnt, idx = lists
+    _dev("cnt", cnt, torch.int32)
+    _dev("idx", idx, torch.int32)
+    if idx.dim() != 4 or cnt.shape != idx.shape[:3] or not cnt.is_contiguous() \
+            or not idx.is_contiguous():
+        raise ValueError("lists must be contiguous int32 [B,H,M] / [B,H,M,N] tensors")
+    B, H, M, N = idx.shape
+    work = torch.empty((B, H, N, M), dtype=torch.uint8, device=idx.device)
+    cnt_t = torch.empty((B, H, N), dtype=torch.int32, device=idx.device)
+    idx_t = torch.empty((B, H, N, M), dtype=torch.int32, device=idx.device)
+    st = lib.bsa_kv_major_lists(_ptr(cnt), _ptr(idx), B, H, M, N, _ptr(work), _ptr(cnt_t),
+                                _ptr(idx_t), _stream(idx))
+    _check("bsa_kv_major_lists", st)
+    return cnt_t, idx_t
 
 
 def bsa_bitmask_to_index(words: torch.Tensor, N: int, H: Optional[int] = None,

@@ -396,6 +396,16 @@ bsa_status bsa_mask_to_index(const uint8_t* mask, int32_t B, int32_t H, int32_t 
   return e == hipSuccess ? BSA_OK : BSA_ERR_HIP;
 }
 
+bsa_status bsa_kv_major_lists(const int32_t* cnt, const int32_t* idx, int32_t B, int32_t H,
+                              int32_t M, int32_t N, uint8_t* work, int32_t* cnt_t,
+                              int32_t* idx_t, hipStream_t stream) {
+  if (B < 0 || H < 0 || M < 0 || N < 0) return BSA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)B * H * N == 0) return BSA_OK;
+  if (!cnt_t || (M > 0 && (!cnt || !idx || !work || !idx_t))) return BSA_ERR_INVALID_ARGUMENT;
+  const hipError_t e = bsa::launch_kv_major_lists(cnt, idx, B, H, M, N, work, cnt_t, idx_t, stream);
+  return e == hipSuccess ? BSA_OK : BSA_ERR_HIP;
+}
+
 bsa_status bsa_bitmask_to_index(const uint32_t* words, int32_t B, int32_t Hkv, int32_t H,
                                 int32_t M, int32_t N, int32_t* cnt, int32_t* idx,
                                 hipStream_t stream) {

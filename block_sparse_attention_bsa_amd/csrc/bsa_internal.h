@@ -66,6 +66,9 @@ hipError_t launch_fwd_proxy_staged(const FwdParams& p, int D, int tile_m, hipStr
 // 256-row ping-pong kernel (bf16, D in {64, 96, 128}).
 hipError_t launch_fwd_pp(const FwdParams& p, int D, hipStream_t s);
 
+hipError_t launch_kv_major_lists(const int32_t* cnt, const int32_t* idx, int32_t B, int32_t H,
+                                 int32_t M, int32_t N, uint8_t* work, int32_t* cnt_t,
+                                 int32_t* idx_t, hipStream_t s);
 hipError_t launch_bitmask_to_index(const uint32_t* words, int32_t B, int32_t Hkv, int32_t H,
                                   int32_t M, int32_t N, int32_t* cnt, int32_t* idx, hipStream_t s);
 hipError_t launch_mask_to_index(const uint8_t* mask, int64_t rows, int32_t N,

@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "bsa_internal.h"
 
 namespace bsa {
@@ -194,6 +196,46 @@ hipError_t launch_bitmask_to_index(const uint32_t* words, int32_t B, int32_t Hkv
   hipLaunchKernelGGL(bitmask_to_index_kernel, dim3((unsigned)blocks), dim3(64 * kWavesPerBlock),
                      0, s, words, rows, H, H / Hkv, M, N, (N + 31) / 32, cnt, idx);
   return hipGetLastError();
+}
+
+// KV-major lists (for a pass that walks, per KV block, the Q blocks that list
+// it): clear a dense transposed mask, scatter every list entry into it, then
+// compact its rows like mask_to_index.
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint8_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0;
+}
+
+__global__ __launch_bounds__(256) void scatter_transposed_kernel(
+    const int32_t* __restrict__ cnt, const int32_t* __restrict__ idx, int64_t rows, int32_t M,
+    int32_t N, uint8_t* __restrict__ mt) {
+  const int64_t total = rows * N;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * 256) {
+    const int64_t row = e / N;  // (b*H + h)*M + i
+    const int32_t s = (int32_t)(e - row * N);
+    if (s >= min(max(cnt[row], 0), N)) continue;
+    const int32_t j = idx[e];
+    if (j < 0 || j >= N) continue;
+    const int64_t bh = row / M;
+    const int32_t i = (int32_t)(row - bh * M);
+    mt[(bh * N + j) * M + i] = 1;
+  }
+}
+
+hipError_t launch_kv_major_lists(const int32_t* cnt, const int32_t* idx, int32_t B, int32_t H,
+                                 int32_t M, int32_t N, uint8_t* work, int32_t* cnt_t,
+                                 int32_t* idx_t, hipStream_t s) {
+  const int64_t rows = (int64_t)B * H * M;
+  const int64_t cells = rows * N;
+  if ((int64_t)B * H * N == 0) return hipSuccess;
+  if (cells > 0) {
+    const unsigned g = (unsigned)std::min<int64_t>((cells + 255) / 256, 65536);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(g), dim3(256), 0, s, work, cells);
+    hipLaunchKernelGGL(scatter_transposed_kernel, dim3(g), dim3(256), 0, s, cnt, idx, rows, M,
+                       N, work);
+  }
+  return launch_mask_to_index(work, (int64_t)B * H * N, M, cnt_t, idx_t, s);
 }
 
 hipError_t launch_varlen_mask_to_index(const uint8_t* mask, int32_t H, int32_t B,

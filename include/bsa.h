@@ -180,6 +180,21 @@ bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, 
 bsa_status bsa_mask_to_index(const uint8_t* mask, int32_t B, int32_t H, int32_t M, int32_t N,
                              int32_t* cnt, int32_t* idx, hipStream_t stream);
 
+/* KV-major ("transposed") block lists: the per-KV-block view that a backward
+ * pass walks (flash-attention pull request 2224, review thread: the backward
+ * needs the block metadata transposed).  cnt: device int32 [B,H,M] and idx:
+ * device int32 [B,H,M,N], contiguous, in the format of bsa_mask_to_index
+ * (the first cnt entries of a row are read; ids outside [0,N) are skipped).
+ * work: device scratch of B*H*N*M bytes, overwritten.  Writes cnt_t: device
+ * int32 [B,H,N] (how many Q blocks list KV block j) and idx_t: device int32
+ * [B,H,N,M] (those Q-block ids in descending order, then -1).  Convert the
+ * mask and full lists separately.  Caller owns every buffer.  Returns
+ * BSA_ERR_INVALID_ARGUMENT for negative sizes or a missing pointer,
+ * BSA_ERR_HIP if a launch fails.  Bit-exact; deterministic. */
+bsa_status bsa_kv_major_lists(const int32_t* cnt, const int32_t* idx, int32_t B, int32_t H,
+                              int32_t M, int32_t N, uint8_t* work, int32_t* cnt_t,
+                              int32_t* idx_t, hipStream_t stream);
+
 /* Packed UInt32 block bitmap -> block lists (the bitmap input of the PrimTS
  * page, "proxy-compensated block-sparse attention", flashinfer pull request
  * 4872: description and test notes).  words: device uint32 [B,Hkv,M,W]

@@ -1,4 +1,4 @@
-"""GPU: the packed UInt32 block bitmap input.  bsa_bitmask_to_index must match
+"""GPU: the packed UInt32 block bitmap input and the KV-major block lists.  bsa_bitmask_to_index must match
 oracle.bitmask_to_index bit for bit (padding bits set on purpose), and a
 forward over bitmap-derived lists must equal, bit for bit, the forward over
 the lists of the same selection given as a dense uint8 mask."""
@@ -108,3 +108,17 @@ def test_bad_bitmaps_are_rejected():
         bsa.bsa_bitmask_to_index(w, 40, H=3)     # H not a multiple of Hkv
     with pytest.raises(ValueError):
         bsa.bsa_bitmask_to_index(w.to(torch.int64), 40)
+
+
+@pytest.mark.parametrize("B,H,M,N,density", [(1, 1, 3, 4, 0.5), (2, 3, 17, 9, 0.3),
+                                              (1, 2, 5, 130, 0.2), (2, 2, 64, 64, 0.0),
+                                              (1, 4, 40, 33, 1.0), (1, 1, 1, 1, 1.0)])
+def test_kv_major_lists_match_oracle_bit_exact(B, H, M, N, density):
+    rng = np.random.default_rng(B * 100 + M + N)
+    mask = rng.random((B, H, M, N)) < density
+    cnt, idx = bsa.bsa_mask_to_index(torch.from_numpy(mask.astype(np.uint8)).cuda())
+    cnt_t, idx_t = bsa.bsa_kv_major_lists((cnt, idx))
+    torch.cuda.synchronize()
+    c_ref, i_ref = oracle.kv_major_lists(mask)
+    np.testing.assert_array_equal(cnt_t.cpu().numpy(), c_ref)
+    np.testing.assert_array_equal(idx_t.cpu().numpy(), i_ref)
