@@ -18,6 +18,7 @@ import torch
 __all__ = [
     "MASK_NONE", "MASK_CAUSAL", "MASK_KV_VALID_COUNT", "MASK_LOCAL", "BsaError",
     "bsa_fwd", "bsa_varlen_fwd", "bsa_mask_to_index", "bsa_bitmask_to_index", "bsa_kv_major_lists",
+    "bsa_bwd",
     "bsa_varlen_mask_to_index",
     "bsa_varlen_offsets", "bsa_expand_kv_blocks", "bsa_block_sparsity", "bsa_status_str",
     "library_path", "load_library",
@@ -97,6 +98,8 @@ def load_library():
                                    P, P, P, P, I32, I32, I32, I64P, I64P, I64P, I64P, BS,
                                    ctypes.c_int, F32, U32, P]
     lib.bsa_mask_to_index.argtypes = [P, I32, I32, I32, I32, P, P, P]
+    lib.bsa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
+                            P, P, P, P, P, P, P, ctypes.c_int, P, ctypes.c_float, P, P]
     lib.bsa_kv_major_lists.argtypes = [P, P, I32, I32, I32, I32, P, P, P, P]
     lib.bsa_bitmask_to_index.argtypes = [P, I32, I32, I32, I32, I32, P, P, P]
     lib.bsa_varlen_mask_to_index.argtypes = [P, I32, I32, P, P, I32, I32, P, P, P]
@@ -334,6 +337,63 @@ def bsa_mask_to_index(mask: torch.Tensor, cnt: Optional[torch.Tensor] = None,
     st = lib.bsa_mask_to_index(_ptr(mask), B, H, M, N, _ptr(cnt), _ptr(idx), _stream(mask))
     _check("bsa_mask_to_index", st)
     return cnt, idx
+
+
+def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+            lse: torch.Tensor, dout: torch.Tensor,
+            mask_list: Optional[Tuple[torch.Tensor, torch.Tensor]],
+            full_list: Optional[Tuple[torch.Tensor, torch.Tensor]],
+            block_q: int, block_kv: int, mask_mod: int = MASK_NONE,
+            kv_valid: Optional[torch.Tensor] = None, softmax_scale: Optional[float] = None,
+            window: Optional[Tuple[int, int]] = None):
+    """Backward of bsa_fwd (bf16, head_dim 64 or 128): returns (dq, dk, dv).
+    o and lse are the forward's outputs, dout the gradient of o; the lists,
+    block sizes, mask_mod, kv_valid, scale and window are the forward's.  The
+    KV-major lists are built here with bsa_kv_major_lists."""
+    lib = load_library()
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _dev(n, t, torch.bfloat16)
+        if t.dim() != 4 or t.stride(-1) != 1:
+            raise ValueError(f"{n} must be 4-D with a contiguous last dimension")
+    _dev("lse", lse, torch.float32)
+    B, Sq, H, D = q.shape
+    Bk, Sk, Hkv, Dk = k.shape
+    if Bk != B or Dk != D or tuple(v.shape) != tuple(k.shape) or o.shape != q.shape \
+            or dout.shape != q.shape or tuple(lse.shape) != (B, H, Sq) or not lse.is_contiguous():
+        raise ValueError("shapes: q/o/dout [B,Sq,H,D], k/v [B,Sk,Hkv,D], lse [B,H,Sq]")
+    if dout.stride() != o.stride():
+        o, dout = o.contiguous(), dout.contiguous()
+    M, N = -(-Sq // block_q), -(-Sk // block_kv)
+
+    def full_shape(lst):
+        if lst is None:
+            return None
+        cnt, idx = lst
+        return (cnt.expand(B, H, M).contiguous(), idx.expand(B, H, M, N).contiguous())
+    ml, fl = full_shape(mask_list), full_shape(full_list)
+    mt = bsa_kv_major_lists(ml) if ml is not None else None
+    ft = bsa_kv_major_lists(fl) if fl is not None else None
+    bs = _BlockSparse(_block_list(ml, True, (B, H, M, N)), _block_list(fl, True, (B, H, M, N)),
+                      int(block_q), int(block_kv), *_window(mask_mod, window))
+    lt_m = _block_list(mt, True, (B, H, N, M))
+    lt_f = _block_list(ft, True, (B, H, N, M))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
+        raise ValueError("q, k and v must be dense (their gradients take their strides)")
+    work = torch.empty(max(B * H * Sq, 1), dtype=torch.float32, device=q.device)
+    if kv_valid is not None:
+        _dev("kv_valid", kv_valid, torch.int32)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    st = lib.bsa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                     _ptr(dk), _ptr(dv), B, H, Hkv, Sq, Sk, D,
+                     _i64([q.stride(0), q.stride(1), q.stride(2)]),
+                     _i64([k.stride(0), k.stride(1), k.stride(2)]),
+                     _i64([v.stride(0), v.stride(1), v.stride(2)]),
+                     _i64([o.stride(0), o.stride(1), o.stride(2)]),
+                     ctypes.byref(bs), ctypes.byref(lt_m), ctypes.byref(lt_f), int(mask_mod),
+                     _ptr(kv_valid), scale, _ptr(work), _stream(q))
+    _check("bsa_bwd", st)
+    return dq, dk, dv
 
 
 def bsa_kv_major_lists(lists: Tuple[torch.Tensor, torch.Tensor]):

@@ -1,0 +1,409 @@
+// Backward of block-sparse attention (gfx950, bf16 Q/K/V/O/dO).
+//
+// The pages name the backward as the missing half of the method and say it
+// walks the block metadata transposed (flash-attention pull request 2224,
+// review thread).  This is the gradient of the forward over the listed
+// blocks, with the forward's LSE:
+//   P = exp(scale*S - LSE), dV = P^T dO, dP = dO V^T, D = rowsum(dO * O),
+//   dS = P * (dP - D), dQ = scale * dS K, dK = scale * dS^T Q.
+// Three launches on the caller's stream:
+//   1. bwd_rowdot_kernel: D per row (fp32 workspace).
+//   2. bwd_dq_kernel: one workgroup per 64 rows of a Q block, walking the
+//      forward's lists in 64-key sub-tiles.  S and dP^T come from K and V
+//      rows in LDS against Q and dO in registers; dQ accumulates dS times K
+//      read transposed from LDS.  The layouts are those of the forward: a lane
+//      owns one query row, P and dS feed the last product straight from
+//      registers.
+//   3. bwd_dkdv_kernel: one workgroup per 64 keys of a KV block, walking the
+//      KV-major lists (the Q blocks that list the KV block) of every Q head of
+//      its KV head, in 64-row sub-tiles.  The roles swap: a lane owns one key,
+//      K and V sit in registers, Q and dO rows (and their transposes) in LDS.
+//      Summing the group's heads in one workgroup needs no atomics.
+// Each sub-tile is loaded, converted and transposed through registers by all
+// threads, then computed; one LDS stage.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bsa_fwd_common.h"
+
+namespace bsa {
+namespace {
+
+using namespace dev;
+
+constexpr int kBwdNW = 2;              // waves per workgroup
+constexpr int kBwdNT = kBwdNW * 64;    // threads
+constexpr int kBwdT = 64;              // rows (dQ) / keys (dK, dV) per workgroup, and sub-tile size
+
+__device__ __forceinline__ uint32_t word4(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Element rule of a mask-list block (row and key are sequence positions;
+// kib is the key's offset inside its KV block j).
+__device__ __forceinline__ bool keep_elem(const BwdParams& p, int row, int key, int j, int kib) {
+  switch (p.mask_mod) {
+    case kMaskCausal: return key <= row;
+    case kMaskKvValid: return kib < p.kv_valid[j];
+    case kMaskLocal:
+      return (p.win_left < 0 || row - key <= p.win_left) &&
+             (p.win_right < 0 || key - row <= p.win_right);
+    default: return true;
+  }
+}
+
+// Rows r0 .. r0+n-1 (n <= 64) of a [*, D] bf16 tensor (row stride ss) into
+// LDS: row-major at rm (row pitch RM bytes) and/or transposed at tr (tr[d] is
+// a row of 64 keys/rows, pitch TR bytes).  Rows past n are zero.  Every
+// thread of the workgroup calls it; no barrier inside.
+template <int D>
+__device__ __forceinline__ void stage_rows(const __bf16* base, int64_t ss, int n,
+                                           unsigned char* rm, unsigned char* tr, int tid) {
+  constexpr int DC = D / 8;
+  constexpr int RM = D * 2 + 16;
+  constexpr int TR = kBwdT * 2 + 16;
+  constexpr int BL = (kBwdT / 4) * DC;  // blocks of 4 rows x 8 dims
+  for (int bi = tid; bi < BL; bi += kBwdNT) {
+    const int g = bi / DC, dc = bi % DC;
+    uint4 r[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int row = 4 * g + rr;
+      r[rr] = row < n ? *reinterpret_cast<const uint4*>(base + (int64_t)row * ss + dc * 8)
+                      : make_uint4(0, 0, 0, 0);
+      if (rm) *reinterpret_cast<uint4*>(rm + row * RM + dc * 16) = r[rr];
+    }
+    if (tr) {
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const uint32_t x0 = word4(r[0], dd >> 1), x1 = word4(r[1], dd >> 1);
+        const uint32_t x2 = word4(r[2], dd >> 1), x3 = word4(r[3], dd >> 1);
+        uint2 out;
+        if ((dd & 1) == 0) {
+          out.x = (x0 & 0xffffu) | (x1 << 16);
+          out.y = (x2 & 0xffffu) | (x3 << 16);
+        } else {
+          out.x = (x0 >> 16) | (x1 & 0xffff0000u);
+          out.y = (x2 >> 16) | (x3 & 0xffff0000u);
+        }
+        *reinterpret_cast<uint2*>(tr + (dc * 8 + dd) * TR + g * 8) = out;
+      }
+    }
+  }
+}
+
+// B-operand fragments of one row (query row for dQ, key for dK/dV):
+// frag[ks] = X[row][16*ks + 8*h32 .. +7], zero when the row is invalid.
+template <int D>
+__device__ __forceinline__ void row_frags(const __bf16* rowp, bool valid, int h32,
+                                          uint4 (&frag)[D / 16]) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    frag[ks] = valid ? *reinterpret_cast<const uint4*>(rowp + ks * 16 + h32 * 8)
+                     : make_uint4(0, 0, 0, 0);
+}
+
+// Product over head_dim of two 32x32 tiles: rows arow / arow+32 of the LDS
+// tile (pitch RM) against this lane's fragments.
+template <int D>
+__device__ __forceinline__ void tile_dot(const unsigned char* lds, int arow, int h32,
+                                         const uint4 (&frag)[D / 16], f32x16_t& s0,
+                                         f32x16_t& s1) {
+  constexpr int RM = D * 2 + 16;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    s0[r] = 0.f;
+    s1[r] = 0.f;
+  }
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const uint4 a0 = *reinterpret_cast<const uint4*>(lds + arow * RM + ks * 32 + h32 * 16);
+    const uint4 a1 = *reinterpret_cast<const uint4*>(lds + (arow + 32) * RM + ks * 32 + h32 * 16);
+    s0 = mfma32(a0, frag[ks], s0);
+    s1 = mfma32(a1, frag[ks], s1);
+  }
+}
+
+// acc[db] += T^T(LDS, transposed tile: tr[d][64]) x operand(pk), over the 64
+// positions of the sub-tile.
+template <int DB>
+__device__ __forceinline__ void tr_product(const unsigned char* tr, int arow, int h32,
+                                           const uint32_t (&pk0)[8], const uint32_t (&pk1)[8],
+                                           f32x16_t (&acc)[DB]) {
+  constexpr int TR = kBwdT * 2 + 16;
+#pragma unroll
+  for (int ps = 0; ps < 4; ++ps) {
+    const uint4 bop = p_operand(pk0, pk1, ps);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const uint4 a =
+          *reinterpret_cast<const uint4*>(tr + (db * 32 + arow) * TR + ps * 32 + h32 * 16);
+      acc[db] = mfma32(a, bop, acc[db]);
+    }
+  }
+}
+
+// acc (rows of head_dim per lane, the forward's output layout) * mul -> bf16 row.
+template <int DB>
+__device__ __forceinline__ void store_row(__bf16* dst, int h32, const f32x16_t (&acc)[DB],
+                                          float mul) {
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int r0 = 8 * half;
+      *reinterpret_cast<uint4*>(dst + db * 32 + 16 * half + 8 * h32) =
+          make_uint4(pack_bf16x2(acc[db][r0] * mul, acc[db][r0 + 1] * mul),
+                     pack_bf16x2(acc[db][r0 + 2] * mul, acc[db][r0 + 3] * mul),
+                     pack_bf16x2(acc[db][r0 + 4] * mul, acc[db][r0 + 5] * mul),
+                     pack_bf16x2(acc[db][r0 + 6] * mul, acc[db][r0 + 7] * mul));
+    }
+}
+
+// D[b,h,r] = sum_d dO * O (fp32), one thread per row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_rowdot_kernel(const BwdParams p) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rows = (int64_t)p.B * p.H * p.Sq;
+  if (t >= rows) return;
+  const int r = (int)(t % p.Sq);
+  const int64_t bh = t / p.Sq;
+  const int h = (int)(bh % p.H), b = (int)(bh / p.H);
+  const __bf16* o = reinterpret_cast<const __bf16*>(p.o) + b * p.o_sb + r * p.o_ss + h * p.o_sh;
+  const __bf16* g = reinterpret_cast<const __bf16*>(p.dout) + b * p.do_sb + r * p.do_ss + h * p.do_sh;
+  float acc = 0.f;
+  for (int c = 0; c < D / 8; ++c) {
+    const uint4 a = *reinterpret_cast<const uint4*>(o + c * 8);
+    const uint4 e = *reinterpret_cast<const uint4*>(g + c * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t x = word4(a, i), y = word4(e, i);
+      acc = fmaf(__uint_as_float(x << 16), __uint_as_float(y << 16), acc);
+      acc = fmaf(__uint_as_float(x & 0xffff0000u), __uint_as_float(y & 0xffff0000u), acc);
+    }
+  }
+  p.drow[t] = acc;
+}
+
+// log2-domain LSE for exp2(s*c - lse2); a row with no key (LSE = -inf) gives
+// +inf, so every p of it is 0.
+__device__ __forceinline__ float lse2_of(float lse) {
+  return lse == neg_inf() ? __builtin_inff() : lse * 1.4426950408889634f;  // log2(e)
+}
+
+template <int D>
+__global__ __launch_bounds__(kBwdNT) void bwd_dq_kernel(const BwdParams p) {
+  constexpr int DS = D / 16, DB = D / 32;
+  constexpr int RM = D * 2 + 16, TR = kBwdT * 2 + 16;
+  __shared__ __attribute__((aligned(16))) unsigned char Kb[kBwdT * RM];
+  __shared__ __attribute__((aligned(16))) unsigned char Vb[kBwdT * RM];
+  __shared__ __attribute__((aligned(16))) unsigned char KTb[D * TR];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h32 = lane >> 5;
+  const int qsub = cdiv(p.block_q, kBwdT);
+  int t = blockIdx.x;
+  const int s = t % qsub;
+  t /= qsub;
+  const int i = t % p.M;
+  t /= p.M;
+  const int h = t % p.H, b = t / p.H, hk = h / p.hrep;
+  const int r0 = i * p.block_q + s * kBwdT;
+  const int rend = min((i + 1) * p.block_q, p.Sq);
+  if (r0 >= rend) return;
+  const int row = r0 + 32 * w + l32;
+  const bool rvalid = row < rend;
+
+  const __bf16* qrow = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sb + (int64_t)row * p.q_ss + h * p.q_sh;
+  const __bf16* grow = reinterpret_cast<const __bf16*>(p.dout) + b * p.do_sb + (int64_t)row * p.do_ss + h * p.do_sh;
+  uint4 qf[DS], gf[DS];
+  row_frags<D>(qrow, rvalid, h32, qf);
+  row_frags<D>(grow, rvalid, h32, gf);
+  const int64_t lrow = ((int64_t)b * p.H + h) * p.Sq + row;
+  const float lse2 = rvalid ? lse2_of(p.lse[lrow]) : __builtin_inff();
+  const float drow = rvalid ? p.drow[lrow] : 0.f;
+  const __bf16* kb0 = reinterpret_cast<const __bf16*>(p.k) + b * p.k_sb + hk * p.k_sh;
+  const __bf16* vb0 = reinterpret_cast<const __bf16*>(p.v) + b * p.v_sb + hk * p.v_sh;
+
+  f32x16_t acc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+  const int arow = swap_b23(l32);
+
+  for (int list = 0; list < 2; ++list) {
+    const int32_t* cntp = list == 0 ? p.mcnt : p.fcnt;
+    if (!cntp) continue;
+    const int64_t* cs = list == 0 ? p.mc_s : p.fc_s;
+    const int64_t* is = list == 0 ? p.mi_s : p.fi_s;
+    const int32_t* idxp = (list == 0 ? p.midx : p.fidx) + b * is[0] + h * is[1] + i * is[2];
+    const int cnt = min(max(cntp[b * cs[0] + h * cs[1] + i * cs[2]], 0), p.N);
+    for (int e = 0; e < cnt; ++e) {
+      const int j = idxp[(int64_t)e * is[3]];
+      if (j < 0 || j >= p.N) continue;
+      const int kend = min((j + 1) * p.block_kv, p.Sk);
+      for (int k0 = j * p.block_kv; k0 < kend; k0 += kBwdT) {
+        const int nk = min(kBwdT, kend - k0);
+        __syncthreads();  // every wave is done with the previous sub-tile
+        stage_rows<D>(kb0 + (int64_t)k0 * p.k_ss, p.k_ss, nk, Kb, KTb, tid);
+        stage_rows<D>(vb0 + (int64_t)k0 * p.v_ss, p.v_ss, nk, Vb, nullptr, tid);
+        __syncthreads();
+        f32x16_t s0, s1, d0, d1;
+        tile_dot<D>(Kb, arow, h32, qf, s0, s1);
+        tile_dot<D>(Vb, arow, h32, gf, d0, d1);
+        uint32_t pk0[8], pk1[8];
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          float v[4];
+#pragma unroll
+          for (int y = 0; y < 4; ++y) {
+            const int reg = 2 * x + (y & 1);
+            const f32x16_t& sv = y < 2 ? s0 : s1;
+            const f32x16_t& dv = y < 2 ? d0 : d1;
+            const int key = 16 * (reg >> 3) + 8 * h32 + (reg & 7) + (y < 2 ? 0 : 32);
+            bool keep = key < nk;
+            if (keep && list == 0) keep = keep_elem(p, row, k0 + key, j, k0 + key - j * p.block_kv);
+            const float pr = keep ? __builtin_amdgcn_exp2f(fmaf(sv[reg], p.c, -lse2)) : 0.f;
+            v[y] = pr * (dv[reg] - drow);
+          }
+          pk0[x] = pack_bf16x2(v[0], v[1]);
+          pk1[x] = pack_bf16x2(v[2], v[3]);
+        }
+        tr_product<DB>(KTb, arow, h32, pk0, pk1, acc);
+      }
+    }
+  }
+  if (rvalid) {
+    __bf16* dst = reinterpret_cast<__bf16*>(p.dq) + b * p.dq_sb + (int64_t)row * p.dq_ss + h * p.dq_sh;
+    store_row<DB>(dst, h32, acc, p.scale);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kBwdNT) void bwd_dkdv_kernel(const BwdParams p) {
+  constexpr int DS = D / 16, DB = D / 32;
+  constexpr int RM = D * 2 + 16, TR = kBwdT * 2 + 16;
+  __shared__ __attribute__((aligned(16))) unsigned char Qb[kBwdT * RM];
+  __shared__ __attribute__((aligned(16))) unsigned char Gb[kBwdT * RM];
+  __shared__ __attribute__((aligned(16))) unsigned char QTb[D * TR];
+  __shared__ __attribute__((aligned(16))) unsigned char GTb[D * TR];
+  __shared__ float lse2s[kBwdT], drows[kBwdT];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h32 = lane >> 5;
+  const int ksub = cdiv(p.block_kv, kBwdT);
+  int t = blockIdx.x;
+  const int s = t % ksub;
+  t /= ksub;
+  const int j = t % p.N;
+  t /= p.N;
+  const int Hkv = p.H / p.hrep;
+  const int hk = t % Hkv, b = t / Hkv;
+  const int k0 = j * p.block_kv + s * kBwdT;
+  const int kend = min((j + 1) * p.block_kv, p.Sk);
+  if (k0 >= kend) return;
+  const int key = k0 + 32 * w + l32;
+  const bool kvalid = key < kend;
+
+  const __bf16* krow = reinterpret_cast<const __bf16*>(p.k) + b * p.k_sb + (int64_t)key * p.k_ss + hk * p.k_sh;
+  const __bf16* vrow = reinterpret_cast<const __bf16*>(p.v) + b * p.v_sb + (int64_t)key * p.v_ss + hk * p.v_sh;
+  uint4 kf[DS], vf[DS];
+  row_frags<D>(krow, kvalid, h32, kf);
+  row_frags<D>(vrow, kvalid, h32, vf);
+
+  f32x16_t dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      dk[db][r] = 0.f;
+      dv[db][r] = 0.f;
+    }
+  const int arow = swap_b23(l32);
+
+  for (int h = hk * p.hrep; h < (hk + 1) * p.hrep; ++h) {
+    const __bf16* qb0 = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh;
+    const __bf16* gb0 = reinterpret_cast<const __bf16*>(p.dout) + b * p.do_sb + h * p.do_sh;
+    const int64_t lbase = ((int64_t)b * p.H + h) * p.Sq;
+    for (int list = 0; list < 2; ++list) {
+      const int32_t* cntp = list == 0 ? p.tmcnt : p.tfcnt;
+      if (!cntp) continue;
+      const int64_t* cs = list == 0 ? p.tmc_s : p.tfc_s;
+      const int64_t* is = list == 0 ? p.tmi_s : p.tfi_s;
+      const int32_t* idxp = (list == 0 ? p.tmidx : p.tfidx) + b * is[0] + h * is[1] + j * is[2];
+      const int cnt = min(max(cntp[b * cs[0] + h * cs[1] + j * cs[2]], 0), p.M);
+      for (int e = 0; e < cnt; ++e) {
+        const int i = idxp[(int64_t)e * is[3]];
+        if (i < 0 || i >= p.M) continue;
+        const int rend = min((i + 1) * p.block_q, p.Sq);
+        for (int r0 = i * p.block_q; r0 < rend; r0 += kBwdT) {
+          const int nr = min(kBwdT, rend - r0);
+          __syncthreads();  // every wave is done with the previous sub-tile
+          stage_rows<D>(qb0 + (int64_t)r0 * p.q_ss, p.q_ss, nr, Qb, QTb, tid);
+          stage_rows<D>(gb0 + (int64_t)r0 * p.do_ss, p.do_ss, nr, Gb, GTb, tid);
+          if (tid < kBwdT) {
+            lse2s[tid] = tid < nr ? lse2_of(p.lse[lbase + r0 + tid]) : __builtin_inff();
+            drows[tid] = tid < nr ? p.drow[lbase + r0 + tid] : 0.f;
+          }
+          __syncthreads();
+          f32x16_t s0, s1, d0, d1;
+          tile_dot<D>(Qb, arow, h32, kf, s0, s1);
+          tile_dot<D>(Gb, arow, h32, vf, d0, d1);
+          uint32_t pk0[8], pk1[8], dk0[8], dk1[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            float pv[4], dsv[4];
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+              const int reg = 2 * x + (y & 1);
+              const f32x16_t& sv = y < 2 ? s0 : s1;
+              const f32x16_t& gv = y < 2 ? d0 : d1;
+              const int rl = 16 * (reg >> 3) + 8 * h32 + (reg & 7) + (y < 2 ? 0 : 32);
+              bool keep = kvalid && rl < nr;
+              if (keep && list == 0) keep = keep_elem(p, r0 + rl, key, j, key - j * p.block_kv);
+              const float pr = keep ? __builtin_amdgcn_exp2f(fmaf(sv[reg], p.c, -lse2s[rl])) : 0.f;
+              pv[y] = pr;
+              dsv[y] = pr * (gv[reg] - drows[rl]);
+            }
+            pk0[x] = pack_bf16x2(pv[0], pv[1]);
+            pk1[x] = pack_bf16x2(pv[2], pv[3]);
+            dk0[x] = pack_bf16x2(dsv[0], dsv[1]);
+            dk1[x] = pack_bf16x2(dsv[2], dsv[3]);
+          }
+          tr_product<DB>(GTb, arow, h32, pk0, pk1, dv);
+          tr_product<DB>(QTb, arow, h32, dk0, dk1, dk);
+        }
+      }
+    }
+  }
+  if (kvalid) {
+    __bf16* kdst = reinterpret_cast<__bf16*>(p.dk) + b * p.dk_sb + (int64_t)key * p.dk_ss + hk * p.dk_sh;
+    __bf16* vdst = reinterpret_cast<__bf16*>(p.dv) + b * p.dv_sb + (int64_t)key * p.dv_ss + hk * p.dv_sh;
+    store_row<DB>(kdst, h32, dk, p.scale);
+    store_row<DB>(vdst, h32, dv, 1.f);
+  }
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
+  const int64_t rows = (int64_t)p.B * p.H * p.Sq;
+  if (rows > 0) {
+    hipLaunchKernelGGL(bwd_rowdot_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, p);
+  }
+  const int64_t gq = (int64_t)p.B * p.H * p.M * ((p.block_q + kBwdT - 1) / kBwdT);
+  const int64_t gk = (int64_t)p.B * (p.H / p.hrep) * p.N * ((p.block_kv + kBwdT - 1) / kBwdT);
+  if (gq > 0) hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)gq), dim3(kBwdNT), 0, st, p);
+  if (gk > 0) hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)gk), dim3(kBwdNT), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const BwdParams& p, int D, hipStream_t s) {
+  switch (D) {
+    case 64: return launch_bwd_d<64>(p, s);
+    case 128: return launch_bwd_d<128>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace bsa

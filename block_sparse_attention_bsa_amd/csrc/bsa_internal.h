@@ -66,6 +66,38 @@ hipError_t launch_fwd_proxy_staged(const FwdParams& p, int D, int tile_m, hipStr
 // 256-row ping-pong kernel (bf16, D in {64, 96, 128}).
 hipError_t launch_fwd_pp(const FwdParams& p, int D, hipStream_t s);
 
+// Backward (bf16, batched): inputs, gradients, the forward's lists (Q-major)
+// and their KV-major transposes.
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* drow;  // workspace [B,H,Sq]: rowsum(dO * O)
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t q_sb, q_ss, q_sh, k_sb, k_ss, k_sh, v_sb, v_ss, v_sh, o_sb, o_ss, o_sh;
+  int64_t do_sb, do_ss, do_sh, dq_sb, dq_ss, dq_sh, dk_sb, dk_ss, dk_sh, dv_sb, dv_ss, dv_sh;
+  const int32_t* mcnt;
+  const int32_t* midx;
+  const int32_t* fcnt;
+  const int32_t* fidx;
+  int64_t mc_s[3], mi_s[4], fc_s[3], fi_s[4];
+  const int32_t* tmcnt;
+  const int32_t* tmidx;
+  const int32_t* tfcnt;
+  const int32_t* tfidx;
+  int64_t tmc_s[3], tmi_s[4], tfc_s[3], tfi_s[4];
+  const int32_t* kv_valid;
+  int32_t B, H, hrep, Sq, Sk, M, N, block_q, block_kv, mask_mod, win_left, win_right;
+  float c;      // softmax_scale * log2(e)
+  float scale;  // softmax_scale
+};
+hipError_t launch_bwd(const BwdParams& p, int D, hipStream_t s);
+
 hipError_t launch_kv_major_lists(const int32_t* cnt, const int32_t* idx, int32_t B, int32_t H,
                                  int32_t M, int32_t N, uint8_t* work, int32_t* cnt_t,
                                  int32_t* idx_t, hipStream_t s);

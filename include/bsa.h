@@ -180,6 +180,33 @@ bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, 
 bsa_status bsa_mask_to_index(const uint8_t* mask, int32_t B, int32_t H, int32_t M, int32_t N,
                              int32_t* cnt, int32_t* idx, hipStream_t stream);
 
+/* Backward of the batched forward (bf16; D in {64, 128}): the gradient of
+ * O over the listed blocks (flash-attention pull request 2224 and the
+ * FastVideo pull request 1354 review name it as the missing half; the
+ * formulas are those of the forward's derivative):
+ *   P = exp(scale*S - LSE), dV = P^T dO, dP = dO V^T, D = rowsum(dO*O),
+ *   dS = P*(dP - D), dQ = scale*dS K, dK = scale*dS^T Q,
+ * dK and dV summed over the Q heads of each KV head.
+ *  q, o, dout, dq [B,Sq,H,D] and k, v, dk, dv [B,Sk,H_kv,D]: device bf16,
+ *    element strides {batch, seq, head} (q_str also describes dq, k_str dk,
+ *    v_str dv, o_str dout), head_dim stride 1, 16-byte aligned rows.
+ *  lse: the forward's LSE, device fp32 [B,H,Sq] contiguous.
+ *  bs: the forward's lists, block sizes and window (as for bsa_fwd).
+ *  mask_t / full_t: their KV-major transposes (bsa_kv_major_lists):
+ *    cnt [B,H,N], idx [B,H,N,M] through the same stride fields (cnt_stride
+ *    over {b, h, j}, idx_stride over {b, h, j, s}); cnt == NULL: absent.
+ *  work: device fp32 scratch of B*H*Sq entries (row dots), overwritten.
+ * dq, dk, dv are overwritten everywhere (zero where nothing is listed).
+ * Returns BSA_ERR_INVALID_ARGUMENT / BSA_ERR_UNSUPPORTED / BSA_ERR_MISALIGNED
+ * for bad arguments, BSA_ERR_HIP if a launch fails.  Deterministic: no atomics. */
+bsa_status bsa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, int32_t B, int32_t H,
+                   int32_t H_kv, int32_t Sq, int32_t Sk, int32_t D, const int64_t q_str[3],
+                   const int64_t k_str[3], const int64_t v_str[3], const int64_t o_str[3],
+                   const bsa_block_sparse* bs, const bsa_block_list* mask_t,
+                   const bsa_block_list* full_t, bsa_mask_mod mask_mod, const int32_t* kv_valid,
+                   float softmax_scale, float* work, hipStream_t stream);
+
 /* KV-major ("transposed") block lists: the per-KV-block view that a backward
  * pass walks (flash-attention pull request 2224, review thread: the backward
  * needs the block metadata transposed).  cnt: device int32 [B,H,M] and idx:
