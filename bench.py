@@ -327,6 +327,22 @@ def table(torch, np, bsa, workloads, oracle_s):
             w = workloads.sparse_sweep(D, bq, bk)
             batched(f"sweep d{D} ({bq},{bk}) (B2 H16 S4096, 25 %)", w,
                     oracle_budget=oracle_s if (D, bq, bk) == (128, 128, 128) else 0)
+    # backward on the d128 sweep workload: row dots, dQ and dK/dV kernels
+    w = workloads.sparse_sweep(128, 128, 128)
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (w.q, w.k, w.v))
+    ml_b = bsa.bsa_mask_to_index(torch.from_numpy(w.part.astype(np.uint8)).to(dev))
+    fl_b = bsa.bsa_mask_to_index(torch.from_numpy(w.full.astype(np.uint8)).to(dev))
+    o, lse = bsa.bsa_fwd(q, k, v, ml_b, fl_b, 128, 128, bsa.MASK_CAUSAL, None, w.scale)
+    g = torch.randn_like(o)
+    run_b = lambda: bsa.bsa_bwd(q, k, v, o, lse, g, ml_b, fl_b, 128, 128, bsa.MASK_CAUSAL, None,
+                                w.scale)
+    run_b()
+    ms = _time_launches(torch, run_b)
+    B, S, H, D = w.q.shape
+    # five products (S, dP, dV, dK, dQ) of 2*D flops per listed (row, key) cell
+    fl = 2.5 * _pairs_flops(w.full, w.part, 128, 128, S, S, D)
+    emit(f"backward, sweep d{D} (128,128) (B{B} H{H} S{S}, 25 %; includes building the KV-major "
+         f"lists; 10*d flops per listed cell)", ms, fl, None, _MaxErr())
     # sliding window: lists from the GPU classifier of the local mask_mod
     w = workloads.sliding_window()
     q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (w.q, w.k, w.v))

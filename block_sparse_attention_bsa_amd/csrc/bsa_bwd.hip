@@ -8,13 +8,13 @@
 //   dS = P * (dP - D), dQ = scale * dS K, dK = scale * dS^T Q.
 // Three launches on the caller's stream:
 //   1. bwd_rowdot_kernel: D per row (fp32 workspace).
-//   2. bwd_dq_kernel: one workgroup per 64 rows of a Q block, walking the
+//   2. bwd_dq_kernel: one workgroup per 128 (or 64) rows of a Q block, walking the
 //      forward's lists in 64-key sub-tiles.  S and dP^T come from K and V
 //      rows in LDS against Q and dO in registers; dQ accumulates dS times K
 //      read transposed from LDS.  The layouts are those of the forward: a lane
 //      owns one query row, P and dS feed the last product straight from
 //      registers.
-//   3. bwd_dkdv_kernel: one workgroup per 64 keys of a KV block, walking the
+//   3. bwd_dkdv_kernel: one workgroup per 128 (or 64) keys of a KV block, walking the
 //      KV-major lists (the Q blocks that list the KV block) of every Q head of
 //      its KV head, in 64-row sub-tiles.  The roles swap: a lane owns one key,
 //      K and V sit in registers, Q and dO rows (and their transposes) in LDS.
@@ -31,9 +31,10 @@ namespace {
 
 using namespace dev;
 
-constexpr int kBwdNW = 2;              // waves per workgroup
-constexpr int kBwdNT = kBwdNW * 64;    // threads
-constexpr int kBwdT = 64;              // rows (dQ) / keys (dK, dV) per workgroup, and sub-tile size
+// A workgroup of NW waves owns 32*NW rows (dQ) or keys (dK, dV): NW = 4 when
+// the block size is a multiple of 128, else 2.  The other side streams in
+// sub-tiles of kBwdT positions.
+constexpr int kBwdT = 64;
 
 __device__ __forceinline__ uint32_t word4(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
@@ -56,14 +57,14 @@ __device__ __forceinline__ bool keep_elem(const BwdParams& p, int row, int key, 
 // LDS: row-major at rm (row pitch RM bytes) and/or transposed at tr (tr[d] is
 // a row of 64 keys/rows, pitch TR bytes).  Rows past n are zero.  Every
 // thread of the workgroup calls it; no barrier inside.
-template <int D>
+template <int D, int NT>
 __device__ __forceinline__ void stage_rows(const __bf16* base, int64_t ss, int n,
                                            unsigned char* rm, unsigned char* tr, int tid) {
   constexpr int DC = D / 8;
   constexpr int RM = D * 2 + 16;
   constexpr int TR = kBwdT * 2 + 16;
   constexpr int BL = (kBwdT / 4) * DC;  // blocks of 4 rows x 8 dims
-  for (int bi = tid; bi < BL; bi += kBwdNT) {
+  for (int bi = tid; bi < BL; bi += NT) {
     const int g = bi / DC, dc = bi % DC;
     uint4 r[4];
 #pragma unroll
@@ -191,8 +192,9 @@ __device__ __forceinline__ float lse2_of(float lse) {
   return lse == neg_inf() ? __builtin_inff() : lse * 1.4426950408889634f;  // log2(e)
 }
 
-template <int D>
-__global__ __launch_bounds__(kBwdNT) void bwd_dq_kernel(const BwdParams p) {
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BwdParams p) {
+  constexpr int NT = NW * 64, TW = NW * 32;
   constexpr int DS = D / 16, DB = D / 32;
   constexpr int RM = D * 2 + 16, TR = kBwdT * 2 + 16;
   __shared__ __attribute__((aligned(16))) unsigned char Kb[kBwdT * RM];
@@ -200,14 +202,14 @@ __global__ __launch_bounds__(kBwdNT) void bwd_dq_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char KTb[D * TR];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h32 = lane >> 5;
-  const int qsub = cdiv(p.block_q, kBwdT);
+  const int qsub = cdiv(p.block_q, TW);
   int t = blockIdx.x;
   const int s = t % qsub;
   t /= qsub;
   const int i = t % p.M;
   t /= p.M;
   const int h = t % p.H, b = t / p.H, hk = h / p.hrep;
-  const int r0 = i * p.block_q + s * kBwdT;
+  const int r0 = i * p.block_q + s * TW;
   const int rend = min((i + 1) * p.block_q, p.Sq);
   if (r0 >= rend) return;
   const int row = r0 + 32 * w + l32;
@@ -245,8 +247,8 @@ __global__ __launch_bounds__(kBwdNT) void bwd_dq_kernel(const BwdParams p) {
       for (int k0 = j * p.block_kv; k0 < kend; k0 += kBwdT) {
         const int nk = min(kBwdT, kend - k0);
         __syncthreads();  // every wave is done with the previous sub-tile
-        stage_rows<D>(kb0 + (int64_t)k0 * p.k_ss, p.k_ss, nk, Kb, KTb, tid);
-        stage_rows<D>(vb0 + (int64_t)k0 * p.v_ss, p.v_ss, nk, Vb, nullptr, tid);
+        stage_rows<D, NT>(kb0 + (int64_t)k0 * p.k_ss, p.k_ss, nk, Kb, KTb, tid);
+        stage_rows<D, NT>(vb0 + (int64_t)k0 * p.v_ss, p.v_ss, nk, Vb, nullptr, tid);
         __syncthreads();
         f32x16_t s0, s1, d0, d1;
         tile_dot<D>(Kb, arow, h32, qf, s0, s1);
@@ -279,8 +281,9 @@ __global__ __launch_bounds__(kBwdNT) void bwd_dq_kernel(const BwdParams p) {
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kBwdNT) void bwd_dkdv_kernel(const BwdParams p) {
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BwdParams p) {
+  constexpr int NT = NW * 64, TW = NW * 32;
   constexpr int DS = D / 16, DB = D / 32;
   constexpr int RM = D * 2 + 16, TR = kBwdT * 2 + 16;
   __shared__ __attribute__((aligned(16))) unsigned char Qb[kBwdT * RM];
@@ -290,7 +293,7 @@ __global__ __launch_bounds__(kBwdNT) void bwd_dkdv_kernel(const BwdParams p) {
   __shared__ float lse2s[kBwdT], drows[kBwdT];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h32 = lane >> 5;
-  const int ksub = cdiv(p.block_kv, kBwdT);
+  const int ksub = cdiv(p.block_kv, TW);
   int t = blockIdx.x;
   const int s = t % ksub;
   t /= ksub;
@@ -298,7 +301,7 @@ __global__ __launch_bounds__(kBwdNT) void bwd_dkdv_kernel(const BwdParams p) {
   t /= p.N;
   const int Hkv = p.H / p.hrep;
   const int hk = t % Hkv, b = t / Hkv;
-  const int k0 = j * p.block_kv + s * kBwdT;
+  const int k0 = j * p.block_kv + s * TW;
   const int kend = min((j + 1) * p.block_kv, p.Sk);
   if (k0 >= kend) return;
   const int key = k0 + 32 * w + l32;
@@ -338,8 +341,8 @@ __global__ __launch_bounds__(kBwdNT) void bwd_dkdv_kernel(const BwdParams p) {
         for (int r0 = i * p.block_q; r0 < rend; r0 += kBwdT) {
           const int nr = min(kBwdT, rend - r0);
           __syncthreads();  // every wave is done with the previous sub-tile
-          stage_rows<D>(qb0 + (int64_t)r0 * p.q_ss, p.q_ss, nr, Qb, QTb, tid);
-          stage_rows<D>(gb0 + (int64_t)r0 * p.do_ss, p.do_ss, nr, Gb, GTb, tid);
+          stage_rows<D, NT>(qb0 + (int64_t)r0 * p.q_ss, p.q_ss, nr, Qb, QTb, tid);
+          stage_rows<D, NT>(gb0 + (int64_t)r0 * p.do_ss, p.do_ss, nr, Gb, GTb, tid);
           if (tid < kBwdT) {
             lse2s[tid] = tid < nr ? lse2_of(p.lse[lbase + r0 + tid]) : __builtin_inff();
             drows[tid] = tid < nr ? p.drow[lbase + r0 + tid] : 0.f;
@@ -389,10 +392,22 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
   if (rows > 0) {
     hipLaunchKernelGGL(bwd_rowdot_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, p);
   }
-  const int64_t gq = (int64_t)p.B * p.H * p.M * ((p.block_q + kBwdT - 1) / kBwdT);
-  const int64_t gk = (int64_t)p.B * (p.H / p.hrep) * p.N * ((p.block_kv + kBwdT - 1) / kBwdT);
-  if (gq > 0) hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)gq), dim3(kBwdNT), 0, st, p);
-  if (gk > 0) hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)gk), dim3(kBwdNT), 0, st, p);
+  const int nwq = p.block_q % 128 == 0 ? 4 : 2, nwk = p.block_kv % 128 == 0 ? 4 : 2;
+  const int64_t gq = (int64_t)p.B * p.H * p.M * ((p.block_q + 32 * nwq - 1) / (32 * nwq));
+  const int64_t gk =
+      (int64_t)p.B * (p.H / p.hrep) * p.N * ((p.block_kv + 32 * nwk - 1) / (32 * nwk));
+  if (gq > 0) {
+    if (nwq == 4)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, 4>), dim3((unsigned)gq), dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, 2>), dim3((unsigned)gq), dim3(128), 0, st, p);
+  }
+  if (gk > 0) {
+    if (nwk == 4)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, 4>), dim3((unsigned)gk), dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, 2>), dim3((unsigned)gk), dim3(128), 0, st, p);
+  }
   return hipGetLastError();
 }
 
