@@ -53,45 +53,100 @@ __device__ __forceinline__ bool keep_elem(const BwdParams& p, int row, int key, 
   }
 }
 
-// Rows r0 .. r0+n-1 (n <= 64) of a [*, D] bf16 tensor (row stride ss) into
-// LDS: row-major at rm (row pitch RM bytes) and/or transposed at tr (tr[d] is
-// a row of 64 keys/rows, pitch TR bytes).  Rows past n are zero.  Every
-// thread of the workgroup calls it; no barrier inside.
+// Staging of rows 0 .. n-1 (n <= 64) of a [*, D] bf16 tensor (row stride ss)
+// into LDS: row-major at rm (row pitch RM bytes) and/or transposed at tr
+// (tr[d] is a row of 64 positions, pitch TR bytes); rows past n are zero.
+// load() issues the global reads into registers, store() writes LDS, so the
+// reads of the next sub-tile can be in flight while the current one is
+// computed.  Every thread of the workgroup takes part; no barrier inside.
 template <int D, int NT>
-__device__ __forceinline__ void stage_rows(const __bf16* base, int64_t ss, int n,
-                                           unsigned char* rm, unsigned char* tr, int tid) {
-  constexpr int DC = D / 8;
-  constexpr int RM = D * 2 + 16;
-  constexpr int TR = kBwdT * 2 + 16;
-  constexpr int BL = (kBwdT / 4) * DC;  // blocks of 4 rows x 8 dims
-  for (int bi = tid; bi < BL; bi += NT) {
-    const int g = bi / DC, dc = bi % DC;
-    uint4 r[4];
+struct Stage {
+  static constexpr int DC = D / 8;
+  static constexpr int RM = D * 2 + 16;
+  static constexpr int TR = kBwdT * 2 + 16;
+  static constexpr int BL = (kBwdT / 4) * DC;  // blocks of 4 rows x 8 dims
+  static constexpr int PER = (BL + NT - 1) / NT;
+  uint4 r[PER][4];
+  __device__ __forceinline__ void load(const __bf16* base, int64_t ss, int n, int tid) {
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int row = 4 * g + rr;
-      r[rr] = row < n ? *reinterpret_cast<const uint4*>(base + (int64_t)row * ss + dc * 8)
-                      : make_uint4(0, 0, 0, 0);
-      if (rm) *reinterpret_cast<uint4*>(rm + row * RM + dc * 16) = r[rr];
-    }
-    if (tr) {
+    for (int c = 0; c < PER; ++c) {
+      const int bi = tid + c * NT;
+      const int g = bi / DC, dc = bi % DC;
 #pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const uint32_t x0 = word4(r[0], dd >> 1), x1 = word4(r[1], dd >> 1);
-        const uint32_t x2 = word4(r[2], dd >> 1), x3 = word4(r[3], dd >> 1);
-        uint2 out;
-        if ((dd & 1) == 0) {
-          out.x = (x0 & 0xffffu) | (x1 << 16);
-          out.y = (x2 & 0xffffu) | (x3 << 16);
-        } else {
-          out.x = (x0 >> 16) | (x1 & 0xffff0000u);
-          out.y = (x2 >> 16) | (x3 & 0xffff0000u);
-        }
-        *reinterpret_cast<uint2*>(tr + (dc * 8 + dd) * TR + g * 8) = out;
+      for (int rr = 0; rr < 4; ++rr) {
+        const int row = 4 * g + rr;
+        r[c][rr] = (bi < BL && row < n)
+                       ? *reinterpret_cast<const uint4*>(base + (int64_t)row * ss + dc * 8)
+                       : make_uint4(0, 0, 0, 0);
       }
     }
   }
-}
+  __device__ __forceinline__ void store(unsigned char* rm, unsigned char* tr, int tid) const {
+#pragma unroll
+    for (int c = 0; c < PER; ++c) {
+      const int bi = tid + c * NT;
+      if (bi >= BL) continue;
+      const int g = bi / DC, dc = bi % DC;
+      if (rm) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          *reinterpret_cast<uint4*>(rm + (4 * g + rr) * RM + dc * 16) = r[c][rr];
+      }
+      if (tr) {
+#pragma unroll
+        for (int dd = 0; dd < 8; ++dd) {
+          const uint32_t x0 = word4(r[c][0], dd >> 1), x1 = word4(r[c][1], dd >> 1);
+          const uint32_t x2 = word4(r[c][2], dd >> 1), x3 = word4(r[c][3], dd >> 1);
+          uint2 out;
+          if ((dd & 1) == 0) {
+            out.x = (x0 & 0xffffu) | (x1 << 16);
+            out.y = (x2 & 0xffffu) | (x3 << 16);
+          } else {
+            out.x = (x0 >> 16) | (x1 & 0xffff0000u);
+            out.y = (x2 >> 16) | (x3 & 0xffff0000u);
+          }
+          *reinterpret_cast<uint2*>(tr + (dc * 8 + dd) * TR + g * 8) = out;
+        }
+      }
+    }
+  }
+};
+
+// The sub-tiles of one walk, in order: for each list (mask, then full), for
+// each listed block id, the block's positions [id*blen, min((id+1)*blen, S))
+// in pieces of 64.  All state is wave-uniform.
+struct SubWalk {
+  const int32_t* idx[2];
+  int64_t istep[2];
+  int cnt[2];
+  int nmax, blen, S;
+  int list, e, id, pos, end;
+  __device__ __forceinline__ bool start_block() {
+    while (list < 2) {
+      while (e < cnt[list]) {
+        const int v = idx[list][(int64_t)e * istep[list]];
+        if (v >= 0 && v < nmax) {
+          id = v;
+          pos = v * blen;
+          end = min((v + 1) * blen, S);
+          return true;
+        }
+        ++e;
+      }
+      ++list;
+      e = 0;
+    }
+    return false;
+  }
+  // first call: list = 0, e = 0 set by the caller, then first(); later next()
+  __device__ __forceinline__ bool first() { return start_block(); }
+  __device__ __forceinline__ bool next() {
+    pos += kBwdT;
+    if (pos < end) return true;
+    ++e;
+    return start_block();
+  }
+};
 
 // B-operand fragments of one row (query row for dQ, key for dK/dV):
 // frag[ks] = X[row][16*ks + 8*h32 .. +7], zero when the row is invalid.
@@ -233,47 +288,67 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BwdParams p) {
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
   const int arow = swap_b23(l32);
 
+  SubWalk W{};
   for (int list = 0; list < 2; ++list) {
     const int32_t* cntp = list == 0 ? p.mcnt : p.fcnt;
-    if (!cntp) continue;
     const int64_t* cs = list == 0 ? p.mc_s : p.fc_s;
     const int64_t* is = list == 0 ? p.mi_s : p.fi_s;
-    const int32_t* idxp = (list == 0 ? p.midx : p.fidx) + b * is[0] + h * is[1] + i * is[2];
-    const int cnt = min(max(cntp[b * cs[0] + h * cs[1] + i * cs[2]], 0), p.N);
-    for (int e = 0; e < cnt; ++e) {
-      const int j = idxp[(int64_t)e * is[3]];
-      if (j < 0 || j >= p.N) continue;
-      const int kend = min((j + 1) * p.block_kv, p.Sk);
-      for (int k0 = j * p.block_kv; k0 < kend; k0 += kBwdT) {
-        const int nk = min(kBwdT, kend - k0);
-        __syncthreads();  // every wave is done with the previous sub-tile
-        stage_rows<D, NT>(kb0 + (int64_t)k0 * p.k_ss, p.k_ss, nk, Kb, KTb, tid);
-        stage_rows<D, NT>(vb0 + (int64_t)k0 * p.v_ss, p.v_ss, nk, Vb, nullptr, tid);
-        __syncthreads();
-        f32x16_t s0, s1, d0, d1;
-        tile_dot<D>(Kb, arow, h32, qf, s0, s1);
-        tile_dot<D>(Vb, arow, h32, gf, d0, d1);
-        uint32_t pk0[8], pk1[8];
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          float v[4];
-#pragma unroll
-          for (int y = 0; y < 4; ++y) {
-            const int reg = 2 * x + (y & 1);
-            const f32x16_t& sv = y < 2 ? s0 : s1;
-            const f32x16_t& dv = y < 2 ? d0 : d1;
-            const int key = 16 * (reg >> 3) + 8 * h32 + (reg & 7) + (y < 2 ? 0 : 32);
-            bool keep = key < nk;
-            if (keep && list == 0) keep = keep_elem(p, row, k0 + key, j, k0 + key - j * p.block_kv);
-            const float pr = keep ? __builtin_amdgcn_exp2f(fmaf(sv[reg], p.c, -lse2)) : 0.f;
-            v[y] = pr * (dv[reg] - drow);
-          }
-          pk0[x] = pack_bf16x2(v[0], v[1]);
-          pk1[x] = pack_bf16x2(v[2], v[3]);
-        }
-        tr_product<DB>(KTb, arow, h32, pk0, pk1, acc);
-      }
+    W.cnt[list] = cntp ? min(max(cntp[b * cs[0] + h * cs[1] + i * cs[2]], 0), p.N) : 0;
+    W.idx[list] = cntp ? (list == 0 ? p.midx : p.fidx) + b * is[0] + h * is[1] + i * is[2] : nullptr;
+    W.istep[list] = is[3];
+  }
+  W.nmax = p.N;
+  W.blen = p.block_kv;
+  W.S = p.Sk;
+  Stage<D, NT> sk, sv;
+  bool have = W.first();
+  if (have) {
+    const int nk = min(kBwdT, W.end - W.pos);
+    sk.load(kb0 + (int64_t)W.pos * p.k_ss, p.k_ss, nk, tid);
+    sv.load(vb0 + (int64_t)W.pos * p.v_ss, p.v_ss, nk, tid);
+    sk.store(Kb, KTb, tid);
+    sv.store(Vb, nullptr, tid);
+  }
+  __syncthreads();
+  while (have) {
+    const int list = W.list, j = W.id, k0 = W.pos, nk = min(kBwdT, W.end - W.pos);
+    const bool more = W.next();
+    if (more) {  // next sub-tile's reads in flight during this one's products
+      const int nn = min(kBwdT, W.end - W.pos);
+      sk.load(kb0 + (int64_t)W.pos * p.k_ss, p.k_ss, nn, tid);
+      sv.load(vb0 + (int64_t)W.pos * p.v_ss, p.v_ss, nn, tid);
     }
+    {
+      f32x16_t s0, s1, d0, d1;
+      tile_dot<D>(Kb, arow, h32, qf, s0, s1);
+      tile_dot<D>(Vb, arow, h32, gf, d0, d1);
+      uint32_t pk0[8], pk1[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        float v[4];
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          const int reg = 2 * x + (y & 1);
+          const f32x16_t& sv_ = y < 2 ? s0 : s1;
+          const f32x16_t& dv_ = y < 2 ? d0 : d1;
+          const int key = 16 * (reg >> 3) + 8 * h32 + (reg & 7) + (y < 2 ? 0 : 32);
+          bool keep = key < nk;
+          if (keep && list == 0) keep = keep_elem(p, row, k0 + key, j, k0 + key - j * p.block_kv);
+          const float pr = keep ? __builtin_amdgcn_exp2f(fmaf(sv_[reg], p.c, -lse2)) : 0.f;
+          v[y] = pr * (dv_[reg] - drow);
+        }
+        pk0[x] = pack_bf16x2(v[0], v[1]);
+        pk1[x] = pack_bf16x2(v[2], v[3]);
+      }
+      tr_product<DB>(KTb, arow, h32, pk0, pk1, acc);
+    }
+    __syncthreads();  // every wave is done with this sub-tile
+    if (more) {
+      sk.store(Kb, KTb, tid);
+      sv.store(Vb, nullptr, tid);
+    }
+    __syncthreads();
+    have = more;
   }
   if (rvalid) {
     __bf16* dst = reinterpret_cast<__bf16*>(p.dq) + b * p.dq_sb + (int64_t)row * p.dq_ss + h * p.dq_sh;
@@ -327,57 +402,82 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BwdParams p) {
     const __bf16* qb0 = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh;
     const __bf16* gb0 = reinterpret_cast<const __bf16*>(p.dout) + b * p.do_sb + h * p.do_sh;
     const int64_t lbase = ((int64_t)b * p.H + h) * p.Sq;
+    SubWalk W{};
     for (int list = 0; list < 2; ++list) {
       const int32_t* cntp = list == 0 ? p.tmcnt : p.tfcnt;
-      if (!cntp) continue;
       const int64_t* cs = list == 0 ? p.tmc_s : p.tfc_s;
       const int64_t* is = list == 0 ? p.tmi_s : p.tfi_s;
-      const int32_t* idxp = (list == 0 ? p.tmidx : p.tfidx) + b * is[0] + h * is[1] + j * is[2];
-      const int cnt = min(max(cntp[b * cs[0] + h * cs[1] + j * cs[2]], 0), p.M);
-      for (int e = 0; e < cnt; ++e) {
-        const int i = idxp[(int64_t)e * is[3]];
-        if (i < 0 || i >= p.M) continue;
-        const int rend = min((i + 1) * p.block_q, p.Sq);
-        for (int r0 = i * p.block_q; r0 < rend; r0 += kBwdT) {
-          const int nr = min(kBwdT, rend - r0);
-          __syncthreads();  // every wave is done with the previous sub-tile
-          stage_rows<D, NT>(qb0 + (int64_t)r0 * p.q_ss, p.q_ss, nr, Qb, QTb, tid);
-          stage_rows<D, NT>(gb0 + (int64_t)r0 * p.do_ss, p.do_ss, nr, Gb, GTb, tid);
-          if (tid < kBwdT) {
-            lse2s[tid] = tid < nr ? lse2_of(p.lse[lbase + r0 + tid]) : __builtin_inff();
-            drows[tid] = tid < nr ? p.drow[lbase + r0 + tid] : 0.f;
-          }
-          __syncthreads();
-          f32x16_t s0, s1, d0, d1;
-          tile_dot<D>(Qb, arow, h32, kf, s0, s1);
-          tile_dot<D>(Gb, arow, h32, vf, d0, d1);
-          uint32_t pk0[8], pk1[8], dk0[8], dk1[8];
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            float pv[4], dsv[4];
-#pragma unroll
-            for (int y = 0; y < 4; ++y) {
-              const int reg = 2 * x + (y & 1);
-              const f32x16_t& sv = y < 2 ? s0 : s1;
-              const f32x16_t& gv = y < 2 ? d0 : d1;
-              const int rl = 16 * (reg >> 3) + 8 * h32 + (reg & 7) + (y < 2 ? 0 : 32);
-              bool keep = kvalid && rl < nr;
-              if (keep && list == 0) keep = keep_elem(p, r0 + rl, key, j, key - j * p.block_kv);
-              const float pr = keep ? __builtin_amdgcn_exp2f(fmaf(sv[reg], p.c, -lse2s[rl])) : 0.f;
-              pv[y] = pr;
-              dsv[y] = pr * (gv[reg] - drows[rl]);
-            }
-            pk0[x] = pack_bf16x2(pv[0], pv[1]);
-            pk1[x] = pack_bf16x2(pv[2], pv[3]);
-            dk0[x] = pack_bf16x2(dsv[0], dsv[1]);
-            dk1[x] = pack_bf16x2(dsv[2], dsv[3]);
-          }
-          tr_product<DB>(GTb, arow, h32, pk0, pk1, dv);
-          tr_product<DB>(QTb, arow, h32, dk0, dk1, dk);
-        }
+      W.cnt[list] = cntp ? min(max(cntp[b * cs[0] + h * cs[1] + j * cs[2]], 0), p.M) : 0;
+      W.idx[list] =
+          cntp ? (list == 0 ? p.tmidx : p.tfidx) + b * is[0] + h * is[1] + j * is[2] : nullptr;
+      W.istep[list] = is[3];
+    }
+    W.nmax = p.M;
+    W.blen = p.block_q;
+    W.S = p.Sq;
+    Stage<D, NT> sq, sg;
+    float l2n = 0.f, drn = 0.f;  // this thread's row (tid < 64) of the next sub-tile
+    auto load = [&]() {
+      const int nr = min(kBwdT, W.end - W.pos), r0 = W.pos;
+      sq.load(qb0 + (int64_t)r0 * p.q_ss, p.q_ss, nr, tid);
+      sg.load(gb0 + (int64_t)r0 * p.do_ss, p.do_ss, nr, tid);
+      if (tid < kBwdT) {
+        l2n = tid < nr ? lse2_of(p.lse[lbase + r0 + tid]) : __builtin_inff();
+        drn = tid < nr ? p.drow[lbase + r0 + tid] : 0.f;
       }
+    };
+    auto store = [&]() {
+      sq.store(Qb, QTb, tid);
+      sg.store(Gb, GTb, tid);
+      if (tid < kBwdT) {
+        lse2s[tid] = l2n;
+        drows[tid] = drn;
+      }
+    };
+    __syncthreads();  // the previous head's last sub-tile is done
+    bool have = W.first();
+    if (have) {
+      load();
+      store();
+    }
+    __syncthreads();
+    while (have) {
+      const int list = W.list, r0 = W.pos, nr = min(kBwdT, W.end - W.pos);
+      const bool more = W.next();
+      if (more) load();  // next sub-tile's reads in flight during this one's products
+      f32x16_t s0, s1, d0, d1;
+      tile_dot<D>(Qb, arow, h32, kf, s0, s1);
+      tile_dot<D>(Gb, arow, h32, vf, d0, d1);
+      uint32_t pk0[8], pk1[8], dk0[8], dk1[8];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        float pv[4], dsv[4];
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          const int reg = 2 * x + (y & 1);
+          const f32x16_t& sv = y < 2 ? s0 : s1;
+          const f32x16_t& gv = y < 2 ? d0 : d1;
+          const int rl = 16 * (reg >> 3) + 8 * h32 + (reg & 7) + (y < 2 ? 0 : 32);
+          bool keep = kvalid && rl < nr;
+          if (keep && list == 0) keep = keep_elem(p, r0 + rl, key, j, key - j * p.block_kv);
+          const float pr = keep ? __builtin_amdgcn_exp2f(fmaf(sv[reg], p.c, -lse2s[rl])) : 0.f;
+          pv[y] = pr;
+          dsv[y] = pr * (gv[reg] - drows[rl]);
+        }
+        pk0[x] = pack_bf16x2(pv[0], pv[1]);
+        pk1[x] = pack_bf16x2(pv[2], pv[3]);
+        dk0[x] = pack_bf16x2(dsv[0], dsv[1]);
+        dk1[x] = pack_bf16x2(dsv[2], dsv[3]);
+      }
+      tr_product<DB>(GTb, arow, h32, pk0, pk1, dv);
+      tr_product<DB>(QTb, arow, h32, dk0, dk1, dk);
+      __syncthreads();  // every wave is done with this sub-tile
+      if (more) store();
+      __syncthreads();
+      have = more;
     }
   }
+
   if (kvalid) {
     __bf16* kdst = reinterpret_cast<__bf16*>(p.dk) + b * p.dk_sb + (int64_t)key * p.dk_ss + hk * p.dk_sh;
     __bf16* vdst = reinterpret_cast<__bf16*>(p.dv) + b * p.dv_sb + (int64_t)key * p.dv_ss + hk * p.dv_sh;
