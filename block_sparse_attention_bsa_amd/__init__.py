@@ -346,7 +346,7 @@ def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
             block_q: int, block_kv: int, mask_mod: int = MASK_NONE,
             kv_valid: Optional[torch.Tensor] = None, softmax_scale: Optional[float] = None,
             window: Optional[Tuple[int, int]] = None):
-    """Backward of bsa_fwd (bf16, head_dim 64 or 128): returns (dq, dk, dv).
+    """Backward of bsa_fwd (bf16, head_dim 64/96/128/192/256): returns (dq, dk, dv).
     o and lse are the forward's outputs, dout the gradient of o; the lists,
     block sizes, mask_mod, kv_valid, scale and window are the forward's.  The
     KV-major lists are built here with bsa_kv_major_lists."""

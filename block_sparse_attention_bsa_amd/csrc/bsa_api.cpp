@@ -412,7 +412,7 @@ bsa_status bsa_bwd(const void* q, const void* k, const void* v, const void* o, c
   if (bs->block_q <= 0 || bs->block_kv <= 0) return BSA_ERR_INVALID_ARGUMENT;
   if (!list_ok(bs->mask) || !list_ok(bs->full) || !list_ok(*mask_t) || !list_ok(*full_t))
     return BSA_ERR_INVALID_ARGUMENT;
-  if (D != 64 && D != 128) return BSA_ERR_UNSUPPORTED;
+  if (!supported_head_dim(D)) return BSA_ERR_UNSUPPORTED;
   if (bs->proxy_k || bs->proxy_v) return BSA_ERR_UNSUPPORTED;
   if ((int64_t)B * H * (Sq + Sk) == 0) return BSA_OK;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !work)

@@ -115,16 +115,22 @@ struct Stage {
 // The sub-tiles of one walk, in order: for each list (mask, then full), for
 // each listed block id, the block's positions [id*blen, min((id+1)*blen, S))
 // in pieces of 64.  All state is wave-uniform.
+// (Two named fields per list, not arrays: an array indexed by the run-time
+// list number would live in scratch memory.)
 struct SubWalk {
-  const int32_t* idx[2];
-  int64_t istep[2];
-  int cnt[2];
+  const int32_t* idx0;
+  const int32_t* idx1;
+  int64_t istep0, istep1;
+  int cnt0, cnt1;
   int nmax, blen, S;
   int list, e, id, pos, end;
   __device__ __forceinline__ bool start_block() {
     while (list < 2) {
-      while (e < cnt[list]) {
-        const int v = idx[list][(int64_t)e * istep[list]];
+      const int cnt = list == 0 ? cnt0 : cnt1;
+      const int32_t* idx = list == 0 ? idx0 : idx1;
+      const int64_t istep = list == 0 ? istep0 : istep1;
+      while (e < cnt) {
+        const int v = idx[(int64_t)e * istep];
         if (v >= 0 && v < nmax) {
           id = v;
           pos = v * blen;
@@ -293,9 +299,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BwdParams p) {
     const int32_t* cntp = list == 0 ? p.mcnt : p.fcnt;
     const int64_t* cs = list == 0 ? p.mc_s : p.fc_s;
     const int64_t* is = list == 0 ? p.mi_s : p.fi_s;
-    W.cnt[list] = cntp ? min(max(cntp[b * cs[0] + h * cs[1] + i * cs[2]], 0), p.N) : 0;
-    W.idx[list] = cntp ? (list == 0 ? p.midx : p.fidx) + b * is[0] + h * is[1] + i * is[2] : nullptr;
-    W.istep[list] = is[3];
+    const int c = cntp ? min(max(cntp[b * cs[0] + h * cs[1] + i * cs[2]], 0), p.N) : 0;
+    const int32_t* ip =
+        cntp ? (list == 0 ? p.midx : p.fidx) + b * is[0] + h * is[1] + i * is[2] : nullptr;
+    if (list == 0) {
+      W.cnt0 = c; W.idx0 = ip; W.istep0 = is[3];
+    } else {
+      W.cnt1 = c; W.idx1 = ip; W.istep1 = is[3];
+    }
   }
   W.nmax = p.N;
   W.blen = p.block_kv;
@@ -407,10 +418,14 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BwdParams p) {
       const int32_t* cntp = list == 0 ? p.tmcnt : p.tfcnt;
       const int64_t* cs = list == 0 ? p.tmc_s : p.tfc_s;
       const int64_t* is = list == 0 ? p.tmi_s : p.tfi_s;
-      W.cnt[list] = cntp ? min(max(cntp[b * cs[0] + h * cs[1] + j * cs[2]], 0), p.M) : 0;
-      W.idx[list] =
+      const int c = cntp ? min(max(cntp[b * cs[0] + h * cs[1] + j * cs[2]], 0), p.M) : 0;
+      const int32_t* ip =
           cntp ? (list == 0 ? p.tmidx : p.tfidx) + b * is[0] + h * is[1] + j * is[2] : nullptr;
-      W.istep[list] = is[3];
+      if (list == 0) {
+        W.cnt0 = c; W.idx0 = ip; W.istep0 = is[3];
+      } else {
+        W.cnt1 = c; W.idx1 = ip; W.istep1 = is[3];
+      }
     }
     W.nmax = p.M;
     W.blen = p.block_q;
@@ -516,7 +531,10 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
 hipError_t launch_bwd(const BwdParams& p, int D, hipStream_t s) {
   switch (D) {
     case 64: return launch_bwd_d<64>(p, s);
+    case 96: return launch_bwd_d<96>(p, s);
     case 128: return launch_bwd_d<128>(p, s);
+    case 192: return launch_bwd_d<192>(p, s);
+    case 256: return launch_bwd_d<256>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -180,7 +180,7 @@ bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, 
 bsa_status bsa_mask_to_index(const uint8_t* mask, int32_t B, int32_t H, int32_t M, int32_t N,
                              int32_t* cnt, int32_t* idx, hipStream_t stream);
 
-/* Backward of the batched forward (bf16; D in {64, 128}): the gradient of
+/* Backward of the batched forward (bf16; D in {64, 96, 128, 192, 256}): the gradient of
  * O over the listed blocks (flash-attention pull request 2224 and the
  * FastVideo pull request 1354 review name it as the missing half; the
  * formulas are those of the forward's derivative):

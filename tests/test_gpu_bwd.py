@@ -33,6 +33,10 @@ def _lists(m):
     dict(mm=LOCAL, Sq=333, Sk=333, D=128, bq=64, bk=128, window=(100, 20)),
     dict(mm=KVV, Sq=200, Sk=450, D=64, bq=128, bk=48),
     dict(mm=NONE, Sq=130, Sk=517, D=128, bq=64, bk=112),
+    dict(mm=CAUSAL, Sq=300, Sk=300, D=96, bq=128, bk=64),
+    dict(mm=LOCAL, Sq=260, Sk=260, D=192, bq=64, bk=128, window=(70, 0)),
+    dict(mm=CAUSAL, Sq=256, Sk=256, D=256, bq=128, bk=128),
+    dict(mm=KVV, Sq=150, Sk=200, D=256, bq=64, bk=64),
 ])
 def test_bwd_matches_oracle(case):
     seed = zlib.crc32(repr(sorted(case.items())).encode())
@@ -80,7 +84,7 @@ def test_bwd_matches_oracle(case):
 
 
 def test_bwd_rejects_unsupported():
-    q = torch.zeros((1, 64, 1, 96), dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros((1, 64, 1, 80), dtype=torch.bfloat16, device="cuda")
     lse = torch.zeros((1, 1, 64), dtype=torch.float32, device="cuda")
     fl = _lists(np.ones((1, 1, 1, 1), bool))
     with pytest.raises(bsa.BsaError):
