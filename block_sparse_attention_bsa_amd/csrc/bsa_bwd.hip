@@ -254,7 +254,9 @@ __device__ __forceinline__ float lse2_of(float lse) {
 }
 
 template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const BwdParams p) {
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))  // two waves per SIMD up to d = 128
+void bwd_dq_kernel(const BwdParams p) {
   constexpr int NT = NW * 64, TW = NW * 32;
   constexpr int DS = D / 16, DB = D / 32;
   constexpr int RM = D * 2 + 16, TR = kBwdT * 2 + 16;
