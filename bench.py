@@ -519,8 +519,9 @@ def main():
         print(_kernel_hash())
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on exactly one GPU: the block-sparse forward here is a "
-              "single-GPU build (see DESIGN.md for how it would shard).", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: this block-sparse forward runs on one GPU "
+              "per process; sharding batch and heads across GPUs needs no change to the "
+              "kernels.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
