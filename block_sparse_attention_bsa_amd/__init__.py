@@ -96,7 +96,7 @@ def load_library():
                             I64P, I64P, I64P, I64P, BS, ctypes.c_int, P, F32, U32, P]
     lib.bsa_varlen_fwd.argtypes = [P, P, P, P, P, ctypes.c_int, I32, I32, I32, I32,
                                    P, P, P, P, I32, I32, I32, I64P, I64P, I64P, I64P, BS,
-                                   ctypes.c_int, F32, U32, P]
+                                   ctypes.c_int, P, ctypes.c_int64, F32, U32, P]
     lib.bsa_mask_to_index.argtypes = [P, I32, I32, I32, I32, P, P, P]
     lib.bsa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
                             P, P, P, P, P, P, P, ctypes.c_int, P, ctypes.c_float, P, P]
@@ -265,11 +265,16 @@ def bsa_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    block_q: int, block_kv: int, mask_mod: int = MASK_NONE,
                    softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                    lse: Optional[torch.Tensor] = None, validate: bool = False,
-                   window: Optional[Tuple[int, int]] = None):
+                   window: Optional[Tuple[int, int]] = None,
+                   kv_valid: Optional[torch.Tensor] = None,
+                   max_seqlen_k: Optional[int] = None):
     """Packed varlen forward.  q [Tq,H,D], k/v [Tk,Hkv,D]; lists (cnt int32
     [H,total_m_blocks], idx int32 [H,total_n_blocks]); cu arrays int32 [B+1]
-    on the device; the two totals are host ints.  Returns (O [Tq,H,D],
-    LSE float32 [H,Tq])."""
+    on the device; the two totals are host ints.  kv_valid (MASK_KV_VALID_COUNT):
+    int32 [B, W] (row b: the valid-token counts of sequence b's KV blocks,
+    sequence-local ids) or [W] shared by every sequence, W >=
+    ceil(max_seqlen_k / block_kv); max_seqlen_k is read from cu_seqlens_k (a
+    device->host copy) when not given.  Returns (O [Tq,H,D], LSE float32 [H,Tq])."""
     lib = load_library()
     for n, t in (("q", q), ("k", k), ("v", v)):
         _dev(n, t)
@@ -305,6 +310,20 @@ def bsa_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     shp = (H, int(total_m_blocks), int(total_n_blocks))
     bs = _BlockSparse(_block_list(mask_list, False, shp), _block_list(full_list, False, shp),
                       int(block_q), int(block_kv), *_window(mask_mod, window))
+    kvv_ld = 0
+    if kv_valid is not None:
+        _dev("kv_valid", kv_valid, torch.int32)
+        if kv_valid.dim() not in (1, 2) or kv_valid.stride(-1) != 1 or \
+                (kv_valid.dim() == 2 and kv_valid.shape[0] != B):
+            raise ValueError("kv_valid must be int32 [B, W] or [W] with a contiguous last dimension")
+        if max_seqlen_k is None:
+            max_seqlen_k = int((cu_seqlens_k[1:] - cu_seqlens_k[:-1]).max().item()) if B else 0
+        need = -(-int(max_seqlen_k) // block_kv) if block_kv > 0 else 0
+        if kv_valid.shape[-1] < need:
+            raise ValueError(f"kv_valid rows need {need} entries (ceil(max_seqlen_k / block_kv))")
+        kvv_ld = kv_valid.stride(0) if kv_valid.dim() == 2 else 0
+    elif mask_mod == MASK_KV_VALID_COUNT and mask_list is not None:
+        raise ValueError("MASK_KV_VALID_COUNT needs kv_valid")
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     st = lib.bsa_varlen_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _DTYPES[q.dtype],
                             B, H, Hkv, D, _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
@@ -312,7 +331,7 @@ def bsa_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                             int(total_m_blocks), int(total_n_blocks), Tq,
                             _i64([q.stride(0), q.stride(1)]), _i64([k.stride(0), k.stride(1)]),
                             _i64([v.stride(0), v.stride(1)]), _i64([out.stride(0), out.stride(1)]),
-                            ctypes.byref(bs), int(mask_mod), scale,
+                            ctypes.byref(bs), int(mask_mod), _ptr(kv_valid), int(kvv_ld), scale,
                             FLAG_VALIDATE if validate else 0, _stream(q))
     _check("bsa_varlen_fwd", st)
     return out, lse
@@ -383,6 +402,10 @@ def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     work = torch.empty(max(B * H * Sq, 1), dtype=torch.float32, device=q.device)
     if kv_valid is not None:
         _dev("kv_valid", kv_valid, torch.int32)
+        if not kv_valid.is_contiguous() or kv_valid.numel() < N:
+            raise ValueError(f"kv_valid must be a contiguous int32 tensor with {N} entries")
+    elif mask_mod == MASK_KV_VALID_COUNT and mask_list is not None:
+        raise ValueError("MASK_KV_VALID_COUNT needs kv_valid")
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     st = lib.bsa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                      _ptr(dk), _ptr(dv), B, H, Hkv, Sq, Sk, D,

@@ -20,19 +20,23 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool supported_head_dim(int D) { return D == 64 || D == 96 || D == 128 || D == 192 || D == 256; }
 
 // Tile fit (runguoli.com "FlashAttention - CuTe Kernels & Block Sparsity":
-// fit the forward tile to the sparse block instead of rejecting it): the
-// workgroup row count is the largest of 256/128/64/32 dividing the sparse Q
-// block (256 only for head_dim <= 128 with bf16 inputs, where eight waves of
-// 32 rows fit two per SIMD), and a larger Q block is covered by
-// block_q / tile_m workgroups that share its block-list row.  KV blocks of
-// any size are cut into 64-key sub-tiles inside the kernel.
+// fit the forward tile to the sparse block instead of rejecting it).  A Q
+// block that is a multiple of 32 rows takes the largest of 256/128/64/32
+// rows dividing it (256 only for head_dim <= 128 with bf16 inputs, where
+// eight waves of 32 rows fit two per SIMD).  Any other Q block takes the
+// smallest of 32/64/128 rows that holds it, or 128-row tiles beyond 128
+// rows; the rows of its last tile stop at the block end.  A Q block is
+// covered by ceil(block_q / tile_m) workgroups sharing its block-list row.
+// KV blocks of any size are cut into 64-key sub-tiles inside the kernel.
 int fit_tile_m(int block_q, int D, bool f32_in, int mask_mod) {
   // the 256-row kernel knows the causal and valid-count masks only
   if (block_q % 256 == 0 && D <= 128 && !f32_in && mask_mod != BSA_MASK_LOCAL) return 256;
   if (block_q % 128 == 0) return 128;
   if (block_q % 64 == 0) return 64;
   if (block_q % 32 == 0) return 32;
-  return 0;
+  if (block_q < 32) return 32;
+  if (block_q < 64) return 64;
+  return 128;
 }
 
 int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -242,7 +246,8 @@ bsa_status bsa_fwd(const void* q, const void* k, const void* v, void* o, float* 
     if (!subtile_offsets_fit(bs->proxy_k_str[1], bs->proxy_v_str[1], es))
       return BSA_ERR_UNSUPPORTED;
   }
-  const int64_t tiles_per_head = cdiv64(Sq, tile_m);
+  const int64_t qsub = cdiv64(bs->block_q, tile_m);
+  const int64_t tiles_per_head = M * qsub;
   const int64_t tiles = (int64_t)B * H * tiles_per_head;
   if (tiles > std::numeric_limits<int32_t>::max() || N > std::numeric_limits<int32_t>::max() / 2)
     return BSA_ERR_UNSUPPORTED;
@@ -262,6 +267,7 @@ bsa_status bsa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   p.o_sb = o_str[0]; p.o_ss = o_str[1]; p.o_sh = o_str[2];
   copy_lists(p, *bs);
   p.kv_valid = kv_valid;
+  p.kvv_ld = 0;
   p.B = B;
   p.H = H;
   p.hrep = H / H_kv;
@@ -269,7 +275,7 @@ bsa_status bsa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   p.Sk = Sk;
   p.block_q = bs->block_q;
   p.block_kv = bs->block_kv;
-  p.qsub = bs->block_q / tile_m;
+  p.qsub = (int32_t)qsub;
   p.mask_mod = mask_mod;
   p.win_left = bs->window_left;
   p.win_right = bs->window_right;
@@ -298,17 +304,16 @@ bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, 
                           int32_t total_m_blocks, int32_t total_n_blocks, int32_t total_q,
                           const int64_t q_str[2], const int64_t k_str[2], const int64_t v_str[2],
                           const int64_t o_str[2], const bsa_block_sparse* bs,
-                          bsa_mask_mod mask_mod, float softmax_scale, uint32_t flags,
+                          bsa_mask_mod mask_mod, const int32_t* kv_valid,
+                          int64_t kv_valid_ld, float softmax_scale, uint32_t flags,
                           hipStream_t stream) {
   if (bs && (bs->proxy_k || bs->proxy_v)) return BSA_ERR_UNSUPPORTED;  // batched only
   if (B < 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || total_m_blocks < 0 || total_n_blocks < 0 ||
       total_q < 0)
     return BSA_ERR_INVALID_ARGUMENT;
   if (dt != BSA_BF16 && dt != BSA_F32) return BSA_ERR_INVALID_ARGUMENT;
-  if (mask_mod != BSA_MASK_NONE && mask_mod != BSA_MASK_CAUSAL && mask_mod != BSA_MASK_LOCAL) {
-    if (mask_mod == BSA_MASK_KV_VALID_COUNT) return BSA_ERR_UNSUPPORTED;
-    return BSA_ERR_INVALID_ARGUMENT;
-  }
+  if (mask_mod < BSA_MASK_NONE || mask_mod > BSA_MASK_LOCAL) return BSA_ERR_INVALID_ARGUMENT;
+  if (kv_valid_ld < 0) return BSA_ERR_INVALID_ARGUMENT;
   if (!bs || !q_str || !k_str || !v_str || !o_str) return BSA_ERR_INVALID_ARGUMENT;
   if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f)) return BSA_ERR_INVALID_ARGUMENT;
   if (bs->block_q <= 0 || bs->block_kv <= 0) return BSA_ERR_INVALID_ARGUMENT;
@@ -320,13 +325,15 @@ bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, 
   if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k || !cu_total_m_blocks ||
       !block_idx_offsets)
     return BSA_ERR_INVALID_ARGUMENT;
+  if (mask_mod == BSA_MASK_KV_VALID_COUNT && !kv_valid && bs->mask.cnt)
+    return BSA_ERR_INVALID_ARGUMENT;
   const int es = dt == BSA_BF16 ? 2 : 4;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return BSA_ERR_MISALIGNED;
   if (!strides_ok(q_str, 2, es) || !strides_ok(k_str, 2, es) || !strides_ok(v_str, 2, es) ||
       !strides_ok(o_str, 2, es))
     return BSA_ERR_MISALIGNED;
   if (!subtile_offsets_fit(k_str[0], v_str[0], es)) return BSA_ERR_UNSUPPORTED;
-  const int qsub = bs->block_q / tile_m;
+  const int qsub = (int)cdiv64(bs->block_q, tile_m);
   const int64_t tiles_per_head = (int64_t)total_m_blocks * qsub;
   const int64_t tiles = tiles_per_head * H;
   if (tiles > std::numeric_limits<int32_t>::max()) return BSA_ERR_UNSUPPORTED;
@@ -346,6 +353,8 @@ bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, 
   p.v_ss = v_str[0]; p.v_sh = v_str[1];
   p.o_ss = o_str[0]; p.o_sh = o_str[1];
   copy_lists(p, *bs);
+  p.kv_valid = mask_mod == BSA_MASK_KV_VALID_COUNT ? kv_valid : nullptr;
+  p.kvv_ld = kv_valid_ld;
   p.cu_q = cu_seqlens_q;
   p.cu_k = cu_seqlens_k;
   p.cu_m = cu_total_m_blocks;

@@ -174,12 +174,15 @@ void bsa_fwd_kernel(const FwdParams p) {
     build_listed_bitmap(xbits, p, ti, tid, NW * 64);
   }
 
-  // Q fragments (S^T MFMA B operand): Q[qrow][16*ks + 8*h32 .. +7]
+  // Q fragments (S^T MFMA B operand): Q[qrow][16*ks + 8*h32 .. +7].  A wave
+  // whose 32 rows all lie past the Q block's end (a block that is not a
+  // multiple of 32 rows) only fetches and waits with the others.
   const int qrow = ti.q0 + 32 * w + l32;
+  const bool live = ti.q0 + 32 * w < ti.qend;
   uint4 qf[DS];
 #pragma unroll
   for (int ks = 0; ks < DS; ++ks)
-    qf[ks] = qrow < ti.Sq
+    qf[ks] = qrow < ti.qend
                  ? *reinterpret_cast<const uint4*>(qp + (int64_t)qrow * p.q_ss + ks * 16 + h32 * 8)
                  : make_uint4(0, 0, 0, 0);
   f32x16_t oacc[DB];
@@ -360,7 +363,7 @@ void bsa_fwd_kernel(const FwdParams p) {
   };
 
   ListWalk L{ti.mrow, p.mi_s[3], ti.mcnt, ti.frow, p.fi_s[3], ti.mcnt + ti.fcnt,
-             p.block_kv, ti.num_n, p.mask_mod, p.kv_valid, -1000000, -1, 0};
+             p.block_kv, ti.num_n, p.mask_mod, ti.kvv, -1000000, -1, 0};
   // Two stages: the sub-tile after the one being computed streams into the
   // other stage.  One stage: the next sub-tile is fetched once every wave is
   // done with the current one.  p0 is the issued, not yet computed sub-tile.
@@ -391,7 +394,7 @@ void bsa_fwd_kernel(const FwdParams p) {
       wait_vmem<0>();
       __syncthreads();
       const Item cur = p0;
-      compute(0, cur);
+      if (live) compute(0, cur);
       if (more) {
         __syncthreads();  // every wave done with the stage before it is refilled
         issue(walker, 0);
@@ -415,7 +418,7 @@ void bsa_fwd_kernel(const FwdParams p) {
     } else {
       pending = false;
     }
-    compute(stage, cur);
+    if (live) compute(stage, cur);
     stage ^= 1;
   }
   epilogue<DB, __bf16>(p, ti, qrow, h32, m_run, l_run, oacc);

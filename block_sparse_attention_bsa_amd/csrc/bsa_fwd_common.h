@@ -59,17 +59,24 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
   return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
-// What one workgroup works on: rows [q0, q0 + TM) of one (sequence, head)
-// and the block-list row of their sparse Q block.
+// What one workgroup works on: rows [q0, min(q0 + TM, qend)) of one
+// (sequence, head), qend being the end of their sparse Q block (clipped to
+// the sequence), and the block-list row of that Q block.
 struct TileInfo {
-  int h, q0, Sq, Sk, num_n;
+  int h, q0, qend, Sq, Sk, num_n;
+  const int32_t* kvv;  // valid-token counts of this sequence's KV blocks (or null)
   int64_t qoff, koff, voff, ooff, lse_base;  // element offsets of row 0 / LSE row 0
   const int32_t* mrow;
   const int32_t* frow;
   int mcnt, fcnt;
 };
 
-// Logical tile t -> TileInfo.  Batched: t = ((b*H + h) * tiles_per_head + qt).
+// Logical tile t -> TileInfo.  A sparse Q block of block_q rows is covered
+// by qsub = ceil(block_q / TM) tiles; tile sub of Q block i starts at row
+// i*block_q + sub*TM and its rows stop at the block end, so a block of any
+// size (112, 80, 48 rows ...) is fitted rather than rejected (runguoli.com
+// "FlashAttention - CuTe Kernels & Block Sparsity", the tile-fit change).
+// Batched: t = ((b*H + h) * tiles_per_head + qt), qt = i * qsub + sub.
 // Varlen (flash-attention PR #2224 layout): t = h * tiles_per_head + tm with
 // tm = Q block * qsub + sub; the sequence is the largest b with
 // cu_total_m_blocks[b] <= Q block (binary search), the list row starts at
@@ -84,12 +91,15 @@ __device__ __forceinline__ bool decode_tile(const FwdParams& p, int t, TileInfo&
     const int qt = t % p.tiles_per_head;
     const int bh = t / p.tiles_per_head;
     const int h = bh % p.H, b = bh / p.H, hk = h / p.hrep;
-    const int i = qt / p.qsub;
+    const int i = qt / p.qsub, sub = qt % p.qsub;
     ti.h = h;
-    ti.q0 = qt * TM;
+    ti.q0 = i * p.block_q + sub * TM;
+    ti.qend = min(p.Sq, min(i * p.block_q + p.block_q, ti.q0 + TM));
+    if (ti.q0 >= ti.qend) return false;
     ti.Sq = p.Sq;
     ti.Sk = p.Sk;
     ti.num_n = cdiv(p.Sk, p.block_kv);
+    ti.kvv = p.kv_valid;
     ti.qoff = b * p.q_sb + h * p.q_sh;
     ti.koff = b * p.k_sb + hk * p.k_sh;
     ti.voff = b * p.v_sb + hk * p.v_sh;
@@ -123,7 +133,11 @@ __device__ __forceinline__ bool decode_tile(const FwdParams& p, int t, TileInfo&
     ti.Sk = p.cu_k[b + 1] - sk0;
     ti.num_n = cdiv(ti.Sk, p.block_kv);
     ti.q0 = m * p.block_q + sub * TM;
-    if (m < 0 || m >= cdiv(ti.Sq, p.block_q) || ti.q0 >= ti.Sq) return false;
+    if (m < 0 || m >= cdiv(ti.Sq, p.block_q)) return false;
+    ti.qend = min(ti.Sq, min(m * p.block_q + p.block_q, ti.q0 + TM));
+    if (ti.q0 >= ti.qend) return false;
+    // valid-token counts: row b of a [B, kv_valid_ld] array (ld 0: one row for all)
+    ti.kvv = p.kv_valid != nullptr ? p.kv_valid + (int64_t)b * p.kvv_ld : nullptr;
     const int64_t row_p = (int64_t)p.blk_off[b] + (int64_t)m * ti.num_n;
     if (row_p < 0 || row_p + ti.num_n > p.total_n) return false;  // inconsistent bookkeeping
     ti.qoff = (int64_t)sq0 * p.q_ss + h * p.q_sh;
@@ -312,7 +326,7 @@ template <int DB, typename T>
 __device__ __forceinline__ void epilogue(const FwdParams& p, const TileInfo& ti, int qrow, int h32,
                                          float m_run, float l_run, const f32x16_t (&oacc)[DB]) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (qrow >= ti.Sq) return;
+  if (qrow >= ti.qend) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   T* op = reinterpret_cast<T*>(p.o) + ti.ooff + (int64_t)qrow * p.o_ss;
 #pragma unroll

@@ -465,7 +465,7 @@ void bsa_fwd_pp_kernel(const FwdParams p) {
 
   ItemStream L{ti.mrow, ti.frow, p.mi_s[3], p.fi_s[3], ti.mcnt, ti.mcnt + ti.fcnt,
                p.block_kv, ti.Sk, ti.num_n,
-               p.mask_mod == kMaskKvValid ? p.kv_valid : nullptr,
+               p.mask_mod == kMaskKvValid ? ti.kvv : nullptr,
                -1, 0, -1000000, 0, 0, 0, 0};
   Sub t0, t1, t2, t3;
   const bool e0 = L.next(lane, t0);
@@ -490,7 +490,7 @@ void bsa_fwd_pp_kernel(const FwdParams p) {
   // issued above) before the loop, not inside it.
 #pragma unroll
   for (int ks = 0; ks < DS; ++ks) {
-    qf[ks] = qrow < ti.Sq
+    qf[ks] = qrow < ti.qend
                  ? *reinterpret_cast<const uint4*>(qp + (int64_t)qrow * p.q_ss + ks * 16 + h32 * 8)
                  : make_uint4(0, 0, 0, 0);
   }

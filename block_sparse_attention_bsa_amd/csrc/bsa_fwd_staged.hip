@@ -93,11 +93,12 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_staged_kernel(const FwdParams
   }
 
   const int qrow = ti.q0 + 32 * w + l32;
+  const bool live = ti.q0 + 32 * w < ti.qend;  // else only stage and wait (rows past the block)
   uint4 qf[DS];
 #pragma unroll
   for (int ks = 0; ks < DS; ++ks) {
     Chunk<F32IN> c;
-    if (qrow < ti.Sq)
+    if (qrow < ti.qend)
       c.load(qp + (int64_t)qrow * p.q_ss + ks * 16 + h32 * 8);
     else
       c.zero();
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_staged_kernel(const FwdParams
   };
 
   ListWalk L{ti.mrow, p.mi_s[3], ti.mcnt, ti.frow, p.fi_s[3], ti.mcnt + ti.fcnt,
-             p.block_kv, ti.num_n, p.mask_mod, p.kv_valid, -1000000, -1, 0};
+             p.block_kv, ti.num_n, p.mask_mod, ti.kvv, -1000000, -1, 0};
   unsigned char* buf0 = smem;
   unsigned char* buf1 = smem + STAGE;
   // listed blocks first, then (PROXY) the chunks of summaries with an unlisted block
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_staged_kernel(const FwdParams
     if (have_nxt) issue(nxt);
     unsigned char* cb = sb ? buf1 : buf0;
     unsigned char* ob = sb ? buf0 : buf1;
-    compute(cb, cb + KBYTES, cur);
+    if (live) compute(cb, cb + KBYTES, cur);
     if (have_nxt) store(ob, ob + KBYTES);
     __syncthreads();
     cur = nxt;

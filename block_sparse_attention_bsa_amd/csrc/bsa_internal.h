@@ -31,6 +31,7 @@ struct FwdParams {
   const int32_t* fidx;
   int64_t mc_s[3], mi_s[4], fc_s[3], fi_s[4];
   const int32_t* kv_valid;
+  int64_t kvv_ld;  // varlen: entries between the kv_valid rows of two sequences (0: shared row)
   // varlen bookkeeping (device, [B+1]); null for batched
   const int32_t* cu_q;
   const int32_t* cu_k;
@@ -39,7 +40,7 @@ struct FwdParams {
   int32_t B, H, hrep, Sq, Sk;
   int32_t block_q, block_kv, qsub;
   int32_t mask_mod, varlen;
-  int32_t tiles_per_head;  // batched: ceil(Sq/TM); varlen: total_m_blocks*qsub
+  int32_t tiles_per_head;  // batched: num_m_blocks*qsub; varlen: total_m_blocks*qsub
   int32_t total_m, total_n;  // varlen only
   int32_t lse_ld;          // batched: Sq; varlen: total_q
   int32_t num_tiles;       // grid size

@@ -97,7 +97,12 @@ typedef struct {
 } bsa_block_list;
 
 /* The (mask, full) pair and the sparse block sizes (in tokens).
- * block_q must be a multiple of 32; block_kv may be any positive size.
+ * block_q and block_kv may be any positive size: the forward fits its tiles
+ * to them (runguoli.com "FlashAttention - CuTe Kernels & Block Sparsity":
+ * tiles fitted to the sparse block size instead of rejecting it).  A Q
+ * block runs as ceil(block_q / tile_m) tiles of tile_m in {256, 128, 64,
+ * 32} rows whose last one stops at the block end; a KV block runs as 64-key
+ * sub-tiles whose last one stops at the block end.
  * window_left / window_right: the bounds of BSA_MASK_LOCAL (ignored by the
  * other mask_mods).
  *
@@ -160,7 +165,14 @@ bsa_status bsa_fwd(const void* q, const void* k, const void* v, void* o, float* 
  *    cu_seqlens_q[B] (the LSE row length), passed from the host so the
  *    launch needs no device->host copy.
  *  Block ids in the lists are sequence-local; mask_mod uses sequence-local
- *  (q_idx, kv_idx).  BSA_MASK_KV_VALID_COUNT is not supported here.
+ *  (q_idx, kv_idx).
+ *  kv_valid, kv_valid_ld: the valid-token counts of BSA_MASK_KV_VALID_COUNT
+ *    (FastVideo PR #1354 review thread: keep kv_off < valid of the KV
+ *    block), per sequence-local KV block: sequence b's KV block j (j <
+ *    ceil(seqlen_k(b)/block_kv)) has count kv_valid[b*kv_valid_ld + j]
+ *    (device int32; kv_valid_ld = 0 gives every sequence one shared row).
+ *    Required when mask_mod is BSA_MASK_KV_VALID_COUNT and a mask list is
+ *    given; ignored otherwise.  kv_valid_ld < 0 is BSA_ERR_INVALID_ARGUMENT.
  * Alignment rules as bsa_fwd. */
 bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                           bsa_dtype dt, int32_t B, int32_t H, int32_t H_kv, int32_t D,
@@ -170,6 +182,7 @@ bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, 
                           const int64_t q_str[2], const int64_t k_str[2],
                           const int64_t v_str[2], const int64_t o_str[2],
                           const bsa_block_sparse* bs, bsa_mask_mod mask_mod,
+                          const int32_t* kv_valid, int64_t kv_valid_ld,
                           float softmax_scale, uint32_t flags, hipStream_t stream);
 
 /* Dense block mask -> block lists ("Dense FlashAttention vs Block-Sparse

@@ -269,6 +269,9 @@ def varlen_blocksparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     """Packed varlen forward (PR #2224): each sequence b is an independent
     batch-1 problem with sequence-local row/column ids.  q [Tq,H,D],
     k/v [Tk,Hkv,D]; full[b]/part[b] dense per-sequence block masks [H,M_b,N_b].
+    kv_valid (valid-count mask_mod): one array of counts shared by every
+    sequence, or one per sequence (a list, or the rows of a 2-D array), each
+    indexed by the sequence-local KV block id.
     q_blocks: optional (b, h, i) with sequence-local i.  Returns O [Tq,H,D],
     LSE [H,Tq]."""
     q = np.asarray(q, np.float64)
@@ -291,8 +294,11 @@ def varlen_blocksparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
         qb = q[None, cq[b]:cq[b + 1]]
         kb = k[None, ck[b]:ck[b + 1]]
         vb = v[None, ck[b]:ck[b + 1]]
+        per_seq = kv_valid is not None and (isinstance(kv_valid, (list, tuple)) or
+                                            np.ndim(kv_valid) == 2)
+        kvb = np.asarray(kv_valid[b]) if per_seq else kv_valid
         o, lse = blocksparse_attention(qb, kb, vb, full[b][None], part[b][None],
-                                       block_q, block_kv, mask_mod, scale, kv_valid,
+                                       block_q, block_kv, mask_mod, scale, kvb,
                                        q_blocks=None if sel is None else sel[b],
                                        window=window)
         O[cq[b]:cq[b + 1]] = o[0]

@@ -339,10 +339,10 @@ def test_argument_errors():
     with pytest.raises(ValueError) as e:
         bsa.bsa_fwd(pad(q), pad(k), pad(v), None, fl, 64, 64)
     assert e.value.status == 2  # head_dim 80: no kernel
+    # a Q block that is not a multiple of 32 rows is fitted, not rejected
+    # (its parity: test_q_blocks_of_any_size)
     fl48 = lists_on_device(np.zeros((2, 4, 7, 5), bool))
-    with pytest.raises(ValueError) as e:
-        bsa.bsa_fwd(q, k, v, None, fl48, 48, 64)
-    assert e.value.status == 2  # block_q not a multiple of 32
+    bsa.bsa_fwd(q, k, v, None, fl48, 48, 64)
     raw = torch.empty(q.numel() + 8, dtype=torch.bfloat16, device="cuda")
     qm = raw[1:1 + q.numel()].view(q.shape)
     qm.copy_(q)
@@ -517,3 +517,111 @@ def test_row_max_sees_every_key_of_the_item(bq, D):
     torch.cuda.synchronize()
     O, L = _oracle_batched(w, qkv)
     check_o_lse(o, lse, O, L, f"bq={bq} D={D} hot keys")
+
+
+# ------------------------------------------ Q blocks of any size (tile fit)
+# A Q block that is not a multiple of 32 rows runs as ceil(block_q / tile)
+# tiles whose last one stops at the block end (the tile-fit change of
+# runguoli.com "FlashAttention - CuTe Kernels & Block Sparsity"): every row
+# against the oracle, causal diagonals included, ragged sequence ends.
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("bq,bk", [(112, 112), (80, 128), (48, 64), (16, 64), (200, 96),
+                                   (144, 48)])
+def test_q_blocks_of_any_size(D, bq, bk):
+    w = workloads.sparse_sweep(D, bq, bk, B=2, H=2, S=650, density=0.4, seed=[11, D, bq, bk])
+    o, lse, qkv = run_batched(w)
+    torch.cuda.synchronize()
+    O, L = _oracle_batched(w, qkv)
+    check_o_lse(o, lse, O, L, f"any-size Q blocks D={D} ({bq},{bk})")
+
+
+def test_q_blocks_of_any_size_fp32_and_local():
+    # the fp32 (register-staged) kernel and the local mask_mod take the same fit
+    w = workloads.sparse_sweep(64, 80, 64, B=1, H=2, S=333, density=0.5, seed=12)
+    o, lse, qkv = run_batched(w, dtype=torch.float32)
+    torch.cuda.synchronize()
+    O, L = _oracle_batched(w, tuple(t.to(torch.bfloat16) for t in qkv))
+    check_o_lse(o, lse, O, L, "fp32 bq=80")
+    S, bq, bk, win = 500, 112, 64, (150, 0)
+    wl = workloads.sliding_window(B=1, H=2, S=S, D=128, bs=64, window=win, seed=13)
+    q, k, v = (to_dev(x) for x in (wl.q, wl.k, wl.v))
+    fu, pa = oracle.block_sparsity(oracle.MASK_LOCAL, S, S, bq, bk, window=win)
+    M, N = fu.shape
+    fb = np.broadcast_to(fu.astype(bool), (1, 2, M, N))
+    pb = np.broadcast_to(pa.astype(bool), (1, 2, M, N))
+    o, lse = bsa.bsa_fwd(q, k, v, lists_on_device(pb), lists_on_device(fb), bq, bk,
+                         bsa.MASK_LOCAL, None, wl.scale, window=win)
+    torch.cuda.synchronize()
+    O, L = oracle.blocksparse_attention(as_oracle(q), as_oracle(k), as_oracle(v), fb, pb, bq, bk,
+                                        oracle.MASK_LOCAL, wl.scale, window=win)
+    check_o_lse(o, lse, O, L, "local bq=112")
+
+
+# ------------------------------------------ varlen under the valid-count mask_mod
+def _varlen_device(w):
+    H, bq, bk = w.q.shape[1], w.block_q, w.block_kv
+    cu, off, tm, tn = bsa.bsa_varlen_offsets(w.seqlens_q, w.seqlens_k, bq, bk)
+    dev = lambda a: torch.tensor(a, dtype=torch.int32, device="cuda")
+    cu_q = dev([0] + list(np.cumsum(w.seqlens_q)))
+    cu_k = dev([0] + list(np.cumsum(w.seqlens_k)))
+
+    def packed(masks):
+        out = np.zeros((H, tn), np.uint8)
+        for b, m in enumerate(masks):
+            nm, nn = m.shape[1:]
+            for i in range(nm):
+                out[:, off[b] + i * nn: off[b] + (i + 1) * nn] = m[:, i]
+        return torch.from_numpy(out).cuda()
+
+    cu_m, offs = dev(cu), dev(off)
+    ml = bsa.bsa_varlen_mask_to_index(packed(w.part), cu_m, offs, tm, tn)
+    fl = bsa.bsa_varlen_mask_to_index(packed(w.full), cu_m, offs, tm, tn)
+    return cu_q, cu_k, cu_m, offs, tm, tn, ml, fl
+
+
+@pytest.mark.parametrize("bq,bk,D", [(256, 128, 128), (128, 128, 128), (112, 80, 64),
+                                     (64, 48, 96)])
+def test_varlen_valid_count(bq, bk, D):
+    # per-sequence valid-token counts (kv_valid [B, W], row b for sequence b's
+    # sequence-local KV blocks), every row against the oracle
+    w = workloads.varlen_valid_count(n_seq=5, H=3, D=D, bq=bq, bk=bk, lo=100, hi=1500,
+                                     seed=[5, bq, bk, D])
+    cu_q, cu_k, cu_m, offs, tm, tn, ml, fl = _varlen_device(w)
+    W = max(len(x) for x in w.kv_valid) + 3
+    kvv = np.full((len(w.kv_valid), W), -7, np.int32)  # padding never read
+    for b, x in enumerate(w.kv_valid):
+        kvv[b, :len(x)] = x
+    kvv_t = torch.from_numpy(kvv).cuda()
+    q, k, v = (to_dev(x) for x in (w.q, w.k, w.v))
+    o, lse = bsa.bsa_varlen_fwd(q, k, v, cu_q, cu_k, cu_m, offs, tm, tn, ml, fl, bq, bk,
+                                KVV, w.scale, kv_valid=kvv_t)
+    torch.cuda.synchronize()
+    O, L = oracle.varlen_blocksparse_attention(as_oracle(q), as_oracle(k), as_oracle(v),
+                                               w.seqlens_q, w.seqlens_k, w.full, w.part, bq, bk,
+                                               KVV, w.scale, kv_valid=w.kv_valid)
+    check_o_lse(o, lse, O, L, f"varlen kvv ({bq},{bk}) D={D}")
+
+
+def test_varlen_valid_count_shared_row_and_errors():
+    # kv_valid_ld = 0: one row of counts shared by every sequence
+    w = workloads.varlen_valid_count(n_seq=3, H=2, D=128, bq=128, bk=64, lo=200, hi=900,
+                                     seed=31)
+    shared = np.minimum.reduce([np.pad(x, (0, 20), constant_values=64)[:20]
+                                for x in w.kv_valid]).astype(np.int32)
+    # masks consistent with the shared counts: selected whole blocks full, others mask
+    cu_q, cu_k, cu_m, offs, tm, tn, ml, fl = _varlen_device(w)
+    q, k, v = (to_dev(x) for x in (w.q, w.k, w.v))
+    o, lse = bsa.bsa_varlen_fwd(q, k, v, cu_q, cu_k, cu_m, offs, tm, tn, ml, fl, 128, 64,
+                                KVV, w.scale, kv_valid=torch.from_numpy(shared).cuda())
+    torch.cuda.synchronize()
+    O, L = oracle.varlen_blocksparse_attention(as_oracle(q), as_oracle(k), as_oracle(v),
+                                               w.seqlens_q, w.seqlens_k, w.full, w.part, 128, 64,
+                                               KVV, w.scale, kv_valid=shared)
+    check_o_lse(o, lse, O, L, "varlen kvv shared row")
+    with pytest.raises(ValueError):  # the valid-count mask needs the counts
+        bsa.bsa_varlen_fwd(q, k, v, cu_q, cu_k, cu_m, offs, tm, tn, ml, fl, 128, 64, KVV,
+                           w.scale)
+    with pytest.raises(ValueError):  # rows shorter than the longest sequence's blocks
+        bsa.bsa_varlen_fwd(q, k, v, cu_q, cu_k, cu_m, offs, tm, tn, ml, fl, 128, 64, KVV,
+                           w.scale, kv_valid=torch.zeros((3, 2), dtype=torch.int32,
+                                                          device="cuda"))

@@ -217,3 +217,34 @@ def test_sampled_q_blocks_match_full_run():
         r = slice(i * 128, min(500, (i + 1) * 128))
         np.testing.assert_array_equal(Os[b, r, h], O[b, r, h])
         np.testing.assert_array_equal(Ls[b, h, r], L[b, h, r])
+
+
+def test_varlen_per_sequence_valid_counts_equal_bruteforce():
+    # packed batch under the valid-count mask_mod with counts of its own per
+    # sequence: each sequence equals brute-force dense attention over the
+    # element mask expanded with that sequence's counts, and SDPA with it
+    w = workloads.varlen_valid_count(n_seq=3, H=2, D=16, bq=48, bk=32, lo=20, hi=150, seed=21)
+    O, L = oracle.varlen_blocksparse_attention(w.q, w.k, w.v, w.seqlens_q, w.seqlens_k,
+                                               w.full, w.part, w.block_q, w.block_kv,
+                                               w.mask_mod, w.scale, kv_valid=w.kv_valid)
+    assert np.isfinite(O).all()
+    off = 0
+    for b, s in enumerate(w.seqlens_q):
+        qb, kb, vb = (x[None, off:off + s].astype(np.float64) for x in (w.q, w.k, w.v))
+        em = oracle.expand_element_mask(w.full[b][None], w.part[b][None], 48, 32, s, s, KVV,
+                                        kv_valid=w.kv_valid[b])
+        Od, Ld = oracle.dense_attention(qb, kb, vb, em, w.scale)
+        np.testing.assert_allclose(O[off:off + s], Od[0], atol=1e-12)
+        np.testing.assert_allclose(L[:, off:off + s], Ld[0], atol=1e-12)
+        live = em.any(-1)[0]  # rows with a visible key (SDPA gives NaN on empty rows)
+        Os = _sdpa(qb, kb, vb, attn_mask=np.where(live[:, :, None], em[0], True)[None],
+                   scale=w.scale)
+        np.testing.assert_allclose(Od[0][live.T], Os[0][live.T], atol=1e-12)
+        off += s
+    # the counts are per sequence: giving every sequence the first one's row
+    # (padded) changes the result wherever a later sequence's counts differ
+    shared = np.concatenate([w.kv_valid[0], np.full(64, 32, np.int32)])
+    O2, _ = oracle.varlen_blocksparse_attention(w.q, w.k, w.v, w.seqlens_q, w.seqlens_k,
+                                                w.full, w.part, w.block_q, w.block_kv,
+                                                w.mask_mod, w.scale, kv_valid=shared)
+    assert not np.allclose(np.nan_to_num(O2), np.nan_to_num(O))

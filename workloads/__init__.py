@@ -65,6 +65,8 @@ class VarlenWorkload:
 
     seqlens_q / seqlens_k: python int lists.  full[b] / part[b] are dense
     per-sequence block masks [H, M_b, N_b] with sequence-local block ids.
+    kv_valid: per-sequence valid-token counts of the KV blocks (valid-count
+    mask_mod only).
     """
     name: str
     q: np.ndarray
@@ -78,6 +80,7 @@ class VarlenWorkload:
     block_kv: int
     mask_mod: int
     scale: float
+    kv_valid: Optional[List[np.ndarray]] = None  # per sequence, int32 [N_b]
 
 
 @dataclass
@@ -217,6 +220,36 @@ def varlen_packed(n_seq=8, H=16, D=128, bs=128, lo=128, hi=8192, p_below=0.3,
         part.append(np.broadcast_to((jj == ii)[None], (H, M, N)).copy())
     return VarlenWorkload("varlen_packed", q, k, v, seqlens, list(seqlens), full, part,
                           bs, bs, MASK_CAUSAL, 1.0 / math.sqrt(D))
+
+
+def varlen_valid_count(n_seq=6, H=4, D=128, bq=256, bk=128, lo=300, hi=3000, p_sel=0.3,
+                       seed: int = 1008) -> VarlenWorkload:
+    """Packed varlen batch under the valid-count mask_mod (FastVideo PR #1354
+    review thread, in the packed layout of flash-attention PR #2224): each
+    sequence's KV blocks hold a random number of real tokens (valid counts
+    drawn per sequence and block, the last block never past its sequence
+    end).  Each (head, Q block, KV block) is selected with probability p_sel;
+    a selected block whose count is the whole block goes to the full list,
+    any other to the mask list.  `extra["kv_valid"]` holds the per-sequence
+    counts."""
+    rng = np.random.default_rng(seed)
+    seqlens = [int(x) for x in rng.integers(lo, hi + 1, size=n_seq)]
+    total = sum(seqlens)
+    q, k, v = _qkv(rng, (total, H, D), (total, H, D))
+    full, part, kvv = [], [], []
+    for s in seqlens:
+        M, N = _cdiv(s, bq), _cdiv(s, bk)
+        cap = np.minimum(bk, s - np.arange(N) * bk)
+        valid = rng.integers(0, cap + 1).astype(np.int32)  # 0 .. block size (or sequence end)
+        whole = rng.random(N) < 0.5
+        valid[whole] = cap[whole]
+        sel = rng.random((H, M, N)) < p_sel
+        is_full = (valid == bk)[None, None, :]
+        full.append(sel & is_full)
+        part.append(sel & ~is_full)
+        kvv.append(valid)
+    return VarlenWorkload("varlen_valid_count", q, k, v, seqlens, list(seqlens), full, part,
+                          bq, bk, MASK_KV_VALID_COUNT, 1.0 / math.sqrt(D), kv_valid=kvv)
 
 
 def sliding_window(B=2, H=16, S=8192, D=128, bs=128, window=(1024, 0),
