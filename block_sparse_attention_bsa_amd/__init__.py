@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "MASK_NONE", "MASK_CAUSAL", "MASK_KV_VALID_COUNT", "MASK_LOCAL", "BsaError",
     "bsa_fwd", "bsa_varlen_fwd", "bsa_mask_to_index", "bsa_bitmask_to_index", "bsa_kv_major_lists",
-    "bsa_bwd",
+    "bsa_bwd", "bsa_bwd_noalloc",
     "bsa_varlen_mask_to_index",
     "bsa_varlen_offsets", "bsa_expand_kv_blocks", "bsa_block_sparsity", "bsa_status_str",
     "library_path", "load_library",
@@ -100,6 +100,8 @@ def load_library():
     lib.bsa_mask_to_index.argtypes = [P, I32, I32, I32, I32, P, P, P]
     lib.bsa_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
                             P, P, P, P, P, P, P, ctypes.c_int, P, ctypes.c_float, P, P]
+    lib.bsa_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
+                                    P, P, P, P, P, P, P, ctypes.c_int, P, ctypes.c_float, P]
     lib.bsa_kv_major_lists.argtypes = [P, P, I32, I32, I32, I32, P, P, P, P]
     lib.bsa_bitmask_to_index.argtypes = [P, I32, I32, I32, I32, I32, P, P, P]
     lib.bsa_varlen_mask_to_index.argtypes = [P, I32, I32, P, P, I32, I32, P, P, P]
@@ -110,6 +112,7 @@ def load_library():
     lib.bsa_status_str.argtypes = [ctypes.c_int]
     lib.bsa_status_str.restype = ctypes.c_char_p
     for fn in ("bsa_fwd", "bsa_varlen_fwd", "bsa_mask_to_index", "bsa_varlen_mask_to_index",
+               "bsa_bwd", "bsa_bwd_noalloc", "bsa_kv_major_lists", "bsa_bitmask_to_index",
                "bsa_varlen_offsets", "bsa_expand_kv_blocks", "bsa_block_sparsity"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -364,11 +367,13 @@ def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
             full_list: Optional[Tuple[torch.Tensor, torch.Tensor]],
             block_q: int, block_kv: int, mask_mod: int = MASK_NONE,
             kv_valid: Optional[torch.Tensor] = None, softmax_scale: Optional[float] = None,
-            window: Optional[Tuple[int, int]] = None):
+            window: Optional[Tuple[int, int]] = None, noalloc: bool = False):
     """Backward of bsa_fwd (bf16, head_dim 64/96/128/192/256): returns (dq, dk, dv).
     o and lse are the forward's outputs, dout the gradient of o; the lists,
     block sizes, mask_mod, kv_valid, scale and window are the forward's.  The
-    KV-major lists are built here with bsa_kv_major_lists."""
+    KV-major lists are built here with bsa_kv_major_lists.  noalloc=True calls
+    bsa_bwd_noalloc (the row dots in the library's static per-device array,
+    B*H*Sq <= 2**22) instead of passing a workspace."""
     lib = load_library()
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         _dev(n, t, torch.bfloat16)
@@ -399,7 +404,8 @@ def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
         raise ValueError("q, k and v must be dense (their gradients take their strides)")
-    work = torch.empty(max(B * H * Sq, 1), dtype=torch.float32, device=q.device)
+    work = None if noalloc else torch.empty(max(B * H * Sq, 1), dtype=torch.float32,
+                                            device=q.device)
     if kv_valid is not None:
         _dev("kv_valid", kv_valid, torch.int32)
         if not kv_valid.is_contiguous() or kv_valid.numel() < N:
@@ -407,15 +413,19 @@ def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     elif mask_mod == MASK_KV_VALID_COUNT and mask_list is not None:
         raise ValueError("MASK_KV_VALID_COUNT needs kv_valid")
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
-    st = lib.bsa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
-                     _ptr(dk), _ptr(dv), B, H, Hkv, Sq, Sk, D,
-                     _i64([q.stride(0), q.stride(1), q.stride(2)]),
-                     _i64([k.stride(0), k.stride(1), k.stride(2)]),
-                     _i64([v.stride(0), v.stride(1), v.stride(2)]),
-                     _i64([o.stride(0), o.stride(1), o.stride(2)]),
-                     ctypes.byref(bs), ctypes.byref(lt_m), ctypes.byref(lt_f), int(mask_mod),
-                     _ptr(kv_valid), scale, _ptr(work), _stream(q))
-    _check("bsa_bwd", st)
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+            _ptr(dv), B, H, Hkv, Sq, Sk, D, _i64([q.stride(0), q.stride(1), q.stride(2)]),
+            _i64([k.stride(0), k.stride(1), k.stride(2)]),
+            _i64([v.stride(0), v.stride(1), v.stride(2)]),
+            _i64([o.stride(0), o.stride(1), o.stride(2)]),
+            ctypes.byref(bs), ctypes.byref(lt_m), ctypes.byref(lt_f), int(mask_mod),
+            _ptr(kv_valid), scale]
+    if noalloc:
+        st = lib.bsa_bwd_noalloc(*args, _stream(q))
+        _check("bsa_bwd_noalloc", st)
+    else:
+        st = lib.bsa_bwd(*args, _ptr(work), _stream(q))
+        _check("bsa_bwd", st)
     return dq, dk, dv
 
 

@@ -405,13 +405,19 @@ bsa_status bsa_mask_to_index(const uint8_t* mask, int32_t B, int32_t H, int32_t 
   return e == hipSuccess ? BSA_OK : BSA_ERR_HIP;
 }
 
-bsa_status bsa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                   const void* dout, void* dq, void* dk, void* dv, int32_t B, int32_t H,
-                   int32_t H_kv, int32_t Sq, int32_t Sk, int32_t D, const int64_t q_str[3],
-                   const int64_t k_str[3], const int64_t v_str[3], const int64_t o_str[3],
-                   const bsa_block_sparse* bs, const bsa_block_list* mask_t,
-                   const bsa_block_list* full_t, bsa_mask_mod mask_mod, const int32_t* kv_valid,
-                   float softmax_scale, float* work, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The backward behind bsa_bwd and bsa_bwd_noalloc.  work == nullptr with
+// noalloc: the row dots go to the library's static per-device array.
+bsa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv, int32_t B, int32_t H,
+                    int32_t H_kv, int32_t Sq, int32_t Sk, int32_t D, const int64_t q_str[3],
+                    const int64_t k_str[3], const int64_t v_str[3], const int64_t o_str[3],
+                    const bsa_block_sparse* bs, const bsa_block_list* mask_t,
+                    const bsa_block_list* full_t, bsa_mask_mod mask_mod, const int32_t* kv_valid,
+                    float softmax_scale, float* work, bool noalloc, hipStream_t stream) {
   if (B < 0 || H <= 0 || H_kv <= 0 || Sq < 0 || Sk < 0 || H % H_kv != 0)
     return BSA_ERR_INVALID_ARGUMENT;
   if (mask_mod < BSA_MASK_NONE || mask_mod > BSA_MASK_LOCAL) return BSA_ERR_INVALID_ARGUMENT;
@@ -424,7 +430,8 @@ bsa_status bsa_bwd(const void* q, const void* k, const void* v, const void* o, c
   if (!supported_head_dim(D)) return BSA_ERR_UNSUPPORTED;
   if (bs->proxy_k || bs->proxy_v) return BSA_ERR_UNSUPPORTED;
   if ((int64_t)B * H * (Sq + Sk) == 0) return BSA_OK;
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !work)
+  if (noalloc && (int64_t)B * H * Sq > bsa::kBwdNoallocMaxRows) return BSA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || (!noalloc && !work))
     return BSA_ERR_INVALID_ARGUMENT;
   if (mask_mod == BSA_MASK_KV_VALID_COUNT && !kv_valid && (bs->mask.cnt || mask_t->cnt))
     return BSA_ERR_INVALID_ARGUMENT;
@@ -466,8 +473,38 @@ bsa_status bsa_bwd(const void* q, const void* k, const void* v, const void* o, c
   p.win_left = bs->window_left; p.win_right = bs->window_right;
   p.c = softmax_scale * kLog2e;
   p.scale = softmax_scale;
+  if (noalloc && bsa::bwd_noalloc_scratch(&p.drow) != hipSuccess) return BSA_ERR_HIP;
   const hipError_t e = bsa::launch_bwd(p, D, stream);
   return e == hipSuccess ? BSA_OK : BSA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+bsa_status bsa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, int32_t B, int32_t H,
+                   int32_t H_kv, int32_t Sq, int32_t Sk, int32_t D, const int64_t q_str[3],
+                   const int64_t k_str[3], const int64_t v_str[3], const int64_t o_str[3],
+                   const bsa_block_sparse* bs, const bsa_block_list* mask_t,
+                   const bsa_block_list* full_t, bsa_mask_mod mask_mod, const int32_t* kv_valid,
+                   float softmax_scale, float* work, hipStream_t stream) {
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, Sq, Sk, D, q_str, k_str, v_str,
+                  o_str, bs, mask_t, full_t, mask_mod, kv_valid, softmax_scale, work, false,
+                  stream);
+}
+
+bsa_status bsa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           int32_t B, int32_t H, int32_t H_kv, int32_t Sq, int32_t Sk, int32_t D,
+                           const int64_t q_str[3], const int64_t k_str[3],
+                           const int64_t v_str[3], const int64_t o_str[3],
+                           const bsa_block_sparse* bs, const bsa_block_list* mask_t,
+                           const bsa_block_list* full_t, bsa_mask_mod mask_mod,
+                           const int32_t* kv_valid, float softmax_scale, hipStream_t stream) {
+  return bwd_impl(q, k, v, o, lse, dout, dq, dk, dv, B, H, H_kv, Sq, Sk, D, q_str, k_str, v_str,
+                  o_str, bs, mask_t, full_t, mask_mod, kv_valid, softmax_scale, nullptr, true,
+                  stream);
 }
 
 bsa_status bsa_kv_major_lists(const int32_t* cnt, const int32_t* idx, int32_t B, int32_t H,

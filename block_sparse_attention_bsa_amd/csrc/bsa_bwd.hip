@@ -24,7 +24,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "bsa_fwd_common.h"
+
+// Row-dot workspace of the allocation-free entry point (bsa_bwd_noalloc):
+// one copy per GPU, held until the process ends.  Host code never passes
+// this name to a kernel (on the host it is a stand-in, not a device
+// address); it uses the address bwd_noalloc_scratch looks up per device.
+static __device__ __align__(256) float scratch[bsa::kBwdNoallocMaxRows];
 
 namespace bsa {
 namespace {
@@ -529,6 +537,25 @@ hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t bwd_noalloc_scratch(float** out) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<float*> addr[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  float* p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {  // once per device, with that device current
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    p = static_cast<float*>(a);
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
 
 hipError_t launch_bwd(const BwdParams& p, int D, hipStream_t s) {
   switch (D) {

@@ -98,6 +98,11 @@ struct BwdParams {
   float scale;  // softmax_scale
 };
 hipError_t launch_bwd(const BwdParams& p, int D, hipStream_t s);
+// Rows (B*H*Sq) the allocation-free backward's static row-dot array holds.
+constexpr int64_t kBwdNoallocMaxRows = (int64_t)1 << 22;
+// Device address of that array on the current device (looked up once per
+// device, then cached).
+hipError_t bwd_noalloc_scratch(float** out);
 
 hipError_t launch_kv_major_lists(const int32_t* cnt, const int32_t* idx, int32_t B, int32_t H,
                                  int32_t M, int32_t N, uint8_t* work, int32_t* cnt_t,

@@ -220,6 +220,28 @@ bsa_status bsa_bwd(const void* q, const void* k, const void* v, const void* o, c
                    const bsa_block_list* full_t, bsa_mask_mod mask_mod, const int32_t* kv_valid,
                    float softmax_scale, float* work, hipStream_t stream);
 
+/* bsa_bwd without the `work` argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving or training
+ * loops, harnesses that forbid hipMalloc.  The row dots go to a static
+ * device array of BSA_BWD_NOALLOC_MAX_ROWS floats (16 MiB) that the library
+ * holds on every GPU it runs on until the process ends; its address is looked
+ * up once per device on the first call there.  The call allocates nothing
+ * (no hipMalloc, hipFree or allocating library routine).  B*H*Sq above the
+ * maximum returns BSA_ERR_UNSUPPORTED.  Every call on one GPU shares that
+ * GPU's array, and each call overwrites all of it that it reads before
+ * reading it: calls ordered on one stream are safe, calls that overlap on one
+ * GPU (unordered streams) race and give undefined results.  Otherwise
+ * exactly bsa_bwd (same kernels, bit-identical results). */
+#define BSA_BWD_NOALLOC_MAX_ROWS (1 << 22)
+bsa_status bsa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           int32_t B, int32_t H, int32_t H_kv, int32_t Sq, int32_t Sk, int32_t D,
+                           const int64_t q_str[3], const int64_t k_str[3],
+                           const int64_t v_str[3], const int64_t o_str[3],
+                           const bsa_block_sparse* bs, const bsa_block_list* mask_t,
+                           const bsa_block_list* full_t, bsa_mask_mod mask_mod,
+                           const int32_t* kv_valid, float softmax_scale, hipStream_t stream);
+
 /* KV-major ("transposed") block lists: the per-KV-block view that a backward
  * pass walks (flash-attention pull request 2224, review thread: the backward
  * needs the block metadata transposed).  cnt: device int32 [B,H,M] and idx:

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     assert names == sorted(["bsa_fwd", "bsa_varlen_fwd", "bsa_mask_to_index",
                             "bsa_varlen_mask_to_index", "bsa_varlen_offsets",
                             "bsa_expand_kv_blocks", "bsa_block_sparsity", "bsa_bitmask_to_index",
-                            "bsa_kv_major_lists", "bsa_bwd",
+                            "bsa_kv_major_lists", "bsa_bwd", "bsa_bwd_noalloc",
                             "bsa_status_str"])
     lib = bsa.load_library()
     for n in names:
