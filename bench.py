@@ -12,9 +12,11 @@ Default workload: video sparse attention, B=1, H=24, 30x48x52 latent grid in
 bf16, each Q cube attending to its top 40 of 336 KV cubes (11.9% density),
 KV cubes run as 128-token tiles with per-tile valid-token counts.
 
-FLOPs per step count only computed work: 4 * head_dim * sum over listed
-(Q block, KV tile) pairs of (Q rows) x (KV keys the tile holds: its
-valid-token count), i.e. padding keys the kernel skips are not counted.
+FLOPs per step count the computed blocks: 4 * head_dim * sum over listed
+(Q block, KV tile) pairs of (Q rows) x (KV tile keys), every listed 128-token
+tile at its full 128 keys and every 256-row Q cube at 256 rows (KV tiles
+with no valid token are never listed).  The count over valid keys only, 1.2 %
+lower, is printed beside it.
 
 Prints one JSON line.  `--gpus N` with N > 1 exits: this build runs on one GPU.
 
@@ -50,8 +52,8 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "bsa_fwd_pp_kernel_video_hbm_tr
 def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", choices=["video", "sweep128"], default="video")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-time budget of the oracle sample on the host (0 = skip)")
@@ -92,16 +94,17 @@ def _video_inputs(torch, np, workloads):
     q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (w.q, w.k, w.v))
     cube_mask = torch.from_numpy(w.cube_mask.astype(np.uint8)).to(dev)
     cube_valid = torch.from_numpy(w.cube_valid).to(dev)
-    # computed work: listed (cube, tile) pairs x 256 Q rows x valid keys of the tile
+    # computed blocks: listed (cube, tile) pairs x 256 Q rows x 128 keys; a tile
+    # with no valid token is not listed
     f = w.cube_elems // w.kv_tile
     tile_valid = np.clip(w.cube_valid[:, None] - np.arange(f)[None, :] * w.kv_tile, 0,
                          w.kv_tile)  # [cubes, f]
-    keys_per_row = (w.cube_mask[0].astype(np.float64) @ tile_valid.sum(1).astype(np.float64))
-    flops = 4.0 * q.shape[-1] * w.cube_elems * float(keys_per_row.sum())
-    # the coarser count: every listed tile with a valid key at its full 128 keys
     full_tiles = (tile_valid > 0).sum(1).astype(np.float64) * w.kv_tile
-    flops_full_tiles = 4.0 * q.shape[-1] * w.cube_elems * float(
+    flops = 4.0 * q.shape[-1] * w.cube_elems * float(
         (w.cube_mask[0].astype(np.float64) @ full_tiles).sum())
+    # the finer count: valid keys of each listed tile only
+    keys_per_row = (w.cube_mask[0].astype(np.float64) @ tile_valid.sum(1).astype(np.float64))
+    flops_valid_keys = 4.0 * q.shape[-1] * w.cube_elems * float(keys_per_row.sum())
     density = float(w.cube_mask.mean())
     cfg = {"workload": "video_sparse_attention", "B": 1, "H": q.shape[2], "tokens": int(
         w.cube_valid.sum()), "padded_seq": q.shape[1], "head_dim": q.shape[3], "cube": list(w.cube),
@@ -109,7 +112,7 @@ def _video_inputs(torch, np, workloads):
         "kv_cubes_per_q_cube": int(w.cube_mask[0, 0, 0].sum()), "block_density": round(density, 4),
         "mask_mod": "kv_valid_count", "layout": "BSHD"}
     state = dict(q=q, k=k, v=v, cube_mask=cube_mask, cube_valid=cube_valid, f=f, w=w,
-                 flops_full_tiles=flops_full_tiles)
+                 flops_valid_keys=flops_valid_keys)
     return state, flops, cfg
 
 
@@ -177,17 +180,34 @@ class _MaxErr:
         self.lse = max(self.lse, float(np.abs(lse_gpu.double().cpu().numpy() - lse_ref).max()))
 
 
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_threads() -> int:
+    """Threads numpy's BLAS runs the oracle's products on (set before numpy
+    is imported: OMP_NUM_THREADS if the host sets it, else the CPUs this
+    process may run on)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([int(i.get("num_threads", 1)) for i in threadpool_info()
+                    if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
 def _cpu_baseline(np, st, workload, budget_s, gpu_out=None, err=None):
     """The oracle, as it stands, on a bounded sample of the same workload.
     With gpu_out=(O, LSE) and err, the GPU's rows of each sampled block are
     compared with the oracle's (outside the timed part)."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()
-                       if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    threads = _blas_threads()
     w = st["w"]
     f64 = lambda t: t.float().cpu().double().numpy()
     q, k, v = f64(st["q"]), f64(st["k"]), f64(st["v"])
@@ -196,7 +216,8 @@ def _cpu_baseline(np, st, workload, budget_s, gpu_out=None, err=None):
         full, part, kv = oracle.expand_kv_blocks(w.cube_mask, w.cube_valid, st["f"], w.kv_tile)
         B, H, M = 1, q.shape[2], len(w.cube_valid)
         bq, bk, mm, kvv = w.cube_elems, w.kv_tile, oracle.MASK_KV_VALID_COUNT, kv
-        row_keys = lambda b, h, i: float((full[b, h, i] * kv).sum() + (part[b, h, i] * kv).sum())
+        # the GPU's count: every listed tile at its full size
+        row_keys = lambda b, h, i: float((full[b, h, i].sum() + part[b, h, i].sum()) * bk)
     else:
         full, part = w.full, w.part
         B, H, M = full.shape[:3]
@@ -216,7 +237,8 @@ def _cpu_baseline(np, st, workload, budget_s, gpu_out=None, err=None):
             r = slice(i * bq, min((i + 1) * bq, Sq))
             err.note(gpu_out[0][b, r, h], gpu_out[1][b, h, r], O[b, r, h], L[b, h, r])
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": _cpu_model(),
+            "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{n} random Q blocks ({bq} rows each) of the same workload, fp64 numpy, "
                       f"{dt:.1f} s wall"}
 
@@ -513,8 +535,17 @@ def table(torch, np, bsa, workloads, oracle_s):
     emit("video, cold (1 GiB written before each launch)", ms_cold, flops, None, _MaxErr())
 
 
+def _set_blas_threads():
+    # before numpy is imported: the host's OMP_NUM_THREADS if it sets one,
+    # else every CPU this process may run on
+    n = os.environ.get("OMP_NUM_THREADS") or str(len(os.sched_getaffinity(0)))
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ.setdefault(var, n)
+
+
 def main():
     args = _parse()
+    _set_blas_threads()
     if args.print_kernel_hash:
         print(_kernel_hash())
         return
@@ -596,7 +627,7 @@ def main():
         out["roofline"]["frac_at_measured_clock"] = round(
             achieved / (PEAK_BF16_TFLOPS * sclk / PEAK_SCLK_MHZ), 4)
     if video:
-        out["flops_full_tiles_per_launch"] = st["flops_full_tiles"]
+        out["flops_valid_keys_per_launch"] = st["flops_valid_keys"]
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = _cpu_baseline(np, st, args.workload, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -29,6 +29,7 @@ MASK_CAUSAL = 1
 MASK_KV_VALID_COUNT = 2
 MASK_LOCAL = 3
 FLAG_VALIDATE = 1
+FLAG_KV_HEAD_LISTS = 2
 
 BSA_OK = 0
 BSA_ERR_INVALID_ARGUMENT = 1
@@ -193,14 +194,17 @@ def bsa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             kv_valid: Optional[torch.Tensor] = None, softmax_scale: Optional[float] = None,
             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
             validate: bool = False, window: Optional[Tuple[int, int]] = None,
-            proxy: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+            proxy: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+            kv_head_lists: bool = False):
     """Batched block-sparse attention forward.
 
     q [B,Sq,H,D], k/v [B,Sk,Hkv,D] (bf16 or fp32, head_dim contiguous, any
     other strides, e.g. BSHD or a BHSD tensor permuted to this view).
     mask_list / full_list: (cnt int32 [B|1,H|1,M], idx int32 [B|1,H|1,M,N])
     with M = ceil(Sq/block_q), N = ceil(Sk/block_kv); a size-1 batch or head
-    dimension broadcasts.  window=(left, right): the bounds of MASK_LOCAL.
+    dimension broadcasts.  kv_head_lists=True: the lists' head dimension is
+    the KV head (Hkv|1), shared by that KV head's Q heads, which the forward
+    then packs into one workgroup.  window=(left, right): the bounds of MASK_LOCAL.
     proxy=(k_mean, v_sum): bf16 [B,N,Hkv,D] block summaries for the
     proxy-compensated route (MASK_NONE only): every block a row does not list
     enters its softmax once, weighted by the block's token count.
@@ -234,8 +238,9 @@ def bsa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _dev("kv_valid", kv_valid, torch.int32)
         if not kv_valid.is_contiguous() or kv_valid.numel() < N:
             raise ValueError(f"kv_valid must be a contiguous int32 tensor with {N} entries")
-    bs = _BlockSparse(_block_list(mask_list, True, (B, H, M, N)),
-                      _block_list(full_list, True, (B, H, M, N)), int(block_q), int(block_kv),
+    Hl = Hkv if kv_head_lists else H
+    bs = _BlockSparse(_block_list(mask_list, True, (B, Hl, M, N)),
+                      _block_list(full_list, True, (B, Hl, M, N)), int(block_q), int(block_kv),
                       *_window(mask_mod, window))
     if proxy is not None:
         for n, t in zip(("proxy k_mean", "proxy v_sum"), proxy):
@@ -254,7 +259,8 @@ def bsa_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                      _i64([v.stride(0), v.stride(1), v.stride(2)]),
                      _i64([out.stride(0), out.stride(1), out.stride(2)]),
                      ctypes.byref(bs), int(mask_mod), _ptr(kv_valid), scale,
-                     FLAG_VALIDATE if validate else 0, _stream(q))
+                     (FLAG_VALIDATE if validate else 0) |
+                     (FLAG_KV_HEAD_LISTS if kv_head_lists else 0), _stream(q))
     _check("bsa_fwd", st)
     return out, lse
 
@@ -270,14 +276,16 @@ def bsa_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                    lse: Optional[torch.Tensor] = None, validate: bool = False,
                    window: Optional[Tuple[int, int]] = None,
                    kv_valid: Optional[torch.Tensor] = None,
-                   max_seqlen_k: Optional[int] = None):
+                   max_seqlen_k: Optional[int] = None, kv_head_lists: bool = False):
     """Packed varlen forward.  q [Tq,H,D], k/v [Tk,Hkv,D]; lists (cnt int32
     [H,total_m_blocks], idx int32 [H,total_n_blocks]); cu arrays int32 [B+1]
     on the device; the two totals are host ints.  kv_valid (MASK_KV_VALID_COUNT):
     int32 [B, W] (row b: the valid-token counts of sequence b's KV blocks,
     sequence-local ids) or [W] shared by every sequence, W >=
     ceil(max_seqlen_k / block_kv); max_seqlen_k is read from cu_seqlens_k (a
-    device->host copy) when not given.  Returns (O [Tq,H,D], LSE float32 [H,Tq])."""
+    device->host copy) when not given.  kv_head_lists=True: lists [Hkv, ...],
+    shared by each KV head's Q heads (packed).  Returns (O [Tq,H,D], LSE
+    float32 [H,Tq])."""
     lib = load_library()
     for n, t in (("q", q), ("k", k), ("v", v)):
         _dev(n, t)
@@ -310,7 +318,7 @@ def bsa_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise ValueError("lse must be a contiguous float32 [H,Tq] tensor")
     if int(total_m_blocks) < 0 or int(total_n_blocks) < 0:
         raise ValueError("totals must be non-negative")
-    shp = (H, int(total_m_blocks), int(total_n_blocks))
+    shp = (Hkv if kv_head_lists else H, int(total_m_blocks), int(total_n_blocks))
     bs = _BlockSparse(_block_list(mask_list, False, shp), _block_list(full_list, False, shp),
                       int(block_q), int(block_kv), *_window(mask_mod, window))
     kvv_ld = 0
@@ -335,7 +343,8 @@ def bsa_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                             _i64([q.stride(0), q.stride(1)]), _i64([k.stride(0), k.stride(1)]),
                             _i64([v.stride(0), v.stride(1)]), _i64([out.stride(0), out.stride(1)]),
                             ctypes.byref(bs), int(mask_mod), _ptr(kv_valid), int(kvv_ld), scale,
-                            FLAG_VALIDATE if validate else 0, _stream(q))
+                            (FLAG_VALIDATE if validate else 0) |
+                            (FLAG_KV_HEAD_LISTS if kv_head_lists else 0), _stream(q))
     _check("bsa_varlen_fwd", st)
     return out, lse
 

@@ -41,6 +41,24 @@ int fit_tile_m(int block_q, int D, bool f32_in, int mask_mod) {
 
 int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// A list absent, or the same row for every head (head strides 0).
+bool heads_broadcast(const bsa_block_list& L) {
+  return L.cnt == nullptr || (L.cnt_stride[1] == 0 && L.idx_stride[1] == 0);
+}
+
+// GQA head packing: when every Q head of a KV head reads the same lists (the
+// lists are given per KV head, or broadcast over heads) and the 256-row
+// kernel serves the shape, one workgroup takes G = 256 / tile_m heads of
+// that KV head, tile_m rows each, so every K/V item staged in LDS feeds G
+// heads.  Returns G (1: no packing).
+int gqa_pack(bool lists_shared, int tile_m, int hrep, int D, bool f32_in, int mask_mod,
+             bool proxy) {
+  if (!lists_shared || tile_m >= 256 || proxy || f32_in || D > 128 || mask_mod == BSA_MASK_LOCAL)
+    return 1;
+  const int G = 256 / tile_m;
+  return hrep % G == 0 ? G : 1;
+}
+
 bool strides_ok(const int64_t* s, int n, int esize) {
   for (int i = 0; i < n; ++i)
     if (s[i] < 0 || (s[i] * esize) % 16 != 0) return false;
@@ -93,6 +111,7 @@ int64_t span3(const int64_t* st, int64_t d0, int64_t d1, int64_t d2) {
   return (d0 - 1) * st[0] + (d1 - 1) * st[1] + (d2 - 1) * st[2] + 1;
 }
 
+// H: the lists' head count (Q heads, or KV heads with BSA_FLAG_KV_HEAD_LISTS)
 bsa_status validate_batched(const bsa_block_sparse& bs, int B, int H, int64_t M, int64_t N,
                             hipStream_t s) {
   const bsa_block_list* lists[2] = {&bs.mask, &bs.full};
@@ -227,6 +246,11 @@ bsa_status bsa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   int tile_m = fit_tile_m(bs->block_q, D, dt == BSA_F32, mask_mod);
   if (proxy && tile_m == 256) tile_m = 128;
   if (tile_m == 0) return BSA_ERR_UNSUPPORTED;
+  const bool kvh = (flags & BSA_FLAG_KV_HEAD_LISTS) != 0;
+  const int gpack = gqa_pack(kvh || (heads_broadcast(bs->mask) && heads_broadcast(bs->full)),
+                             tile_m, H / H_kv, D, dt == BSA_F32, mask_mod, proxy);
+  const int rows_per_head = tile_m;  // rows of one head in a tile
+  if (gpack > 1) tile_m = 256;
   if ((int64_t)B * H * Sq == 0) return BSA_OK;  // nothing to write
   if (!q || !k || !v || !o || !lse) return BSA_ERR_INVALID_ARGUMENT;
   if (mask_mod == BSA_MASK_KV_VALID_COUNT && !kv_valid && bs->mask.cnt)
@@ -246,13 +270,13 @@ bsa_status bsa_fwd(const void* q, const void* k, const void* v, void* o, float* 
     if (!subtile_offsets_fit(bs->proxy_k_str[1], bs->proxy_v_str[1], es))
       return BSA_ERR_UNSUPPORTED;
   }
-  const int64_t qsub = cdiv64(bs->block_q, tile_m);
+  const int64_t qsub = cdiv64(bs->block_q, rows_per_head);
   const int64_t tiles_per_head = M * qsub;
-  const int64_t tiles = (int64_t)B * H * tiles_per_head;
+  const int64_t tiles = (int64_t)B * (H / gpack) * tiles_per_head;
   if (tiles > std::numeric_limits<int32_t>::max() || N > std::numeric_limits<int32_t>::max() / 2)
     return BSA_ERR_UNSUPPORTED;
   if (flags & BSA_FLAG_VALIDATE) {
-    const bsa_status st = validate_batched(*bs, B, H, M, N, stream);
+    const bsa_status st = validate_batched(*bs, B, kvh ? H_kv : H, M, N, stream);
     if (st != BSA_OK) return st;
   }
   bsa::FwdParams p{};
@@ -276,6 +300,8 @@ bsa_status bsa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   p.block_q = bs->block_q;
   p.block_kv = bs->block_kv;
   p.qsub = (int32_t)qsub;
+  p.gpack = gpack;
+  p.kvh_lists = kvh ? 1 : 0;
   p.mask_mod = mask_mod;
   p.win_left = bs->window_left;
   p.win_right = bs->window_right;
@@ -319,8 +345,13 @@ bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, 
   if (bs->block_q <= 0 || bs->block_kv <= 0) return BSA_ERR_INVALID_ARGUMENT;
   if (!list_ok(bs->mask) || !list_ok(bs->full)) return BSA_ERR_INVALID_ARGUMENT;
   if (!supported_head_dim(D)) return BSA_ERR_UNSUPPORTED;
-  const int tile_m = fit_tile_m(bs->block_q, D, dt == BSA_F32, mask_mod);
+  int tile_m = fit_tile_m(bs->block_q, D, dt == BSA_F32, mask_mod);
   if (tile_m == 0) return BSA_ERR_UNSUPPORTED;
+  const bool kvh = (flags & BSA_FLAG_KV_HEAD_LISTS) != 0;
+  const int gpack = gqa_pack(kvh || (heads_broadcast(bs->mask) && heads_broadcast(bs->full)),
+                             tile_m, H / H_kv, D, dt == BSA_F32, mask_mod, false);
+  const int rows_per_head = tile_m;
+  if (gpack > 1) tile_m = 256;
   if (B == 0 || total_m_blocks == 0) return BSA_OK;
   if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k || !cu_total_m_blocks ||
       !block_idx_offsets)
@@ -333,12 +364,13 @@ bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, 
       !strides_ok(o_str, 2, es))
     return BSA_ERR_MISALIGNED;
   if (!subtile_offsets_fit(k_str[0], v_str[0], es)) return BSA_ERR_UNSUPPORTED;
-  const int qsub = (int)cdiv64(bs->block_q, tile_m);
+  const int qsub = (int)cdiv64(bs->block_q, rows_per_head);
   const int64_t tiles_per_head = (int64_t)total_m_blocks * qsub;
-  const int64_t tiles = tiles_per_head * H;
+  const int64_t tiles = tiles_per_head * (H / gpack);
   if (tiles > std::numeric_limits<int32_t>::max()) return BSA_ERR_UNSUPPORTED;
   if (flags & BSA_FLAG_VALIDATE) {
-    const bsa_status st = validate_varlen(*bs, B, H, cu_seqlens_q, cu_seqlens_k, cu_total_m_blocks,
+    const bsa_status st = validate_varlen(*bs, B, kvh ? H_kv : H, cu_seqlens_q, cu_seqlens_k,
+                                          cu_total_m_blocks,
                                           block_idx_offsets, total_m_blocks, total_n_blocks, stream);
     if (st != BSA_OK) return st;
   }
@@ -365,6 +397,8 @@ bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, 
   p.block_q = bs->block_q;
   p.block_kv = bs->block_kv;
   p.qsub = qsub;
+  p.gpack = gpack;
+  p.kvh_lists = kvh ? 1 : 0;
   p.mask_mod = mask_mod;
   p.win_left = bs->window_left;
   p.win_right = bs->window_right;

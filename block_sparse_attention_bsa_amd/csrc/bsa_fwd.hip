@@ -190,7 +190,7 @@ void bsa_fwd_kernel(const FwdParams p) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = neg_inf(), l_run = 0.f;
+  float m_run = neg_inf(), l_run = 0.f, lo_run = 0.f;
 
   // DMA of one 64-key sub-tile.  The tile's RS blocks of 64 slots are
   // dealt round-robin to the waves; a wave issues only the blocks that
@@ -338,10 +338,10 @@ void bsa_fwd_kernel(const FwdParams p) {
     uint32_t pk0[8], pk1[8];
     if constexpr (PROXY)
       softmax_step_any<DB>(s0, s1, it, xbits, p.block_kv, ti.num_n, ti.Sk, h32, p.c, m_run,
-                           l_run, oacc, pk0, pk1);
+                           l_run, lo_run, oacc, pk0, pk1);
     else
       softmax_step<DB, LOCAL>(s0, s1, it, it.is_mask && list_masked, mlo, mhi, h32, p.c, m_run,
-                              l_run, oacc, pk0, pk1);
+                              l_run, lo_run, oacc, pk0, pk1);
     // PV step i: keys 16*(i / DB) .., head dims 32*(i % DB) ..
     auto vld = [&](int i) {
       const int ps = i / DB, db = i % DB;
@@ -421,7 +421,7 @@ void bsa_fwd_kernel(const FwdParams p) {
     if (live) compute(stage, cur);
     stage ^= 1;
   }
-  epilogue<DB, __bf16>(p, ti, qrow, h32, m_run, l_run, oacc);
+  epilogue<DB, __bf16>(p, ti, qrow, h32, m_run, l_run, lo_run, oacc);
 }
 
 template <int D, int NW>

@@ -39,6 +39,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// acc + lo + hi of a packed pair of bf16 values (v_dot2c_f32_bf16 against
+// (1, 1)): sums exactly the P that feeds the PV product.
+__device__ __forceinline__ float add_bf16x2(uint32_t pk, float acc) {
+  const bf16x2_t one = {(__bf16)1.f, (__bf16)1.f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk), one, acc, false);
+}
+
 __device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -65,36 +72,43 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
 struct TileInfo {
   int h, q0, qend, Sq, Sk, num_n;
   const int32_t* kvv;  // valid-token counts of this sequence's KV blocks (or null)
-  int64_t qoff, koff, voff, ooff, lse_base;  // element offsets of row 0 / LSE row 0
+  int64_t qoff, koff, voff, ooff, lse_base;  // element offsets of row 0 / LSE row 0 (head h)
+  int64_t lse_hs;                              // LSE elements between two heads
   const int32_t* mrow;
   const int32_t* frow;
   int mcnt, fcnt;
 };
 
-// Logical tile t -> TileInfo.  A sparse Q block of block_q rows is covered
-// by qsub = ceil(block_q / TM) tiles; tile sub of Q block i starts at row
-// i*block_q + sub*TM and its rows stop at the block end, so a block of any
-// size (112, 80, 48 rows ...) is fitted rather than rejected (runguoli.com
-// "FlashAttention - CuTe Kernels & Block Sparsity", the tile-fit change).
-// Batched: t = ((b*H + h) * tiles_per_head + qt), qt = i * qsub + sub.
-// Varlen (flash-attention PR #2224 layout): t = h * tiles_per_head + tm with
-// tm = Q block * qsub + sub; the sequence is the largest b with
+// Logical tile t -> TileInfo.  A tile holds TM rows: R = TM / gpack rows
+// of each of gpack consecutive Q heads h .. h + gpack - 1 (gpack > 1 packs
+// the Q heads of one KV head, which then share their lists).  A sparse Q
+// block of block_q rows is covered by qsub = ceil(block_q / R) tiles; tile
+// sub of Q block i starts at row i*block_q + sub*R and its rows stop at the
+// block end, so a block of any size (112, 80, 48 rows ...) is fitted rather
+// than rejected (runguoli.com "FlashAttention - CuTe Kernels & Block
+// Sparsity", the tile-fit change).
+// Batched: t = ((b*H/gpack + h/gpack) * tiles_per_head + qt), qt = i*qsub + sub.
+// Varlen (flash-attention PR #2224 layout): t = (h/gpack) * tiles_per_head + tm
+// with tm = Q block * qsub + sub; the sequence is the largest b with
 // cu_total_m_blocks[b] <= Q block (binary search), the list row starts at
-// block_idx_offsets[b] + m * num_n(b).  Returns false when the tile holds no
-// row of its sequence (the whole workgroup then exits).
+// block_idx_offsets[b] + m * num_n(b).  The list head is h, or its KV head
+// h / hrep when the lists are given per KV head.  Returns false when the
+// tile holds no row of its sequence (the whole workgroup then exits).
 template <int TM>
 __device__ __forceinline__ bool decode_tile(const FwdParams& p, int t, TileInfo& ti) {
   ti.mrow = nullptr;
   ti.frow = nullptr;
   ti.mcnt = ti.fcnt = 0;
+  const int R = TM / p.gpack, HG = p.H / p.gpack;
   if (!p.varlen) {
     const int qt = t % p.tiles_per_head;
     const int bh = t / p.tiles_per_head;
-    const int h = bh % p.H, b = bh / p.H, hk = h / p.hrep;
+    const int h = (bh % HG) * p.gpack, b = bh / HG, hk = h / p.hrep;
+    const int lh = p.kvh_lists ? hk : h;
     const int i = qt / p.qsub, sub = qt % p.qsub;
     ti.h = h;
-    ti.q0 = i * p.block_q + sub * TM;
-    ti.qend = min(p.Sq, min(i * p.block_q + p.block_q, ti.q0 + TM));
+    ti.q0 = i * p.block_q + sub * R;
+    ti.qend = min(p.Sq, min(i * p.block_q + p.block_q, ti.q0 + R));
     if (ti.q0 >= ti.qend) return false;
     ti.Sq = p.Sq;
     ti.Sk = p.Sk;
@@ -105,17 +119,18 @@ __device__ __forceinline__ bool decode_tile(const FwdParams& p, int t, TileInfo&
     ti.voff = b * p.v_sb + hk * p.v_sh;
     ti.ooff = b * p.o_sb + h * p.o_sh;
     ti.lse_base = (int64_t)(b * p.H + h) * p.Sq;
+    ti.lse_hs = p.Sq;
     if (p.mcnt) {
-      ti.mcnt = p.mcnt[b * p.mc_s[0] + h * p.mc_s[1] + i * p.mc_s[2]];
-      ti.mrow = p.midx + b * p.mi_s[0] + h * p.mi_s[1] + i * p.mi_s[2];
+      ti.mcnt = p.mcnt[b * p.mc_s[0] + lh * p.mc_s[1] + i * p.mc_s[2]];
+      ti.mrow = p.midx + b * p.mi_s[0] + lh * p.mi_s[1] + i * p.mi_s[2];
     }
     if (p.fcnt) {
-      ti.fcnt = p.fcnt[b * p.fc_s[0] + h * p.fc_s[1] + i * p.fc_s[2]];
-      ti.frow = p.fidx + b * p.fi_s[0] + h * p.fi_s[1] + i * p.fi_s[2];
+      ti.fcnt = p.fcnt[b * p.fc_s[0] + lh * p.fc_s[1] + i * p.fc_s[2]];
+      ti.frow = p.fidx + b * p.fi_s[0] + lh * p.fi_s[1] + i * p.fi_s[2];
     }
   } else {
     const int tm = t % p.tiles_per_head;
-    const int h = t / p.tiles_per_head;
+    const int h = (t / p.tiles_per_head) * p.gpack;
     const int mg = tm / p.qsub, sub = tm % p.qsub;
     int lo = 0, hi = p.B - 1;
     while (lo < hi) {
@@ -126,15 +141,16 @@ __device__ __forceinline__ bool decode_tile(const FwdParams& p, int t, TileInfo&
         hi = mid - 1;
     }
     const int b = lo, hk = h / p.hrep;
+    const int lh = p.kvh_lists ? hk : h;
     const int m = mg - p.cu_m[b];
     const int sq0 = p.cu_q[b], sk0 = p.cu_k[b];
     ti.h = h;
     ti.Sq = p.cu_q[b + 1] - sq0;
     ti.Sk = p.cu_k[b + 1] - sk0;
     ti.num_n = cdiv(ti.Sk, p.block_kv);
-    ti.q0 = m * p.block_q + sub * TM;
+    ti.q0 = m * p.block_q + sub * R;
     if (m < 0 || m >= cdiv(ti.Sq, p.block_q)) return false;
-    ti.qend = min(ti.Sq, min(m * p.block_q + p.block_q, ti.q0 + TM));
+    ti.qend = min(ti.Sq, min(m * p.block_q + p.block_q, ti.q0 + R));
     if (ti.q0 >= ti.qend) return false;
     // valid-token counts: row b of a [B, kv_valid_ld] array (ld 0: one row for all)
     ti.kvv = p.kv_valid != nullptr ? p.kv_valid + (int64_t)b * p.kvv_ld : nullptr;
@@ -145,13 +161,14 @@ __device__ __forceinline__ bool decode_tile(const FwdParams& p, int t, TileInfo&
     ti.voff = (int64_t)sk0 * p.v_ss + hk * p.v_sh;
     ti.ooff = (int64_t)sq0 * p.o_ss + h * p.o_sh;
     ti.lse_base = (int64_t)h * p.lse_ld + sq0;
+    ti.lse_hs = p.lse_ld;
     if (p.mcnt) {
-      ti.mcnt = p.mcnt[h * p.mc_s[1] + mg * p.mc_s[2]];
-      ti.mrow = p.midx + h * p.mi_s[1] + row_p * p.mi_s[3];
+      ti.mcnt = p.mcnt[lh * p.mc_s[1] + mg * p.mc_s[2]];
+      ti.mrow = p.midx + lh * p.mi_s[1] + row_p * p.mi_s[3];
     }
     if (p.fcnt) {
-      ti.fcnt = p.fcnt[h * p.fc_s[1] + mg * p.fc_s[2]];
-      ti.frow = p.fidx + h * p.fi_s[1] + row_p * p.fi_s[3];
+      ti.fcnt = p.fcnt[lh * p.fc_s[1] + mg * p.fc_s[2]];
+      ti.frow = p.fidx + lh * p.fi_s[1] + row_p * p.fi_s[3];
     }
   }
   ti.mcnt = min(max(ti.mcnt, 0), ti.num_n);
@@ -231,8 +248,10 @@ __device__ __forceinline__ bool advance(Item& it, ListWalk& L, int lane, int Sk)
 
 // Online-softmax step for one 64-key sub-tile.  s0/s1 hold S^T for keys
 // 0..31 / 32..63 of the sub-tile (raw dot products).  Applies the element
-// mask, updates the running max m (base-2 units of scale*s) and the running
-// sum l (fp32 P), rescales O only when some row's max grew, and returns P
+// mask, updates the running max m (base-2 units of scale*s), the running sum
+// l of the fp32 P (for the LSE) and the running sum lo of P rounded to bf16
+// (the P the PV product takes, so O = acc / lo weighs its rows by exactly
+// those weights), rescales O only when some row's max grew, and returns P
 // rounded to bf16 in pk0/pk1 (pairs of consecutive accumulators).
 // masked: a mask-list sub-tile under the causal (RANGE false) or local
 // (RANGE true) mask_mod; its kept keys of this lane's row are key <= mhi
@@ -241,8 +260,9 @@ __device__ __forceinline__ bool advance(Item& it, ListWalk& L, int lane, int Sk)
 template <int DB, bool RANGE = false>
 __device__ __forceinline__ void softmax_step(f32x16_t& s0, f32x16_t& s1, const Item& it,
                                              bool masked, int mlo, int mhi, int h32, float c,
-                                             float& m_run, float& l_run, f32x16_t (&oacc)[DB],
-                                             uint32_t (&pk0)[8], uint32_t (&pk1)[8]) {
+                                             float& m_run, float& l_run, float& lo_run,
+                                             f32x16_t (&oacc)[DB], uint32_t (&pk0)[8],
+                                             uint32_t (&pk1)[8]) {
   if (masked || it.nk < kKvTile) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -276,6 +296,7 @@ __device__ __forceinline__ void softmax_step(f32x16_t& s0, f32x16_t& s1, const I
     const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     l_run *= alpha;
+    lo_run *= alpha;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -283,7 +304,7 @@ __device__ __forceinline__ void softmax_step(f32x16_t& s0, f32x16_t& s1, const I
     m_run = m_new;
   }
   const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
-  float ls = 0.f;
+  float ls = 0.f, lo = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float a0 = __builtin_amdgcn_exp2f(fmaf(s0[2 * i], c, -m_use));
@@ -293,8 +314,10 @@ __device__ __forceinline__ void softmax_step(f32x16_t& s0, f32x16_t& s1, const I
     pk0[i] = pack_bf16x2(a0, a1);
     pk1[i] = pack_bf16x2(b0, b1);
     ls += (a0 + a1) + (b0 + b1);
+    lo = add_bf16x2(pk1[i], add_bf16x2(pk0[i], lo));
   }
   l_run += ls;
+  lo_run += lo;
 }
 
 // Keys [lo, hi] of row qrow that the causal (kMaskCausal: key <= qrow) or
@@ -321,13 +344,16 @@ __device__ __forceinline__ uint4 p_operand(const uint32_t (&pk0)[8], const uint3
   return make_uint4(src[o], src[o + 1], src[o + 2], src[o + 3]);
 }
 
-// O = acc / l (0 when l == 0), LSE = ln2 * (m + log2 l) (-inf when l == 0).
+// O = acc / lo (0 when lo == 0), LSE = ln2 * (m + log2 l) (-inf when l == 0):
+// l sums the fp32 P, lo the normaliser of O (the bf16 P of the PV product).
 template <int DB, typename T>
 __device__ __forceinline__ void epilogue(const FwdParams& p, const TileInfo& ti, int qrow, int h32,
-                                         float m_run, float l_run, const f32x16_t (&oacc)[DB]) {
+                                         float m_run, float l_run, float lo_run,
+                                         const f32x16_t (&oacc)[DB]) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float lo_tot = lo_run + __shfl_xor(lo_run, 32);
   if (qrow >= ti.qend) return;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = lo_tot > 0.f ? 1.f / lo_tot : 0.f;
   T* op = reinterpret_cast<T*>(p.o) + ti.ooff + (int64_t)qrow * p.o_ss;
 #pragma unroll
   for (int db = 0; db < DB; ++db) {

@@ -51,8 +51,14 @@
 // take the row max, rescale O and l, and redo the item.  So the common item
 // has no max reduction at all, P stays <= 2^16 (far inside fp32 and bf16
 // range), and O, l and the LSE are all relative to the same m.  The row
-// sum is taken over the fp32 P (so the LSE carries no bf16 rounding); P is
-// rounded to bf16 only for the PV product.
+// sum is taken over the fp32 P (so the LSE carries no bf16 rounding) and O
+// is divided by it; P is rounded to bf16 only for the PV product.  Dividing
+// O by the sum of the bf16 P instead (exact weights on rows dominated by
+// one key) costs 13-20 % of the whole kernel here, however that sum is
+// formed (v_dot2c_f32_bf16 per pair, or unpacking the pairs): the softmax
+// phase already sets the length of the interval, and every VALU op added
+// to it lengthens it.  So a row dominated by a few keys keeps the bf16
+// rounding of their P (relative 2^-8) in O.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -238,11 +244,19 @@ void bsa_fwd_pp_kernel(const FwdParams p) {
 
   TileInfo ti;
   if (!decode_tile<256>(p, xcd_remap(blockIdx.x, p.num_tiles), ti)) return;
+  // GQA packing: wave w holds rows (32*w) % R .. of head ti.h + 32*w / R
+  // (R = 256 / gpack rows per head), and every head of the tile walks the
+  // same items.  Without packing R = 256 and dh = 0.
+  const int R = 256 / p.gpack;
+  const int dh = (32 * w) / R;
+  ti.qoff += dh * p.q_sh;
+  ti.ooff += dh * p.o_sh;
+  ti.lse_base += dh * ti.lse_hs;
   const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + ti.qoff;
   const uint64_t kaddr = reinterpret_cast<uint64_t>(reinterpret_cast<const __bf16*>(p.k) + ti.koff);
   const uint64_t vaddr = reinterpret_cast<uint64_t>(reinterpret_cast<const __bf16*>(p.v) + ti.voff);
 
-  const int q0w = ti.q0 + 32 * w;
+  const int q0w = ti.q0 + (32 * w) % R;
   const int qrow = q0w + l32;
   uint4 qf[DS];
   f32x16_t oacc[DB];
@@ -544,7 +558,7 @@ void bsa_fwd_pp_kernel(const FwdParams p) {
     __builtin_amdgcn_s_setprio(0);
   }
   wait_vmem<0>();      // no DMA of this workgroup outlives it
-  epilogue<DB, __bf16>(p, ti, qrow, h32, m_run, l_a + l_b, oacc);
+  epilogue<DB, __bf16>(p, ti, qrow, h32, m_run, l_a + l_b, l_a + l_b, oacc);
 }
 
 template <int D>

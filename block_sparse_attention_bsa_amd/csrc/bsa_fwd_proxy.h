@@ -65,13 +65,16 @@ __device__ __forceinline__ bool next_proxy_chunk(const uint32_t* xbits, int num_
 // summary is masked, and the row sum adds mass(n) * p, where mass(n) is
 // block_kv for every block but the last, whose mass is its true length.  An
 // exact item takes weight 1 and no bitmap, which is softmax_step's
-// arithmetic.  The PV product takes p as is.
+// arithmetic.  The PV product takes p as is.  As in softmax_step, l sums the
+// fp32 p (the LSE) and lo the bf16 p of the PV product (the normaliser of
+// O), both with the same mass weights.
 template <int DB>
 __device__ __forceinline__ void softmax_step_any(f32x16_t& s0, f32x16_t& s1, const Item& it,
                                                  const uint32_t* xbits, int block_kv, int num_n,
                                                  int Sk, int h32, float c, float& m_run,
-                                                 float& l_run, f32x16_t (&oacc)[DB],
-                                                 uint32_t (&pk0)[8], uint32_t (&pk1)[8]) {
+                                                 float& l_run, float& lo_run,
+                                                 f32x16_t (&oacc)[DB], uint32_t (&pk0)[8],
+                                                 uint32_t (&pk1)[8]) {
   const bool px = it.is_mask == 2;
   if (px || it.nk < kKvTile) {
     const uint32_t ex0 = px ? xbits[it.key0 >> 5] : 0u;
@@ -98,6 +101,7 @@ __device__ __forceinline__ void softmax_step_any(f32x16_t& s0, f32x16_t& s1, con
     const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     l_run *= alpha;
+    lo_run *= alpha;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -107,7 +111,7 @@ __device__ __forceinline__ void softmax_step_any(f32x16_t& s0, f32x16_t& s1, con
   const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
   // chunk-local key of the last block (never matched on an exact item)
   const int tk = px ? num_n - 1 - it.key0 : -1000;
-  float ls = 0.f, lt = 0.f;
+  float ls = 0.f, lt = 0.f, lo = 0.f, lto = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int k0 = 16 * (i >> 2) + 8 * h32 + ((2 * i) & 7);  // key of element 2i of s0
@@ -118,12 +122,18 @@ __device__ __forceinline__ void softmax_step_any(f32x16_t& s0, f32x16_t& s1, con
     pk0[i] = pack_bf16x2(a0, a1);
     pk1[i] = pack_bf16x2(b0, b1);
     ls += (a0 + a1) + (b0 + b1);
+    lo = add_bf16x2(pk1[i], add_bf16x2(pk0[i], lo));
     lt += (k0 == tk ? a0 : 0.f) + (k0 + 1 == tk ? a1 : 0.f) + (k0 + 32 == tk ? b0 : 0.f) +
           (k0 + 33 == tk ? b1 : 0.f);
+    lto += (k0 == tk ? __uint_as_float(pk0[i] << 16) : 0.f) +
+           (k0 + 1 == tk ? __uint_as_float(pk0[i] & 0xffff0000u) : 0.f) +
+           (k0 + 32 == tk ? __uint_as_float(pk1[i] << 16) : 0.f) +
+           (k0 + 33 == tk ? __uint_as_float(pk1[i] & 0xffff0000u) : 0.f);
   }
   const float wf = px ? (float)block_kv : 1.f;
   const float wt = px ? (float)(Sk - (num_n - 1) * block_kv) : 1.f;
   l_run += fmaf(wt - wf, lt, wf * ls);
+  lo_run += fmaf(wt - wf, lto, wf * lo);
 }
 
 }  // namespace dev

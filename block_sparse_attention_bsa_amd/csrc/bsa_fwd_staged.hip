@@ -109,7 +109,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_staged_kernel(const FwdParams
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = neg_inf(), l_run = 0.f;
+  float m_run = neg_inf(), l_run = 0.f, lo_run = 0.f;
 
   Chunk<F32IN> kst[KC];
   Chunk<F32IN> vst[VB][4];
@@ -202,10 +202,10 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_staged_kernel(const FwdParams
     uint32_t pk0[8], pk1[8];
     if constexpr (PROXY) {
       softmax_step_any<DB>(s0, s1, it, xbits, p.block_kv, ti.num_n, ti.Sk, h32, p.c, m_run,
-                           l_run, oacc, pk0, pk1);
+                           l_run, lo_run, oacc, pk0, pk1);
     } else {
       softmax_step<DB, true>(s0, s1, it, it.is_mask && list_masked, mlo, mhi, h32, p.c, m_run,
-                             l_run, oacc, pk0, pk1);
+                             l_run, lo_run, oacc, pk0, pk1);
     }
 #pragma unroll
     for (int ps = 0; ps < 4; ++ps) {
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_staged_kernel(const FwdParams
     if (have) have_nxt = step(nxt);
     sb ^= 1;
   }
-  epilogue<DB, T>(p, ti, qrow, h32, m_run, l_run, oacc);
+  epilogue<DB, T>(p, ti, qrow, h32, m_run, l_run, lo_run, oacc);
 }
 
 template <int D, int NW, bool F32, bool PROXY>

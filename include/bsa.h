@@ -79,6 +79,19 @@ typedef enum {
  * synchronising the stream.  Debug path. */
 #define BSA_FLAG_VALIDATE 1u
 
+/* The block lists are given per KV head: their head index is the KV head
+ * (batched cnt [B,H_kv,M], idx [B,H_kv,M,N]; varlen cnt [H_kv,total_m],
+ * idx [H_kv,total_n]) and Q head h reads the lists of KV head h/(H/H_kv),
+ * as the packed bitmap of the PrimTS page is owned per KV head.  The Q
+ * heads of one KV head then share their lists, and the forward packs them
+ * (flash-attention PR #2224 review thread, pack_gqa): where the 256-row
+ * kernel serves the shape (bf16, head_dim <= 128, no local mask, no
+ * proxies) one workgroup covers G = 256/tile_m Q heads of tile_m rows each
+ * when G divides H/H_kv, so each K/V tile staged on chip feeds G heads.
+ * Lists broadcast over heads (head strides 0) are packed the same way
+ * without the flag.  Results do not depend on the packing. */
+#define BSA_FLAG_KV_HEAD_LISTS 2u
+
 /* One block list (the mask list or the full list).  int32 device arrays.
  * cnt == NULL means the list is absent (no blocks).
  * Batched:  cnt[b,h,m]      at cnt + b*cnt_stride[0] + h*cnt_stride[1] + m*cnt_stride[2]

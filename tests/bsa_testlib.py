@@ -72,6 +72,26 @@ def check_o_lse(o_gpu: torch.Tensor, lse_gpu: torch.Tensor, o_ref: np.ndarray, l
     return float(err.max()) if err.size else 0.0, lerr
 
 
+def check_o_lse_fp32_normaliser(o_gpu, lse_gpu, o_ref, lse_ref, vmax: float, what: str = ""):
+    """The bound of the 256-row kernel, which divides O by the sum of the fp32
+    P while the PV product takes P rounded to bf16 (relative error <= 2^-8
+    per weight): on rows dominated by a few keys these errors do not average
+    out, and |O - O_oracle| <= 2^-8 * max|v| + half a bf16 ulp of O (1e-4
+    slack for the fp32 arithmetic).  The LSE keeps its 1e-3.  Returns the
+    raw max |dO|."""
+    o = o_gpu.detach().float().cpu().double().numpy()
+    lse = lse_gpu.detach().float().cpu().double().numpy()
+    assert np.isfinite(o).all() and np.isfinite(o_ref).all(), what
+    err = np.abs(o - o_ref)
+    bound = 2.0 ** -8 * vmax + 0.5 * bf16_ulp(np.maximum(np.abs(o), np.abs(o_ref))) + 1e-4
+    assert (err <= bound).all(), f"{what}: O error over 2^-8 max|v| by {float((err - bound).max()):.3e}"
+    ninf = np.isneginf(lse_ref)
+    assert (np.isneginf(lse) == ninf).all(), f"{what}: LSE -inf pattern differs"
+    lerr = float(np.abs(lse[~ninf] - lse_ref[~ninf]).max()) if (~ninf).any() else 0.0
+    assert lerr <= LSE_TOL, f"{what}: LSE error {lerr:.3e}"
+    return float(err.max())
+
+
 def run_batched(w, dtype=torch.bfloat16, lists=None, validate=False, q_view=None):
     """Upload a BatchedWorkload, build its lists on the GPU and run bsa_fwd.
     Returns (O, LSE, (q, k, v) device tensors)."""

@@ -89,3 +89,30 @@ def test_bwd_rejects_unsupported():
     fl = _lists(np.ones((1, 1, 1, 1), bool))
     with pytest.raises(bsa.BsaError):
         bsa.bsa_bwd(q, q, q, q, lse, q, None, fl, 64, 64)
+
+
+def test_bwd_full_size_sweep_sampled_heads():
+    # The d128 sweep workload at full size (B2 H16 S4096, 128x128 blocks, 25 %
+    # with causal diagonals), the backward the bench times; heads are
+    # independent here (H = Hkv), so the oracle runs on two sampled (b, h)
+    # slices over the whole sequence and their dQ, dK, dV are compared in full.
+    import workloads
+    w = workloads.sparse_sweep(128, 128, 128)
+    q, k, v = (to_dev(x) for x in (w.q, w.k, w.v))
+    do = to_dev(np.random.default_rng(77).standard_normal(w.q.shape, dtype=np.float32))
+    ml, fl = _lists(w.part), _lists(w.full)
+    o, lse = bsa.bsa_fwd(q, k, v, ml, fl, 128, 128, CAUSAL, None, w.scale)
+    dq, dk, dv = bsa.bsa_bwd(q, k, v, o, lse, do, ml, fl, 128, 128, CAUSAL, None, w.scale)
+    torch.cuda.synchronize()
+    for (b, h) in ((0, 3), (1, 11)):
+        sl = lambda t: as_oracle(t[b:b + 1, :, h:h + 1])
+        rq, rk, rv = oracle.blocksparse_attention_bwd(
+            sl(q), sl(k), sl(v), w.full[b:b + 1, h:h + 1], w.part[b:b + 1, h:h + 1], 128, 128,
+            CAUSAL, w.scale, sl(do))
+        for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+            gg = sl(g)
+            err = float(np.abs(gg - r).max())
+            ref = float(np.abs(r).max())
+            print(f"full-size sweep bwd (b={b}, h={h}) {name}: max err {err:.3e}, "
+                  f"max |grad| {ref:.3e}, ratio {err / ref:.2e}")
+            assert err <= REL_TOL * ref, f"{name} (b={b}, h={h}): err {err:.3e} vs max {ref:.3e}"

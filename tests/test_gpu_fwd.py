@@ -14,8 +14,8 @@ import torch
 import block_sparse_attention_bsa_amd as bsa
 import oracle
 import workloads
-from bsa_testlib import (as_oracle, bf16_ulp, check_o_lse, lists_on_device, rows_of, run_batched,
-                         sample_q_blocks, to_dev)
+from bsa_testlib import (as_oracle, bf16_ulp, check_o_lse, check_o_lse_fp32_normaliser,
+                         lists_on_device, rows_of, run_batched, sample_q_blocks, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -61,9 +61,11 @@ def test_sweep_reduced(D, bq, bk):
     check_o_lse(o, lse, O, L, f"sweep D={D} ({bq},{bk})")
 
 
-@pytest.mark.parametrize("D,bq,bk", [(64, 128, 128), (96, 64, 128), (128, 128, 128),
-                                     (192, 64, 64), (256, 128, 112), (128, 128, 64)])
+@pytest.mark.parametrize("D", workloads.SWEEP_HEAD_DIMS)
+@pytest.mark.parametrize("bq,bk", workloads.SWEEP_BLOCKS)
 def test_sweep_full_size_sampled(D, bq, bk):
+    # all 25 runs of the head_dim x block-size sweep at full size
+    # (B2 H16 S4096, 25 %), 12 sampled Q blocks each
     w = workloads.sparse_sweep(D, bq, bk)
     o, lse, qkv = run_batched(w)
     torch.cuda.synchronize()
@@ -472,12 +474,15 @@ def test_running_max_raised_and_dropped_along_the_list(bq, D):
 
 
 @pytest.mark.parametrize("bq", [256, 128])
-def test_peaked_rows_error_bounded_by_bf16_p(bq):
-    # Key gains up to 12 make many rows nearly one-hot.  There the bf16
-    # rounding of P (relative error <= 2^-8) is not averaged out: the O error
-    # is bounded by 2^-8 * max|v| plus the output rounding, which for |v| ~ 4
-    # exceeds the 4e-3 that holds for the N(0,1) workloads.  The LSE (taken
-    # over the fp32 P) keeps its 1e-3.
+def test_peaked_rows_within_tolerance(bq):
+    # Key gains up to 12 make many rows nearly one-hot, where the bf16
+    # rounding of P (relative error <= 2^-8 per weight) does not average out.
+    # The 128-row kernel divides O by the sum of the same bf16 P the PV
+    # product takes, so the weights it applies sum to one and a one-hot row
+    # gets its key's V row exactly: O keeps the 4e-3 bound there too.  The
+    # 256-row kernel divides by the fp32 sum (see
+    # check_o_lse_fp32_normaliser): O within 2^-8 * max|v| beyond its output
+    # rounding.  The LSE (over the fp32 P) keeps 1e-3 in both.
     w, N, blk = _ramped(bq, 128, seed=11 + bq)
     g = (1.0 + 11.0 * (N - 1 - blk) / (N - 1)).astype(np.float32)
     w.k[:, :, 0, :] *= g[:, None]
@@ -485,13 +490,12 @@ def test_peaked_rows_error_bounded_by_bf16_p(bq):
     o, lse, qkv = run_batched(w, validate=True)
     torch.cuda.synchronize()
     O, L = _oracle_batched(w, qkv)
-    fin = np.isfinite(L)
-    assert np.abs(lse.cpu().double().numpy()[fin] - L[fin]).max() <= 1e-3
-    o_k = o.float().cpu().double().numpy()
-    vmax = np.abs(as_oracle(qkv[2])).max()
-    bound = 2.0 ** -8 * vmax + 0.5 * bf16_ulp(np.maximum(np.abs(O), np.abs(o_k))) + 1e-4
-    assert (np.abs(o_k - O) <= bound).all(), float((np.abs(o_k - O) - bound).max())
-
+    if bq == 256:
+        err = check_o_lse_fp32_normaliser(o, lse, O, L, np.abs(as_oracle(qkv[2])).max(),
+                                          f"peaked rows bq={bq}")
+    else:
+        err, _ = check_o_lse(o, lse, O, L, f"peaked rows bq={bq}")
+    print(f"peaked rows bq={bq}: raw max|dO| {err:.3e}")
 
 
 @pytest.mark.parametrize("bq,D", [(256, 128), (256, 64), (128, 128)])
@@ -599,7 +603,11 @@ def test_varlen_valid_count(bq, bk, D):
     O, L = oracle.varlen_blocksparse_attention(as_oracle(q), as_oracle(k), as_oracle(v),
                                                w.seqlens_q, w.seqlens_k, w.full, w.part, bq, bk,
                                                KVV, w.scale, kv_valid=w.kv_valid)
-    check_o_lse(o, lse, O, L, f"varlen kvv ({bq},{bk}) D={D}")
+    if bq % 256 == 0:  # the 256-row kernel: random small valid counts leave rows of few keys
+        check_o_lse_fp32_normaliser(o, lse, O, L, np.abs(as_oracle(v)).max(),
+                                    f"varlen kvv ({bq},{bk}) D={D}")
+    else:
+        check_o_lse(o, lse, O, L, f"varlen kvv ({bq},{bk}) D={D}")
 
 
 def test_varlen_valid_count_shared_row_and_errors():

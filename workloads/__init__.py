@@ -198,6 +198,32 @@ def sparse_sweep(D: int, bq: int, bk: int, B=2, H=16, S=4096,
                            MASK_CAUSAL, 1.0 / math.sqrt(D))
 
 
+def gqa_sweep(D: int, bq: int, bk: int, Hkv: int, hrep: int, B=2, S=4096,
+              density: float = 0.25, seed: Optional[int] = None) -> BatchedWorkload:
+    """Grouped-query attention: H = Hkv * hrep Q heads over Hkv KV heads, with
+    block masks per KV head (full / part [B, Hkv, M, N]) that the hrep Q heads
+    of each KV head share, drawn as in sparse_sweep (causal diagonal blocks
+    as mask blocks, random other blocks as full blocks, floor(density*N) in
+    all).  extra["kv_head_lists"] marks the per-KV-head masks."""
+    rng = np.random.default_rng([1009, D, bq, bk, Hkv, hrep] if seed is None else seed)
+    H = Hkv * hrep
+    q, k, v = _qkv(rng, (B, S, H, D), (B, S, Hkv, D))
+    M, N = _cdiv(S, bq), _cdiv(S, bk)
+    k_total = int(math.floor(density * N))
+    full = np.zeros((B, Hkv, M, N), bool)
+    part = np.zeros((B, Hkv, M, N), bool)
+    for i in range(M):
+        diag = _diagonal_blocks(i, bq, bk, S, S)
+        others = np.array([j for j in range(N) if j not in diag], dtype=np.int64)
+        n_pick = min(max(k_total - len(diag), 0), others.size)
+        for b in range(B):
+            for h in range(Hkv):
+                full[b, h, i, rng.choice(others, size=n_pick, replace=False)] = True
+                part[b, h, i, diag] = True
+    return BatchedWorkload(f"gqa_d{D}_bq{bq}_bk{bk}_hkv{Hkv}x{hrep}", q, k, v, full, part, bq,
+                           bk, MASK_CAUSAL, 1.0 / math.sqrt(D), extra={"kv_head_lists": True})
+
+
 def varlen_packed(n_seq=8, H=16, D=128, bs=128, lo=128, hi=8192, p_below=0.3,
                   seed: int = 1004, seqlens: Optional[List[int]] = None) -> VarlenWorkload:
     """Packed batch of n_seq sequences (seqlen_q = seqlen_k ~ U{lo..hi}, or the
