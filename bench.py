@@ -54,7 +54,7 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=["video", "sweep128"], default="video")
+    ap.add_argument("--workload", choices=["video", "sweep128", "varlen"], default="video")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-time budget of the oracle sample on the host (0 = skip)")
     ap.add_argument("--print-kernel-hash", action="store_true",
@@ -152,6 +152,55 @@ def _sweep_step(bsa, st, events=None):
         events[0].record()
     o, lse = bsa.bsa_fwd(st["q"], st["k"], st["v"], ml, fl, 128, 128, bsa.MASK_CAUSAL, None,
                          st["w"].scale, out=st.get("o"), lse=st.get("lse"))
+    if events is not None:
+        events[1].record()
+    st["o"], st["lse"] = o, lse
+
+
+def _varlen_inputs(torch, np, workloads):
+    w = workloads.varlen_packed()
+    dev = torch.device("cuda")
+    H, bq, bk, D = w.q.shape[1], w.block_q, w.block_kv, w.q.shape[-1]
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (w.q, w.k, w.v))
+    flops = sum(_pairs_flops(fu[None], pa[None], bq, bk, sq, sk, D)
+                for fu, pa, sq, sk in zip(w.full, w.part, w.seqlens_q, w.seqlens_k))
+    M = sum(-(-s // bq) for s in w.seqlens_q)
+    dens = sum(float((fu | pa).sum()) for fu, pa in zip(w.full, w.part)) / sum(
+        fu.size for fu in w.full)
+    cfg = {"workload": "varlen_packed", "sequences": len(w.seqlens_q), "tokens": int(
+        sum(w.seqlens_q)), "H": H, "head_dim": D, "block_q": bq, "block_kv": bk,
+        "total_m_blocks": M, "block_density": round(dens, 4),
+        "mask_mod": "causal_diagonal_plus_random_30pct", "layout": "THD"}
+    return dict(q=q, k=k, v=v, w=w), flops, cfg
+
+
+def _varlen_step(bsa, st, events=None):
+    import numpy as np
+    import torch
+    w = st["w"]
+    bq, bk, H = w.block_q, w.block_kv, w.q.shape[1]
+    if "cu" not in st:  # host bookkeeping and the packed masks, once (inputs of the step)
+        cu, off, tm, tn = bsa.bsa_varlen_offsets(w.seqlens_q, w.seqlens_k, bq, bk)
+        dv = lambda a: torch.tensor(a, dtype=torch.int32, device="cuda")
+        st["cu_q"] = dv([0] + list(np.cumsum(w.seqlens_q)))
+        st["cu_k"] = dv([0] + list(np.cumsum(w.seqlens_k)))
+        st["cu"], st["off"], st["tm"], st["tn"] = dv(cu), dv(off), tm, tn
+
+        def packed(masks):
+            out = np.zeros((H, tn), np.uint8)
+            for b, m in enumerate(masks):
+                nm, nn = m.shape[1:]
+                for i in range(nm):
+                    out[:, off[b] + i * nn: off[b] + (i + 1) * nn] = m[:, i]
+            return torch.from_numpy(out).cuda()
+        st["pm"], st["pf"] = packed(w.part), packed(w.full)
+    ml = bsa.bsa_varlen_mask_to_index(st["pm"], st["cu"], st["off"], st["tm"], st["tn"])
+    fl = bsa.bsa_varlen_mask_to_index(st["pf"], st["cu"], st["off"], st["tm"], st["tn"])
+    if events is not None:
+        events[0].record()
+    o, lse = bsa.bsa_varlen_fwd(st["q"], st["k"], st["v"], st["cu_q"], st["cu_k"], st["cu"],
+                                st["off"], st["tm"], st["tn"], ml, fl, bq, bk, w.mask_mod, w.scale,
+                                out=st.get("o"), lse=st.get("lse"))
     if events is not None:
         events[1].record()
     st["o"], st["lse"] = o, lse
@@ -577,8 +626,8 @@ def main():
         print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
                           "launches": 3}))
         return
-    make, step = ((_video_inputs, _video_step) if args.workload == "video"
-                  else (_sweep_inputs, _sweep_step))
+    make, step = {"video": (_video_inputs, _video_step), "sweep128": (_sweep_inputs, _sweep_step),
+                  "varlen": (_varlen_inputs, _varlen_step)}[args.workload]
     st, flops, cfg = make(torch, np, workloads)
     for _ in range(args.warmup):
         step(bsa, st)
@@ -607,6 +656,8 @@ def main():
     # head_dim 128; 256-row workgroups for 256-token Q cubes, 128 rows otherwise
     kernel_name = "bsa_fwd_pp_kernel<128> (256-row workgroup, 8 waves)" \
         if args.workload == "video" else "bsa_fwd_kernel<128,4> (128-row workgroup)"
+    if args.workload == "varlen":
+        args.cpu_seconds = 0  # the oracle leg samples the video and sweep workloads only
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),

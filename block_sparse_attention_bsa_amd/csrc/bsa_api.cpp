@@ -403,6 +403,8 @@ bsa_status bsa_varlen_fwd(const void* q, const void* k, const void* v, void* o, 
   p.win_left = bs->window_left;
   p.win_right = bs->window_right;
   p.varlen = 1;
+  // long-list-first order when its per-workgroup cost (B log total_m reads) is small
+  p.lpt = B <= 64 ? 1 : 0;
   p.tiles_per_head = (int32_t)tiles_per_head;
   p.total_m = total_m_blocks;
   p.total_n = total_n_blocks;

@@ -143,7 +143,7 @@ struct FwdCfg {
 
 // LOCAL: the local mask_mod's key range on mask-list sub-tiles (a separate
 // instance, so the others keep the plain causal test).
-template <int D, int NW, bool LOCAL, bool PROXY>
+template <int D, int NW, bool LOCAL, bool PROXY, bool VARLEN>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(FwdCfg<D, NW>::WAVES_PER_EU)))
 void bsa_fwd_kernel(const FwdParams p) {
@@ -158,7 +158,7 @@ void bsa_fwd_kernel(const FwdParams p) {
 
   TileInfo ti;
   const int tix = xcd_remap(blockIdx.x, p.num_tiles);
-  if (!decode_tile<C::TM>(p, tix, ti)) return;
+  if (!decode_tile<C::TM, VARLEN ? 1 : 0>(p, tix, ti)) return;
   const __bf16* qp = reinterpret_cast<const __bf16*>(p.q) + ti.qoff;
   const __bf16* kp = reinterpret_cast<const __bf16*>(p.k) + ti.koff;
   const __bf16* vp = reinterpret_cast<const __bf16*>(p.v) + ti.voff;
@@ -428,10 +428,14 @@ template <int D, int NW>
 hipError_t launch_one(const FwdParams& p, hipStream_t s) {
   FwdParams copy = p;
   void* args[] = {&copy};
-  const void* k = p.ksum ? reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, false, true>)
-                  : p.mask_mod == kMaskLocal
-                      ? reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, true, false>)
-                      : reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, false, false>);
+  // batched and packed-varlen tile decodes are separate instances
+  const void* k =
+      p.ksum ? reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, false, true, false>)
+      : p.mask_mod == kMaskLocal
+          ? (p.varlen ? reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, true, false, true>)
+                      : reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, true, false, false>))
+          : (p.varlen ? reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, false, false, true>)
+                      : reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, false, false, false>));
   return hipLaunchKernel(k, dim3(p.num_tiles), dim3(NW * 64), args, 0, s);
 }
 

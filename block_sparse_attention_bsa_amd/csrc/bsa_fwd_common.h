@@ -79,6 +79,43 @@ struct TileInfo {
   int mcnt, fcnt;
 };
 
+// Varlen work order: Q block of rank q (0 <= q < total_m_blocks) in the
+// order "block index within its sequence descending, then sequence
+// ascending", so the blocks late in long sequences, which list the most KV
+// blocks under a causal mask, are dispatched first and the short ones fill
+// the tail.  With C(L) = sum_b max(0, num_m(b) - L) blocks at local index >=
+// L, rank q lies at the level L where C(L+1) <= q < C(L) (binary search over
+// L), and is the (q - C(L+1))-th sequence, counted from b = 0, that has a
+// block at index L.  O(B log total_m) reads of cu_total_m_blocks.
+__device__ __forceinline__ int blocks_at_or_above(const FwdParams& p, int L) {
+  int c = 0;
+  for (int b = 0; b < p.B; ++b) c += max(0, (p.cu_m[b + 1] - p.cu_m[b]) - L);
+  return c;
+}
+
+__device__ __forceinline__ void varlen_block_by_rank(const FwdParams& p, int q, int& b, int& m) {
+  int lo = 0, hi = p.total_m - 1;  // the largest L with C(L) > q
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (blocks_at_or_above(p, mid) > q)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  int k = q - blocks_at_or_above(p, lo + 1);
+  b = 0;
+  for (int s = 0; s < p.B; ++s) {
+    if (p.cu_m[s + 1] - p.cu_m[s] > lo) {
+      if (k == 0) {
+        b = s;
+        break;
+      }
+      --k;
+    }
+  }
+  m = lo;
+}
+
 // Logical tile t -> TileInfo.  A tile holds TM rows: R = TM / gpack rows
 // of each of gpack consecutive Q heads h .. h + gpack - 1 (gpack > 1 packs
 // the Q heads of one KV head, which then share their lists).  A sparse Q
@@ -94,13 +131,16 @@ struct TileInfo {
 // block_idx_offsets[b] + m * num_n(b).  The list head is h, or its KV head
 // h / hrep when the lists are given per KV head.  Returns false when the
 // tile holds no row of its sequence (the whole workgroup then exits).
-template <int TM>
+// VL: 0 batched, 1 varlen (compile-time: the other layout's code is not in
+// the kernel), 2 taken from p.varlen at run time.
+template <int TM, int VL = 2>
 __device__ __forceinline__ bool decode_tile(const FwdParams& p, int t, TileInfo& ti) {
   ti.mrow = nullptr;
   ti.frow = nullptr;
   ti.mcnt = ti.fcnt = 0;
   const int R = TM / p.gpack, HG = p.H / p.gpack;
-  if (!p.varlen) {
+  const bool varlen = VL == 2 ? p.varlen != 0 : VL == 1;
+  if (!varlen) {
     const int qt = t % p.tiles_per_head;
     const int bh = t / p.tiles_per_head;
     const int h = (bh % HG) * p.gpack, b = bh / HG, hk = h / p.hrep;
@@ -131,18 +171,26 @@ __device__ __forceinline__ bool decode_tile(const FwdParams& p, int t, TileInfo&
   } else {
     const int tm = t % p.tiles_per_head;
     const int h = (t / p.tiles_per_head) * p.gpack;
-    const int mg = tm / p.qsub, sub = tm % p.qsub;
-    int lo = 0, hi = p.B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.cu_m[mid] <= mg)
-        lo = mid;
-      else
-        hi = mid - 1;
+    const int sub = tm % p.qsub;
+    int b, m;
+    if (p.lpt) {
+      varlen_block_by_rank(p, tm / p.qsub, b, m);
+    } else {
+      const int mg = tm / p.qsub;
+      int lo = 0, hi = p.B - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (p.cu_m[mid] <= mg)
+          lo = mid;
+        else
+          hi = mid - 1;
+      }
+      b = lo;
+      m = mg - p.cu_m[b];
     }
-    const int b = lo, hk = h / p.hrep;
+    const int mg = p.cu_m[b] + m;
+    const int hk = h / p.hrep;
     const int lh = p.kvh_lists ? hk : h;
-    const int m = mg - p.cu_m[b];
     const int sq0 = p.cu_q[b], sk0 = p.cu_k[b];
     ti.h = h;
     ti.Sq = p.cu_q[b + 1] - sq0;
@@ -245,6 +293,9 @@ __device__ __forceinline__ bool advance(Item& it, ListWalk& L, int lane, int Sk)
     L.entry(g, lane, j, blen);
   }
 }
+
+// Cap on a lane's sum of P in the 256-row kernel's lazy running max.
+constexpr float kSumCap = 65536.f;
 
 // Online-softmax step for one 64-key sub-tile.  s0/s1 hold S^T for keys
 // 0..31 / 32..63 of the sub-tile (raw dot products).  Applies the element

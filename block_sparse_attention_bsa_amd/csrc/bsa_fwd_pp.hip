@@ -76,7 +76,6 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
 typedef __attribute__((address_space(3))) char lds_char;
 
-constexpr float kSumCap = 65536.f;
 // Word 3 of a raw (unstrided) buffer descriptor on the gfx9 family: 32-bit
 // data format, no swizzle; accesses at or past num_records return zero.
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
@@ -229,7 +228,7 @@ struct PPCfg {
   }
 };
 
-template <int D>
+template <int D, bool VARLEN>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void bsa_fwd_pp_kernel(const FwdParams p) {
   using C = PPCfg<D>;
@@ -243,7 +242,7 @@ void bsa_fwd_pp_kernel(const FwdParams p) {
   const bool g1 = w >= 4;
 
   TileInfo ti;
-  if (!decode_tile<256>(p, xcd_remap(blockIdx.x, p.num_tiles), ti)) return;
+  if (!decode_tile<256, VARLEN ? 1 : 0>(p, xcd_remap(blockIdx.x, p.num_tiles), ti)) return;
   // GQA packing: wave w holds rows (32*w) % R .. of head ti.h + 32*w / R
   // (R = 256 / gpack rows per head), and every head of the tile walks the
   // same items.  Without packing R = 256 and dh = 0.
@@ -565,7 +564,9 @@ template <int D>
 hipError_t launch_pp(const FwdParams& p, hipStream_t s) {
   FwdParams copy = p;
   void* args[] = {&copy};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&bsa_fwd_pp_kernel<D>), dim3(p.num_tiles),
+  const void* k = p.varlen ? reinterpret_cast<const void*>(&bsa_fwd_pp_kernel<D, true>)
+                           : reinterpret_cast<const void*>(&bsa_fwd_pp_kernel<D, false>);
+  return hipLaunchKernel(k, dim3(p.num_tiles),
                          dim3(512), args, 0, s);
 }
 
