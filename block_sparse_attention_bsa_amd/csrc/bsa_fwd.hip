@@ -57,9 +57,14 @@ typedef __attribute__((address_space(3))) char lds_char;
 // at LDS byte address lds_addr + 16*l.  base (64-bit) and lds_addr must be
 // wave-uniform: base goes in SGPRs (global "saddr" form, so a precomputed
 // 32-bit lane offset is all the address arithmetic a lane needs), lds_addr
-// in M0 (the s_nop covers the M0-write hazard).
+// in M0.  The compiler's hazard checks do not see inside the asm, so its
+// s_nop 4 provides the wait states the load needs after the instructions
+// that set its operands: one after the M0 write, and five after a VALU
+// instruction that writes an SGPR a vector-memory instruction reads (the
+// base is often restored from a spill with v_readlane just before; with
+// fewer wait states the load can take a stale base and fault).
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_addr) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
                "{m0}"(lds_addr)
                : "memory");
 }
@@ -143,7 +148,9 @@ struct FwdCfg {
 
 // LOCAL: the local mask_mod's key range on mask-list sub-tiles (a separate
 // instance, so the others keep the plain causal test).
-template <int D, int NW, bool LOCAL, bool PROXY, bool VARLEN>
+// PACK: items are packed from the keys of consecutive listed blocks
+// (advance_packed), K/V rows gathered per lane from up to kPackSeg runs.
+template <int D, int NW, bool LOCAL, bool PROXY, bool VARLEN, bool PACK>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(FwdCfg<D, NW>::WAVES_PER_EU)))
 void bsa_fwd_kernel(const FwdParams p) {
@@ -250,7 +257,46 @@ void bsa_fwd_kernel(const FwdParams p) {
     // block ii*NW + w exists unless it is the last one of a wave and past RS
     auto kblk = [&](int ii) { return !(RSK % NW != 0 && ii == KIPW - 1 && ii * NW + w >= RSK); };
     auto vblk = [&](int ii) { return !(RSV % NW != 0 && ii == VIPW - 1 && ii * NW + w >= RSV); };
-    if (it.nk == kKvTile) {
+    if constexpr (PACK) {
+      // gathered item: row r of the tile holds sequence key r + d_s of the run
+      // s it falls in (rows past nk repeat the last key); byte offsets from
+      // the sequence's first K/V row fit in 31 bits (checked by the host)
+      const int last = it.nk - 1;
+      // wave-uniform run bounds and offsets as plain values (selects between
+      // struct fields would become an indexed load from scratch)
+      const int e0 = __builtin_amdgcn_readfirstlane(it.e0);
+      const int e1 = __builtin_amdgcn_readfirstlane(it.e1);
+      const int e2 = __builtin_amdgcn_readfirstlane(it.e2);
+      const int d0 = __builtin_amdgcn_readfirstlane(it.d0);
+      const int d1 = __builtin_amdgcn_readfirstlane(it.d1);
+      const int d2 = __builtin_amdgcn_readfirstlane(it.d2);
+      const int d3 = __builtin_amdgcn_readfirstlane(it.d3);
+      // sum of steps rather than a select chain, which the compiler would
+      // turn into a lookup table in scratch memory
+      const int q1 = d1 - d0, q2 = d2 - d1, q3 = d3 - d2;
+      auto gkey = [=](int r) {
+        const int rr = min(r, last);
+        return rr + d0 + q1 * (int)(rr >= e0) + q2 * (int)(rr >= e1) + q3 * (int)(rr >= e2);
+      };
+      const char* kb = reinterpret_cast<const char*>(kp);
+      const char* vb = reinterpret_cast<const char*>(vp);
+#pragma unroll
+      for (int ii = 0; ii < KIPW; ++ii) {
+        if (!kblk(ii)) continue;
+        const int slot = (ii * NW + w) * 64 + lane;
+        const int r = slot / RSK;
+        dma16(kb, (uint32_t)(gkey(r) * kss2 + kchunk(r, slot % RSK) * 16),
+              kl + (ii * NW + w) * 1024);
+      }
+#pragma unroll
+      for (int ii = 0; ii < VIPW; ++ii) {
+        if (!vblk(ii)) continue;
+        const int slot = (ii * NW + w) * 64 + lane;
+        const int r = slot / RSV;
+        dma16(vb, (uint32_t)(gkey(r) * vss2 + vchunk(r, slot % RSV) * 16),
+              vl + (ii * NW + w) * 1024);
+      }
+    } else if (it.nk == kKvTile) {
 #pragma unroll
       for (int ii = 0; ii < KIPW; ++ii)
         if (kblk(ii))
@@ -340,8 +386,8 @@ void bsa_fwd_kernel(const FwdParams p) {
       softmax_step_any<DB>(s0, s1, it, xbits, p.block_kv, ti.num_n, ti.Sk, h32, p.c, m_run,
                            l_run, lo_run, oacc, pk0, pk1);
     else
-      softmax_step<DB, LOCAL>(s0, s1, it, it.is_mask && list_masked, mlo, mhi, h32, p.c, m_run,
-                              l_run, lo_run, oacc, pk0, pk1);
+      softmax_step<DB, LOCAL, PACK>(s0, s1, it, it.is_mask != 0 && list_masked, mlo, mhi, h32,
+                                    p.c, m_run, l_run, lo_run, oacc, pk0, pk1);
     // PV step i: keys 16*(i / DB) .., head dims 32*(i % DB) ..
     auto vld = [&](int i) {
       const int ps = i / DB, db = i % DB;
@@ -372,13 +418,14 @@ void bsa_fwd_kernel(const FwdParams p) {
   int pn = 0;
   auto step = [&](Item& it) -> bool {
     if (!in_proxy) {
+      if constexpr (PACK) return advance_packed(it, L, lane, ti.Sk, list_masked);
       if (advance(it, L, lane, ti.Sk)) return true;
       in_proxy = true;
     }
     if constexpr (PROXY) return next_proxy_chunk(xbits, ti.num_n, pn, it);
     return false;
   };
-  Item walker{-1, 0, 0, 0, 0, 0, 0};
+  Item walker{-1, 0, 0, 0, 0, 0, 0, kKvTile, kKvTile, kKvTile, 0, 0, 0, 0};
   bool more = step(walker);
   Item p0 = walker;
   bool pending = false;
@@ -424,18 +471,31 @@ void bsa_fwd_kernel(const FwdParams p) {
   epilogue<DB, __bf16>(p, ti, qrow, h32, m_run, l_run, lo_run, oacc);
 }
 
+// The packed-item instance (none for 32-row tiles at head_dim >= 192, whose
+// registers would spill; the host does not pack those).
+template <int D, int NW>
+const void* pack_kernel() {
+  if constexpr (NW == 1 && D >= 192)
+    return reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, false, false, false, false>);
+  else
+    return reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, false, false, false, true>);
+}
+
 template <int D, int NW>
 hipError_t launch_one(const FwdParams& p, hipStream_t s) {
   FwdParams copy = p;
   void* args[] = {&copy};
-  // batched and packed-varlen tile decodes are separate instances
+  // batched and packed-varlen tile decodes are separate instances; packed
+  // items (route packing) are batched only
   const void* k =
-      p.ksum ? reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, false, true, false>)
+      p.ksum ? reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, false, true, false, false>)
       : p.mask_mod == kMaskLocal
-          ? (p.varlen ? reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, true, false, true>)
-                      : reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, true, false, false>))
-          : (p.varlen ? reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, false, false, true>)
-                      : reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, false, false, false>));
+          ? (p.varlen
+                 ? reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, true, false, true, false>)
+                 : reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, true, false, false, false>))
+      : p.varlen ? reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, false, false, true, false>)
+      : p.pack   ? pack_kernel<D, NW>()
+                 : reinterpret_cast<const void*>(&bsa_fwd_kernel<D, NW, false, false, false, false>);
   return hipLaunchKernel(k, dim3(p.num_tiles), dim3(NW * 64), args, 0, s);
 }
 

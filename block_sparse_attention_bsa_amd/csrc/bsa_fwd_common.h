@@ -268,7 +268,75 @@ struct ListWalk {
 // position g; its keys [key0, key0 + nk) are the ones that can be visible.
 struct Item {
   int g, st, j, blen, key0, nk, is_mask;
+  // packed items (advance_packed): item key r < nk is sequence key r + d_s,
+  // s = (r >= e0) + (r >= e1) + (r >= e2); unused ends are kKvTile
+  int e0, e1, e2, d0, d1, d2, d3;
 };
+
+// Route packing (the PrimTS page's fixed-width physical routes, here 64
+// keys): the visible keys of consecutive listed blocks (the block size
+// clipped to the sequence, and for a mask-list block under the valid-count
+// mask_mod to its count) are packed into 64-key items of up to kPackSeg
+// contiguous runs, so a block of 112, 80 or 16 keys leaves no MFMA slot
+// empty except at the end of the list.  Runs from mask-list blocks under
+// the causal mask are marked in bit s of it.is_mask, and the element mask
+// tests their keys (softmax_step with SEG).  it.g / it.st hold the list
+// position and the keys of block it.g already taken; it.j / it.blen that
+// block's id and visible length.  Returns false past the end.
+constexpr int kPackSeg = 4;
+
+__device__ __forceinline__ bool advance_packed(Item& it, ListWalk& L, int lane, int Sk,
+                                               bool causal_mask_list) {
+  int g = it.g, pos = it.st, j = it.j, blen = it.blen;
+  int nk = 0, nseg = 0, cmask = 0;
+  int e0 = kKvTile, e1 = kKvTile, e2 = kKvTile, d0 = 0, d1 = 0, d2 = 0, d3 = 0;
+  while (true) {
+    if (g < 0 || pos >= blen) {  // the next listed block with a visible key
+      ++g;
+      pos = 0;
+      if (g >= L.total) {  // past the end: the state stays exhausted for later calls
+        g = L.total;
+        blen = 0;
+        break;
+      }
+      L.entry(g, lane, j, blen);
+      blen = min(blen, Sk - j * L.bk);
+      continue;
+    }
+    const int t = min(kKvTile - nk, blen - pos);
+    const int dd = j * L.bk + pos - nk;  // sequence key = item key + dd over this run
+    // (unconditional selects: an if-chain over nseg becomes a scratch array)
+    d0 = nseg == 0 ? dd : d0;
+    d1 = nseg == 1 ? dd : d1;
+    d2 = nseg == 2 ? dd : d2;
+    d3 = nseg == 3 ? dd : d3;
+    if (causal_mask_list && g < L.mcnt) cmask |= 1 << nseg;
+    nk += t;
+    ++nseg;
+    pos += t;
+    if (nk == kKvTile || nseg == kPackSeg) break;
+    // the run ends inside the item: the next one starts at item key nk
+    e0 = nseg == 1 ? nk : e0;
+    e1 = nseg == 2 ? nk : e1;
+    e2 = nseg == 3 ? nk : e2;
+  }
+  if (nk == 0) return false;
+  it.g = g;
+  it.st = pos;
+  it.j = j;
+  it.blen = blen;
+  it.nk = nk;
+  it.key0 = d0;
+  it.is_mask = cmask;
+  it.e0 = e0;
+  it.e1 = e1;
+  it.e2 = e2;
+  it.d0 = d0;
+  it.d1 = d1;
+  it.d2 = d2;
+  it.d3 = d3;
+  return true;
+}
 
 __device__ __forceinline__ bool advance(Item& it, ListWalk& L, int lane, int Sk) {
   int g = it.g, st = it.st + 1, j = it.j, blen = it.blen;
@@ -308,7 +376,9 @@ constexpr float kSumCap = 65536.f;
 // (RANGE true) mask_mod; its kept keys of this lane's row are key <= mhi
 // (causal: mhi = qrow) or mlo <= key <= mhi (local, absolute ids;
 // row_key_range gives them).  The valid-count mask is already in it.nk.
-template <int DB, bool RANGE = false>
+// SEG: a packed item (advance_packed); bit s of it.is_mask marks run s as
+// causal-masked, and item key k is sequence key k + d_s of its run s.
+template <int DB, bool RANGE = false, bool SEG = false>
 __device__ __forceinline__ void softmax_step(f32x16_t& s0, f32x16_t& s1, const Item& it,
                                              bool masked, int mlo, int mhi, int h32, float c,
                                              float& m_run, float& l_run, float& lo_run,
@@ -319,7 +389,20 @@ __device__ __forceinline__ void softmax_step(f32x16_t& s0, f32x16_t& s1, const I
     for (int r = 0; r < 16; ++r) {
       const int key = 16 * (r >> 3) + 8 * h32 + (r & 7);
       bool keep0 = key < it.nk, keep1 = key + 32 < it.nk;
-      if (masked) {
+      if constexpr (SEG) {
+        if (masked) {
+          // run of item key k, its sequence key, and the causal test where
+          // the run is marked (sums of steps: no select chains)
+          auto keep = [&](int k) {
+            const int s = (int)(k >= it.e0) + (int)(k >= it.e1) + (int)(k >= it.e2);
+            const int ck = k + it.d0 + (it.d1 - it.d0) * (int)(k >= it.e0) +
+                           (it.d2 - it.d1) * (int)(k >= it.e1) + (it.d3 - it.d2) * (int)(k >= it.e2);
+            return ((it.is_mask >> s) & 1) == 0 || ck <= mhi;
+          };
+          keep0 = keep0 && keep(key);
+          keep1 = keep1 && keep(key + 32);
+        }
+      } else if (masked) {
         const int c0 = it.key0 + key, c1 = c0 + 32;
         keep0 = keep0 && c0 <= mhi;
         keep1 = keep1 && c1 <= mhi;

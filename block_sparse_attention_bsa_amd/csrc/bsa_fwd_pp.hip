@@ -90,10 +90,16 @@ __device__ __forceinline__ u32x4_t make_rsrc(uint64_t addr, uint32_t bytes) {
 }
 
 // One wave-wide 16-byte-per-lane DMA: lane l's 16 bytes at descriptor
-// offset `off` land at LDS byte address lds_addr + 16*l (lds_addr in M0;
-// the s_nop covers the M0-write hazard).  Issued from inline assembly so the
-// compiler neither waits for it nor reorders LDS accesses across it; the
-// kernel orders it with vmcnt waits and barriers.
+// offset `off` land at LDS byte address lds_addr + 16*l (lds_addr in M0).
+// Issued from inline assembly so the compiler neither waits for it nor
+// reorders LDS accesses across it; the kernel orders it with vmcnt waits and
+// barriers.  The compiler's hazard checks do not see inside the asm: its
+// s_nop 0 covers the M0 write only.  A VALU write of a descriptor SGPR
+// (v_readlane restoring a spill) needs five wait states before a
+// vector-memory read of it; this kernel builds its descriptors with scalar
+// instructions and keeps them in SGPRs, which tests/test_asm_hazards.py
+// checks in the compiled code (four more wait states per DMA cost 1.2 % of
+// the video workload).
 __device__ __forceinline__ void dma16(u32x4_t rsrc, uint32_t off, uint32_t lds_addr) {
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rsrc),
                "{m0}"(lds_addr)

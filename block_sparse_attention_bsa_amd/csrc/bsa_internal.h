@@ -49,6 +49,7 @@ struct FwdParams {
   int32_t gpack;      // Q heads per tile (> 1: heads of one KV head packed, sharing lists)
   int32_t kvh_lists;  // lists indexed by KV head (cnt [B,H_kv,M] ...) instead of Q head
   int32_t lpt;        // varlen: Q blocks late in their sequence first (varlen_block_by_rank)
+  int32_t pack;       // route packing: 64-key items gathered from consecutive listed blocks
   // proxy-compensated route: mean-K / summed-V block summaries [B, N, H_kv, D]
   const void* ksum;
   const void* vsum;

@@ -633,3 +633,44 @@ def test_varlen_valid_count_shared_row_and_errors():
         bsa.bsa_varlen_fwd(q, k, v, cu_q, cu_k, cu_m, offs, tm, tn, ml, fl, 128, 64, KVV,
                            w.scale, kv_valid=torch.zeros((3, 2), dtype=torch.int32,
                                                           device="cuda"))
+
+
+# ------------------------------------------ route packing
+# KV blocks whose size is not a multiple of 64 are packed into 64-key items
+# of up to four runs from consecutive listed blocks (the fixed-width routes
+# of the PrimTS page); runs from causal mask-list blocks keep their element
+# mask inside a packed item.  Every row against the oracle: causal
+# diagonals, random valid counts, no mask, blocks of 16/17/48/80/100 keys,
+# ragged sequence ends, every head_dim.
+@pytest.mark.parametrize("D", [64, 96, 128, 192, 256])
+@pytest.mark.parametrize("bq,bk,mm", [(128, 16, CAUSAL), (64, 48, CAUSAL), (128, 80, KVV),
+                                      (32, 100, NONE), (128, 17, CAUSAL)])
+def test_packed_routes(D, bq, bk, mm):
+    seed = [13, D, bq, bk, mm]
+    if mm == CAUSAL:
+        w = workloads.sparse_sweep(D, bq, bk, B=2, H=2, S=650, density=0.4, seed=seed)
+    else:
+        w = _small(seed=zlib.crc32(repr(seed).encode()), B=2, S=500, H=2, Hkv=1, D=D, bq=bq,
+                   bk=bk, p_full=0.35, p_part=0.3, mask_mod=mm, Sk=777)
+    o, lse, qkv = run_batched(w, validate=True)
+    torch.cuda.synchronize()
+    O, L = _oracle_batched(w, qkv)
+    check_o_lse(o, lse, O, L, f"packed routes D={D} ({bq},{bk}) mm={mm}")
+
+
+def test_packed_routes_all_causal_runs():
+    # 16-key blocks up to each Q block's diagonal, all in the causal mask list:
+    # items made of four causal runs each
+    rng = np.random.default_rng(21)
+    S, D, bq, bk = 300, 128, 128, 16
+    q, k, v = (rng.standard_normal((1, S, 2, D), dtype=np.float32) for _ in range(3))
+    M, N = -(-S // bq), -(-S // bk)
+    part = np.zeros((1, 2, M, N), bool)
+    for i in range(M):
+        part[:, :, i, :min(bq * (i + 1) // bk, N)] = True
+    w = workloads.BatchedWorkload("causal_runs16", q, k, v, np.zeros_like(part), part, bq, bk,
+                                  CAUSAL, 1 / math.sqrt(D))
+    o, lse, qkv = run_batched(w, validate=True)
+    torch.cuda.synchronize()
+    O, L = _oracle_batched(w, qkv)
+    check_o_lse(o, lse, O, L, "packed causal runs")
