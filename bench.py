@@ -398,6 +398,44 @@ def table(torch, np, bsa, workloads, oracle_s):
             w = workloads.sparse_sweep(D, bq, bk)
             batched(f"sweep d{D} ({bq},{bk}) (B2 H16 S4096, 25 %)", w,
                     oracle_budget=oracle_s if (D, bq, bk) == (128, 128, 128) else 0)
+    # route packing: KV blocks of 16 and 48 keys beside 64 (d128, 128-row Q blocks)
+    for bk in (16, 48, 64):
+        w = workloads.sparse_sweep(128, 128, bk)
+        batched(f"sweep d128 (128,{bk}) (B2 H16 S4096, 25 %; "
+                f"{'packed 64-key items' if bk % 64 else 'one block per item'})", w,
+                oracle_budget=oracle_s / 4 if bk == 16 else 0)
+    # GQA head packing: H 32 over H_kv 4, lists per KV head (shared by 8 Q heads)
+    w = workloads.gqa_sweep(128, 128, 128, Hkv=4, hrep=8, B=2, S=4096)
+    q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (w.q, w.k, w.v))
+    B, S, H, D = w.q.shape
+    mk, fk = (bsa.bsa_mask_to_index(torch.from_numpy(m.astype(np.uint8)).to(dev))
+              for m in (w.part, w.full))
+    rep = lambda m: np.repeat(m, H // w.full.shape[1], axis=1)
+    mq, fq = (bsa.bsa_mask_to_index(torch.from_numpy(rep(m).astype(np.uint8)).to(dev))
+              for m in (w.part, w.full))
+    run_pk = lambda **kw: bsa.bsa_fwd(q, k, v, mk, fk, 128, 128, bsa.MASK_CAUSAL, None, w.scale,
+                                      kv_head_lists=True, **kw)
+    run_un = lambda **kw: bsa.bsa_fwd(q, k, v, mq, fq, 128, 128, bsa.MASK_CAUSAL, None, w.scale,
+                                      **kw)
+    o1, l1 = run_pk()
+    o2, l2 = run_un()
+    ms_pk = _time_launches(torch, lambda: run_pk(out=o1, lse=l1))
+    ms_un = _time_launches(torch, lambda: run_un(out=o2, lse=l2))
+    fl = _pairs_flops(rep(w.full), rep(w.part), 128, 128, S, S, D)
+    err = _MaxErr()
+    if oracle_s > 0:
+        qo, ko, vo = (f64(t) for t in (q, k, v))
+        rng = np.random.default_rng(0)
+        for _ in range(4):
+            b, h, i = int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(S // 128))
+            O, L = oracle.blocksparse_attention(qo, ko, vo, rep(w.full), rep(w.part), 128, 128,
+                                                bsa.MASK_CAUSAL, w.scale, q_blocks=[(b, h, i)])
+            r = slice(i * 128, (i + 1) * 128)
+            err.note(o1[b, r, h], l1[b, h, r], O[b, r, h], L[b, h, r])
+    tag = f"B{B} H{H} over H_kv {w.full.shape[1]}, S{S} d{D}, 128x128, 25 %"
+    emit(f"GQA, lists per KV head, 2 Q heads packed per 256-row workgroup ({tag})", ms_pk, fl,
+         None, err)
+    emit(f"GQA, the same lists per Q head, unpacked ({tag})", ms_un, fl, None, _MaxErr())
     # backward on the d128 sweep workload: row dots, dQ and dK/dV kernels
     w = workloads.sparse_sweep(128, 128, 128)
     q, k, v = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (w.q, w.k, w.v))
