@@ -76,7 +76,7 @@ def blocksparse_attention_bwd(q, k, v, full, part, block_q: int, block_kv: int, 
             hk = h // (H // Hkv)
             Q, K, V, dO = q[b, :, h], k[b, :, hk], v[b, :, hk], dout[b, :, h]
             S = np.where(keep[b, h], scale * Q @ K.T, -np.inf)
-            m = S.max(axis=1, keepdims=True)
+            m = S.max(axis=1, keepdims=True, initial=-np.inf)  # Sk = 0: no key
             has = np.isfinite(m[:, 0])
             E = np.where(keep[b, h], np.exp(S - np.where(has[:, None], m, 0.0)), 0.0)
             den = E.sum(axis=1, keepdims=True)
@@ -96,3 +96,42 @@ def kv_major_lists(mask: np.ndarray):
     KV block: (cnt [B,H,N], idx [B,H,N,M]) with the Q-block ids that list it,
     in the order of mask_to_index (descending, then -1)."""
     return mask_to_index(np.swapaxes(np.asarray(mask), -1, -2))
+
+
+def varlen_blocksparse_attention_bwd(q, k, v, seqlens_q, seqlens_k, full, part, block_q: int,
+                                     block_kv: int, mask_mod: int, scale: float, dout,
+                                     kv_valid=None, window=None):
+    """Backward of the packed varlen forward (flash-attention PR #2224
+    layout): each sequence is its own batch-1 problem with sequence-local
+    row and key ids, so its gradients are those of blocksparse_attention_bwd
+    on its slices.  q, dout [Tq,H,D], k/v [Tk,Hkv,D]; full[b]/part[b] dense
+    block masks [H,M_b,N_b]; kv_valid as for the varlen forward (one shared
+    array, or one per sequence).  Returns dq [Tq,H,D], dk and dv [Tk,Hkv,D]."""
+    q, k, v, dout = (np.asarray(x, np.float64) for x in (q, k, v, dout))
+    cq = np.concatenate([[0], np.cumsum(seqlens_q)]).astype(np.int64)
+    ck = np.concatenate([[0], np.cumsum(seqlens_k)]).astype(np.int64)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    per_seq = kv_valid is not None and (isinstance(kv_valid, (list, tuple)) or
+                                        np.ndim(kv_valid) == 2)
+    for b in range(len(seqlens_q)):
+        kvb = np.asarray(kv_valid[b]) if per_seq else kv_valid
+        g = blocksparse_attention_bwd(q[None, cq[b]:cq[b + 1]], k[None, ck[b]:ck[b + 1]],
+                                      v[None, ck[b]:ck[b + 1]], full[b][None], part[b][None],
+                                      block_q, block_kv, mask_mod, scale,
+                                      dout[None, cq[b]:cq[b + 1]], kvb, window)
+        dq[cq[b]:cq[b + 1]] = g[0][0]
+        dk[ck[b]:ck[b + 1]] = g[1][0]
+        dv[ck[b]:ck[b + 1]] = g[2][0]
+    return dq, dk, dv
+
+
+def varlen_kv_major_lists(masks, seqlens_q, seqlens_k, block_q: int, block_kv: int):
+    """Per-sequence block masks [H,M_b,N_b] -> KV-major lists in the packed
+    varlen layout with the roles of Q and KV blocks swapped: cnt_t
+    [H, sum_b N_b] (row (b, j) at sum_{b'<b} N_b' + j) and idx_t
+    [H, sum_b M_b*N_b] (row (b, j) at offsets[b] + j*M_b, width M_b), holding
+    the sequence-local Q-block ids that list KV block j, descending, then -1.
+    The offsets sum M_b*N_b, the same as the forward's."""
+    from .metadata import pack_varlen_lists
+    return pack_varlen_lists([np.swapaxes(np.asarray(m), -1, -2) for m in masks],
+                             seqlens_k, seqlens_q, block_kv, block_q)
