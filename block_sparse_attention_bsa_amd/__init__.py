@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "MASK_NONE", "MASK_CAUSAL", "MASK_KV_VALID_COUNT", "MASK_LOCAL", "BsaError",
     "bsa_fwd", "bsa_varlen_fwd", "bsa_mask_to_index", "bsa_bitmask_to_index", "bsa_kv_major_lists",
-    "bsa_bwd", "bsa_bwd_noalloc",
+    "bsa_bwd", "bsa_bwd_noalloc", "bsa_varlen_bwd", "bsa_varlen_kv_major_lists",
     "bsa_varlen_mask_to_index",
     "bsa_varlen_offsets", "bsa_expand_kv_blocks", "bsa_block_sparsity", "bsa_status_str",
     "library_path", "load_library",
@@ -104,6 +104,10 @@ def load_library():
     lib.bsa_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
                                     P, P, P, P, P, P, P, ctypes.c_int, P, ctypes.c_float, P]
     lib.bsa_kv_major_lists.argtypes = [P, P, I32, I32, I32, I32, P, P, P, P]
+    lib.bsa_varlen_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32,
+                                   P, P, P, P, P, I32, I32, I32, P, P, P, P, P, P, P,
+                                   ctypes.c_int, P, ctypes.c_int64, ctypes.c_float, P, P]
+    lib.bsa_varlen_kv_major_lists.argtypes = [P, P, I32, I32, P, P, P, I32, I32, I32, P, P, P, P]
     lib.bsa_bitmask_to_index.argtypes = [P, I32, I32, I32, I32, I32, P, P, P]
     lib.bsa_varlen_mask_to_index.argtypes = [P, I32, I32, P, P, I32, I32, P, P, P]
     I32P = ctypes.POINTER(ctypes.c_int32)
@@ -114,6 +118,7 @@ def load_library():
     lib.bsa_status_str.restype = ctypes.c_char_p
     for fn in ("bsa_fwd", "bsa_varlen_fwd", "bsa_mask_to_index", "bsa_varlen_mask_to_index",
                "bsa_bwd", "bsa_bwd_noalloc", "bsa_kv_major_lists", "bsa_bitmask_to_index",
+               "bsa_varlen_bwd", "bsa_varlen_kv_major_lists",
                "bsa_varlen_offsets", "bsa_expand_kv_blocks", "bsa_block_sparsity"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -436,6 +441,122 @@ def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         st = lib.bsa_bwd(*args, _ptr(work), _stream(q))
         _check("bsa_bwd", st)
     return dq, dk, dv
+
+
+def bsa_varlen_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                   lse: torch.Tensor, dout: torch.Tensor,
+                   cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                   cu_total_m_blocks: torch.Tensor, cu_total_kv_blocks: torch.Tensor,
+                   block_idx_offsets: torch.Tensor, total_m_blocks: int, total_kv_blocks: int,
+                   total_n_blocks: int,
+                   mask_list: Optional[Tuple[torch.Tensor, torch.Tensor]],
+                   full_list: Optional[Tuple[torch.Tensor, torch.Tensor]],
+                   block_q: int, block_kv: int, mask_mod: int = MASK_NONE,
+                   kv_valid: Optional[torch.Tensor] = None,
+                   softmax_scale: Optional[float] = None,
+                   window: Optional[Tuple[int, int]] = None):
+    """Backward of bsa_varlen_fwd (bf16): returns (dq [Tq,H,D], dk, dv [Tk,Hkv,D]).
+    o and lse [H,Tq] are the forward's outputs, dout the gradient of o; the cu
+    arrays, totals, lists (cnt [H,total_m_blocks], idx [H,total_n_blocks]),
+    block sizes, mask_mod, kv_valid ([B, W] or [W]), scale and window are the
+    forward's.  cu_total_kv_blocks (int32 [B+1] on the device) and
+    total_kv_blocks count the KV blocks per sequence (bsa_varlen_offsets with
+    the Q and KV roles swapped gives them).  The KV-major lists are built here
+    with bsa_varlen_kv_major_lists."""
+    lib = load_library()
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _dev(n, t, torch.bfloat16)
+        if t.dim() != 3 or t.stride(-1) != 1:
+            raise ValueError(f"{n} must be 3-D [tokens,heads,D] with a contiguous last dimension")
+    _dev("lse", lse, torch.float32)
+    cus = (cu_seqlens_q, cu_seqlens_k, cu_total_m_blocks, cu_total_kv_blocks, block_idx_offsets)
+    for n, t in zip(("cu_seqlens_q", "cu_seqlens_k", "cu_total_m_blocks", "cu_total_kv_blocks",
+                     "block_idx_offsets"), cus):
+        _dev(n, t, torch.int32)
+        if t.dim() != 1 or not t.is_contiguous():
+            raise ValueError(f"{n} must be a contiguous 1-D int32 tensor")
+    B = cu_seqlens_q.numel() - 1
+    if any(t.numel() != B + 1 for t in cus):
+        raise ValueError("cu arrays must all have B+1 entries")
+    Tq, H, D = q.shape
+    Tk, Hkv, Dk = k.shape
+    if Dk != D or tuple(v.shape) != tuple(k.shape) or o.shape != q.shape \
+            or dout.shape != q.shape or tuple(lse.shape) != (H, Tq) or not lse.is_contiguous():
+        raise ValueError("shapes: q/o/dout [Tq,H,D], k/v [Tk,Hkv,D], lse [H,Tq]")
+    if dout.stride() != o.stride():
+        o, dout = o.contiguous(), dout.contiguous()
+    tm, tkv, tn = int(total_m_blocks), int(total_kv_blocks), int(total_n_blocks)
+
+    def transposed(lst):
+        if lst is None:
+            return None
+        cnt, idx = (x.expand(H, x.shape[1]).contiguous() for x in lst)
+        return (cnt, idx), bsa_varlen_kv_major_lists((cnt, idx), cu_total_m_blocks,
+                                                     cu_total_kv_blocks, block_idx_offsets,
+                                                     tm, tkv)
+    mp, fp = transposed(mask_list), transposed(full_list)
+    ml, mt = mp if mp is not None else (None, None)
+    fl, ft = fp if fp is not None else (None, None)
+    bs = _BlockSparse(_block_list(ml, False, (H, tm, tn)), _block_list(fl, False, (H, tm, tn)),
+                      int(block_q), int(block_kv), *_window(mask_mod, window))
+    lt_m = _block_list(mt, False, (H, tkv, tn))
+    lt_f = _block_list(ft, False, (H, tkv, tn))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
+        raise ValueError("q, k and v must be dense (their gradients take their strides)")
+    work = torch.empty(max(H * Tq, 1), dtype=torch.float32, device=q.device)
+    kvv_ld = 0
+    if kv_valid is not None:
+        _dev("kv_valid", kv_valid, torch.int32)
+        if kv_valid.dim() not in (1, 2) or kv_valid.stride(-1) != 1 or \
+                (kv_valid.dim() == 2 and kv_valid.shape[0] != B):
+            raise ValueError("kv_valid must be int32 [B, W] or [W] with a contiguous last dimension")
+        kvv_ld = kv_valid.stride(0) if kv_valid.dim() == 2 else 0
+    elif mask_mod == MASK_KV_VALID_COUNT and mask_list is not None:
+        raise ValueError("MASK_KV_VALID_COUNT needs kv_valid")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    st = lib.bsa_varlen_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                            _ptr(dk), _ptr(dv), B, H, Hkv, D, *(_ptr(t) for t in cus[:4]),
+                            _ptr(block_idx_offsets), tm, tkv, Tq,
+                            _i64([q.stride(0), q.stride(1)]), _i64([k.stride(0), k.stride(1)]),
+                            _i64([v.stride(0), v.stride(1)]), _i64([o.stride(0), o.stride(1)]),
+                            ctypes.byref(bs), ctypes.byref(lt_m), ctypes.byref(lt_f),
+                            int(mask_mod), _ptr(kv_valid), int(kvv_ld), scale, _ptr(work),
+                            _stream(q))
+    _check("bsa_varlen_bwd", st)
+    return dq, dk, dv
+
+
+def bsa_varlen_kv_major_lists(lists: Tuple[torch.Tensor, torch.Tensor],
+                              cu_total_m_blocks: torch.Tensor, cu_total_kv_blocks: torch.Tensor,
+                              block_idx_offsets: torch.Tensor, total_m_blocks: int,
+                              total_kv_blocks: int):
+    """Packed varlen lists (cnt int32 [H,total_m_blocks], idx int32
+    [H,total_n_blocks], contiguous) -> KV-major lists (cnt_t int32
+    [H,total_kv_blocks], idx_t int32 [H,total_n_blocks]; row (b, j) at
+    block_idx_offsets[b] + j*num_m(b)): per KV block of each sequence, its
+    Q blocks that list it, descending, then -1."""
+    lib = load_library()
+    cnt, idx = lists
+    _dev("cnt", cnt, torch.int32)
+    _dev("idx", idx, torch.int32)
+    if cnt.dim() != 2 or idx.dim() != 2 or cnt.shape[0] != idx.shape[0] or \
+            cnt.shape[1] != total_m_blocks or not cnt.is_contiguous() or not idx.is_contiguous():
+        raise ValueError("lists must be contiguous int32 [H,total_m_blocks] / [H,total_n_blocks]")
+    for n, t in (("cu_total_m_blocks", cu_total_m_blocks), ("cu_total_kv_blocks", cu_total_kv_blocks),
+                 ("block_idx_offsets", block_idx_offsets)):
+        _dev(n, t, torch.int32)
+    H, tn = idx.shape
+    B = cu_total_m_blocks.numel() - 1
+    work = torch.empty((H, tn), dtype=torch.uint8, device=idx.device)
+    cnt_t = torch.empty((H, int(total_kv_blocks)), dtype=torch.int32, device=idx.device)
+    idx_t = torch.empty((H, tn), dtype=torch.int32, device=idx.device)
+    st = lib.bsa_varlen_kv_major_lists(_ptr(cnt), _ptr(idx), H, B, _ptr(cu_total_m_blocks),
+                                       _ptr(cu_total_kv_blocks), _ptr(block_idx_offsets),
+                                       int(total_m_blocks), int(total_kv_blocks), tn, _ptr(work),
+                                       _ptr(cnt_t), _ptr(idx_t), _stream(idx))
+    _check("bsa_varlen_kv_major_lists", st)
+    return cnt_t, idx_t
 
 
 def bsa_kv_major_lists(lists: Tuple[torch.Tensor, torch.Tensor]):

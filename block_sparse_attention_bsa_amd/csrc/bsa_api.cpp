@@ -556,6 +556,101 @@ bsa_status bsa_bwd_noalloc(const void* q, const void* k, const void* v, const vo
                   stream);
 }
 
+bsa_status bsa_varlen_bwd(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                          int32_t B, int32_t H, int32_t H_kv, int32_t D,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          const int32_t* cu_total_m_blocks, const int32_t* cu_total_kv_blocks,
+                          const int32_t* block_idx_offsets, int32_t total_m_blocks,
+                          int32_t total_kv_blocks, int32_t total_q, const int64_t q_str[2],
+                          const int64_t k_str[2], const int64_t v_str[2], const int64_t o_str[2],
+                          const bsa_block_sparse* bs, const bsa_block_list* mask_t,
+                          const bsa_block_list* full_t, bsa_mask_mod mask_mod,
+                          const int32_t* kv_valid, int64_t kv_valid_ld, float softmax_scale,
+                          float* work, hipStream_t stream) {
+  if (B < 0 || H <= 0 || H_kv <= 0 || H % H_kv != 0 || total_m_blocks < 0 ||
+      total_kv_blocks < 0 || total_q < 0 || kv_valid_ld < 0)
+    return BSA_ERR_INVALID_ARGUMENT;
+  if (mask_mod < BSA_MASK_NONE || mask_mod > BSA_MASK_LOCAL) return BSA_ERR_INVALID_ARGUMENT;
+  if (!bs || !mask_t || !full_t || !q_str || !k_str || !v_str || !o_str)
+    return BSA_ERR_INVALID_ARGUMENT;
+  if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f)) return BSA_ERR_INVALID_ARGUMENT;
+  if (bs->block_q <= 0 || bs->block_kv <= 0) return BSA_ERR_INVALID_ARGUMENT;
+  if (!list_ok(bs->mask) || !list_ok(bs->full) || !list_ok(*mask_t) || !list_ok(*full_t))
+    return BSA_ERR_INVALID_ARGUMENT;
+  if (!supported_head_dim(D)) return BSA_ERR_UNSUPPORTED;
+  if (bs->proxy_k || bs->proxy_v) return BSA_ERR_UNSUPPORTED;
+  if (B == 0 || (int64_t)total_m_blocks + total_kv_blocks == 0) return BSA_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !work || !cu_seqlens_q ||
+      !cu_seqlens_k || !cu_total_m_blocks || !cu_total_kv_blocks || !block_idx_offsets)
+    return BSA_ERR_INVALID_ARGUMENT;
+  if (mask_mod == BSA_MASK_KV_VALID_COUNT && !kv_valid && (bs->mask.cnt || mask_t->cnt))
+    return BSA_ERR_INVALID_ARGUMENT;
+  for (const void* ptr : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned16(ptr)) return BSA_ERR_MISALIGNED;
+  if (!strides_ok(q_str, 2, 2) || !strides_ok(k_str, 2, 2) || !strides_ok(v_str, 2, 2) ||
+      !strides_ok(o_str, 2, 2))
+    return BSA_ERR_MISALIGNED;
+  const int64_t gq = (int64_t)H * total_m_blocks * cdiv64(bs->block_q, 64);
+  const int64_t gk = (int64_t)H_kv * total_kv_blocks * cdiv64(bs->block_kv, 64);
+  if (gq > std::numeric_limits<int32_t>::max() || gk > std::numeric_limits<int32_t>::max())
+    return BSA_ERR_UNSUPPORTED;
+  bsa::BwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse; p.drow = work;
+  p.dq = dq; p.dk = dk; p.dv = dv;
+  // token-major layouts: no batch stride, the sequence start moves the base
+  p.q_ss = q_str[0]; p.q_sh = q_str[1];
+  p.k_ss = k_str[0]; p.k_sh = k_str[1];
+  p.v_ss = v_str[0]; p.v_sh = v_str[1];
+  p.o_ss = o_str[0]; p.o_sh = o_str[1];
+  p.do_ss = o_str[0]; p.do_sh = o_str[1];
+  p.dq_ss = q_str[0]; p.dq_sh = q_str[1];
+  p.dk_ss = k_str[0]; p.dk_sh = k_str[1];
+  p.dv_ss = v_str[0]; p.dv_sh = v_str[1];
+  p.mcnt = bs->mask.cnt; p.midx = bs->mask.idx; p.fcnt = bs->full.cnt; p.fidx = bs->full.idx;
+  p.tmcnt = mask_t->cnt; p.tmidx = mask_t->idx; p.tfcnt = full_t->cnt; p.tfidx = full_t->idx;
+  for (int i = 0; i < 3; ++i) {
+    p.mc_s[i] = bs->mask.cnt_stride[i]; p.fc_s[i] = bs->full.cnt_stride[i];
+    p.tmc_s[i] = mask_t->cnt_stride[i]; p.tfc_s[i] = full_t->cnt_stride[i];
+  }
+  for (int i = 0; i < 4; ++i) {
+    p.mi_s[i] = bs->mask.idx_stride[i]; p.fi_s[i] = bs->full.idx_stride[i];
+    p.tmi_s[i] = mask_t->idx_stride[i]; p.tfi_s[i] = full_t->idx_stride[i];
+  }
+  p.kv_valid = mask_mod == BSA_MASK_KV_VALID_COUNT ? kv_valid : nullptr;
+  p.kvv_ld = kv_valid_ld;
+  p.B = B; p.H = H; p.hrep = H / H_kv; p.Sq = total_q; p.Sk = 0;
+  p.M = total_m_blocks; p.N = total_kv_blocks;
+  p.block_q = bs->block_q; p.block_kv = bs->block_kv; p.mask_mod = mask_mod;
+  p.win_left = bs->window_left; p.win_right = bs->window_right;
+  p.c = softmax_scale * kLog2e;
+  p.scale = softmax_scale;
+  p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k; p.cu_m = cu_total_m_blocks;
+  p.cu_n = cu_total_kv_blocks; p.boff = block_idx_offsets;
+  p.varlen = true;
+  const hipError_t e = bsa::launch_bwd(p, D, stream);
+  return e == hipSuccess ? BSA_OK : BSA_ERR_HIP;
+}
+
+bsa_status bsa_varlen_kv_major_lists(const int32_t* cnt, const int32_t* idx, int32_t H, int32_t B,
+                                     const int32_t* cu_total_m_blocks,
+                                     const int32_t* cu_total_kv_blocks,
+                                     const int32_t* block_idx_offsets, int32_t total_m_blocks,
+                                     int32_t total_kv_blocks, int32_t total_n_blocks,
+                                     uint8_t* work, int32_t* cnt_t, int32_t* idx_t,
+                                     hipStream_t stream) {
+  if (H < 0 || B < 0 || total_m_blocks < 0 || total_kv_blocks < 0 || total_n_blocks < 0)
+    return BSA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)H * total_kv_blocks == 0 || B == 0) return BSA_OK;
+  if (!cnt_t || !cu_total_m_blocks || !cu_total_kv_blocks || !block_idx_offsets)
+    return BSA_ERR_INVALID_ARGUMENT;
+  if (total_n_blocks > 0 && (!cnt || !idx || !work || !idx_t)) return BSA_ERR_INVALID_ARGUMENT;
+  const hipError_t e = bsa::launch_varlen_kv_major_lists(
+      cnt, idx, H, B, cu_total_m_blocks, cu_total_kv_blocks, block_idx_offsets, total_m_blocks,
+      total_kv_blocks, total_n_blocks, work, cnt_t, idx_t, stream);
+  return e == hipSuccess ? BSA_OK : BSA_ERR_HIP;
+}
+
 bsa_status bsa_kv_major_lists(const int32_t* cnt, const int32_t* idx, int32_t B, int32_t H,
                               int32_t M, int32_t N, uint8_t* work, int32_t* cnt_t,
                               int32_t* idx_t, hipStream_t stream) {

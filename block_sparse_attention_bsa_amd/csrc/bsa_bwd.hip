@@ -49,11 +49,13 @@ __device__ __forceinline__ uint32_t word4(const uint4& v, int i) {
 }
 
 // Element rule of a mask-list block (row and key are sequence positions;
-// kib is the key's offset inside its KV block j).
-__device__ __forceinline__ bool keep_elem(const BwdParams& p, int row, int key, int j, int kib) {
+// kib is the key's offset inside its KV block j; kvv the sequence's
+// valid counts).
+__device__ __forceinline__ bool keep_elem(const BwdParams& p, const int32_t* kvv, int row, int key,
+                                          int j, int kib) {
   switch (p.mask_mod) {
     case kMaskCausal: return key <= row;
-    case kMaskKvValid: return kib < p.kv_valid[j];
+    case kMaskKvValid: return kib < kvv[j];
     case kMaskLocal:
       return (p.win_left < 0 || row - key <= p.win_left) &&
              (p.win_right < 0 || key - row <= p.win_right);
@@ -119,6 +121,58 @@ struct Stage {
     }
   }
 };
+
+// Largest b < B with cu[b] <= x (cu: B+1 nondecreasing prefix sums), i.e.
+// the sequence of packed block x.  Wave-uniform.
+__device__ __forceinline__ int seq_of(const int32_t* cu, int B, int x) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= x)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+// One sequence's view for a workgroup: token starts of its Q rows and keys,
+// its lengths and block counts, the index of its valid counts.  Batched:
+// sequence b of the batch (starts 0, lengths Sq and Sk).  Packed varlen:
+// sequence b of the pack, found from the workgroup's global block id.
+struct SeqView {
+  int b;
+  int tq0, tk0;  // token starts (varlen) or 0
+  int Sq, Sk, M, N;
+  int64_t slot0;  // varlen: list-slot offset of the sequence
+  const int32_t* kvv;
+};
+
+template <bool VL>
+__device__ __forceinline__ SeqView seq_view(const BwdParams& p, int b) {
+  SeqView v;
+  v.b = b;
+  if constexpr (VL) {
+    v.tq0 = p.cu_q[b];
+    v.tk0 = p.cu_k[b];
+    v.Sq = p.cu_q[b + 1] - v.tq0;
+    v.Sk = p.cu_k[b + 1] - v.tk0;
+    v.M = p.cu_m[b + 1] - p.cu_m[b];
+    v.N = p.cu_n[b + 1] - p.cu_n[b];
+    v.slot0 = p.boff[b];
+    v.kvv = p.kv_valid ? p.kv_valid + (int64_t)b * p.kvv_ld : nullptr;
+  } else {
+    v.tq0 = 0;
+    v.tk0 = 0;
+    v.Sq = p.Sq;
+    v.Sk = p.Sk;
+    v.M = p.M;
+    v.N = p.N;
+    v.slot0 = 0;
+    v.kvv = p.kv_valid;
+  }
+  return v;
+}
 
 // The sub-tiles of one walk, in order: for each list (mask, then full), for
 // each listed block id, the block's positions [id*blen, min((id+1)*blen, S))
@@ -261,7 +315,7 @@ __device__ __forceinline__ float lse2_of(float lse) {
   return lse == neg_inf() ? __builtin_inff() : lse * 1.4426950408889634f;  // log2(e)
 }
 
-template <int D, int NW>
+template <int D, int NW, bool VL>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))  // two waves per SIMD up to d = 128
 void bwd_dq_kernel(const BwdParams p) {
@@ -277,25 +331,34 @@ void bwd_dq_kernel(const BwdParams p) {
   int t = blockIdx.x;
   const int s = t % qsub;
   t /= qsub;
-  const int i = t % p.M;
+  // mrow: the list row (batched: Q block i; varlen: global Q block id)
+  const int mrow = t % p.M;
   t /= p.M;
-  const int h = t % p.H, b = t / p.H, hk = h / p.hrep;
+  const int h = VL ? t : t % p.H, hk = h / p.hrep;
+  const SeqView sv0 = seq_view<VL>(p, VL ? seq_of(p.cu_m, p.B, mrow) : t / p.H);
+  const int b = sv0.b;
+  const int i = VL ? mrow - p.cu_m[b] : mrow;
   const int r0 = i * p.block_q + s * TW;
-  const int rend = min((i + 1) * p.block_q, p.Sq);
+  const int rend = min((i + 1) * p.block_q, sv0.Sq);
   if (r0 >= rend) return;
-  const int row = r0 + 32 * w + l32;
+  const int row = r0 + 32 * w + l32;  // sequence-local
   const bool rvalid = row < rend;
 
-  const __bf16* qrow = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sb + (int64_t)row * p.q_ss + h * p.q_sh;
-  const __bf16* grow = reinterpret_cast<const __bf16*>(p.dout) + b * p.do_sb + (int64_t)row * p.do_ss + h * p.do_sh;
+  // VL: batch strides are 0 and the token start moves the base
+  const int64_t qtok = (int64_t)sv0.tq0 + row;
+  const __bf16* qrow = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sb + qtok * p.q_ss + h * p.q_sh;
+  const __bf16* grow = reinterpret_cast<const __bf16*>(p.dout) + b * p.do_sb + qtok * p.do_ss + h * p.do_sh;
   uint4 qf[DS], gf[DS];
   row_frags<D>(qrow, rvalid, h32, qf);
   row_frags<D>(grow, rvalid, h32, gf);
-  const int64_t lrow = ((int64_t)b * p.H + h) * p.Sq + row;
+  // LSE and row dots: [B,H,Sq], or [H,total_q] for varlen (Sq = total_q)
+  const int64_t lrow = VL ? (int64_t)h * p.Sq + qtok : ((int64_t)b * p.H + h) * p.Sq + row;
   const float lse2 = rvalid ? lse2_of(p.lse[lrow]) : __builtin_inff();
   const float drow = rvalid ? p.drow[lrow] : 0.f;
-  const __bf16* kb0 = reinterpret_cast<const __bf16*>(p.k) + b * p.k_sb + hk * p.k_sh;
-  const __bf16* vb0 = reinterpret_cast<const __bf16*>(p.v) + b * p.v_sb + hk * p.v_sh;
+  const __bf16* kb0 = reinterpret_cast<const __bf16*>(p.k) + b * p.k_sb +
+                      (int64_t)sv0.tk0 * p.k_ss + hk * p.k_sh;
+  const __bf16* vb0 = reinterpret_cast<const __bf16*>(p.v) + b * p.v_sb +
+                      (int64_t)sv0.tk0 * p.v_ss + hk * p.v_sh;
 
   f32x16_t acc[DB];
 #pragma unroll
@@ -309,18 +372,23 @@ void bwd_dq_kernel(const BwdParams p) {
     const int32_t* cntp = list == 0 ? p.mcnt : p.fcnt;
     const int64_t* cs = list == 0 ? p.mc_s : p.fc_s;
     const int64_t* is = list == 0 ? p.mi_s : p.fi_s;
-    const int c = cntp ? min(max(cntp[b * cs[0] + h * cs[1] + i * cs[2]], 0), p.N) : 0;
+    const int c = cntp ? min(max(cntp[VL ? h * cs[1] + mrow * cs[2]
+                                        : b * cs[0] + h * cs[1] + i * cs[2]], 0), sv0.N)
+                       : 0;
     const int32_t* ip =
-        cntp ? (list == 0 ? p.midx : p.fidx) + b * is[0] + h * is[1] + i * is[2] : nullptr;
+        cntp ? (list == 0 ? p.midx : p.fidx) +
+                   (VL ? h * is[1] + (sv0.slot0 + (int64_t)i * sv0.N) * is[3]
+                       : b * is[0] + h * is[1] + i * is[2])
+             : nullptr;
     if (list == 0) {
       W.cnt0 = c; W.idx0 = ip; W.istep0 = is[3];
     } else {
       W.cnt1 = c; W.idx1 = ip; W.istep1 = is[3];
     }
   }
-  W.nmax = p.N;
+  W.nmax = sv0.N;
   W.blen = p.block_kv;
-  W.S = p.Sk;
+  W.S = sv0.Sk;
   Stage<D, NT> sk, sv;
   bool have = W.first();
   if (have) {
@@ -354,7 +422,8 @@ void bwd_dq_kernel(const BwdParams p) {
           const f32x16_t& dv_ = y < 2 ? d0 : d1;
           const int key = 16 * (reg >> 3) + 8 * h32 + (reg & 7) + (y < 2 ? 0 : 32);
           bool keep = key < nk;
-          if (keep && list == 0) keep = keep_elem(p, row, k0 + key, j, k0 + key - j * p.block_kv);
+          if (keep && list == 0)
+            keep = keep_elem(p, sv0.kvv, row, k0 + key, j, k0 + key - j * p.block_kv);
           const float pr = keep ? __builtin_amdgcn_exp2f(fmaf(sv_[reg], p.c, -lse2)) : 0.f;
           v[y] = pr * (dv_[reg] - drow);
         }
@@ -372,12 +441,12 @@ void bwd_dq_kernel(const BwdParams p) {
     have = more;
   }
   if (rvalid) {
-    __bf16* dst = reinterpret_cast<__bf16*>(p.dq) + b * p.dq_sb + (int64_t)row * p.dq_ss + h * p.dq_sh;
+    __bf16* dst = reinterpret_cast<__bf16*>(p.dq) + b * p.dq_sb + qtok * p.dq_ss + h * p.dq_sh;
     store_row<DB>(dst, h32, acc, p.scale);
   }
 }
 
-template <int D, int NW>
+template <int D, int NW, bool VL>
 __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BwdParams p) {
   constexpr int NT = NW * 64, TW = NW * 32;
   constexpr int DS = D / 16, DB = D / 32;
@@ -393,18 +462,23 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BwdParams p) {
   int t = blockIdx.x;
   const int s = t % ksub;
   t /= ksub;
-  const int j = t % p.N;
+  // nrow: the KV-major list row (batched: KV block j; varlen: global KV block id)
+  const int nrow = t % p.N;
   t /= p.N;
   const int Hkv = p.H / p.hrep;
-  const int hk = t % Hkv, b = t / Hkv;
+  const int hk = VL ? t : t % Hkv;
+  const SeqView sv0 = seq_view<VL>(p, VL ? seq_of(p.cu_n, p.B, nrow) : t / Hkv);
+  const int b = sv0.b;
+  const int j = VL ? nrow - p.cu_n[b] : nrow;
   const int k0 = j * p.block_kv + s * TW;
-  const int kend = min((j + 1) * p.block_kv, p.Sk);
+  const int kend = min((j + 1) * p.block_kv, sv0.Sk);
   if (k0 >= kend) return;
-  const int key = k0 + 32 * w + l32;
+  const int key = k0 + 32 * w + l32;  // sequence-local
   const bool kvalid = key < kend;
 
-  const __bf16* krow = reinterpret_cast<const __bf16*>(p.k) + b * p.k_sb + (int64_t)key * p.k_ss + hk * p.k_sh;
-  const __bf16* vrow = reinterpret_cast<const __bf16*>(p.v) + b * p.v_sb + (int64_t)key * p.v_ss + hk * p.v_sh;
+  const int64_t ktok = (int64_t)sv0.tk0 + key;
+  const __bf16* krow = reinterpret_cast<const __bf16*>(p.k) + b * p.k_sb + ktok * p.k_ss + hk * p.k_sh;
+  const __bf16* vrow = reinterpret_cast<const __bf16*>(p.v) + b * p.v_sb + ktok * p.v_ss + hk * p.v_sh;
   uint4 kf[DS], vf[DS];
   row_frags<D>(krow, kvalid, h32, kf);
   row_frags<D>(vrow, kvalid, h32, vf);
@@ -420,26 +494,34 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BwdParams p) {
   const int arow = swap_b23(l32);
 
   for (int h = hk * p.hrep; h < (hk + 1) * p.hrep; ++h) {
-    const __bf16* qb0 = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh;
-    const __bf16* gb0 = reinterpret_cast<const __bf16*>(p.dout) + b * p.do_sb + h * p.do_sh;
-    const int64_t lbase = ((int64_t)b * p.H + h) * p.Sq;
+    const __bf16* qb0 = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sb +
+                        (int64_t)sv0.tq0 * p.q_ss + h * p.q_sh;
+    const __bf16* gb0 = reinterpret_cast<const __bf16*>(p.dout) + b * p.do_sb +
+                        (int64_t)sv0.tq0 * p.do_ss + h * p.do_sh;
+    // row r of the sequence at lbase + r in the LSE and row dots
+    const int64_t lbase = VL ? (int64_t)h * p.Sq + sv0.tq0 : ((int64_t)b * p.H + h) * p.Sq;
     SubWalk W{};
     for (int list = 0; list < 2; ++list) {
       const int32_t* cntp = list == 0 ? p.tmcnt : p.tfcnt;
       const int64_t* cs = list == 0 ? p.tmc_s : p.tfc_s;
       const int64_t* is = list == 0 ? p.tmi_s : p.tfi_s;
-      const int c = cntp ? min(max(cntp[b * cs[0] + h * cs[1] + j * cs[2]], 0), p.M) : 0;
+      const int c = cntp ? min(max(cntp[VL ? h * cs[1] + nrow * cs[2]
+                                          : b * cs[0] + h * cs[1] + j * cs[2]], 0), sv0.M)
+                         : 0;
       const int32_t* ip =
-          cntp ? (list == 0 ? p.tmidx : p.tfidx) + b * is[0] + h * is[1] + j * is[2] : nullptr;
+          cntp ? (list == 0 ? p.tmidx : p.tfidx) +
+                     (VL ? h * is[1] + (sv0.slot0 + (int64_t)j * sv0.M) * is[3]
+                         : b * is[0] + h * is[1] + j * is[2])
+               : nullptr;
       if (list == 0) {
         W.cnt0 = c; W.idx0 = ip; W.istep0 = is[3];
       } else {
         W.cnt1 = c; W.idx1 = ip; W.istep1 = is[3];
       }
     }
-    W.nmax = p.M;
+    W.nmax = sv0.M;
     W.blen = p.block_q;
-    W.S = p.Sq;
+    W.S = sv0.Sq;
     Stage<D, NT> sq, sg;
     float l2n = 0.f, drn = 0.f;  // this thread's row (tid < 64) of the next sub-tile
     auto load = [&]() {
@@ -484,7 +566,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BwdParams p) {
           const f32x16_t& gv = y < 2 ? d0 : d1;
           const int rl = 16 * (reg >> 3) + 8 * h32 + (reg & 7) + (y < 2 ? 0 : 32);
           bool keep = kvalid && rl < nr;
-          if (keep && list == 0) keep = keep_elem(p, r0 + rl, key, j, key - j * p.block_kv);
+          if (keep && list == 0)
+            keep = keep_elem(p, sv0.kvv, r0 + rl, key, j, key - j * p.block_kv);
           const float pr = keep ? __builtin_amdgcn_exp2f(fmaf(sv[reg], p.c, -lse2s[rl])) : 0.f;
           pv[y] = pr;
           dsv[y] = pr * (gv[reg] - drows[rl]);
@@ -504,36 +587,47 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BwdParams p) {
   }
 
   if (kvalid) {
-    __bf16* kdst = reinterpret_cast<__bf16*>(p.dk) + b * p.dk_sb + (int64_t)key * p.dk_ss + hk * p.dk_sh;
-    __bf16* vdst = reinterpret_cast<__bf16*>(p.dv) + b * p.dv_sb + (int64_t)key * p.dv_ss + hk * p.dv_sh;
+    __bf16* kdst = reinterpret_cast<__bf16*>(p.dk) + b * p.dk_sb + ktok * p.dk_ss + hk * p.dk_sh;
+    __bf16* vdst = reinterpret_cast<__bf16*>(p.dv) + b * p.dv_sb + ktok * p.dv_ss + hk * p.dv_sh;
     store_row<DB>(kdst, h32, dk, p.scale);
     store_row<DB>(vdst, h32, dv, 1.f);
   }
 }
 
-template <int D>
-hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
-  const int64_t rows = (int64_t)p.B * p.H * p.Sq;
+template <int D, bool VL>
+hipError_t launch_bwd_dv(const BwdParams& p, hipStream_t st) {
+  // varlen: the row dots run over [H, total_q] as one sequence of Sq rows
+  const int64_t rows = (VL ? 1 : (int64_t)p.B) * p.H * p.Sq;
   if (rows > 0) {
-    hipLaunchKernelGGL(bwd_rowdot_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, st, p);
+    BwdParams pr = p;
+    if (VL) pr.B = 1;
+    hipLaunchKernelGGL(bwd_rowdot_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                       st, pr);
   }
+  // batched: B*H*M Q-block rows and B*H_kv*N KV-block rows; varlen: the
+  // M and N totals over the sequences carry the batch
+  const int64_t nb = VL ? 1 : p.B;
   const int nwq = p.block_q % 128 == 0 ? 4 : 2, nwk = p.block_kv % 128 == 0 ? 4 : 2;
-  const int64_t gq = (int64_t)p.B * p.H * p.M * ((p.block_q + 32 * nwq - 1) / (32 * nwq));
-  const int64_t gk =
-      (int64_t)p.B * (p.H / p.hrep) * p.N * ((p.block_kv + 32 * nwk - 1) / (32 * nwk));
+  const int64_t gq = nb * p.H * p.M * ((p.block_q + 32 * nwq - 1) / (32 * nwq));
+  const int64_t gk = nb * (p.H / p.hrep) * p.N * ((p.block_kv + 32 * nwk - 1) / (32 * nwk));
   if (gq > 0) {
     if (nwq == 4)
-      hipLaunchKernelGGL((bwd_dq_kernel<D, 4>), dim3((unsigned)gq), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, 4, VL>), dim3((unsigned)gq), dim3(256), 0, st, p);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<D, 2>), dim3((unsigned)gq), dim3(128), 0, st, p);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, 2, VL>), dim3((unsigned)gq), dim3(128), 0, st, p);
   }
   if (gk > 0) {
     if (nwk == 4)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, 4>), dim3((unsigned)gk), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, 4, VL>), dim3((unsigned)gk), dim3(256), 0, st, p);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, 2>), dim3((unsigned)gk), dim3(128), 0, st, p);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, 2, VL>), dim3((unsigned)gk), dim3(128), 0, st, p);
   }
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
+  return p.varlen ? launch_bwd_dv<D, true>(p, st) : launch_bwd_dv<D, false>(p, st);
 }
 
 }  // namespace

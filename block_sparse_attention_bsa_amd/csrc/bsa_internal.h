@@ -100,6 +100,17 @@ struct BwdParams {
   int32_t B, H, hrep, Sq, Sk, M, N, block_q, block_kv, mask_mod, win_left, win_right;
   float c;      // softmax_scale * log2(e)
   float scale;  // softmax_scale
+  // Packed varlen layout (the varlen kernel instances): B sequences, Sq =
+  // total Q tokens (the LSE row length), M = total Q blocks, N = total KV
+  // blocks; per-sequence token starts, block prefix sums and list-slot
+  // offsets (sum of M_b*N_b); kv_valid row b at kv_valid + b*kvv_ld.
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* cu_m;
+  const int32_t* cu_n;
+  const int32_t* boff;
+  int64_t kvv_ld;
+  bool varlen;
 };
 hipError_t launch_bwd(const BwdParams& p, int D, hipStream_t s);
 // Rows (B*H*Sq) the allocation-free backward's static row-dot array holds.
@@ -111,6 +122,11 @@ hipError_t bwd_noalloc_scratch(float** out);
 hipError_t launch_kv_major_lists(const int32_t* cnt, const int32_t* idx, int32_t B, int32_t H,
                                  int32_t M, int32_t N, uint8_t* work, int32_t* cnt_t,
                                  int32_t* idx_t, hipStream_t s);
+hipError_t launch_varlen_kv_major_lists(const int32_t* cnt, const int32_t* idx, int32_t H,
+                                        int32_t B, const int32_t* cu_m, const int32_t* cu_n,
+                                        const int32_t* off, int32_t total_m, int32_t total_kv,
+                                        int32_t total_n, uint8_t* work, int32_t* cnt_t,
+                                        int32_t* idx_t, hipStream_t s);
 hipError_t launch_bitmask_to_index(const uint32_t* words, int32_t B, int32_t Hkv, int32_t H,
                                   int32_t M, int32_t N, int32_t* cnt, int32_t* idx, hipStream_t s);
 hipError_t launch_mask_to_index(const uint8_t* mask, int64_t rows, int32_t N,

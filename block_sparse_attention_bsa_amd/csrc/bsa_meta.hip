@@ -238,6 +238,56 @@ hipError_t launch_kv_major_lists(const int32_t* cnt, const int32_t* idx, int32_t
   return launch_mask_to_index(work, (int64_t)B * H * N, M, cnt_t, idx_t, s);
 }
 
+// Varlen KV-major transposition: one thread per (head, list slot p) of the
+// forward's packed lists; slot p of sequence b's Q-block row i (p = off[b] +
+// i*N_b + s) that holds a listed KV block j marks cell (j, i) of the
+// transposed row layout, at off[b] + j*M_b + i.
+__global__ __launch_bounds__(256) void varlen_scatter_transposed_kernel(
+    const int32_t* __restrict__ cnt, const int32_t* __restrict__ idx, int32_t H, int32_t B,
+    const int32_t* __restrict__ cu_m, const int32_t* __restrict__ cu_n,
+    const int32_t* __restrict__ off, int32_t total_m, int32_t total_n, uint8_t* __restrict__ mt) {
+  const int64_t total = (int64_t)H * total_n;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * 256) {
+    const int h = (int)(e / total_n);
+    const int pslot = (int)(e - (int64_t)h * total_n);
+    int lo = 0, hi = B - 1;  // largest b with off[b] <= pslot
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (off[mid] <= pslot)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    const int b = lo;
+    const int mb = cu_m[b + 1] - cu_m[b], nb = cu_n[b + 1] - cu_n[b];
+    const int local = pslot - off[b];
+    if (mb <= 0 || nb <= 0 || local < 0 || local >= mb * nb) continue;
+    const int i = local / nb, s = local - i * nb;
+    if (s >= min(max(cnt[(int64_t)h * total_m + cu_m[b] + i], 0), nb)) continue;
+    const int32_t j = idx[e];
+    if (j < 0 || j >= nb) continue;
+    mt[(int64_t)h * total_n + off[b] + (int64_t)j * mb + i] = 1;
+  }
+}
+
+hipError_t launch_varlen_kv_major_lists(const int32_t* cnt, const int32_t* idx, int32_t H,
+                                        int32_t B, const int32_t* cu_m, const int32_t* cu_n,
+                                        const int32_t* off, int32_t total_m, int32_t total_kv,
+                                        int32_t total_n, uint8_t* work, int32_t* cnt_t,
+                                        int32_t* idx_t, hipStream_t s) {
+  const int64_t cells = (int64_t)H * total_n;
+  if ((int64_t)H * total_kv == 0) return hipSuccess;
+  if (cells > 0) {
+    const unsigned g = (unsigned)std::min<int64_t>((cells + 255) / 256, 65536);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(g), dim3(256), 0, s, work, cells);
+    hipLaunchKernelGGL(varlen_scatter_transposed_kernel, dim3(g), dim3(256), 0, s, cnt, idx, H, B,
+                       cu_m, cu_n, off, total_m, total_n, work);
+  }
+  // the transposed rows: (b, j) over cu_n, width M_b = span / N_b
+  return launch_varlen_mask_to_index(work, H, B, cu_n, off, total_kv, total_n, cnt_t, idx_t, s);
+}
+
 hipError_t launch_varlen_mask_to_index(const uint8_t* mask, int32_t H, int32_t B,
                                        const int32_t* cu_m, const int32_t* off, int32_t total_m,
                                        int32_t total_n, int32_t* cnt, int32_t* idx,

@@ -270,6 +270,67 @@ bsa_status bsa_kv_major_lists(const int32_t* cnt, const int32_t* idx, int32_t B,
                               int32_t M, int32_t N, uint8_t* work, int32_t* cnt_t,
                               int32_t* idx_t, hipStream_t stream);
 
+/* Backward of the packed varlen forward (bsa_varlen_fwd's layout,
+ * flash-attention pull request 2224: its review thread names the backward
+ * over transposed metadata across the varlen features).  Each sequence is an
+ * independent problem with sequence-local ids, so the gradients are those of
+ * bsa_bwd per sequence (same formulas, bf16, same D set, same mask_mods).
+ *  q, o, dout, dq [total_q,H,D] and k, v, dk, dv [total_k,H_kv,D]: device
+ *    bf16, element strides {token, head} (q_str also describes dq, k_str dk,
+ *    v_str dv, o_str dout), head_dim stride 1, 16-byte aligned rows.
+ *  lse: the varlen forward's LSE, device fp32 [H,total_q] contiguous.
+ *  cu_seqlens_q/k, cu_total_m_blocks, block_idx_offsets, total_m_blocks,
+ *    total_q: as for bsa_varlen_fwd (device int32 arrays of B+1 entries).
+ *  cu_total_kv_blocks: device int32 [B+1], [0, cumsum ceil(seqlen_k(b)/block_kv)]
+ *    (bsa_varlen_offsets with the Q and KV roles swapped gives it as its
+ *    cu_total_m_blocks), total_kv_blocks its last entry.
+ *  bs: the forward's lists (cnt [H,total_m_blocks], idx [H,total_n_blocks]),
+ *    block sizes and window.
+ *  mask_t / full_t: their KV-major transposes (bsa_varlen_kv_major_lists):
+ *    cnt [H,total_kv_blocks] through cnt_stride[1] (head) and cnt_stride[2]
+ *    (global KV block), idx [H,total_n_blocks] through idx_stride[1] (head)
+ *    and idx_stride[3] (slot), row (b, j) at slot block_idx_offsets[b] +
+ *    j*num_m(b); cnt == NULL: absent.
+ *  kv_valid, kv_valid_ld: as for bsa_varlen_fwd (per sequence-local KV block).
+ *  work: device fp32 scratch of H*total_q entries (row dots), overwritten.
+ * dq and dk, dv are overwritten on every token of the sequences (zero where
+ * nothing is listed).  Errors as bsa_bwd.  Deterministic: no atomics. */
+bsa_status bsa_varlen_bwd(const void* q, const void* k, const void* v, const void* o,
+                          const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                          int32_t B, int32_t H, int32_t H_kv, int32_t D,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          const int32_t* cu_total_m_blocks, const int32_t* cu_total_kv_blocks,
+                          const int32_t* block_idx_offsets, int32_t total_m_blocks,
+                          int32_t total_kv_blocks, int32_t total_q, const int64_t q_str[2],
+                          const int64_t k_str[2], const int64_t v_str[2], const int64_t o_str[2],
+                          const bsa_block_sparse* bs, const bsa_block_list* mask_t,
+                          const bsa_block_list* full_t, bsa_mask_mod mask_mod,
+                          const int32_t* kv_valid, int64_t kv_valid_ld, float softmax_scale,
+                          float* work, hipStream_t stream);
+
+/* KV-major lists in the packed varlen layout (the transposed metadata of the
+ * varlen backward, flash-attention pull request 2224 review thread).  cnt:
+ * device int32 [H,total_m_blocks] and idx [H,total_n_blocks], contiguous, as
+ * bsa_varlen_mask_to_index writes them (row (b,i) at block_idx_offsets[b] +
+ * i*num_n(b); ids outside [0, num_n(b)) and entries past cnt are skipped).
+ * cu_total_m_blocks, cu_total_kv_blocks, block_idx_offsets: device int32
+ * [B+1] as for bsa_varlen_bwd.  work: device scratch of H*total_n_blocks
+ * bytes, overwritten.  Writes cnt_t: device int32 [H,total_kv_blocks] (row
+ * (b,j) at cu_total_kv_blocks[b] + j: how many Q blocks of sequence b list
+ * its KV block j) and idx_t: device int32 [H,total_n_blocks] (row (b,j) at
+ * block_idx_offsets[b] + j*num_m(b), width num_m(b): those sequence-local
+ * Q-block ids in descending order, then -1).  Convert the mask and full
+ * lists separately.  Caller owns every buffer.  Returns
+ * BSA_ERR_INVALID_ARGUMENT for negative sizes or a missing pointer,
+ * BSA_ERR_HIP if a launch fails.  Bit-exact; deterministic. */
+bsa_status bsa_varlen_kv_major_lists(const int32_t* cnt, const int32_t* idx, int32_t H, int32_t B,
+                                     const int32_t* cu_total_m_blocks,
+                                     const int32_t* cu_total_kv_blocks,
+                                     const int32_t* block_idx_offsets, int32_t total_m_blocks,
+                                     int32_t total_kv_blocks, int32_t total_n_blocks,
+                                     uint8_t* work, int32_t* cnt_t, int32_t* idx_t,
+                                     hipStream_t stream);
+
 /* Packed UInt32 block bitmap -> block lists (the bitmap input of the PrimTS
  * page, "proxy-compensated block-sparse attention", flashinfer pull request
  * 4872: description and test notes).  words: device uint32 [B,Hkv,M,W]

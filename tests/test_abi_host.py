@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
                             "bsa_varlen_mask_to_index", "bsa_varlen_offsets",
                             "bsa_expand_kv_blocks", "bsa_block_sparsity", "bsa_bitmask_to_index",
                             "bsa_kv_major_lists", "bsa_bwd", "bsa_bwd_noalloc",
-                            "bsa_status_str"])
+                            "bsa_varlen_bwd", "bsa_varlen_kv_major_lists", "bsa_status_str"])
     lib = bsa.load_library()
     for n in names:
         assert hasattr(lib, n), n
@@ -76,3 +76,27 @@ def test_product_never_imports_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle", text, re.M), f
                 assert "oracle/" not in text, f
+
+
+def test_varlen_backward_argument_errors_on_the_host():
+    # Rejected before any device work: negative sizes, H not a multiple of
+    # H_kv, a negative kv_valid row stride; an empty pack is a no-op.
+    lib = bsa.load_library()
+    z = [None] * 9
+    i64 = (ctypes.c_int64 * 2)(8, 8)
+    bs = bsa._BlockSparse(bsa._BlockList(), bsa._BlockList(), 64, 64, -1, -1)
+    lt = bsa._BlockList()
+
+    def call(B, H, Hkv, tm, tkv, ld):
+        return lib.bsa_varlen_bwd(*z, B, H, Hkv, 128, None, None, None, None, None, tm, tkv, 0,
+                                  i64, i64, i64, i64, ctypes.byref(bs), ctypes.byref(lt),
+                                  ctypes.byref(lt), 0, None, ld, 0.1, None, None)
+    assert call(-1, 2, 2, 1, 1, 0) == 1
+    assert call(1, 3, 2, 1, 1, 0) == 1
+    assert call(1, 2, 2, 1, 1, -1) == 1
+    assert call(1, 2, 2, -1, 1, 0) == 1
+    assert call(0, 2, 2, 0, 0, 0) == 0
+    assert lib.bsa_varlen_kv_major_lists(None, None, -1, 1, None, None, None, 0, 0, 0, None, None,
+                                         None, None) == 1
+    assert lib.bsa_varlen_kv_major_lists(None, None, 2, 1, None, None, None, 0, 0, 0, None, None,
+                                         None, None) == 0

@@ -79,6 +79,8 @@ def test_bwd_matches_oracle(case):
         assert np.isfinite(gg).all(), f"{name}: NaN/inf"
         err = float(np.abs(gg - r).max())
         ref = float(np.abs(r).max())
+        print(f"bwd {case} {name}: max err {err:.3e}, max |grad| {ref:.3e}, "
+              f"ratio {err / max(ref, 1e-6):.2e}")
         assert err <= REL_TOL * max(ref, 1e-6), f"{name} {case}: err {err:.3e} vs max {ref:.3e}"
     assert (dq[0, :bq, 0] == 0).all()  # the Q block with nothing listed
 
@@ -116,3 +118,101 @@ def test_bwd_full_size_sweep_sampled_heads():
             print(f"full-size sweep bwd (b={b}, h={h}) {name}: max err {err:.3e}, "
                   f"max |grad| {ref:.3e}, ratio {err / ref:.2e}")
             assert err <= REL_TOL * ref, f"{name} (b={b}, h={h}): err {err:.3e} vs max {ref:.3e}"
+
+
+def _varlen_setup(rng, mm, sq, sk, H, Hkv, D, bq, bk, window=None):
+    """Random per-sequence block masks (CAUSAL / LOCAL: the classifier's
+    partial blocks plus 70 % of its full ones; NONE / KVV: 40 % of the
+    blocks, split between the lists), the packed device lists, the cu arrays
+    of both roles and per-sequence valid counts (KVV)."""
+    full, part = [], []
+    for a, c in zip(sq, sk):
+        M, N = -(-a // bq), -(-c // bk)
+        if mm in (CAUSAL, LOCAL):
+            f_c, p_c = oracle.block_sparsity(mm, a, c, bq, bk, window=window)
+            f = np.broadcast_to(f_c.astype(bool), (H, M, N)) & (rng.random((H, M, N)) < 0.7)
+            p = np.broadcast_to(p_c.astype(bool), (H, M, N)).copy()
+        else:
+            sel = rng.random((H, M, N)) < 0.4
+            split = rng.random((H, M, N)) < 0.5 if mm == KVV else np.ones((H, M, N), bool)
+            f, p = sel & split, sel & ~split
+        full.append(f)
+        part.append(p)
+    cu, off, tm, tn = bsa.bsa_varlen_offsets(sq, sk, bq, bk)
+    cu_kv, off_t, tkv, tn_t = bsa.bsa_varlen_offsets(sk, sq, bk, bq)
+    assert off_t == off and tn_t == tn
+    dev = lambda a: torch.tensor(a, dtype=torch.int32, device="cuda")
+
+    def packed(masks):
+        out = np.zeros((H, tn), np.uint8)
+        for b, m in enumerate(masks):
+            nm, nn = m.shape[1:]
+            for i in range(nm):
+                out[:, off[b] + i * nn: off[b] + (i + 1) * nn] = m[:, i]
+        return torch.from_numpy(out).cuda()
+    cu_m, offs = dev(cu), dev(off)
+    ml = bsa.bsa_varlen_mask_to_index(packed(part), cu_m, offs, tm, tn) if tn else None
+    fl = bsa.bsa_varlen_mask_to_index(packed(full), cu_m, offs, tm, tn) if tn else None
+    kvv = None
+    if mm == KVV:
+        W = max(-(-c // bk) for c in sk) + 2
+        kvv = rng.integers(0, bk + 3, size=(len(sk), W)).astype(np.int32)
+    meta = dict(cu_q=dev([0] + list(np.cumsum(sq))), cu_k=dev([0] + list(np.cumsum(sk))),
+                cu_m=cu_m, cu_kv=dev(cu_kv), offs=offs, tm=tm, tkv=tkv, tn=tn)
+    return full, part, ml, fl, kvv, meta
+
+
+@pytest.mark.parametrize("case", [
+    dict(mm=CAUSAL, sq=[300, 0, 129, 517, 64], sk=[300, 0, 129, 517, 64], D=128, bq=64, bk=64),
+    dict(mm=KVV, sq=[200, 450, 33], sk=[260, 120, 500], D=64, bq=128, bk=48),
+    dict(mm=NONE, sq=[130, 77, 400], sk=[517, 0, 90], D=96, bq=64, bk=112),
+    dict(mm=LOCAL, sq=[333, 260], sk=[333, 260], D=256, bq=128, bk=128, window=(70, 10)),
+    dict(mm=CAUSAL, sq=[250, 190, 31], sk=[250, 190, 31], D=192, bq=64, bk=64),
+    dict(mm=CAUSAL, sq=[384, 128], sk=[384, 128], D=128, bq=128, bk=128),
+])
+def test_varlen_bwd_matches_oracle(case):
+    # packed varlen backward (bsa_varlen_bwd) against the varlen oracle,
+    # every token of every sequence; empty sequences and Sq != Sk included
+    seed = zlib.crc32(repr(sorted(case.items())).encode())
+    rng = np.random.default_rng(seed)
+    mm, sq, sk, D, bq, bk = case["mm"], case["sq"], case["sk"], case["D"], case["bq"], case["bk"]
+    window = case.get("window")
+    H, Hkv = 4, 2
+    full, part, ml, fl, kvv, m = _varlen_setup(rng, mm, sq, sk, H, Hkv, D, bq, bk, window)
+    q, k, v = (to_dev(rng.standard_normal(s, dtype=np.float32))
+               for s in ((sum(sq), H, D), (sum(sk), Hkv, D), (sum(sk), Hkv, D)))
+    do = to_dev(rng.standard_normal((sum(sq), H, D), dtype=np.float32))
+    kvv_d = None if kvv is None else torch.from_numpy(kvv).cuda()
+    scale = 1 / math.sqrt(D)
+    print(f"varlen bwd case {case}", flush=True)
+    o, lse = bsa.bsa_varlen_fwd(q, k, v, m["cu_q"], m["cu_k"], m["cu_m"], m["offs"], m["tm"],
+                                m["tn"], ml, fl, bq, bk, mm, scale, window=window, kv_valid=kvv_d,
+                                max_seqlen_k=max(sk))
+    dq, dk, dv = bsa.bsa_varlen_bwd(q, k, v, o, lse, do, m["cu_q"], m["cu_k"], m["cu_m"],
+                                    m["cu_kv"], m["offs"], m["tm"], m["tkv"], m["tn"], ml, fl,
+                                    bq, bk, mm, kvv_d, scale, window=window)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.varlen_blocksparse_attention_bwd(
+        as_oracle(q), as_oracle(k), as_oracle(v), sq, sk, full, part, bq, bk, mm, scale,
+        as_oracle(do), kv_valid=None if kvv is None else list(kvv), window=window)
+    for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        gg = as_oracle(g)
+        assert np.isfinite(gg).all(), f"{name}: NaN/inf"
+        err = float(np.abs(gg - r).max())
+        ref = float(np.abs(r).max())
+        print(f"  {name}: max err {err:.3e}, max |grad| {ref:.3e}")
+        assert err <= REL_TOL * max(ref, 1e-6), f"{name} {case}: err {err:.3e} vs max {ref:.3e}"
+
+
+@pytest.mark.parametrize("sq,sk,bq,bk", [([300, 0, 129, 517], [250, 100, 1, 0], 64, 48),
+                                         ([1000, 64, 333], [1000, 64, 333], 128, 128)])
+def test_varlen_kv_major_lists_bit_exact(sq, sk, bq, bk):
+    rng = np.random.default_rng(len(sq) * 7 + bq)
+    H = 3
+    full, part, ml, fl, _, m = _varlen_setup(rng, NONE, sq, sk, H, H, 64, bq, bk)
+    cnt_t, idx_t = bsa.bsa_varlen_kv_major_lists(fl, m["cu_m"], m["cu_kv"], m["offs"], m["tm"],
+                                                 m["tkv"])
+    torch.cuda.synchronize()
+    rc, ri = oracle.varlen_kv_major_lists(full, sq, sk, bq, bk)
+    np.testing.assert_array_equal(cnt_t.cpu().numpy(), rc)
+    np.testing.assert_array_equal(idx_t.cpu().numpy(), ri)
