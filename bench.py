@@ -54,7 +54,8 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", choices=["video", "sweep128", "varlen"], default="video")
+    ap.add_argument("--workload", choices=["video", "sweep128", "varlen", "bwd_sweep128"],
+                    default="video")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-time budget of the oracle sample on the host (0 = skip)")
     ap.add_argument("--print-kernel-hash", action="store_true",
@@ -155,6 +156,30 @@ def _sweep_step(bsa, st, events=None):
     if events is not None:
         events[1].record()
     st["o"], st["lse"] = o, lse
+
+
+def _bwd_inputs(torch, np, workloads):
+    # the d128 sweep's forward outputs and an upstream gradient, once
+    import block_sparse_attention_bsa_amd as bsa
+    st, flops, cfg = _sweep_inputs(torch, np, workloads)
+    _sweep_step(bsa, st)
+    st["do"] = torch.randn(st["q"].shape, generator=torch.Generator().manual_seed(77)).to(
+        torch.bfloat16).to("cuda")
+    st["ml"] = bsa.bsa_mask_to_index(st["part"])
+    st["fl"] = bsa.bsa_mask_to_index(st["full"])
+    cfg = dict(cfg, workload="blocksparse_sweep_d128_backward",
+               flops="10*d per listed (row, key) cell: S, dP, dV, dK, dQ")
+    return st, 2.5 * flops, cfg
+
+
+def _bwd_step(bsa, st, events=None):
+    # timed: the KV-major lists, the row dots, dQ and dK/dV
+    if events is not None:
+        events[0].record()
+    bsa.bsa_bwd(st["q"], st["k"], st["v"], st["o"], st["lse"], st["do"], st["ml"], st["fl"],
+                128, 128, bsa.MASK_CAUSAL, None, st["w"].scale)
+    if events is not None:
+        events[1].record()
 
 
 def _varlen_inputs(torch, np, workloads):
@@ -665,7 +690,8 @@ def main():
                           "launches": 3}))
         return
     make, step = {"video": (_video_inputs, _video_step), "sweep128": (_sweep_inputs, _sweep_step),
-                  "varlen": (_varlen_inputs, _varlen_step)}[args.workload]
+                  "varlen": (_varlen_inputs, _varlen_step),
+                  "bwd_sweep128": (_bwd_inputs, _bwd_step)}[args.workload]
     st, flops, cfg = make(torch, np, workloads)
     for _ in range(args.warmup):
         step(bsa, st)
@@ -694,10 +720,14 @@ def main():
     # head_dim 128; 256-row workgroups for 256-token Q cubes, 128 rows otherwise
     kernel_name = "bsa_fwd_pp_kernel<128> (256-row workgroup, 8 waves)" \
         if args.workload == "video" else "bsa_fwd_kernel<128,4> (128-row workgroup)"
-    if args.workload == "varlen":
+    metric = METRIC
+    if args.workload == "bwd_sweep128":
+        kernel_name = "backward: KV-major lists, bwd_rowdot, bwd_dq_kernel<128,4>, bwd_dkdv_kernel<128,4>"
+        metric = "effective TFLOP/s bf16 block-sparse attn bwd (10*d flops per listed cell)"
+    if args.workload in ("varlen", "bwd_sweep128"):
         args.cpu_seconds = 0  # the oracle leg samples the video and sweep workloads only
     out = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": metric, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) Q/K/V, seeded top-k block selection)",

@@ -489,6 +489,9 @@ bsa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, 
   if (!strides_ok(q_str, 3, 2) || !strides_ok(k_str, 3, 2) || !strides_ok(v_str, 3, 2) ||
       !strides_ok(o_str, 3, 2))
     return BSA_ERR_MISALIGNED;
+  // the tiles of 64 rows are staged with 32-bit byte offsets from their first row
+  if (!subtile_offsets_fit(q_str[1], o_str[1], 2) || !subtile_offsets_fit(k_str[1], v_str[1], 2))
+    return BSA_ERR_UNSUPPORTED;
   const int64_t M = cdiv64(Sq, bs->block_q), N = cdiv64(Sk, bs->block_kv);
   const int64_t gq = (int64_t)B * H * M * cdiv64(bs->block_q, 64);
   const int64_t gk = (int64_t)B * H_kv * N * cdiv64(bs->block_kv, 64);
@@ -591,6 +594,8 @@ bsa_status bsa_varlen_bwd(const void* q, const void* k, const void* v, const voi
   if (!strides_ok(q_str, 2, 2) || !strides_ok(k_str, 2, 2) || !strides_ok(v_str, 2, 2) ||
       !strides_ok(o_str, 2, 2))
     return BSA_ERR_MISALIGNED;
+  if (!subtile_offsets_fit(q_str[0], o_str[0], 2) || !subtile_offsets_fit(k_str[0], v_str[0], 2))
+    return BSA_ERR_UNSUPPORTED;
   const int64_t gq = (int64_t)H * total_m_blocks * cdiv64(bs->block_q, 64);
   const int64_t gk = (int64_t)H_kv * total_kv_blocks * cdiv64(bs->block_kv, 64);
   if (gq > std::numeric_limits<int32_t>::max() || gk > std::numeric_limits<int32_t>::max())

@@ -8,19 +8,23 @@
 //   dS = P * (dP - D), dQ = scale * dS K, dK = scale * dS^T Q.
 // Three launches on the caller's stream:
 //   1. bwd_rowdot_kernel: D per row (fp32 workspace).
-//   2. bwd_dq_kernel: one workgroup per 128 (or 64) rows of a Q block, walking the
-//      forward's lists in 64-key sub-tiles.  S and dP^T come from K and V
-//      rows in LDS against Q and dO in registers; dQ accumulates dS times K
-//      read transposed from LDS.  The layouts are those of the forward: a lane
-//      owns one query row, P and dS feed the last product straight from
-//      registers.
-//   3. bwd_dkdv_kernel: one workgroup per 128 (or 64) keys of a KV block, walking the
+//   2. bwd_dq_kernel: one workgroup per 128 (or 64) rows of a Q block, walking
+//      the forward's lists in 64-key sub-tiles.  S^T and dP^T come from K and
+//      V rows in LDS against Q and dO in registers; dQ^T accumulates K^T (the
+//      K tile read transposed) times dS^T.  A lane owns one query row, as in
+//      the forward, and dS feeds the last product straight from registers.
+//   3. bwd_dkdv_kernel: one workgroup per 128 keys of a KV block, walking the
 //      KV-major lists (the Q blocks that list the KV block) of every Q head of
 //      its KV head, in 64-row sub-tiles.  The roles swap: a lane owns one key,
-//      K and V sit in registers, Q and dO rows (and their transposes) in LDS.
-//      Summing the group's heads in one workgroup needs no atomics.
-// Each sub-tile is loaded, converted and transposed through registers by all
-// threads, then computed; one LDS stage.
+//      K and V sit in registers, Q and dO tiles in LDS.  Up to d = 128 the
+//      workgroup has two groups of four waves over the same 128 keys: one
+//      computes P and dV, the other dP, dS and dK, so each wave holds one
+//      accumulator and two waves share a SIMD.  Summing the group's heads in
+//      one workgroup needs no atomics.
+// Tiles move from HBM straight into LDS (global_load_lds) in a swizzled
+// row-major layout that both the row reads and the transposing reads
+// (ds_read_b64_tr_b16) take without bank conflicts; two LDS stages up to
+// d = 128 (the next sub-tile streams in while the current one computes).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -39,88 +43,117 @@ namespace {
 
 using namespace dev;
 
-// A workgroup of NW waves owns 32*NW rows (dQ) or keys (dK, dV): NW = 4 when
-// the block size is a multiple of 128, else 2.  The other side streams in
-// sub-tiles of kBwdT positions.
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
+typedef __attribute__((address_space(3))) char lds_char;
+
+// A dQ workgroup of NW waves owns 32*NW rows, a dK/dV workgroup 32*NQ keys
+// (per group): 4 when the block size is a multiple of 128, else 2.  The
+// other side streams in sub-tiles of kBwdT positions.
 constexpr int kBwdT = 64;
 
 __device__ __forceinline__ uint32_t word4(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// Element rule of a mask-list block (row and key are sequence positions;
-// kib is the key's offset inside its KV block j; kvv the sequence's
-// valid counts).
-__device__ __forceinline__ bool keep_elem(const BwdParams& p, const int32_t* kvv, int row, int key,
-                                          int j, int kib) {
+// The positions [lo, hi] of a 64-position sub-tile that the element rule of
+// a mask-list block keeps for this lane, so the inner loops compare instead
+// of branching per element.  Keys (dQ: the lane owns sequence row `row`, the
+// sub-tile holds keys k0 ..) or rows (dK/dV: the lane owns key `key`, the
+// sub-tile holds rows r0 ..) of KV block j.
+__device__ __forceinline__ void keys_kept(const BwdParams& p, const int32_t* kvv, int row, int k0,
+                                          int j, int& lo, int& hi) {
+  lo = 0;
+  hi = kBwdT - 1;
   switch (p.mask_mod) {
-    case kMaskCausal: return key <= row;
-    case kMaskKvValid: return kib < kvv[j];
+    case kMaskCausal: hi = row - k0; break;
+    case kMaskKvValid: hi = kvv[j] + j * p.block_kv - k0 - 1; break;
     case kMaskLocal:
-      return (p.win_left < 0 || row - key <= p.win_left) &&
-             (p.win_right < 0 || key - row <= p.win_right);
-    default: return true;
+      if (p.win_left >= 0) lo = row - p.win_left - k0;
+      if (p.win_right >= 0) hi = row + p.win_right - k0;
+      break;
+    default: break;
   }
 }
 
-// Staging of rows 0 .. n-1 (n <= 64) of a [*, D] bf16 tensor (row stride ss)
-// into LDS: row-major at rm (row pitch RM bytes) and/or transposed at tr
-// (tr[d] is a row of 64 positions, pitch TR bytes); rows past n are zero.
-// load() issues the global reads into registers, store() writes LDS, so the
-// reads of the next sub-tile can be in flight while the current one is
-// computed.  Every thread of the workgroup takes part; no barrier inside.
-template <int D, int NT>
-struct Stage {
-  static constexpr int DC = D / 8;
-  static constexpr int RM = D * 2 + 16;
-  static constexpr int TR = kBwdT * 2 + 16;
-  static constexpr int BL = (kBwdT / 4) * DC;  // blocks of 4 rows x 8 dims
-  static constexpr int PER = (BL + NT - 1) / NT;
-  uint4 r[PER][4];
-  __device__ __forceinline__ void load(const __bf16* base, int64_t ss, int n, int tid) {
-#pragma unroll
-    for (int c = 0; c < PER; ++c) {
-      const int bi = tid + c * NT;
-      const int g = bi / DC, dc = bi % DC;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int row = 4 * g + rr;
-        r[c][rr] = (bi < BL && row < n)
-                       ? *reinterpret_cast<const uint4*>(base + (int64_t)row * ss + dc * 8)
-                       : make_uint4(0, 0, 0, 0);
-      }
-    }
+__device__ __forceinline__ void rows_kept(const BwdParams& p, const int32_t* kvv, int key, int r0,
+                                          int j, int& lo, int& hi) {
+  lo = 0;
+  hi = kBwdT - 1;
+  switch (p.mask_mod) {
+    case kMaskCausal: lo = key - r0; break;
+    case kMaskKvValid:
+      if (key - j * p.block_kv >= kvv[j]) hi = -1;
+      break;
+    case kMaskLocal:
+      if (p.win_right >= 0) lo = key - p.win_right - r0;
+      if (p.win_left >= 0) hi = key + p.win_left - r0;
+      break;
+    default: break;
   }
-  __device__ __forceinline__ void store(unsigned char* rm, unsigned char* tr, int tid) const {
-#pragma unroll
-    for (int c = 0; c < PER; ++c) {
-      const int bi = tid + c * NT;
-      if (bi >= BL) continue;
-      const int g = bi / DC, dc = bi % DC;
-      if (rm) {
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          *reinterpret_cast<uint4*>(rm + (4 * g + rr) * RM + dc * 16) = r[c][rr];
-      }
-      if (tr) {
-#pragma unroll
-        for (int dd = 0; dd < 8; ++dd) {
-          const uint32_t x0 = word4(r[c][0], dd >> 1), x1 = word4(r[c][1], dd >> 1);
-          const uint32_t x2 = word4(r[c][2], dd >> 1), x3 = word4(r[c][3], dd >> 1);
-          uint2 out;
-          if ((dd & 1) == 0) {
-            out.x = (x0 & 0xffffu) | (x1 << 16);
-            out.y = (x2 & 0xffffu) | (x3 << 16);
-          } else {
-            out.x = (x0 >> 16) | (x1 & 0xffff0000u);
-            out.y = (x2 >> 16) | (x3 & 0xffff0000u);
-          }
-          *reinterpret_cast<uint2*>(tr + (dc * 8 + dd) * TR + g * 8) = out;
-        }
-      }
-    }
+}
+
+// Backward tiles in LDS: 64 positions (keys, or query rows) x D bf16, rows
+// unpadded: chunk c (16 bytes) of row r at slot r*DC + (c ^ swz(r)).  A tile
+// is read as rows (ds_read_b128: the 16 lanes of a quarter-wave read one
+// chunk of 16 consecutive rows) and transposed (ds_read_b64_tr_b16: half a
+// wave reads 4 consecutive rows x 4 consecutive chunks).  swz maps both
+// patterns onto 16 different 16-byte bank groups (the transposed reads at
+// d = 192 pair up two to a group).  swz depends on r mod 16 only.
+template <int D>
+struct BTile {
+  static constexpr int DC = D / 8;
+  static constexpr int BYTES = kBwdT * DC * 16;
+  __device__ __forceinline__ static int swz(int r) {
+    return D == 64 ? 4 * ((r >> 1) & 1) + ((r >> 2) & 3)
+         : D == 96 ? (r >> 2) & 3
+         : D == 192 ? (r >> 1) & 7
+                    : 4 * (r & 3) + ((r >> 2) & 3);
   }
 };
+
+// One 16-byte global_load_lds per lane: the lane's 16 bytes at base + off go
+// to LDS address lds_addr + 16 * lane.  The base is a scalar (SGPR) operand
+// and the LDS address goes in M0.  The compiler's hazard checks do not see
+// inside the asm, so its s_nop 4 provides the wait states the load needs
+// after the instructions that set its operands (five after a VALU write of
+// an SGPR it reads, e.g. a base restored with v_readlane).
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds_addr) {
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+               "{m0}"(lds_addr)
+               : "memory");
+}
+
+__device__ __forceinline__ uint2 read_tr(const unsigned char* lds, int byte_off) {
+  lds_char* base = (lds_char*)(lds);  // generic -> LDS address space
+  const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(base + byte_off));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Rows 0 .. n-1 (1 <= n <= 64) of a [*, D] bf16 tensor (row stride ss
+// elements, first row at base) into a BTile at LDS address lds, by the
+// workgroup's first NS waves (wave ws of them).  Rows past n repeat row n-1:
+// every product that reads them multiplies by a zero P or dS.  64*ss*2 must
+// fit 31 bits (checked by the caller).
+template <int D, int NS>
+__device__ __forceinline__ void stage_tile(const __bf16* base, int64_t ss, int n, uint32_t lds,
+                                           int ws, int lane) {
+  constexpr int DC = D / 8, NI = DC;  // 1 KiB DMA blocks per tile (64 slots each)
+  // the base is wave-uniform; say so, since it is an SGPR operand
+  const uint64_t u = (uint64_t)(size_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  const void* ub = (const void*)(size_t)(((uint64_t)hi << 32) | lo);
+  const int rs = (int)(ss * 2);
+#pragma unroll
+  for (int m = 0; m < (NI + NS - 1) / NS; ++m) {
+    const int ii = m * NS + ws;
+    if (ii >= NI) break;
+    const int slot = ii * 64 + lane;
+    const int r = slot / DC, c = (slot % DC) ^ BTile<D>::swz(r);
+    dma16(ub, (uint32_t)(min(r, n - 1) * rs + c * 16), lds + ii * 1024);
+  }
+}
 
 // Largest b < B with cu[b] <= x (cu: B+1 nondecreasing prefix sums), i.e.
 // the sequence of packed block x.  Wave-uniform.
@@ -227,43 +260,67 @@ __device__ __forceinline__ void row_frags(const __bf16* rowp, bool valid, int h3
                      : make_uint4(0, 0, 0, 0);
 }
 
-// Product over head_dim of two 32x32 tiles: rows arow / arow+32 of the LDS
-// tile (pitch RM) against this lane's fragments.
+// Product over head_dim of two 32x32 tiles: rows arow and arow + 32 of an
+// LDS tile (A operand, row reads; sw = swz(arow), also that of arow + 32)
+// against this lane's fragments (B operand).
 template <int D>
-__device__ __forceinline__ void tile_dot(const unsigned char* lds, int arow, int h32,
+__device__ __forceinline__ void tile_dot(const unsigned char* t, int arow, int sw, int h32,
                                          const uint4 (&frag)[D / 16], f32x16_t& s0,
                                          f32x16_t& s1) {
-  constexpr int RM = D * 2 + 16;
+  constexpr int DC = D / 8;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     s0[r] = 0.f;
     s1[r] = 0.f;
   }
+  const unsigned char* r0 = t + arow * DC * 16;
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    const uint4 a0 = *reinterpret_cast<const uint4*>(lds + arow * RM + ks * 32 + h32 * 16);
-    const uint4 a1 = *reinterpret_cast<const uint4*>(lds + (arow + 32) * RM + ks * 32 + h32 * 16);
+    const int c = ((2 * ks + h32) ^ sw) * 16;
+    const uint4 a0 = *reinterpret_cast<const uint4*>(r0 + c);
+    const uint4 a1 = *reinterpret_cast<const uint4*>(r0 + 32 * DC * 16 + c);
     s0 = mfma32(a0, frag[ks], s0);
     s1 = mfma32(a1, frag[ks], s1);
   }
 }
 
-// acc[db] += T^T(LDS, transposed tile: tr[d][64]) x operand(pk), over the 64
-// positions of the sub-tile.
-template <int DB>
-__device__ __forceinline__ void tr_product(const unsigned char* tr, int arow, int h32,
+// A lane's transposing reads of a tile (the forward's V^T reads): two reads
+// of 4 positions each give the A operand [32 head dims x 16 positions] of
+// head-dim block db and position block ps.
+template <int D>
+struct TrGeo {
+  int base[2], sw[2], c0, half8;
+  __device__ __forceinline__ explicit TrGeo(int lane) {
+    const int h32 = lane >> 5, vs = lane & 15, vg = lane >> 4;
+    const int pos = 8 * h32 + (vs >> 2);
+    const int vd = 16 * (vg & 1) + 4 * (((vs & 1) << 1) | ((vs >> 1) & 1));
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      base[t] = (pos + 4 * t) * (D / 8) * 16;
+      sw[t] = BTile<D>::swz(pos + 4 * t);  // swz(pos + 16 ps) = swz(pos)
+    }
+    c0 = vd >> 3;
+    half8 = 8 * ((vd >> 2) & 1);
+  }
+  __device__ __forceinline__ uint4 op(const unsigned char* t, int ps, int db) const {
+    const int po = ps * 16 * (D / 8) * 16;
+    const uint2 x = read_tr(t, base[0] + po + ((c0 + 4 * db) ^ sw[0]) * 16 + half8);
+    const uint2 y = read_tr(t, base[1] + po + ((c0 + 4 * db) ^ sw[1]) * 16 + half8);
+    return make_uint4(x.x, x.y, y.x, y.y);
+  }
+};
+
+// acc[db] += X^T (the tile read transposed: head dims x positions) times the
+// operand of pk (positions x this lane's column), over the 64 positions.
+template <int D>
+__device__ __forceinline__ void tr_product(const unsigned char* t, const TrGeo<D>& g,
                                            const uint32_t (&pk0)[8], const uint32_t (&pk1)[8],
-                                           f32x16_t (&acc)[DB]) {
-  constexpr int TR = kBwdT * 2 + 16;
+                                           f32x16_t (&acc)[D / 32]) {
 #pragma unroll
   for (int ps = 0; ps < 4; ++ps) {
     const uint4 bop = p_operand(pk0, pk1, ps);
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const uint4 a =
-          *reinterpret_cast<const uint4*>(tr + (db * 32 + arow) * TR + ps * 32 + h32 * 16);
-      acc[db] = mfma32(a, bop, acc[db]);
-    }
+    for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(g.op(t, ps, db), bop, acc[db]);
   }
 }
 
@@ -315,18 +372,21 @@ __device__ __forceinline__ float lse2_of(float lse) {
   return lse == neg_inf() ? __builtin_inff() : lse * 1.4426950408889634f;  // log2(e)
 }
 
+// s_waitcnt vmcnt(0): this wave's vector-memory ops, DMA included, are done.
+__device__ __forceinline__ void wait_vmem0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int D, int NW, bool VL>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))  // two waves per SIMD up to d = 128
 void bwd_dq_kernel(const BwdParams p) {
-  constexpr int NT = NW * 64, TW = NW * 32;
+  constexpr int TW = NW * 32;
   constexpr int DS = D / 16, DB = D / 32;
-  constexpr int RM = D * 2 + 16, TR = kBwdT * 2 + 16;
-  __shared__ __attribute__((aligned(16))) unsigned char Kb[kBwdT * RM];
-  __shared__ __attribute__((aligned(16))) unsigned char Vb[kBwdT * RM];
-  __shared__ __attribute__((aligned(16))) unsigned char KTb[D * TR];
+  constexpr int ST = D <= 128 ? 2 : 1;  // LDS stages of (K, V) tiles
+  using T = BTile<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[ST * 2 * T::BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h32 = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h32 = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qsub = cdiv(p.block_q, TW);
   int t = blockIdx.x;
   const int s = t % qsub;
@@ -365,7 +425,8 @@ void bwd_dq_kernel(const BwdParams p) {
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-  const int arow = swap_b23(l32);
+  const int arow = swap_b23(l32), asw = T::swz(arow);
+  const TrGeo<D> tg(lane);
 
   SubWalk W{};
   for (int list = 0; list < 2; ++list) {
@@ -389,28 +450,33 @@ void bwd_dq_kernel(const BwdParams p) {
   W.nmax = sv0.N;
   W.blen = p.block_kv;
   W.S = sv0.Sk;
-  Stage<D, NT> sk, sv;
-  bool have = W.first();
-  if (have) {
+  const uint32_t lds0 = (uint32_t)(size_t)((lds_char*)smem);
+  // K and V rows of the walk's current sub-tile into a stage
+  auto issue = [&](int stage) {
     const int nk = min(kBwdT, W.end - W.pos);
-    sk.load(kb0 + (int64_t)W.pos * p.k_ss, p.k_ss, nk, tid);
-    sv.load(vb0 + (int64_t)W.pos * p.v_ss, p.v_ss, nk, tid);
-    sk.store(Kb, KTb, tid);
-    sv.store(Vb, nullptr, tid);
-  }
+    const uint32_t kl = lds0 + stage * 2 * T::BYTES;
+    stage_tile<D, NW>(kb0 + (int64_t)W.pos * p.k_ss, p.k_ss, nk, kl, w, lane);
+    stage_tile<D, NW>(vb0 + (int64_t)W.pos * p.v_ss, p.v_ss, nk, kl + T::BYTES, w, lane);
+  };
+  bool have = W.first();
+  if (have) issue(0);
+  wait_vmem0();
   __syncthreads();
+  int st = 0;
   while (have) {
     const int list = W.list, j = W.id, k0 = W.pos, nk = min(kBwdT, W.end - W.pos);
     const bool more = W.next();
-    if (more) {  // next sub-tile's reads in flight during this one's products
-      const int nn = min(kBwdT, W.end - W.pos);
-      sk.load(kb0 + (int64_t)W.pos * p.k_ss, p.k_ss, nn, tid);
-      sv.load(vb0 + (int64_t)W.pos * p.v_ss, p.v_ss, nn, tid);
-    }
+    if (ST == 2 && more) issue(st ^ 1);  // streams in while this sub-tile computes
     {
+      const unsigned char* kt = smem + st * 2 * T::BYTES;
+      const unsigned char* vt = kt + T::BYTES;
       f32x16_t s0, s1, d0, d1;
-      tile_dot<D>(Kb, arow, h32, qf, s0, s1);
-      tile_dot<D>(Vb, arow, h32, gf, d0, d1);
+      tile_dot<D>(kt, arow, asw, h32, qf, s0, s1);
+      tile_dot<D>(vt, arow, asw, h32, gf, d0, d1);
+      // kept keys of this sub-tile for this lane's row
+      int klo = 0, khi = kBwdT - 1;
+      if (list == 0) keys_kept(p, sv0.kvv, row, k0, j, klo, khi);
+      khi = min(khi, nk - 1);
       uint32_t pk0[8], pk1[8];
 #pragma unroll
       for (int x = 0; x < 8; ++x) {
@@ -421,23 +487,22 @@ void bwd_dq_kernel(const BwdParams p) {
           const f32x16_t& sv_ = y < 2 ? s0 : s1;
           const f32x16_t& dv_ = y < 2 ? d0 : d1;
           const int key = 16 * (reg >> 3) + 8 * h32 + (reg & 7) + (y < 2 ? 0 : 32);
-          bool keep = key < nk;
-          if (keep && list == 0)
-            keep = keep_elem(p, sv0.kvv, row, k0 + key, j, k0 + key - j * p.block_kv);
+          const bool keep = key >= klo && key <= khi;
           const float pr = keep ? __builtin_amdgcn_exp2f(fmaf(sv_[reg], p.c, -lse2)) : 0.f;
           v[y] = pr * (dv_[reg] - drow);
         }
         pk0[x] = pack_bf16x2(v[0], v[1]);
         pk1[x] = pack_bf16x2(v[2], v[3]);
       }
-      tr_product<DB>(KTb, arow, h32, pk0, pk1, acc);
+      tr_product<D>(kt, tg, pk0, pk1, acc);  // dQ^T += K^T dS^T
     }
-    __syncthreads();  // every wave is done with this sub-tile
-    if (more) {
-      sk.store(Kb, KTb, tid);
-      sv.store(Vb, nullptr, tid);
+    if (ST == 1) {
+      __syncthreads();  // every wave is done with the stage
+      if (more) issue(0);
     }
-    __syncthreads();
+    wait_vmem0();
+    __syncthreads();  // the next sub-tile has landed
+    st = ST == 2 ? st ^ 1 : 0;
     have = more;
   }
   if (rvalid) {
@@ -446,18 +511,26 @@ void bwd_dq_kernel(const BwdParams p) {
   }
 }
 
-template <int D, int NW, bool VL>
-__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BwdParams p) {
-  constexpr int NT = NW * 64, TW = NW * 32;
+// NQ waves per group own 32 keys each (NQ*32 keys per workgroup).  Up to
+// d = 128 (SPLIT) two groups share them: group 0 computes P and dV, group 1
+// dP, dS and dK, each wave holding one accumulator; above, NQ waves compute
+// both.  Group 0 stages the Q and dO tiles and the rows' LSE and row dots.
+template <int D, int NQ, bool VL>
+__global__ __launch_bounds__(NQ * 64 * (D <= 128 ? 2 : 1))
+__attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
+void bwd_dkdv_kernel(const BwdParams p) {
+  constexpr bool SPLIT = D <= 128;
+  constexpr int TW = NQ * 32;
   constexpr int DS = D / 16, DB = D / 32;
-  constexpr int RM = D * 2 + 16, TR = kBwdT * 2 + 16;
-  __shared__ __attribute__((aligned(16))) unsigned char Qb[kBwdT * RM];
-  __shared__ __attribute__((aligned(16))) unsigned char Gb[kBwdT * RM];
-  __shared__ __attribute__((aligned(16))) unsigned char QTb[D * TR];
-  __shared__ __attribute__((aligned(16))) unsigned char GTb[D * TR];
-  __shared__ float lse2s[kBwdT], drows[kBwdT];
+  constexpr int ST = D <= 128 ? 2 : 1;  // LDS stages of (Q, dO) tiles
+  using T = BTile<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[ST * 2 * T::BYTES];
+  __shared__ float lse2s[ST][kBwdT], drows[ST][kBwdT];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, h32 = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h32 = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wq = w % NQ;
+  const bool g_dv = !SPLIT || w < NQ, g_dk = !SPLIT || w >= NQ;
   const int ksub = cdiv(p.block_kv, TW);
   int t = blockIdx.x;
   const int s = t % ksub;
@@ -473,7 +546,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BwdParams p) {
   const int k0 = j * p.block_kv + s * TW;
   const int kend = min((j + 1) * p.block_kv, sv0.Sk);
   if (k0 >= kend) return;
-  const int key = k0 + 32 * w + l32;  // sequence-local
+  const int key = k0 + 32 * wq + l32;  // sequence-local
   const bool kvalid = key < kend;
 
   const int64_t ktok = (int64_t)sv0.tk0 + key;
@@ -481,18 +554,23 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BwdParams p) {
   const __bf16* vrow = reinterpret_cast<const __bf16*>(p.v) + b * p.v_sb + ktok * p.v_ss + hk * p.v_sh;
   uint4 kf[DS], vf[DS];
   row_frags<D>(krow, kvalid, h32, kf);
-  row_frags<D>(vrow, kvalid, h32, vf);
+  row_frags<D>(vrow, kvalid && g_dk, h32, vf);
 
-  f32x16_t dk[DB], dv[DB];
+  // acc: dV (group 0, or every wave) or dK (group 1); acc2: dK when a wave
+  // computes both
+  f32x16_t acc[DB], acc2[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      dk[db][r] = 0.f;
-      dv[db][r] = 0.f;
+      acc[db][r] = 0.f;
+      acc2[db][r] = 0.f;
     }
-  const int arow = swap_b23(l32);
+  const int arow = swap_b23(l32), asw = T::swz(arow);
+  const TrGeo<D> tg(lane);
+  const uint32_t lds0 = (uint32_t)(size_t)((lds_char*)smem);
 
+  int st = 0;
   for (int h = hk * p.hrep; h < (hk + 1) * p.hrep; ++h) {
     const __bf16* qb0 = reinterpret_cast<const __bf16*>(p.q) + b * p.q_sb +
                         (int64_t)sv0.tq0 * p.q_ss + h * p.q_sh;
@@ -522,66 +600,114 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BwdParams p) {
     W.nmax = sv0.M;
     W.blen = p.block_q;
     W.S = sv0.Sq;
-    Stage<D, NT> sq, sg;
-    float l2n = 0.f, drn = 0.f;  // this thread's row (tid < 64) of the next sub-tile
-    auto load = [&]() {
+    float l2n = 0.f, drn = 0.f;  // wave 0: its lane's row of the staged sub-tile
+    // Q and dO rows (and the rows' LSE and row dots) of the walk's current
+    // sub-tile into a stage, by group 0
+    auto issue = [&](int stage) {
+      if (w >= NQ) return;
       const int nr = min(kBwdT, W.end - W.pos), r0 = W.pos;
-      sq.load(qb0 + (int64_t)r0 * p.q_ss, p.q_ss, nr, tid);
-      sg.load(gb0 + (int64_t)r0 * p.do_ss, p.do_ss, nr, tid);
-      if (tid < kBwdT) {
-        l2n = tid < nr ? lse2_of(p.lse[lbase + r0 + tid]) : __builtin_inff();
-        drn = tid < nr ? p.drow[lbase + r0 + tid] : 0.f;
+      const uint32_t ql = lds0 + stage * 2 * T::BYTES;
+      stage_tile<D, NQ>(qb0 + (int64_t)r0 * p.q_ss, p.q_ss, nr, ql, w, lane);
+      stage_tile<D, NQ>(gb0 + (int64_t)r0 * p.do_ss, p.do_ss, nr, ql + T::BYTES, w, lane);
+      if (w == 0) {
+        l2n = lane < nr ? lse2_of(p.lse[lbase + r0 + lane]) : __builtin_inff();
+        drn = lane < nr ? p.drow[lbase + r0 + lane] : 0.f;
       }
     };
-    auto store = [&]() {
-      sq.store(Qb, QTb, tid);
-      sg.store(Gb, GTb, tid);
-      if (tid < kBwdT) {
-        lse2s[tid] = l2n;
-        drows[tid] = drn;
+    auto put_rows = [&](int stage) {
+      if (w == 0) {
+        lse2s[stage][lane] = l2n;
+        drows[stage][lane] = drn;
       }
     };
-    __syncthreads();  // the previous head's last sub-tile is done
+    // The stage about to be filled was last read before the previous
+    // sub-tile's closing barrier.
     bool have = W.first();
     if (have) {
-      load();
-      store();
+      issue(st);
+      put_rows(st);
     }
+    wait_vmem0();
     __syncthreads();
     while (have) {
       const int list = W.list, r0 = W.pos, nr = min(kBwdT, W.end - W.pos);
       const bool more = W.next();
-      if (more) load();  // next sub-tile's reads in flight during this one's products
-      f32x16_t s0, s1, d0, d1;
-      tile_dot<D>(Qb, arow, h32, kf, s0, s1);
-      tile_dot<D>(Gb, arow, h32, vf, d0, d1);
-      uint32_t pk0[8], pk1[8], dk0[8], dk1[8];
+      if (ST == 2 && more) issue(st ^ 1);  // streams in while this sub-tile computes
+      {
+        const unsigned char* qt = smem + st * 2 * T::BYTES;
+        const unsigned char* gt = qt + T::BYTES;
+        // per half (rows 32*hf ..): S, and dP where dK is computed, then P
+        // or dS packed for the last product; one half at a time keeps the
+        // registers of the other free
+        // kept rows of this sub-tile for this lane's key
+        int rlo = 0, rhi = kBwdT - 1;
+        if (list == 0) rows_kept(p, sv0.kvv, key, r0, j, rlo, rhi);
+        rhi = kvalid ? min(rhi, nr - 1) : -1;
+        uint32_t pk[2][8];                 // P (dV group) or dS (dK group)
+        uint32_t pks[SPLIT ? 1 : 2][8];    // dS, when one wave computes both
 #pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        float pv[4], dsv[4];
+        for (int hf = 0; hf < 2; ++hf) {
+          f32x16_t sa, da;
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-          const int reg = 2 * x + (y & 1);
-          const f32x16_t& sv = y < 2 ? s0 : s1;
-          const f32x16_t& gv = y < 2 ? d0 : d1;
-          const int rl = 16 * (reg >> 3) + 8 * h32 + (reg & 7) + (y < 2 ? 0 : 32);
-          bool keep = kvalid && rl < nr;
-          if (keep && list == 0)
-            keep = keep_elem(p, sv0.kvv, r0 + rl, key, j, key - j * p.block_kv);
-          const float pr = keep ? __builtin_amdgcn_exp2f(fmaf(sv[reg], p.c, -lse2s[rl])) : 0.f;
-          pv[y] = pr;
-          dsv[y] = pr * (gv[reg] - drows[rl]);
+          for (int r = 0; r < 16; ++r) {
+            sa[r] = 0.f;
+            da[r] = 0.f;
+          }
+          const unsigned char* qr = qt + (arow + 32 * hf) * (D / 8) * 16;
+          const unsigned char* gr = gt + (arow + 32 * hf) * (D / 8) * 16;
+          if (g_dk) {
+#pragma unroll
+            for (int ks = 0; ks < DS; ++ks) {
+              const int c = ((2 * ks + h32) ^ asw) * 16;
+              sa = mfma32(*reinterpret_cast<const uint4*>(qr + c), kf[ks], sa);
+              da = mfma32(*reinterpret_cast<const uint4*>(gr + c), vf[ks], da);
+            }
+          } else {
+#pragma unroll
+            for (int ks = 0; ks < DS; ++ks) {
+              const int c = ((2 * ks + h32) ^ asw) * 16;
+              sa = mfma32(*reinterpret_cast<const uint4*>(qr + c), kf[ks], sa);
+            }
+          }
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            float v[2], w2[2];
+#pragma unroll
+            for (int y = 0; y < 2; ++y) {
+              const int reg = 2 * x + y;
+              const int rl = 16 * (reg >> 3) + 8 * h32 + (reg & 7) + 32 * hf;
+              const bool keep = rl >= rlo && rl <= rhi;
+              const float pr =
+                  keep ? __builtin_amdgcn_exp2f(fmaf(sa[reg], p.c, -lse2s[st][rl])) : 0.f;
+              if constexpr (SPLIT) {
+                v[y] = g_dv ? pr : pr * (da[reg] - drows[st][rl]);
+              } else {
+                v[y] = pr;
+                w2[y] = pr * (da[reg] - drows[st][rl]);
+              }
+            }
+            pk[hf][x] = pack_bf16x2(v[0], v[1]);
+            if constexpr (!SPLIT) pks[hf][x] = pack_bf16x2(w2[0], w2[1]);
+          }
         }
-        pk0[x] = pack_bf16x2(pv[0], pv[1]);
-        pk1[x] = pack_bf16x2(pv[2], pv[3]);
-        dk0[x] = pack_bf16x2(dsv[0], dsv[1]);
-        dk1[x] = pack_bf16x2(dsv[2], dsv[3]);
+        if (g_dv) tr_product<D>(gt, tg, pk[0], pk[1], acc);  // dV^T += dO^T P
+        if constexpr (SPLIT) {
+          if (g_dk) tr_product<D>(qt, tg, pk[0], pk[1], acc);  // dK^T += Q^T dS
+        } else {
+          tr_product<D>(qt, tg, pks[0], pks[1], acc2);
+        }
       }
-      tr_product<DB>(GTb, arow, h32, pk0, pk1, dv);
-      tr_product<DB>(QTb, arow, h32, dk0, dk1, dk);
-      __syncthreads();  // every wave is done with this sub-tile
-      if (more) store();
-      __syncthreads();
+      if (ST == 2 && more) put_rows(st ^ 1);
+      if (ST == 1) {
+        __syncthreads();  // every wave is done with the stage
+        if (more) {
+          issue(0);
+          put_rows(0);
+        }
+      }
+      wait_vmem0();
+      __syncthreads();  // the next sub-tile has landed
+      st = ST == 2 ? st ^ 1 : 0;
       have = more;
     }
   }
@@ -589,8 +715,15 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const BwdParams p) {
   if (kvalid) {
     __bf16* kdst = reinterpret_cast<__bf16*>(p.dk) + b * p.dk_sb + ktok * p.dk_ss + hk * p.dk_sh;
     __bf16* vdst = reinterpret_cast<__bf16*>(p.dv) + b * p.dv_sb + ktok * p.dv_ss + hk * p.dv_sh;
-    store_row<DB>(kdst, h32, dk, p.scale);
-    store_row<DB>(vdst, h32, dv, 1.f);
+    if constexpr (SPLIT) {
+      if (g_dk)
+        store_row<DB>(kdst, h32, acc, p.scale);
+      else
+        store_row<DB>(vdst, h32, acc, 1.f);
+    } else {
+      store_row<DB>(kdst, h32, acc2, p.scale);
+      store_row<DB>(vdst, h32, acc, 1.f);
+    }
   }
 }
 
@@ -607,9 +740,10 @@ hipError_t launch_bwd_dv(const BwdParams& p, hipStream_t st) {
   // batched: B*H*M Q-block rows and B*H_kv*N KV-block rows; varlen: the
   // M and N totals over the sequences carry the batch
   const int64_t nb = VL ? 1 : p.B;
-  const int nwq = p.block_q % 128 == 0 ? 4 : 2, nwk = p.block_kv % 128 == 0 ? 4 : 2;
+  const int nwq = p.block_q % 128 == 0 ? 4 : 2, nqk = p.block_kv % 128 == 0 ? 4 : 2;
   const int64_t gq = nb * p.H * p.M * ((p.block_q + 32 * nwq - 1) / (32 * nwq));
-  const int64_t gk = nb * (p.H / p.hrep) * p.N * ((p.block_kv + 32 * nwk - 1) / (32 * nwk));
+  const int64_t gk = nb * (p.H / p.hrep) * p.N * ((p.block_kv + 32 * nqk - 1) / (32 * nqk));
+  const int kthreads = nqk * 64 * (D <= 128 ? 2 : 1);
   if (gq > 0) {
     if (nwq == 4)
       hipLaunchKernelGGL((bwd_dq_kernel<D, 4, VL>), dim3((unsigned)gq), dim3(256), 0, st, p);
@@ -617,10 +751,12 @@ hipError_t launch_bwd_dv(const BwdParams& p, hipStream_t st) {
       hipLaunchKernelGGL((bwd_dq_kernel<D, 2, VL>), dim3((unsigned)gq), dim3(128), 0, st, p);
   }
   if (gk > 0) {
-    if (nwk == 4)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, 4, VL>), dim3((unsigned)gk), dim3(256), 0, st, p);
+    if (nqk == 4)
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, 4, VL>), dim3((unsigned)gk), dim3(kthreads), 0, st,
+                         p);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, 2, VL>), dim3((unsigned)gk), dim3(128), 0, st, p);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, 2, VL>), dim3((unsigned)gk), dim3(kthreads), 0, st,
+                         p);
   }
   return hipGetLastError();
 }

@@ -3,7 +3,7 @@
 into.  A vector-memory instruction needs five wait states after a VALU
 instruction writes an SGPR it reads (on this chip family a base address or
 buffer descriptor restored from a spill with v_readlane); with fewer it can
-read a stale address.  This compiles the two DMA kernels' sources for gfx950
+read a stale address.  This compiles the forward and backward DMA kernels' sources for gfx950
 with the library's flags and checks every DMA in the assembly: no VALU write
 of its base SGPRs within the five wait states before it (an s_nop N counts
 N + 1).  CPU only; needs hipcc."""
@@ -75,8 +75,8 @@ def test_scanner_finds_a_planted_hazard():
 
 @pytest.mark.skipif(HIPCC is None, reason="hipcc not available")
 def test_dma_base_sgprs_are_stable(tmp_path):
-    srcs = ["bsa_fwd.hip", "bsa_fwd_pp.hip"]
-    with ThreadPoolExecutor(2) as ex:
+    srcs = ["bsa_fwd.hip", "bsa_fwd_pp.hip", "bsa_bwd.hip"]
+    with ThreadPoolExecutor(3) as ex:
         asms = list(ex.map(lambda s: _asm(s, str(tmp_path / (s + ".s"))), srcs))
     for src, lines in zip(srcs, asms):
         sites, bad = _hazards(lines)
