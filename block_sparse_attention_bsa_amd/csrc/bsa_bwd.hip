@@ -13,14 +13,11 @@
 //      V rows in LDS against Q and dO in registers; dQ^T accumulates K^T (the
 //      K tile read transposed) times dS^T.  A lane owns one query row, as in
 //      the forward, and dS feeds the last product straight from registers.
-//   3. bwd_dkdv_kernel: one workgroup per 128 keys of a KV block, walking the
-//      KV-major lists (the Q blocks that list the KV block) of every Q head of
-//      its KV head, in 64-row sub-tiles.  The roles swap: a lane owns one key,
-//      K and V sit in registers, Q and dO tiles in LDS.  Up to d = 128 the
-//      workgroup has two groups of four waves over the same 128 keys: one
-//      computes P and dV, the other dP, dS and dK, so each wave holds one
-//      accumulator and two waves share a SIMD.  Summing the group's heads in
-//      one workgroup needs no atomics.
+//   3. bwd_dkdv_kernel: one workgroup per 128 (or 64) keys of a KV block,
+//      walking the KV-major lists (the Q blocks that list the KV block) of
+//      every Q head of its KV head, in 64-row sub-tiles.  The roles swap: a
+//      lane owns one key, K and V sit in registers, Q and dO tiles in LDS.
+//      Summing the group's heads in one workgroup needs no atomics.
 // Tiles move from HBM straight into LDS (global_load_lds) in a swizzled
 // row-major layout that both the row reads and the transposing reads
 // (ds_read_b64_tr_b16) take without bank conflicts; two LDS stages up to
@@ -47,9 +44,9 @@ typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
 typedef __attribute__((address_space(3))) char lds_char;
 
-// A dQ workgroup of NW waves owns 32*NW rows, a dK/dV workgroup 32*NQ keys
-// (per group): 4 when the block size is a multiple of 128, else 2.  The
-// other side streams in sub-tiles of kBwdT positions.
+// A dQ workgroup of NW waves owns 32*NW rows, a dK/dV workgroup of NQ waves
+// 32*NQ keys: 4 when the block size is a multiple of 128, else 2.  The other
+// side streams in sub-tiles of kBwdT positions.
 constexpr int kBwdT = 64;
 
 __device__ __forceinline__ uint32_t word4(const uint4& v, int i) {
@@ -511,26 +508,27 @@ void bwd_dq_kernel(const BwdParams p) {
   }
 }
 
-// NQ waves per group own 32 keys each (NQ*32 keys per workgroup).  Up to
-// d = 128 (SPLIT) two groups share them: group 0 computes P and dV, group 1
-// dP, dS and dK, each wave holding one accumulator; above, NQ waves compute
-// both.  Group 0 stages the Q and dO tiles and the rows' LSE and row dots.
+// NQ waves own 32 keys each (NQ*32 keys per workgroup); each computes P,
+// dV, dP, dS and dK for its keys.  (Two groups of waves, one for dV and one
+// for dK, each holding one accumulator at two waves per SIMD, measured
+// slower at d = 128: 1.03 against 0.56 ms on the d128 sweep, the registers
+// of the shared path spilled.)  The waves stage the Q and dO tiles and the
+// rows' LSE and row dots.
 template <int D, int NQ, bool VL>
-__global__ __launch_bounds__(NQ * 64 * (D <= 128 ? 2 : 1))
-__attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
+__global__ __launch_bounds__(NQ * 64)
+__attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1)))
 void bwd_dkdv_kernel(const BwdParams p) {
-  constexpr bool SPLIT = D <= 128;
   constexpr int TW = NQ * 32;
   constexpr int DS = D / 16, DB = D / 32;
   constexpr int ST = D <= 128 ? 2 : 1;  // LDS stages of (Q, dO) tiles
   using T = BTile<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[ST * 2 * T::BYTES];
-  __shared__ float lse2s[ST][kBwdT], drows[ST][kBwdT];
+  __shared__ __attribute__((aligned(16))) float lse2s[ST][kBwdT];
+  __shared__ __attribute__((aligned(16))) float drows[ST][kBwdT];
 
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, h32 = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wq = w % NQ;
-  const bool g_dv = !SPLIT || w < NQ, g_dk = !SPLIT || w >= NQ;
   const int ksub = cdiv(p.block_kv, TW);
   int t = blockIdx.x;
   const int s = t % ksub;
@@ -554,17 +552,15 @@ void bwd_dkdv_kernel(const BwdParams p) {
   const __bf16* vrow = reinterpret_cast<const __bf16*>(p.v) + b * p.v_sb + ktok * p.v_ss + hk * p.v_sh;
   uint4 kf[DS], vf[DS];
   row_frags<D>(krow, kvalid, h32, kf);
-  row_frags<D>(vrow, kvalid && g_dk, h32, vf);
+  row_frags<D>(vrow, kvalid, h32, vf);
 
-  // acc: dV (group 0, or every wave) or dK (group 1); acc2: dK when a wave
-  // computes both
-  f32x16_t acc[DB], acc2[DB];
+  f32x16_t dv[DB], dk[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      acc[db][r] = 0.f;
-      acc2[db][r] = 0.f;
+      dv[db][r] = 0.f;
+      dk[db][r] = 0.f;
     }
   const int arow = swap_b23(l32), asw = T::swz(arow);
   const TrGeo<D> tg(lane);
@@ -602,9 +598,8 @@ void bwd_dkdv_kernel(const BwdParams p) {
     W.S = sv0.Sq;
     float l2n = 0.f, drn = 0.f;  // wave 0: its lane's row of the staged sub-tile
     // Q and dO rows (and the rows' LSE and row dots) of the walk's current
-    // sub-tile into a stage, by group 0
+    // sub-tile into a stage
     auto issue = [&](int stage) {
-      if (w >= NQ) return;
       const int nr = min(kBwdT, W.end - W.pos), r0 = W.pos;
       const uint32_t ql = lds0 + stage * 2 * T::BYTES;
       stage_tile<D, NQ>(qb0 + (int64_t)r0 * p.q_ss, p.q_ss, nr, ql, w, lane);
@@ -636,15 +631,14 @@ void bwd_dkdv_kernel(const BwdParams p) {
       {
         const unsigned char* qt = smem + st * 2 * T::BYTES;
         const unsigned char* gt = qt + T::BYTES;
-        // per half (rows 32*hf ..): S, and dP where dK is computed, then P
-        // or dS packed for the last product; one half at a time keeps the
-        // registers of the other free
         // kept rows of this sub-tile for this lane's key
         int rlo = 0, rhi = kBwdT - 1;
         if (list == 0) rows_kept(p, sv0.kvv, key, r0, j, rlo, rhi);
         rhi = kvalid ? min(rhi, nr - 1) : -1;
-        uint32_t pk[2][8];                 // P (dV group) or dS (dK group)
-        uint32_t pks[SPLIT ? 1 : 2][8];    // dS, when one wave computes both
+        // per half (rows 32*hf ..): S and dP, then P and dS packed for the
+        // last products; one half at a time keeps the registers of the other
+        // free
+        uint32_t pk[2][8], pks[2][8];  // P, dS
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           f32x16_t sa, da;
@@ -655,19 +649,21 @@ void bwd_dkdv_kernel(const BwdParams p) {
           }
           const unsigned char* qr = qt + (arow + 32 * hf) * (D / 8) * 16;
           const unsigned char* gr = gt + (arow + 32 * hf) * (D / 8) * 16;
-          if (g_dk) {
+          // this lane's rows of the half, 32 hf + 16 r8 + 8 h32 + 0..7 (r8 = 0,
+          // 1): their LSE and row dots read as vectors ahead of the products
+          // (element by element, each read's latency was exposed)
+          float4 l4[4], d4[4];
 #pragma unroll
-            for (int ks = 0; ks < DS; ++ks) {
-              const int c = ((2 * ks + h32) ^ asw) * 16;
-              sa = mfma32(*reinterpret_cast<const uint4*>(qr + c), kf[ks], sa);
-              da = mfma32(*reinterpret_cast<const uint4*>(gr + c), vf[ks], da);
-            }
-          } else {
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int r = 32 * hf + 16 * (q4 >> 1) + 8 * h32 + 4 * (q4 & 1);
+            l4[q4] = *reinterpret_cast<const float4*>(&lse2s[st][r]);
+            d4[q4] = *reinterpret_cast<const float4*>(&drows[st][r]);
+          }
 #pragma unroll
-            for (int ks = 0; ks < DS; ++ks) {
-              const int c = ((2 * ks + h32) ^ asw) * 16;
-              sa = mfma32(*reinterpret_cast<const uint4*>(qr + c), kf[ks], sa);
-            }
+          for (int ks = 0; ks < DS; ++ks) {
+            const int c = ((2 * ks + h32) ^ asw) * 16;
+            sa = mfma32(*reinterpret_cast<const uint4*>(qr + c), kf[ks], sa);  // S
+            da = mfma32(*reinterpret_cast<const uint4*>(gr + c), vf[ks], da);  // dP
           }
 #pragma unroll
           for (int x = 0; x < 8; ++x) {
@@ -677,25 +673,19 @@ void bwd_dkdv_kernel(const BwdParams p) {
               const int reg = 2 * x + y;
               const int rl = 16 * (reg >> 3) + 8 * h32 + (reg & 7) + 32 * hf;
               const bool keep = rl >= rlo && rl <= rhi;
-              const float pr =
-                  keep ? __builtin_amdgcn_exp2f(fmaf(sa[reg], p.c, -lse2s[st][rl])) : 0.f;
-              if constexpr (SPLIT) {
-                v[y] = g_dv ? pr : pr * (da[reg] - drows[st][rl]);
-              } else {
-                v[y] = pr;
-                w2[y] = pr * (da[reg] - drows[st][rl]);
-              }
+              const int q4 = 2 * (reg >> 3) + ((reg & 7) >> 2), e4 = reg & 3;
+              const float l2 = e4 == 0 ? l4[q4].x : e4 == 1 ? l4[q4].y : e4 == 2 ? l4[q4].z : l4[q4].w;
+              const float dr = e4 == 0 ? d4[q4].x : e4 == 1 ? d4[q4].y : e4 == 2 ? d4[q4].z : d4[q4].w;
+              const float pr = keep ? __builtin_amdgcn_exp2f(fmaf(sa[reg], p.c, -l2)) : 0.f;
+              v[y] = pr;
+              w2[y] = pr * (da[reg] - dr);
             }
             pk[hf][x] = pack_bf16x2(v[0], v[1]);
-            if constexpr (!SPLIT) pks[hf][x] = pack_bf16x2(w2[0], w2[1]);
+            pks[hf][x] = pack_bf16x2(w2[0], w2[1]);
           }
         }
-        if (g_dv) tr_product<D>(gt, tg, pk[0], pk[1], acc);  // dV^T += dO^T P
-        if constexpr (SPLIT) {
-          if (g_dk) tr_product<D>(qt, tg, pk[0], pk[1], acc);  // dK^T += Q^T dS
-        } else {
-          tr_product<D>(qt, tg, pks[0], pks[1], acc2);
-        }
+        tr_product<D>(gt, tg, pk[0], pk[1], dv);    // dV^T += dO^T P
+        tr_product<D>(qt, tg, pks[0], pks[1], dk);  // dK^T += Q^T dS
       }
       if (ST == 2 && more) put_rows(st ^ 1);
       if (ST == 1) {
@@ -715,15 +705,8 @@ void bwd_dkdv_kernel(const BwdParams p) {
   if (kvalid) {
     __bf16* kdst = reinterpret_cast<__bf16*>(p.dk) + b * p.dk_sb + ktok * p.dk_ss + hk * p.dk_sh;
     __bf16* vdst = reinterpret_cast<__bf16*>(p.dv) + b * p.dv_sb + ktok * p.dv_ss + hk * p.dv_sh;
-    if constexpr (SPLIT) {
-      if (g_dk)
-        store_row<DB>(kdst, h32, acc, p.scale);
-      else
-        store_row<DB>(vdst, h32, acc, 1.f);
-    } else {
-      store_row<DB>(kdst, h32, acc2, p.scale);
-      store_row<DB>(vdst, h32, acc, 1.f);
-    }
+    store_row<DB>(kdst, h32, dk, p.scale);
+    store_row<DB>(vdst, h32, dv, 1.f);
   }
 }
 
@@ -743,7 +726,7 @@ hipError_t launch_bwd_dv(const BwdParams& p, hipStream_t st) {
   const int nwq = p.block_q % 128 == 0 ? 4 : 2, nqk = p.block_kv % 128 == 0 ? 4 : 2;
   const int64_t gq = nb * p.H * p.M * ((p.block_q + 32 * nwq - 1) / (32 * nwq));
   const int64_t gk = nb * (p.H / p.hrep) * p.N * ((p.block_kv + 32 * nqk - 1) / (32 * nqk));
-  const int kthreads = nqk * 64 * (D <= 128 ? 2 : 1);
+  const int kthreads = nqk * 64;
   if (gq > 0) {
     if (nwq == 4)
       hipLaunchKernelGGL((bwd_dq_kernel<D, 4, VL>), dim3((unsigned)gq), dim3(256), 0, st, p);
