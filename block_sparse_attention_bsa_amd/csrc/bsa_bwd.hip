@@ -142,11 +142,17 @@ __device__ __forceinline__ void stage_tile(const __bf16* base, int64_t ss, int n
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
   const void* ub = (const void*)(size_t)(((uint64_t)hi << 32) | lo);
   const int rs = (int)(ss * 2);
+  // The lane's offsets are recomputed at every call (a few VALU) instead of
+  // being hoisted as loop invariants: kept live across the kernel they
+  // spilled, and each reload from scratch waits for every vector-memory op
+  // in flight, these DMAs included, which serialized them.
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
 #pragma unroll
   for (int m = 0; m < (NI + NS - 1) / NS; ++m) {
     const int ii = m * NS + ws;
     if (ii >= NI) break;
-    const int slot = ii * 64 + lane;
+    const int slot = ii * 64 + ln;
     const int r = slot / DC, c = (slot % DC) ^ BTile<D>::swz(r);
     dma16(ub, (uint32_t)(min(r, n - 1) * rs + c * 16), lds + ii * 1024);
   }
@@ -255,30 +261,6 @@ __device__ __forceinline__ void row_frags(const __bf16* rowp, bool valid, int h3
   for (int ks = 0; ks < D / 16; ++ks)
     frag[ks] = valid ? *reinterpret_cast<const uint4*>(rowp + ks * 16 + h32 * 8)
                      : make_uint4(0, 0, 0, 0);
-}
-
-// Product over head_dim of two 32x32 tiles: rows arow and arow + 32 of an
-// LDS tile (A operand, row reads; sw = swz(arow), also that of arow + 32)
-// against this lane's fragments (B operand).
-template <int D>
-__device__ __forceinline__ void tile_dot(const unsigned char* t, int arow, int sw, int h32,
-                                         const uint4 (&frag)[D / 16], f32x16_t& s0,
-                                         f32x16_t& s1) {
-  constexpr int DC = D / 8;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    s0[r] = 0.f;
-    s1[r] = 0.f;
-  }
-  const unsigned char* r0 = t + arow * DC * 16;
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const int c = ((2 * ks + h32) ^ sw) * 16;
-    const uint4 a0 = *reinterpret_cast<const uint4*>(r0 + c);
-    const uint4 a1 = *reinterpret_cast<const uint4*>(r0 + 32 * DC * 16 + c);
-    s0 = mfma32(a0, frag[ks], s0);
-    s1 = mfma32(a1, frag[ks], s1);
-  }
 }
 
 // A lane's transposing reads of a tile (the forward's V^T reads): two reads
@@ -467,31 +449,44 @@ void bwd_dq_kernel(const BwdParams p) {
     {
       const unsigned char* kt = smem + st * 2 * T::BYTES;
       const unsigned char* vt = kt + T::BYTES;
-      f32x16_t s0, s1, d0, d1;
-      tile_dot<D>(kt, arow, asw, h32, qf, s0, s1);
-      tile_dot<D>(vt, arow, asw, h32, gf, d0, d1);
       // kept keys of this sub-tile for this lane's row
       int klo = 0, khi = kBwdT - 1;
       if (list == 0) keys_kept(p, sv0.kvv, row, k0, j, klo, khi);
       khi = min(khi, nk - 1);
-      uint32_t pk0[8], pk1[8];
+      // per half (keys 32*hf ..): S^T and dP^T, then dS packed for the last
+      // product; one half at a time keeps the registers of the other free
+      uint32_t pk[2][8];
 #pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        float v[4];
+      for (int hf = 0; hf < 2; ++hf) {
+        f32x16_t sa, da;
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-          const int reg = 2 * x + (y & 1);
-          const f32x16_t& sv_ = y < 2 ? s0 : s1;
-          const f32x16_t& dv_ = y < 2 ? d0 : d1;
-          const int key = 16 * (reg >> 3) + 8 * h32 + (reg & 7) + (y < 2 ? 0 : 32);
-          const bool keep = key >= klo && key <= khi;
-          const float pr = keep ? __builtin_amdgcn_exp2f(fmaf(sv_[reg], p.c, -lse2)) : 0.f;
-          v[y] = pr * (dv_[reg] - drow);
+        for (int r = 0; r < 16; ++r) {
+          sa[r] = 0.f;
+          da[r] = 0.f;
         }
-        pk0[x] = pack_bf16x2(v[0], v[1]);
-        pk1[x] = pack_bf16x2(v[2], v[3]);
+        const unsigned char* kr = kt + (arow + 32 * hf) * (D / 8) * 16;
+        const unsigned char* vr = vt + (arow + 32 * hf) * (D / 8) * 16;
+#pragma unroll
+        for (int ks = 0; ks < DS; ++ks) {
+          const int c = ((2 * ks + h32) ^ asw) * 16;
+          sa = mfma32(*reinterpret_cast<const uint4*>(kr + c), qf[ks], sa);  // S^T
+          da = mfma32(*reinterpret_cast<const uint4*>(vr + c), gf[ks], da);  // dP^T
+        }
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          float v[2];
+#pragma unroll
+          for (int y = 0; y < 2; ++y) {
+            const int reg = 2 * x + y;
+            const int key = 16 * (reg >> 3) + 8 * h32 + (reg & 7) + 32 * hf;
+            const bool keep = key >= klo && key <= khi;
+            const float pr = keep ? __builtin_amdgcn_exp2f(fmaf(sa[reg], p.c, -lse2)) : 0.f;
+            v[y] = pr * (da[reg] - drow);
+          }
+          pk[hf][x] = pack_bf16x2(v[0], v[1]);
+        }
       }
-      tr_product<D>(kt, tg, pk0, pk1, acc);  // dQ^T += K^T dS^T
+      tr_product<D>(kt, tg, pk[0], pk[1], acc);  // dQ^T += K^T dS^T
     }
     if (ST == 1) {
       __syncthreads();  // every wave is done with the stage
