@@ -418,8 +418,9 @@ def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
         raise ValueError("q, k and v must be dense (their gradients take their strides)")
-    work = None if noalloc else torch.empty(max(B * H * Sq, 1), dtype=torch.float32,
-                                            device=q.device)
+    # row dots, then the dK/dV start order
+    work = None if noalloc else torch.empty(max(B * H * Sq + B * Hkv * N, 1),
+                                            dtype=torch.float32, device=q.device)
     if kv_valid is not None:
         _dev("kv_valid", kv_valid, torch.int32)
         if not kv_valid.is_contiguous() or kv_valid.numel() < N:
@@ -504,7 +505,8 @@ def bsa_varlen_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.T
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
         raise ValueError("q, k and v must be dense (their gradients take their strides)")
-    work = torch.empty(max(H * Tq, 1), dtype=torch.float32, device=q.device)
+    # row dots, then the dK/dV start order
+    work = torch.empty(max(H * Tq + Hkv * tkv, 1), dtype=torch.float32, device=q.device)
     kvv_ld = 0
     if kv_valid is not None:
         _dev("kv_valid", kv_valid, torch.int32)

@@ -526,6 +526,11 @@ bsa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, 
   p.c = softmax_scale * kLog2e;
   p.scale = softmax_scale;
   if (noalloc && bsa::bwd_noalloc_scratch(&p.drow) != hipSuccess) return BSA_ERR_HIP;
+  // the dK/dV launch order follows the row dots in the workspace (the static
+  // array of the allocation-free entry point holds it when it fits)
+  const int64_t rows = (int64_t)B * H * Sq, items = (int64_t)B * H_kv * N;
+  if (items <= bsa::kBwdOrderMaxItems && (!noalloc || rows + items <= bsa::kBwdNoallocMaxRows))
+    p.kv_order = reinterpret_cast<int32_t*>(p.drow + rows);
   const hipError_t e = bsa::launch_bwd(p, D, stream);
   return e == hipSuccess ? BSA_OK : BSA_ERR_HIP;
 }
@@ -633,6 +638,10 @@ bsa_status bsa_varlen_bwd(const void* q, const void* k, const void* v, const voi
   p.cu_q = cu_seqlens_q; p.cu_k = cu_seqlens_k; p.cu_m = cu_total_m_blocks;
   p.cu_n = cu_total_kv_blocks; p.boff = block_idx_offsets;
   p.varlen = true;
+  // the dK/dV launch order follows the row dots in the workspace
+  const int64_t items = (int64_t)H_kv * total_kv_blocks;
+  if (items <= bsa::kBwdOrderMaxItems)
+    p.kv_order = reinterpret_cast<int32_t*>(work + (int64_t)H * total_q);
   const hipError_t e = bsa::launch_bwd(p, D, stream);
   return e == hipSuccess ? BSA_OK : BSA_ERR_HIP;
 }

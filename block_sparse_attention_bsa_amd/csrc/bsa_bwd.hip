@@ -528,6 +528,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
   int t = blockIdx.x;
   const int s = t % ksub;
   t /= ksub;
+  if (p.kv_order) t = p.kv_order[t];  // longest lists first
   // nrow: the KV-major list row (batched: KV block j; varlen: global KV block id)
   const int nrow = t % p.N;
   t /= p.N;
@@ -705,6 +706,53 @@ void bwd_dkdv_kernel(const BwdParams p) {
   }
 }
 
+// The dK/dV workgroups' work varies with their KV-major list lengths (the
+// number of Q blocks that list the KV block, over the KV head's Q heads);
+// started in index order, a long one can start last and set the kernel's
+// end.  One workgroup counting-sorts the n rows by decreasing length into
+// `order` (buckets of one length each up to 1023, longer ones together;
+// order inside a bucket is arbitrary and does not change any result).
+constexpr int kOrderBuckets = 1024;
+
+template <bool VL>
+__global__ __launch_bounds__(kOrderBuckets) void bwd_kv_order_kernel(const BwdParams p, int n) {
+  __shared__ int hist[kOrderBuckets];
+  const int tid = threadIdx.x;
+  const int Hkv = p.H / p.hrep;
+  auto bucket = [&](int t) {  // kOrderBuckets - 1 - min(length, kOrderBuckets - 1)
+    const int nrow = t % p.N, rest = t / p.N;
+    const int hk = VL ? rest : rest % Hkv, b = VL ? 0 : rest / Hkv;
+    int len = 0;
+    for (int h = hk * p.hrep; h < (hk + 1) * p.hrep; ++h) {
+      if (p.tmcnt)
+        len += max(p.tmcnt[VL ? h * p.tmc_s[1] + nrow * p.tmc_s[2]
+                              : b * p.tmc_s[0] + h * p.tmc_s[1] + nrow * p.tmc_s[2]], 0);
+      if (p.tfcnt)
+        len += max(p.tfcnt[VL ? h * p.tfc_s[1] + nrow * p.tfc_s[2]
+                              : b * p.tfc_s[0] + h * p.tfc_s[1] + nrow * p.tfc_s[2]], 0);
+    }
+    return kOrderBuckets - 1 - min(len, kOrderBuckets - 1);
+  };
+  hist[tid] = 0;
+  __syncthreads();
+  for (int t = tid; t < n; t += kOrderBuckets) atomicAdd(&hist[bucket(t)], 1);
+  __syncthreads();
+  // exclusive prefix sum over the buckets (one per thread)
+  const int mine = hist[tid];
+  int incl = mine;
+  for (int o = 1; o < kOrderBuckets; o <<= 1) {
+    __syncthreads();
+    const int add = tid >= o ? hist[tid - o] : 0;
+    __syncthreads();
+    incl += add;
+    hist[tid] = incl;
+  }
+  __syncthreads();
+  hist[tid] = incl - mine;
+  __syncthreads();
+  for (int t = tid; t < n; t += kOrderBuckets) p.kv_order[atomicAdd(&hist[bucket(t)], 1)] = t;
+}
+
 template <int D, bool VL>
 hipError_t launch_bwd_dv(const BwdParams& p, hipStream_t st) {
   // varlen: the row dots run over [H, total_q] as one sequence of Sq rows
@@ -727,6 +775,11 @@ hipError_t launch_bwd_dv(const BwdParams& p, hipStream_t st) {
       hipLaunchKernelGGL((bwd_dq_kernel<D, 4, VL>), dim3((unsigned)gq), dim3(256), 0, st, p);
     else
       hipLaunchKernelGGL((bwd_dq_kernel<D, 2, VL>), dim3((unsigned)gq), dim3(128), 0, st, p);
+  }
+  if (gk > 0 && p.kv_order) {
+    const int64_t items = nb * (p.H / p.hrep) * p.N;
+    hipLaunchKernelGGL(bwd_kv_order_kernel<VL>, dim3(1), dim3(kOrderBuckets), 0, st, p,
+                       (int)items);
   }
   if (gk > 0) {
     if (nqk == 4)

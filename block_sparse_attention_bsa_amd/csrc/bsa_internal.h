@@ -111,7 +111,12 @@ struct BwdParams {
   const int32_t* boff;
   int64_t kvv_ld;
   bool varlen;
+  // dK/dV launch order (workspace, written by the launch): the KV-block
+  // rows by decreasing KV-major list length, or nullptr for index order
+  int32_t* kv_order;
 };
+// Rows the dK/dV launch order covers at most (beyond it: index order).
+constexpr int64_t kBwdOrderMaxItems = (int64_t)1 << 20;
 hipError_t launch_bwd(const BwdParams& p, int D, hipStream_t s);
 // Rows (B*H*Sq) the allocation-free backward's static row-dot array holds.
 constexpr int64_t kBwdNoallocMaxRows = (int64_t)1 << 22;

@@ -221,7 +221,9 @@ bsa_status bsa_mask_to_index(const uint8_t* mask, int32_t B, int32_t H, int32_t 
  *  mask_t / full_t: their KV-major transposes (bsa_kv_major_lists):
  *    cnt [B,H,N], idx [B,H,N,M] through the same stride fields (cnt_stride
  *    over {b, h, j}, idx_stride over {b, h, j, s}); cnt == NULL: absent.
- *  work: device fp32 scratch of B*H*Sq entries (row dots), overwritten.
+ *  work: device scratch of B*H*Sq + B*H_kv*ceil(Sk/block_kv) 4-byte
+ *    entries (fp32 row dots, then the int32 order in which the dK/dV
+ *    workgroups start: longest KV-major lists first), overwritten.
  * dq, dk, dv are overwritten everywhere (zero where nothing is listed).
  * Returns BSA_ERR_INVALID_ARGUMENT / BSA_ERR_UNSUPPORTED / BSA_ERR_MISALIGNED
  * for bad arguments, BSA_ERR_HIP if a launch fails.  Deterministic: no atomics. */
@@ -235,8 +237,9 @@ bsa_status bsa_bwd(const void* q, const void* k, const void* v, const void* o, c
 
 /* bsa_bwd without the `work` argument, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving or training
- * loops, harnesses that forbid hipMalloc.  The row dots go to a static
- * device array of BSA_BWD_NOALLOC_MAX_ROWS floats (16 MiB) that the library
+ * loops, harnesses that forbid hipMalloc.  The row dots (and, when they fit
+ * beside them, the dK/dV start order) go to a static device array of
+ * BSA_BWD_NOALLOC_MAX_ROWS 4-byte entries (16 MiB) that the library
  * holds on every GPU it runs on until the process ends; its address is looked
  * up once per device on the first call there.  The call allocates nothing
  * (no hipMalloc, hipFree or allocating library routine).  B*H*Sq above the
@@ -292,7 +295,8 @@ bsa_status bsa_kv_major_lists(const int32_t* cnt, const int32_t* idx, int32_t B,
  *    and idx_stride[3] (slot), row (b, j) at slot block_idx_offsets[b] +
  *    j*num_m(b); cnt == NULL: absent.
  *  kv_valid, kv_valid_ld: as for bsa_varlen_fwd (per sequence-local KV block).
- *  work: device fp32 scratch of H*total_q entries (row dots), overwritten.
+ *  work: device scratch of H*total_q + H_kv*total_kv_blocks 4-byte entries
+ *    (fp32 row dots, then the int32 dK/dV start order), overwritten.
  * dq and dk, dv are overwritten on every token of the sequences (zero where
  * nothing is listed).  Errors as bsa_bwd.  Deterministic: no atomics. */
 bsa_status bsa_varlen_bwd(const void* q, const void* k, const void* v, const void* o,
