@@ -320,29 +320,40 @@ __device__ __forceinline__ void store_row(__bf16* dst, int h32, const f32x16_t (
     }
 }
 
-// D[b,h,r] = sum_d dO * O (fp32), one thread per row.
+// D[b,h,r] = sum_d dO * O (fp32).  16 lanes per row, each summing 16-byte
+// chunks c = l16, l16 + 16, ... of both rows, so a row's loads coalesce;
+// the lanes' sums are added with shuffles.  The summation order is fixed.
+constexpr int kRowdotLanes = 16;
+
 template <int D>
 __global__ __launch_bounds__(256) void bwd_rowdot_kernel(const BwdParams p) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t t = ((int64_t)blockIdx.x * 256 + threadIdx.x) / kRowdotLanes;
+  const int l16 = threadIdx.x % kRowdotLanes;
   const int64_t rows = (int64_t)p.B * p.H * p.Sq;
-  if (t >= rows) return;
-  const int r = (int)(t % p.Sq);
-  const int64_t bh = t / p.Sq;
+  const bool live = t < rows;
+  const int64_t tt = live ? t : 0;
+  const int r = (int)(tt % p.Sq);
+  const int64_t bh = tt / p.Sq;
   const int h = (int)(bh % p.H), b = (int)(bh / p.H);
-  const __bf16* o = reinterpret_cast<const __bf16*>(p.o) + b * p.o_sb + r * p.o_ss + h * p.o_sh;
-  const __bf16* g = reinterpret_cast<const __bf16*>(p.dout) + b * p.do_sb + r * p.do_ss + h * p.do_sh;
+  const __bf16* o = reinterpret_cast<const __bf16*>(p.o) + b * p.o_sb + (int64_t)r * p.o_ss + h * p.o_sh;
+  const __bf16* g = reinterpret_cast<const __bf16*>(p.dout) + b * p.do_sb + (int64_t)r * p.do_ss + h * p.do_sh;
   float acc = 0.f;
-  for (int c = 0; c < D / 8; ++c) {
-    const uint4 a = *reinterpret_cast<const uint4*>(o + c * 8);
-    const uint4 e = *reinterpret_cast<const uint4*>(g + c * 8);
+  if (live) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t x = word4(a, i), y = word4(e, i);
-      acc = fmaf(__uint_as_float(x << 16), __uint_as_float(y << 16), acc);
-      acc = fmaf(__uint_as_float(x & 0xffff0000u), __uint_as_float(y & 0xffff0000u), acc);
+    for (int c = l16; c < D / 8; c += kRowdotLanes) {
+      const uint4 a = *reinterpret_cast<const uint4*>(o + c * 8);
+      const uint4 e = *reinterpret_cast<const uint4*>(g + c * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t x = word4(a, i), y = word4(e, i);
+        acc = fmaf(__uint_as_float(x << 16), __uint_as_float(y << 16), acc);
+        acc = fmaf(__uint_as_float(x & 0xffff0000u), __uint_as_float(y & 0xffff0000u), acc);
+      }
     }
   }
-  p.drow[t] = acc;
+#pragma unroll
+  for (int m = kRowdotLanes / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m);
+  if (live && l16 == 0) p.drow[t] = acc;
 }
 
 // log2-domain LSE for exp2(s*c - lse2); a row with no key (LSE = -inf) gives
@@ -760,8 +771,9 @@ hipError_t launch_bwd_dv(const BwdParams& p, hipStream_t st) {
   if (rows > 0) {
     BwdParams pr = p;
     if (VL) pr.B = 1;
-    hipLaunchKernelGGL(bwd_rowdot_kernel<D>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
-                       st, pr);
+    const int64_t per = 256 / kRowdotLanes;
+    hipLaunchKernelGGL(bwd_rowdot_kernel<D>, dim3((unsigned)((rows + per - 1) / per)), dim3(256),
+                       0, st, pr);
   }
   // batched: B*H*M Q-block rows and B*H_kv*N KV-block rows; varlen: the
   // M and N totals over the sequences carry the batch
