@@ -365,6 +365,20 @@ __device__ __forceinline__ bool advance(Item& it, ListWalk& L, int lane, int Sk)
 // Cap on a lane's sum of P in the 256-row kernel's lazy running max.
 constexpr float kSumCap = 65536.f;
 
+// max over the two lane halves (lanes l and l ^ 32).  v_permlane32_swap
+// trades the upper half of its first operand for the lower half of its
+// second, so with x in both, one result holds x of the lower half in every
+// lane and the other x of the upper half (no LDS round trip, unlike a
+// shuffle through ds_bpermute).  The two results are copied out as scalars
+// before the cast: a __builtin_bit_cast of a vector element reads the
+// vector's first element, whatever the index.
+__device__ __forceinline__ float half_swap_max(float x) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+  const uint32_t lo = r[0], hi = r[1];
+  return fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
+}
+
 // Online-softmax step for one 64-key sub-tile.  s0/s1 hold S^T for keys
 // 0..31 / 32..63 of the sub-tile (raw dot products).  Applies the element
 // mask, updates the running max m (base-2 units of scale*s), the running sum
@@ -424,7 +438,7 @@ __device__ __forceinline__ void softmax_step(f32x16_t& s0, f32x16_t& s1, const I
   t[10] = fmaxf(s0[15], s1[15]);
   float mx = fmaxf(fmaxf(fmaxf(fmaxf(t[0], t[1]), t[2]), fmaxf(fmaxf(t[3], t[4]), t[5])),
                    fmaxf(fmaxf(fmaxf(t[6], t[7]), t[8]), fmaxf(t[9], t[10])));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = half_swap_max(mx);
   const float m_new = fmaxf(m_run, mx * c);
   if (__any(m_new > m_run)) {
     const float m_use = (m_new == neg_inf()) ? 0.f : m_new;

@@ -126,19 +126,6 @@ __device__ __forceinline__ uint2 read_tr(const char* lds, int byte_off) {
   return __builtin_bit_cast(uint2, v);
 }
 
-// max over the two lane halves (lanes l and l ^ 32).  v_permlane32_swap
-// trades the upper half of its first operand for the lower half of its
-// second, so with x in both, one result holds x of the lower half in every
-// lane and the other x of the upper half.  The two results are copied out
-// as scalars before the cast: a __builtin_bit_cast of a vector element
-// reads the vector's first element, whatever the index.
-__device__ __forceinline__ float half_swap_max(float x) {
-  const uint32_t a = __builtin_bit_cast(uint32_t, x);
-  const auto r = __builtin_amdgcn_permlane32_swap(a, a, false, false);
-  const uint32_t lo = r[0], hi = r[1];
-  return fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
-}
-
 // What the pipeline keeps of an item: first key, and the visible-key count
 // (1..64) with the mask-list flag in bit 7.  nm == 0: no item (past the end).
 struct Sub {

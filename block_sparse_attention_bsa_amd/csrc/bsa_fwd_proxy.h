@@ -95,7 +95,7 @@ __device__ __forceinline__ void softmax_step_any(f32x16_t& s0, f32x16_t& s1, con
   t[10] = fmaxf(s0[15], s1[15]);
   float mx = fmaxf(fmaxf(fmaxf(fmaxf(t[0], t[1]), t[2]), fmaxf(fmaxf(t[3], t[4]), t[5])),
                    fmaxf(fmaxf(fmaxf(t[6], t[7]), t[8]), fmaxf(t[9], t[10])));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = half_swap_max(mx);
   const float m_new = fmaxf(m_run, mx * c);
   if (__any(m_new > m_run)) {
     const float m_use = (m_new == neg_inf()) ? 0.f : m_new;
