@@ -455,7 +455,8 @@ def bsa_varlen_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.T
                    block_q: int, block_kv: int, mask_mod: int = MASK_NONE,
                    kv_valid: Optional[torch.Tensor] = None,
                    softmax_scale: Optional[float] = None,
-                   window: Optional[Tuple[int, int]] = None):
+                   window: Optional[Tuple[int, int]] = None,
+                   max_seqlen_k: Optional[int] = None):
     """Backward of bsa_varlen_fwd (bf16): returns (dq [Tq,H,D], dk, dv [Tk,Hkv,D]).
     o and lse [H,Tq] are the forward's outputs, dout the gradient of o; the cu
     arrays, totals, lists (cnt [H,total_m_blocks], idx [H,total_n_blocks]),
@@ -513,6 +514,11 @@ def bsa_varlen_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.T
         if kv_valid.dim() not in (1, 2) or kv_valid.stride(-1) != 1 or \
                 (kv_valid.dim() == 2 and kv_valid.shape[0] != B):
             raise ValueError("kv_valid must be int32 [B, W] or [W] with a contiguous last dimension")
+        if max_seqlen_k is None:
+            max_seqlen_k = int((cu_seqlens_k[1:] - cu_seqlens_k[:-1]).max().item()) if B else 0
+        need = -(-int(max_seqlen_k) // block_kv) if block_kv > 0 else 0
+        if kv_valid.shape[-1] < need:
+            raise ValueError(f"kv_valid rows need {need} entries (ceil(max_seqlen_k / block_kv))")
         kvv_ld = kv_valid.stride(0) if kv_valid.dim() == 2 else 0
     elif mask_mod == MASK_KV_VALID_COUNT and mask_list is not None:
         raise ValueError("MASK_KV_VALID_COUNT needs kv_valid")

@@ -3,8 +3,9 @@ the same bf16 inputs.  The forward's O and LSE come from bsa_fwd.
 
 Tolerance: P and dS enter their MFMA products rounded to bf16 (relative
 error up to 2^-9 each), O enters rowsum(dO * O) as stored (bf16), and the
-gradients are stored in bf16.  Each gradient must be within 2 % of its
-largest magnitude of the float64 gradient, element by element."""
+gradients are stored in bf16.  Each gradient must be within 1 % of its
+largest magnitude of the float64 gradient, element by element (the cases
+here, full-size ones included, reach at most 0.46 %)."""
 import math
 import zlib
 
@@ -19,7 +20,7 @@ from bsa_testlib import as_oracle, to_dev
 pytestmark = pytest.mark.gpu
 
 NONE, CAUSAL, KVV, LOCAL = bsa.MASK_NONE, bsa.MASK_CAUSAL, bsa.MASK_KV_VALID_COUNT, bsa.MASK_LOCAL
-REL_TOL = 2e-2
+REL_TOL = 1e-2
 
 
 def _lists(m):
@@ -91,6 +92,16 @@ def test_bwd_rejects_unsupported():
     fl = _lists(np.ones((1, 1, 1, 1), bool))
     with pytest.raises(bsa.BsaError):
         bsa.bsa_bwd(q, q, q, q, lse, q, None, fl, 64, 64)
+    # valid counts shorter than the KV-block count, strided, or missing
+    q = torch.zeros((1, 128, 1, 64), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((1, 1, 128), dtype=torch.float32, device="cuda")
+    ml = _lists(np.ones((1, 1, 2, 2), bool))
+    for kvv in (torch.zeros(1, dtype=torch.int32, device="cuda"),
+                torch.zeros(4, dtype=torch.int32, device="cuda")[::2]):
+        with pytest.raises(ValueError):
+            bsa.bsa_bwd(q, q, q, q, lse, q, ml, None, 64, 64, KVV, kvv)
+    with pytest.raises(ValueError):
+        bsa.bsa_bwd(q, q, q, q, lse, q, ml, None, 64, 64, KVV, None)
 
 
 def test_bwd_full_size_sweep_sampled_heads():
@@ -216,3 +227,17 @@ def test_varlen_kv_major_lists_bit_exact(sq, sk, bq, bk):
     rc, ri = oracle.varlen_kv_major_lists(full, sq, sk, bq, bk)
     np.testing.assert_array_equal(cnt_t.cpu().numpy(), rc)
     np.testing.assert_array_equal(idx_t.cpu().numpy(), ri)
+
+
+def test_varlen_bwd_rejects_short_valid_counts():
+    # per-sequence valid counts must cover ceil(max_seqlen_k / block_kv) blocks
+    rng = np.random.default_rng(3)
+    sq, sk, H, D, bq, bk = [100, 60], [200, 90], 2, 64, 64, 64
+    full, part, ml, fl, kvv, m = _varlen_setup(rng, KVV, sq, sk, H, H, D, bq, bk)
+    q = torch.zeros((sum(sq), H, D), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((sum(sk), H, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((H, sum(sq)), dtype=torch.float32, device="cuda")
+    short = torch.from_numpy(kvv[:, :2].copy()).cuda()  # 4 blocks needed (200 keys)
+    with pytest.raises(ValueError):
+        bsa.bsa_varlen_bwd(q, k, k, q, lse, q, m["cu_q"], m["cu_k"], m["cu_m"], m["cu_kv"],
+                           m["offs"], m["tm"], m["tkv"], m["tn"], ml, fl, bq, bk, KVV, short)
