@@ -235,7 +235,14 @@ void bsa_fwd_pp_kernel(const FwdParams p) {
   const bool g1 = w >= 4;
 
   TileInfo ti;
-  if (!decode_tile<256, VARLEN ? 1 : 0>(p, xcd_remap(blockIdx.x, p.num_tiles), ti)) return;
+  // Batched tiles in dispatch order: the GPU then works on about one head's Q
+  // tiles at a time, whose K/V the 256 MB last-level cache holds (each XCD a
+  // contiguous range, as the other kernels do, keeps eight heads in flight
+  // and measured 2 % slower on the video workload); varlen keeps the XCD
+  // ranges, which its longest-first order was measured with.
+  if (!decode_tile<256, VARLEN ? 1 : 0>(p, VARLEN ? xcd_remap(blockIdx.x, p.num_tiles)
+                                                   : (int)blockIdx.x, ti))
+    return;
   // GQA packing: wave w holds rows (32*w) % R .. of head ti.h + 32*w / R
   // (R = 256 / gpack rows per head), and every head of the tile walks the
   // same items.  Without packing R = 256 and dh = 0.
