@@ -26,6 +26,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "bsa_fwd_common.h"
 
@@ -520,10 +521,15 @@ void bwd_dq_kernel(const BwdParams p) {
 // slower at d = 128: 1.03 against 0.56 ms on the d128 sweep, the registers
 // of the shared path spilled.)  The waves stage the Q and dO tiles and the
 // rows' LSE and row dots.
-template <int D, int NQ, bool VL>
+// MODE: 0 computes dV and dK; 1 dV only; 2 dK only.  At d = 256 the two
+// accumulators, K and V fragments and the products' operands need more than
+// the 512 registers of a wave, so dV and dK run as two launches (S computed
+// in both) instead of one that spills.
+template <int D, int NQ, bool VL, int MODE>
 __global__ __launch_bounds__(NQ * 64)
 __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1)))
 void bwd_dkdv_kernel(const BwdParams p) {
+  constexpr bool DO_DV = MODE != 2, DO_DK = MODE != 1;
   constexpr int TW = NQ * 32;
   constexpr int DS = D / 16, DB = D / 32;
   constexpr int ST = D <= 128 ? 2 : 1;  // LDS stages of (Q, dO) tiles
@@ -559,7 +565,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
   const __bf16* vrow = reinterpret_cast<const __bf16*>(p.v) + b * p.v_sb + ktok * p.v_ss + hk * p.v_sh;
   uint4 kf[DS], vf[DS];
   row_frags<D>(krow, kvalid, h32, kf);
-  row_frags<D>(vrow, kvalid, h32, vf);
+  if (DO_DK) row_frags<D>(vrow, kvalid, h32, vf);
 
   f32x16_t dv[DB], dk[DB];
 #pragma unroll
@@ -670,7 +676,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
           for (int ks = 0; ks < DS; ++ks) {
             const int c = ((2 * ks + h32) ^ asw) * 16;
             sa = mfma32(*reinterpret_cast<const uint4*>(qr + c), kf[ks], sa);  // S
-            da = mfma32(*reinterpret_cast<const uint4*>(gr + c), vf[ks], da);  // dP
+            if (DO_DK) da = mfma32(*reinterpret_cast<const uint4*>(gr + c), vf[ks], da);  // dP
           }
 #pragma unroll
           for (int x = 0; x < 8; ++x) {
@@ -685,14 +691,14 @@ void bwd_dkdv_kernel(const BwdParams p) {
               const float dr = e4 == 0 ? d4[q4].x : e4 == 1 ? d4[q4].y : e4 == 2 ? d4[q4].z : d4[q4].w;
               const float pr = keep ? __builtin_amdgcn_exp2f(fmaf(sa[reg], p.c, -l2)) : 0.f;
               v[y] = pr;
-              w2[y] = pr * (da[reg] - dr);
+              w2[y] = DO_DK ? pr * (da[reg] - dr) : 0.f;
             }
-            pk[hf][x] = pack_bf16x2(v[0], v[1]);
-            pks[hf][x] = pack_bf16x2(w2[0], w2[1]);
+            if (DO_DV) pk[hf][x] = pack_bf16x2(v[0], v[1]);
+            if (DO_DK) pks[hf][x] = pack_bf16x2(w2[0], w2[1]);
           }
         }
-        tr_product<D>(gt, tg, pk[0], pk[1], dv);    // dV^T += dO^T P
-        tr_product<D>(qt, tg, pks[0], pks[1], dk);  // dK^T += Q^T dS
+        if (DO_DV) tr_product<D>(gt, tg, pk[0], pk[1], dv);    // dV^T += dO^T P
+        if (DO_DK) tr_product<D>(qt, tg, pks[0], pks[1], dk);  // dK^T += Q^T dS
       }
       if (ST == 2 && more) put_rows(st ^ 1);
       if (ST == 1) {
@@ -712,8 +718,8 @@ void bwd_dkdv_kernel(const BwdParams p) {
   if (kvalid) {
     __bf16* kdst = reinterpret_cast<__bf16*>(p.dk) + b * p.dk_sb + ktok * p.dk_ss + hk * p.dk_sh;
     __bf16* vdst = reinterpret_cast<__bf16*>(p.dv) + b * p.dv_sb + ktok * p.dv_ss + hk * p.dv_sh;
-    store_row<DB>(kdst, h32, dk, p.scale);
-    store_row<DB>(vdst, h32, dv, 1.f);
+    if (DO_DK) store_row<DB>(kdst, h32, dk, p.scale);
+    if (DO_DV) store_row<DB>(vdst, h32, dv, 1.f);
   }
 }
 
@@ -793,13 +799,22 @@ hipError_t launch_bwd_dv(const BwdParams& p, hipStream_t st) {
     hipLaunchKernelGGL(bwd_kv_order_kernel<VL>, dim3(1), dim3(kOrderBuckets), 0, st, p,
                        (int)items);
   }
-  if (gk > 0) {
+  auto dkdv = [&](auto mode) {
+    constexpr int M = decltype(mode)::value;
     if (nqk == 4)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, 4, VL>), dim3((unsigned)gk), dim3(kthreads), 0, st,
-                         p);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, 4, VL, M>), dim3((unsigned)gk), dim3(kthreads), 0,
+                         st, p);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, 2, VL>), dim3((unsigned)gk), dim3(kthreads), 0, st,
-                         p);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, 2, VL, M>), dim3((unsigned)gk), dim3(kthreads), 0,
+                         st, p);
+  };
+  if (gk > 0) {
+    if constexpr (D >= 256) {
+      dkdv(std::integral_constant<int, 1>{});
+      dkdv(std::integral_constant<int, 2>{});
+    } else {
+      dkdv(std::integral_constant<int, 0>{});
+    }
   }
   return hipGetLastError();
 }
