@@ -621,6 +621,17 @@ def table(torch, np, bsa, workloads, oracle_s):
         cpu = _oracle_rate(one, fl_of, oracle_s, check)
     emit(f"varlen packed (8 seqs, {sum(w.seqlens_q)} tokens, H16 d128, 128x128)", ms, fl, cpu,
          err)
+    # backward of the same packed batch (KV-block prefix from the offsets with roles swapped)
+    cu_kv, _, tkv, _ = bsa.bsa_varlen_offsets(w.seqlens_k, w.seqlens_q, bk, bq)
+    g = torch.randn_like(o)
+    run_vb = lambda: bsa.bsa_varlen_bwd(q, k, v, o, lse, g, cu_q, cu_k, cu_m, dv(cu_kv), offs,
+                                        tm, tkv, tn, ml, fl_, bq, bk, w.mask_mod,
+                                        softmax_scale=w.scale)
+    run_vb()
+    ms = _time_launches(torch, run_vb)
+    emit(f"backward, varlen packed (8 seqs, {sum(w.seqlens_q)} tokens, H16 d128, 128x128; "
+         f"includes building the KV-major lists; 10*d flops per listed cell)", ms, 2.5 * fl,
+         None, _MaxErr())
     # video (forward only; the step's metadata kernels add < 1 %)
     st, flops, _ = _video_inputs(torch, np, workloads)
     wv = st["w"]
