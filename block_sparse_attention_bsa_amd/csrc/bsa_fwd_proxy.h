@@ -109,12 +109,26 @@ __device__ __forceinline__ void softmax_step_any(f32x16_t& s0, f32x16_t& s1, con
     m_run = m_new;
   }
   const float m_use = (m_run == neg_inf()) ? 0.f : m_run;
-  // chunk-local key of the last block (never matched on an exact item)
-  const int tk = px ? num_n - 1 - it.key0 : -1000;
-  float ls = 0.f, lt = 0.f, lo = 0.f, lto = 0.f;
+  // p of the last block's summary, in fp32 (lt) and as rounded for the PV
+  // product (lto).  Only the chunk that holds it does this (a wave-uniform
+  // branch): chunk-local key tk is element 8 * ((tk >> 4) & 1) + (tk & 7) of
+  // s0 (tk < 32) or s1, in the lanes of half (tk >> 3) & 1.
+  float lt = 0.f, lto = 0.f;
+  const int tk = num_n - 1 - it.key0;
+  if (px && tk < kKvTile) {
+    const int e = 8 * ((tk >> 4) & 1) + (tk & 7);
+    float sv = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (r == e) sv = (tk & 32) ? s1[r] : s0[r];
+    if (((tk >> 3) & 1) == h32) {
+      lt = __builtin_amdgcn_exp2f(fmaf(sv, c, -m_use));
+      lto = __uint_as_float(pack_bf16x2(lt, 0.f) << 16);
+    }
+  }
+  float ls = 0.f, lo = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int k0 = 16 * (i >> 2) + 8 * h32 + ((2 * i) & 7);  // key of element 2i of s0
     const float a0 = __builtin_amdgcn_exp2f(fmaf(s0[2 * i], c, -m_use));
     const float a1 = __builtin_amdgcn_exp2f(fmaf(s0[2 * i + 1], c, -m_use));
     const float b0 = __builtin_amdgcn_exp2f(fmaf(s1[2 * i], c, -m_use));
@@ -123,12 +137,6 @@ __device__ __forceinline__ void softmax_step_any(f32x16_t& s0, f32x16_t& s1, con
     pk1[i] = pack_bf16x2(b0, b1);
     ls += (a0 + a1) + (b0 + b1);
     lo = add_bf16x2(pk1[i], add_bf16x2(pk0[i], lo));
-    lt += (k0 == tk ? a0 : 0.f) + (k0 + 1 == tk ? a1 : 0.f) + (k0 + 32 == tk ? b0 : 0.f) +
-          (k0 + 33 == tk ? b1 : 0.f);
-    lto += (k0 == tk ? __uint_as_float(pk0[i] << 16) : 0.f) +
-           (k0 + 1 == tk ? __uint_as_float(pk0[i] & 0xffff0000u) : 0.f) +
-           (k0 + 32 == tk ? __uint_as_float(pk1[i] << 16) : 0.f) +
-           (k0 + 33 == tk ? __uint_as_float(pk1[i] & 0xffff0000u) : 0.f);
   }
   const float wf = px ? (float)block_kv : 1.f;
   const float wt = px ? (float)(Sk - (num_n - 1) * block_kv) : 1.f;
