@@ -116,6 +116,62 @@ __device__ __forceinline__ void varlen_block_by_rank(const FwdParams& p, int q, 
   m = lo;
 }
 
+// The same lookup for B < 64 sequences, one per lane: Q block q of the work
+// order (rank q of the longest-first order when p.lpt, else global Q block
+// q) -> sequence b, its local block m, global block mg, and the sequence's
+// token and list-slot bounds.  Every lane loads entry `lane` of the four
+// bookkeeping arrays at once; the level search evaluates C(L) for 64 levels
+// per pass (lane = level), and ballots pick the sequence.  Same results as
+// varlen_block_by_rank and the binary search over cu_total_m_blocks.
+__device__ __forceinline__ void varlen_seq_lookup(const FwdParams& p, int q, int& b, int& m,
+                                                  int& mg, int& sq0, int& sq1, int& sk0,
+                                                  int& sk1, int& boff) {
+  const int lane = (int)(threadIdx.x & 63);
+  const bool in = lane <= p.B;
+  const int cm = in ? p.cu_m[lane] : 0;
+  const int cm1 = lane < p.B ? p.cu_m[lane + 1] : cm;
+  const int cq = in ? p.cu_q[lane] : 0;
+  const int ck = in ? p.cu_k[lane] : 0;
+  const int bo = in ? p.blk_off[lane] : 0;
+  const int nm = lane < p.B ? cm1 - cm : 0;  // Q blocks of sequence `lane`
+  if (p.lpt) {
+    // the largest level L with C(L) > q, C(L) = sum_s max(0, nm_s - L):
+    // C(0) = total_m > q, and C is non-increasing, so the levels with C > q
+    // are a prefix
+    int L = 0;
+    for (int c0 = 0;; c0 += 64) {
+      int cl = 0;
+      for (int s = 0; s < p.B; ++s) cl += max(0, __builtin_amdgcn_readlane(nm, s) - (c0 + lane));
+      const int n_above = __popcll(__ballot(cl > q));
+      if (n_above < 64) {
+        L = c0 + n_above - 1;
+        break;
+      }
+    }
+    int c_next = 0;  // C(L + 1)
+    for (int s = 0; s < p.B; ++s) c_next += max(0, __builtin_amdgcn_readlane(nm, s) - (L + 1));
+    // the k-th sequence, counted from b = 0, that has a block at level L
+    const int k = q - c_next;
+    const uint64_t has = __ballot(nm > L);
+    const int before = __popcll(has & ((1ull << lane) - 1ull));
+    const uint64_t pick = __ballot(((has >> lane) & 1ull) != 0 && before == k);
+    b = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)pick) - 1);
+    m = L;
+    mg = __builtin_amdgcn_readlane(cm, b) + m;
+  } else {
+    // the last sequence whose first global block is <= q (cu_m is non-decreasing)
+    const uint64_t le = __ballot(lane < p.B && cm <= q);
+    b = __builtin_amdgcn_readfirstlane(63 - __clzll((long long)le));
+    mg = q;
+    m = q - __builtin_amdgcn_readlane(cm, b);
+  }
+  sq0 = __builtin_amdgcn_readlane(cq, b);
+  sq1 = __builtin_amdgcn_readlane(cq, b + 1);
+  sk0 = __builtin_amdgcn_readlane(ck, b);
+  sk1 = __builtin_amdgcn_readlane(ck, b + 1);
+  boff = __builtin_amdgcn_readlane(bo, b);
+}
+
 // Logical tile t -> TileInfo.  A tile holds TM rows: R = TM / gpack rows
 // of each of gpack consecutive Q heads h .. h + gpack - 1 (gpack > 1 packs
 // the Q heads of one KV head, which then share their lists).  A sparse Q
@@ -172,29 +228,39 @@ __device__ __forceinline__ bool decode_tile(const FwdParams& p, int t, TileInfo&
     const int tm = t % p.tiles_per_head;
     const int h = (t / p.tiles_per_head) * p.gpack;
     const int sub = tm % p.qsub;
-    int b, m;
-    if (p.lpt) {
-      varlen_block_by_rank(p, tm / p.qsub, b, m);
+    int b, m, mg, sq0, sq1, sk0, sk1, boff;
+    if (p.B < 64) {
+      // one sequence per lane: its bookkeeping arrives in one round of loads,
+      // and the search below runs on registers and ballots
+      varlen_seq_lookup(p, tm / p.qsub, b, m, mg, sq0, sq1, sk0, sk1, boff);
     } else {
-      const int mg = tm / p.qsub;
-      int lo = 0, hi = p.B - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (p.cu_m[mid] <= mg)
-          lo = mid;
-        else
-          hi = mid - 1;
+      if (p.lpt) {
+        varlen_block_by_rank(p, tm / p.qsub, b, m);
+      } else {
+        const int mq = tm / p.qsub;
+        int lo = 0, hi = p.B - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (p.cu_m[mid] <= mq)
+            lo = mid;
+          else
+            hi = mid - 1;
+        }
+        b = lo;
+        m = mq - p.cu_m[b];
       }
-      b = lo;
-      m = mg - p.cu_m[b];
+      mg = p.cu_m[b] + m;
+      sq0 = p.cu_q[b];
+      sq1 = p.cu_q[b + 1];
+      sk0 = p.cu_k[b];
+      sk1 = p.cu_k[b + 1];
+      boff = p.blk_off[b];
     }
-    const int mg = p.cu_m[b] + m;
     const int hk = h / p.hrep;
     const int lh = p.kvh_lists ? hk : h;
-    const int sq0 = p.cu_q[b], sk0 = p.cu_k[b];
     ti.h = h;
-    ti.Sq = p.cu_q[b + 1] - sq0;
-    ti.Sk = p.cu_k[b + 1] - sk0;
+    ti.Sq = sq1 - sq0;
+    ti.Sk = sk1 - sk0;
     ti.num_n = cdiv(ti.Sk, p.block_kv);
     ti.q0 = m * p.block_q + sub * R;
     if (m < 0 || m >= cdiv(ti.Sq, p.block_q)) return false;
@@ -202,7 +268,7 @@ __device__ __forceinline__ bool decode_tile(const FwdParams& p, int t, TileInfo&
     if (ti.q0 >= ti.qend) return false;
     // valid-token counts: row b of a [B, kv_valid_ld] array (ld 0: one row for all)
     ti.kvv = p.kv_valid != nullptr ? p.kv_valid + (int64_t)b * p.kvv_ld : nullptr;
-    const int64_t row_p = (int64_t)p.blk_off[b] + (int64_t)m * ti.num_n;
+    const int64_t row_p = (int64_t)boff + (int64_t)m * ti.num_n;
     if (row_p < 0 || row_p + ti.num_n > p.total_n) return false;  // inconsistent bookkeeping
     ti.qoff = (int64_t)sq0 * p.q_ss + h * p.q_sh;
     ti.koff = (int64_t)sk0 * p.k_ss + hk * p.k_sh;
