@@ -186,12 +186,19 @@ void bsa_fwd_kernel(const FwdParams p) {
   // multiple of 32 rows) only fetches and waits with the others.
   const int qrow = ti.q0 + 32 * w + l32;
   const bool live = ti.q0 + 32 * w < ti.qend;
+  // The first 64 list entries are fetched before Q: the first K/V DMA waits
+  // only for them, while Q is still in flight (vector loads complete in
+  // order, so a wait for a list entry fetched after Q would wait for Q too).
+  ListWalk L{ti.mrow, p.mi_s[3], ti.mcnt, ti.frow, p.fi_s[3], ti.mcnt + ti.fcnt,
+             p.block_kv, ti.num_n, p.mask_mod, ti.kvv, -1000000, -1, 0};
+  L.fetch(0, lane);
   uint4 qf[DS];
 #pragma unroll
   for (int ks = 0; ks < DS; ++ks)
     qf[ks] = qrow < ti.qend
                  ? *reinterpret_cast<const uint4*>(qp + (int64_t)qrow * p.q_ss + ks * 16 + h32 * 8)
                  : make_uint4(0, 0, 0, 0);
+  L.lengths(lane);
   f32x16_t oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -408,8 +415,6 @@ void bsa_fwd_kernel(const FwdParams p) {
     }
   };
 
-  ListWalk L{ti.mrow, p.mi_s[3], ti.mcnt, ti.frow, p.fi_s[3], ti.mcnt + ti.fcnt,
-             p.block_kv, ti.num_n, p.mask_mod, ti.kvv, -1000000, -1, 0};
   // Two stages: the sub-tile after the one being computed streams into the
   // other stage.  One stage: the next sub-tile is fetched once every wave is
   // done with the current one.  p0 is the issued, not yet computed sub-tile.

@@ -116,6 +116,20 @@ __device__ __forceinline__ void varlen_block_by_rank(const FwdParams& p, int q, 
   m = lo;
 }
 
+// The two list lengths of a tile's Q-block row (an absent list has none),
+// fetched together when both lists are given.
+__device__ __forceinline__ void load_counts(const FwdParams& p, int64_t mo, int64_t fo,
+                                            TileInfo& ti) {
+  if (p.mcnt && p.fcnt) {
+    ti.mcnt = p.mcnt[mo];
+    ti.fcnt = p.fcnt[fo];
+  } else if (p.mcnt) {
+    ti.mcnt = p.mcnt[mo];
+  } else if (p.fcnt) {
+    ti.fcnt = p.fcnt[fo];
+  }
+}
+
 // The same lookup for B < 64 sequences, one per lane: Q block q of the work
 // order (rank q of the longest-first order when p.lpt, else global Q block
 // q) -> sequence b, its local block m, global block mg, and the sequence's
@@ -216,14 +230,10 @@ __device__ __forceinline__ bool decode_tile(const FwdParams& p, int t, TileInfo&
     ti.ooff = b * p.o_sb + h * p.o_sh;
     ti.lse_base = (int64_t)(b * p.H + h) * p.Sq;
     ti.lse_hs = p.Sq;
-    if (p.mcnt) {
-      ti.mcnt = p.mcnt[b * p.mc_s[0] + lh * p.mc_s[1] + i * p.mc_s[2]];
-      ti.mrow = p.midx + b * p.mi_s[0] + lh * p.mi_s[1] + i * p.mi_s[2];
-    }
-    if (p.fcnt) {
-      ti.fcnt = p.fcnt[b * p.fc_s[0] + lh * p.fc_s[1] + i * p.fc_s[2]];
-      ti.frow = p.fidx + b * p.fi_s[0] + lh * p.fi_s[1] + i * p.fi_s[2];
-    }
+    load_counts(p, b * p.mc_s[0] + lh * p.mc_s[1] + i * p.mc_s[2],
+                b * p.fc_s[0] + lh * p.fc_s[1] + i * p.fc_s[2], ti);
+    if (p.mcnt) ti.mrow = p.midx + b * p.mi_s[0] + lh * p.mi_s[1] + i * p.mi_s[2];
+    if (p.fcnt) ti.frow = p.fidx + b * p.fi_s[0] + lh * p.fi_s[1] + i * p.fi_s[2];
   } else {
     const int tm = t % p.tiles_per_head;
     const int h = (t / p.tiles_per_head) * p.gpack;
@@ -276,14 +286,9 @@ __device__ __forceinline__ bool decode_tile(const FwdParams& p, int t, TileInfo&
     ti.ooff = (int64_t)sq0 * p.o_ss + h * p.o_sh;
     ti.lse_base = (int64_t)h * p.lse_ld + sq0;
     ti.lse_hs = p.lse_ld;
-    if (p.mcnt) {
-      ti.mcnt = p.mcnt[lh * p.mc_s[1] + mg * p.mc_s[2]];
-      ti.mrow = p.midx + lh * p.mi_s[1] + row_p * p.mi_s[3];
-    }
-    if (p.fcnt) {
-      ti.fcnt = p.fcnt[lh * p.fc_s[1] + mg * p.fc_s[2]];
-      ti.frow = p.fidx + lh * p.fi_s[1] + row_p * p.fi_s[3];
-    }
+    load_counts(p, lh * p.mc_s[1] + mg * p.mc_s[2], lh * p.fc_s[1] + mg * p.fc_s[2], ti);
+    if (p.mcnt) ti.mrow = p.midx + lh * p.mi_s[1] + row_p * p.mi_s[3];
+    if (p.fcnt) ti.frow = p.fidx + lh * p.fi_s[1] + row_p * p.fi_s[3];
   }
   ti.mcnt = min(max(ti.mcnt, 0), ti.num_n);
   ti.fcnt = min(max(ti.fcnt, 0), ti.num_n);
@@ -307,7 +312,8 @@ struct ListWalk {
   int base;
   int chunk_j, chunk_len;
 
-  __device__ __forceinline__ void load(int g, int lane) {
+  // issue the loads of entries g .. g + 63 (one per lane)
+  __device__ __forceinline__ void fetch(int g, int lane) {
     base = g;
     const int gg = g + lane;
     int j = -1;
@@ -315,13 +321,21 @@ struct ListWalk {
       j = mrow[gg * ms];
     else if (gg < total)
       j = frow[(gg - mcnt) * fs];
+    chunk_j = j;
+  }
+  // the visible lengths of the fetched entries (waits for them)
+  __device__ __forceinline__ void lengths(int lane) {
+    const int gg = base + lane, j = chunk_j;
     int len = 0;
     if (gg < total && j >= 0 && j < num_n) {
       len = bk;
       if (mask_mod == kMaskKvValid && gg < mcnt) len = min(bk, kv_valid[j]);
     }
-    chunk_j = j;
     chunk_len = len;
+  }
+  __device__ __forceinline__ void load(int g, int lane) {
+    fetch(g, lane);
+    lengths(lane);
   }
   __device__ __forceinline__ void entry(int g, int lane, int& j, int& len) {
     if (g < base || g >= base + 64) load(g, lane);
@@ -354,37 +368,34 @@ constexpr int kPackSeg = 4;
 __device__ __forceinline__ bool advance_packed(Item& it, ListWalk& L, int lane, int Sk,
                                                bool causal_mask_list) {
   int g = it.g, pos = it.st, j = it.j, blen = it.blen;
-  int nk = 0, nseg = 0, cmask = 0;
-  int e0 = kKvTile, e1 = kKvTile, e2 = kKvTile, d0 = 0, d1 = 0, d2 = 0, d3 = 0;
-  while (true) {
-    if (g < 0 || pos >= blen) {  // the next listed block with a visible key
+  int nk = 0, cmask = 0;
+  int d[kPackSeg] = {0, 0, 0, 0}, e[kPackSeg - 1] = {kKvTile, kKvTile, kKvTile};
+  // One pass per run, unrolled: run s writes d[s] and e[s] directly (a loop
+  // over a run counter selected among them with scalar compare chains, which
+  // made the list walk the largest scalar cost of an item).
+#pragma unroll
+  for (int s = 0; s < kPackSeg; ++s) {
+    bool end = false;
+    while (g < 0 || pos >= blen) {  // the next listed block with a visible key
       ++g;
       pos = 0;
       if (g >= L.total) {  // past the end: the state stays exhausted for later calls
         g = L.total;
         blen = 0;
+        end = true;
         break;
       }
       L.entry(g, lane, j, blen);
       blen = min(blen, Sk - j * L.bk);
-      continue;
     }
+    if (end) break;
     const int t = min(kKvTile - nk, blen - pos);
-    const int dd = j * L.bk + pos - nk;  // sequence key = item key + dd over this run
-    // (unconditional selects: an if-chain over nseg becomes a scratch array)
-    d0 = nseg == 0 ? dd : d0;
-    d1 = nseg == 1 ? dd : d1;
-    d2 = nseg == 2 ? dd : d2;
-    d3 = nseg == 3 ? dd : d3;
-    if (causal_mask_list && g < L.mcnt) cmask |= 1 << nseg;
+    d[s] = j * L.bk + pos - nk;  // sequence key = item key + d[s] over this run
+    if (causal_mask_list && g < L.mcnt) cmask |= 1 << s;
     nk += t;
-    ++nseg;
     pos += t;
-    if (nk == kKvTile || nseg == kPackSeg) break;
-    // the run ends inside the item: the next one starts at item key nk
-    e0 = nseg == 1 ? nk : e0;
-    e1 = nseg == 2 ? nk : e1;
-    e2 = nseg == 3 ? nk : e2;
+    if (nk == kKvTile) break;
+    if (s + 1 < kPackSeg) e[s] = nk;  // the run ends inside the item
   }
   if (nk == 0) return false;
   it.g = g;
@@ -392,15 +403,15 @@ __device__ __forceinline__ bool advance_packed(Item& it, ListWalk& L, int lane, 
   it.j = j;
   it.blen = blen;
   it.nk = nk;
-  it.key0 = d0;
+  it.key0 = d[0];
   it.is_mask = cmask;
-  it.e0 = e0;
-  it.e1 = e1;
-  it.e2 = e2;
-  it.d0 = d0;
-  it.d1 = d1;
-  it.d2 = d2;
-  it.d3 = d3;
+  it.e0 = e[0];
+  it.e1 = e[1];
+  it.e2 = e[2];
+  it.d0 = d[0];
+  it.d1 = d[1];
+  it.d2 = d[2];
+  it.d3 = d[3];
   return true;
 }
 
