@@ -367,51 +367,73 @@ constexpr int kPackSeg = 4;
 
 __device__ __forceinline__ bool advance_packed(Item& it, ListWalk& L, int lane, int Sk,
                                                bool causal_mask_list) {
-  int g = it.g, pos = it.st, j = it.j, blen = it.blen;
-  int nk = 0, cmask = 0;
-  int d[kPackSeg] = {0, 0, 0, 0}, e[kPackSeg - 1] = {kKvTile, kKvTile, kKvTile};
-  // One pass per run, unrolled: run s writes d[s] and e[s] directly (a loop
-  // over a run counter selected among them with scalar compare chains, which
-  // made the list walk the largest scalar cost of an item).
+  // The item's runs are the next (up to kPackSeg) list entries with a visible
+  // key, the first one possibly part-taken.  They are found in the lanes that
+  // hold the fetched entries (a ballot of the entries with keys left) and
+  // read out with readlane; the run lengths are a running sum capped at 64.
+  int first = (it.g >= 0 && it.st < it.blen) ? it.g : it.g + 1;
+  int pos0 = first == it.g ? it.st : 0;
+  uint64_t nz = 0;
+  int av = 0;
+  while (true) {
+    if (first >= L.total) return false;  // past the end (the walk is not called again)
+    // keep at least kPackSeg entries from `first` in the fetched window
+    if (first < L.base || (first + kPackSeg > L.base + 64 && L.base + 64 < L.total))
+      L.load(first, lane);
+    const int rel = L.base + lane - first;  // candidate order of this lane's entry
+    const int vis = max(0, min(L.chunk_len, Sk - L.chunk_j * L.bk));
+    av = (rel >= 0 && L.base + lane < L.total) ? vis - (rel == 0 ? pos0 : 0) : 0;
+    nz = __ballot(av > 0);
+    if (nz != 0) break;
+    // no visible key left in the window
+    first = L.base + 64;
+    pos0 = 0;
+  }
+  int nk = 0, cmask = 0, last_lane = 0, last_end = 0, last_vis = 0, last_j = 0;
+  int d0 = 0, d1 = 0, d2 = 0, d3 = 0, e0 = kKvTile, e1 = kKvTile, e2 = kKvTile;
+  // (unrolled, and no arrays: d and e stay in registers)
 #pragma unroll
   for (int s = 0; s < kPackSeg; ++s) {
-    bool end = false;
-    while (g < 0 || pos >= blen) {  // the next listed block with a visible key
-      ++g;
-      pos = 0;
-      if (g >= L.total) {  // past the end: the state stays exhausted for later calls
-        g = L.total;
-        blen = 0;
-        end = true;
-        break;
+    if (nz != 0 && nk < kKvTile) {
+      const int pl = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)nz) - 1);
+      nz &= nz - 1;
+      const int a = __builtin_amdgcn_readlane(av, pl);
+      const int j = __builtin_amdgcn_readlane(L.chunk_j, pl);
+      const int g = L.base + pl;
+      const int start = g == first ? pos0 : 0;
+      const int t = min(kKvTile - nk, a);
+      const int dd = j * L.bk + start - nk;  // sequence key = item key + dd over this run
+      if (s == 0) d0 = dd;
+      if (s == 1) d1 = dd;
+      if (s == 2) d2 = dd;
+      if (s == 3) d3 = dd;
+      if (causal_mask_list && g < L.mcnt) cmask |= 1 << s;
+      last_lane = pl;
+      last_end = start + t;
+      last_vis = start + a;
+      last_j = j;
+      nk += t;
+      if (nk < kKvTile) {  // the run ends inside the item
+        if (s == 0) e0 = nk;
+        if (s == 1) e1 = nk;
+        if (s == 2) e2 = nk;
       }
-      L.entry(g, lane, j, blen);
-      blen = min(blen, Sk - j * L.bk);
     }
-    if (end) break;
-    const int t = min(kKvTile - nk, blen - pos);
-    d[s] = j * L.bk + pos - nk;  // sequence key = item key + d[s] over this run
-    if (causal_mask_list && g < L.mcnt) cmask |= 1 << s;
-    nk += t;
-    pos += t;
-    if (nk == kKvTile) break;
-    if (s + 1 < kPackSeg) e[s] = nk;  // the run ends inside the item
   }
-  if (nk == 0) return false;
-  it.g = g;
-  it.st = pos;
-  it.j = j;
-  it.blen = blen;
+  it.g = L.base + last_lane;
+  it.st = last_end;
+  it.j = last_j;
+  it.blen = last_vis;
   it.nk = nk;
-  it.key0 = d[0];
+  it.key0 = d0;
   it.is_mask = cmask;
-  it.e0 = e[0];
-  it.e1 = e[1];
-  it.e2 = e[2];
-  it.d0 = d[0];
-  it.d1 = d[1];
-  it.d2 = d[2];
-  it.d3 = d[3];
+  it.e0 = e0;
+  it.e1 = e1;
+  it.e2 = e2;
+  it.d0 = d0;
+  it.d1 = d1;
+  it.d2 = d2;
+  it.d3 = d3;
   return true;
 }
 
