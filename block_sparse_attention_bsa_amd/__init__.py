@@ -103,6 +103,8 @@ def load_library():
                             P, P, P, P, P, P, P, ctypes.c_int, P, ctypes.c_float, P, P]
     lib.bsa_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
                                     P, P, P, P, P, P, P, ctypes.c_int, P, ctypes.c_float, P]
+    lib.bsa_bwd_f32.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
+                                P, P, P, P, P, P, P, ctypes.c_int, P, ctypes.c_float, P, P]
     lib.bsa_kv_major_lists.argtypes = [P, P, I32, I32, I32, I32, P, P, P, P]
     lib.bsa_varlen_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32,
                                    P, P, P, P, P, I32, I32, I32, P, P, P, P, P, P, P,
@@ -117,7 +119,8 @@ def load_library():
     lib.bsa_status_str.argtypes = [ctypes.c_int]
     lib.bsa_status_str.restype = ctypes.c_char_p
     for fn in ("bsa_fwd", "bsa_varlen_fwd", "bsa_mask_to_index", "bsa_varlen_mask_to_index",
-               "bsa_bwd", "bsa_bwd_noalloc", "bsa_kv_major_lists", "bsa_bitmask_to_index",
+               "bsa_bwd", "bsa_bwd_noalloc", "bsa_bwd_f32", "bsa_kv_major_lists",
+               "bsa_bitmask_to_index",
                "bsa_varlen_bwd", "bsa_varlen_kv_major_lists",
                "bsa_varlen_offsets", "bsa_expand_kv_blocks", "bsa_block_sparsity"):
         getattr(lib, fn).restype = ctypes.c_int
@@ -382,15 +385,20 @@ def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
             block_q: int, block_kv: int, mask_mod: int = MASK_NONE,
             kv_valid: Optional[torch.Tensor] = None, softmax_scale: Optional[float] = None,
             window: Optional[Tuple[int, int]] = None, noalloc: bool = False):
-    """Backward of bsa_fwd (bf16, head_dim 64/96/128/192/256): returns (dq, dk, dv).
-    o and lse are the forward's outputs, dout the gradient of o; the lists,
-    block sizes, mask_mod, kv_valid, scale and window are the forward's.  The
+    """Backward of bsa_fwd (head_dim 64/96/128/192/256): returns (dq, dk, dv).
+    bf16 tensors call bsa_bwd; fp32 tensors (all five) call bsa_bwd_f32, which
+    rounds them to bf16 in its workspace and returns fp32 gradients.  o and
+    lse are the forward's outputs, dout the gradient of o; the lists, block
+    sizes, mask_mod, kv_valid, scale and window are the forward's.  The
     KV-major lists are built here with bsa_kv_major_lists.  noalloc=True calls
-    bsa_bwd_noalloc (the row dots in the library's static per-device array,
-    B*H*Sq <= 2**22) instead of passing a workspace."""
+    bsa_bwd_noalloc (bf16 only; the row dots in the library's static
+    per-device array, B*H*Sq <= 2**22) instead of passing a workspace."""
     lib = load_library()
+    f32 = q.dtype == torch.float32
+    if f32 and noalloc:
+        raise ValueError("noalloc is bf16 only")
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
-        _dev(n, t, torch.bfloat16)
+        _dev(n, t, torch.float32 if f32 else torch.bfloat16)
         if t.dim() != 4 or t.stride(-1) != 1:
             raise ValueError(f"{n} must be 4-D with a contiguous last dimension")
     _dev("lse", lse, torch.float32)
@@ -418,9 +426,11 @@ def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
         raise ValueError("q, k and v must be dense (their gradients take their strides)")
-    # row dots, then the dK/dV start order
-    work = None if noalloc else torch.empty(max(B * H * Sq + B * Hkv * N, 1),
-                                            dtype=torch.float32, device=q.device)
+    # row dots, then the dK/dV start order (fp32: then the bf16 copies)
+    nwork = B * H * Sq + B * Hkv * N
+    if f32:
+        nwork = -(-nwork // 4) * 4 + 2 * (B * Sq * H * D + B * Sk * Hkv * D)
+    work = None if noalloc else torch.empty(max(nwork, 1), dtype=torch.float32, device=q.device)
     if kv_valid is not None:
         _dev("kv_valid", kv_valid, torch.int32)
         if not kv_valid.is_contiguous() or kv_valid.numel() < N:
@@ -438,6 +448,9 @@ def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     if noalloc:
         st = lib.bsa_bwd_noalloc(*args, _stream(q))
         _check("bsa_bwd_noalloc", st)
+    elif f32:
+        st = lib.bsa_bwd_f32(*args, _ptr(work), _stream(q))
+        _check("bsa_bwd_f32", st)
     else:
         st = lib.bsa_bwd(*args, _ptr(work), _stream(q))
         _check("bsa_bwd", st)

@@ -551,6 +551,57 @@ bsa_status bsa_bwd(const void* q, const void* k, const void* v, const void* o, c
                   stream);
 }
 
+bsa_status bsa_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+                       const float* lse, const float* dout, float* dq, float* dk, float* dv,
+                       int32_t B, int32_t H, int32_t H_kv, int32_t Sq, int32_t Sk, int32_t D,
+                       const int64_t q_str[3], const int64_t k_str[3], const int64_t v_str[3],
+                       const int64_t o_str[3], const bsa_block_sparse* bs,
+                       const bsa_block_list* mask_t, const bsa_block_list* full_t,
+                       bsa_mask_mod mask_mod, const int32_t* kv_valid, float softmax_scale,
+                       float* work, hipStream_t stream) {
+  if (B < 0 || H <= 0 || H_kv <= 0 || Sq < 0 || Sk < 0 || H % H_kv != 0)
+    return BSA_ERR_INVALID_ARGUMENT;
+  if (!bs || !q_str || !k_str || !v_str || !o_str || bs->block_kv <= 0)
+    return BSA_ERR_INVALID_ARGUMENT;
+  if (!supported_head_dim(D)) return BSA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H * (Sq + Sk) == 0) return BSA_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !work)
+    return BSA_ERR_INVALID_ARGUMENT;
+  for (const void* ptr : {(const void*)q, (const void*)k, (const void*)v, (const void*)o,
+                          (const void*)dout, (const void*)dq, (const void*)dk, (const void*)dv,
+                          (const void*)work})
+    if (!aligned16(ptr)) return BSA_ERR_MISALIGNED;
+  if (!strides_ok(q_str, 3, 4) || !strides_ok(k_str, 3, 4) || !strides_ok(v_str, 3, 4) ||
+      !strides_ok(o_str, 3, 4))
+    return BSA_ERR_MISALIGNED;
+  // work: the bf16 backward's entries, then contiguous bf16 copies of
+  // q, o, dout, dq [B,Sq,H,D] and k, v, dk, dv [B,Sk,H_kv,D] (16-byte aligned:
+  // every size below is a multiple of 8 elements)
+  const int64_t N = cdiv64(Sk, bs->block_kv);
+  const int64_t head = (int64_t)B * H * Sq + (int64_t)B * H_kv * N;
+  const int64_t nq = (int64_t)B * Sq * H * D, nk = (int64_t)B * Sk * H_kv * D;
+  uint16_t* base = reinterpret_cast<uint16_t*>(work + (head + 3) / 4 * 4);
+  uint16_t *q16 = base, *o16 = q16 + nq, *do16 = o16 + nq, *dq16 = do16 + nq;
+  uint16_t *k16 = dq16 + nq, *v16 = k16 + nk, *dk16 = v16 + nk, *dv16 = dk16 + nk;
+  const int64_t sq16[3] = {(int64_t)Sq * H * D, (int64_t)H * D, D};
+  const int64_t sk16[3] = {(int64_t)Sk * H_kv * D, (int64_t)H_kv * D, D};
+  if (bsa::launch_cast_f32_bf16(q, q_str, B, Sq, H, D, q16, stream) != hipSuccess ||
+      bsa::launch_cast_f32_bf16(o, o_str, B, Sq, H, D, o16, stream) != hipSuccess ||
+      bsa::launch_cast_f32_bf16(dout, o_str, B, Sq, H, D, do16, stream) != hipSuccess ||
+      bsa::launch_cast_f32_bf16(k, k_str, B, Sk, H_kv, D, k16, stream) != hipSuccess ||
+      bsa::launch_cast_f32_bf16(v, v_str, B, Sk, H_kv, D, v16, stream) != hipSuccess)
+    return BSA_ERR_HIP;
+  const bsa_status st = bwd_impl(q16, k16, v16, o16, lse, do16, dq16, dk16, dv16, B, H, H_kv, Sq,
+                                 Sk, D, sq16, sk16, sk16, sq16, bs, mask_t, full_t, mask_mod,
+                                 kv_valid, softmax_scale, work, false, stream);
+  if (st != BSA_OK) return st;
+  if (bsa::launch_cast_bf16_f32(dq16, q_str, B, Sq, H, D, dq, stream) != hipSuccess ||
+      bsa::launch_cast_bf16_f32(dk16, k_str, B, Sk, H_kv, D, dk, stream) != hipSuccess ||
+      bsa::launch_cast_bf16_f32(dv16, v_str, B, Sk, H_kv, D, dv, stream) != hipSuccess)
+    return BSA_ERR_HIP;
+  return BSA_OK;
+}
+
 bsa_status bsa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
                            int32_t B, int32_t H, int32_t H_kv, int32_t Sq, int32_t Sk, int32_t D,

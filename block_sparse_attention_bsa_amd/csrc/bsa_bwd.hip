@@ -819,6 +819,54 @@ hipError_t launch_bwd_dv(const BwdParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+// fp32 <-> bf16 staging of the fp32 backward (HBM-bound elementwise).  A
+// thread moves 8 consecutive head_dim elements of one (b, s, h) row: two
+// 16-byte fp32 accesses and one 16-byte bf16 access, consecutive threads on
+// consecutive chunks of a row.  The bf16 side is contiguous [B,S,H,D]; the
+// fp32 side has element strides {sb, ss, sh} and a unit head_dim stride.
+// fp32 -> bf16 rounds to nearest even (as the fp32 forward does at load).
+__global__ __launch_bounds__(256) void cast_f32_bf16_kernel(const float* __restrict__ src,
+                                                             int64_t sb, int64_t ss, int64_t sh,
+                                                             int32_t S, int32_t H, int32_t D,
+                                                             int64_t chunks,
+                                                             __bf16* __restrict__ dst) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= chunks) return;
+  const int cpr = D / 8;
+  const int64_t row = c / cpr;
+  const int d0 = (int)(c % cpr) * 8;
+  const int h = (int)(row % H);
+  const int64_t bs = row / H;
+  const int64_t s = bs % S, b = bs / S;
+  const float* a = src + b * sb + s * ss + (int64_t)h * sh + d0;
+  const float4 x = *reinterpret_cast<const float4*>(a);
+  const float4 y = *reinterpret_cast<const float4*>(a + 4);
+  *reinterpret_cast<uint4*>(dst + row * D + d0) =
+      make_uint4(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w), pack_bf16x2(y.x, y.y),
+                 pack_bf16x2(y.z, y.w));
+}
+
+__global__ __launch_bounds__(256) void cast_bf16_f32_kernel(const __bf16* __restrict__ src,
+                                                             int64_t sb, int64_t ss, int64_t sh,
+                                                             int32_t S, int32_t H, int32_t D,
+                                                             int64_t chunks,
+                                                             float* __restrict__ dst) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= chunks) return;
+  const int cpr = D / 8;
+  const int64_t row = c / cpr;
+  const int d0 = (int)(c % cpr) * 8;
+  const int h = (int)(row % H);
+  const int64_t bs = row / H;
+  const int64_t s = bs % S, b = bs / S;
+  const uint4 v = *reinterpret_cast<const uint4*>(src + row * D + d0);
+  auto lo = [](uint32_t u) { return __uint_as_float(u << 16); };
+  auto hi = [](uint32_t u) { return __uint_as_float(u & 0xffff0000u); };
+  float* a = dst + b * sb + s * ss + (int64_t)h * sh + d0;
+  *reinterpret_cast<float4*>(a) = make_float4(lo(v.x), hi(v.x), lo(v.y), hi(v.y));
+  *reinterpret_cast<float4*>(a + 4) = make_float4(lo(v.z), hi(v.z), lo(v.w), hi(v.w));
+}
+
 template <int D>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
   return p.varlen ? launch_bwd_dv<D, true>(p, st) : launch_bwd_dv<D, false>(p, st);
@@ -843,6 +891,26 @@ hipError_t bwd_noalloc_scratch(float** out) {
   }
   *out = p;
   return hipSuccess;
+}
+
+hipError_t launch_cast_f32_bf16(const float* src, const int64_t str[3], int32_t B, int32_t S,
+                                int32_t H, int32_t D, uint16_t* dst, hipStream_t st) {
+  const int64_t chunks = (int64_t)B * S * H * (D / 8);
+  if (chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(cast_f32_bf16_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
+                     st, src, str[0], str[1], str[2], S, H, D, chunks,
+                     reinterpret_cast<__bf16*>(dst));
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_bf16_f32(const uint16_t* src, const int64_t str[3], int32_t B, int32_t S,
+                                int32_t H, int32_t D, float* dst, hipStream_t st) {
+  const int64_t chunks = (int64_t)B * S * H * (D / 8);
+  if (chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(cast_bf16_f32_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
+                     st, reinterpret_cast<const __bf16*>(src), str[0], str[1], str[2], S, H, D,
+                     chunks, dst);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd(const BwdParams& p, int D, hipStream_t s) {

@@ -118,6 +118,12 @@ struct BwdParams {
 // Rows the dK/dV launch order covers at most (beyond it: index order).
 constexpr int64_t kBwdOrderMaxItems = (int64_t)1 << 20;
 hipError_t launch_bwd(const BwdParams& p, int D, hipStream_t s);
+// fp32 [B,S,H,D] (element strides str, unit head_dim stride) <-> contiguous bf16
+// (bf16 as its 16-bit pattern)
+hipError_t launch_cast_f32_bf16(const float* src, const int64_t str[3], int32_t B, int32_t S,
+                                int32_t H, int32_t D, uint16_t* dst, hipStream_t st);
+hipError_t launch_cast_bf16_f32(const uint16_t* src, const int64_t str[3], int32_t B, int32_t S,
+                                int32_t H, int32_t D, float* dst, hipStream_t st);
 // Rows (B*H*Sq) the allocation-free backward's static row-dot array holds.
 constexpr int64_t kBwdNoallocMaxRows = (int64_t)1 << 22;
 // Device address of that array on the current device (looked up once per

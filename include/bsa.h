@@ -235,6 +235,30 @@ bsa_status bsa_bwd(const void* q, const void* k, const void* v, const void* o, c
                    const bsa_block_list* full_t, bsa_mask_mod mask_mod, const int32_t* kv_valid,
                    float softmax_scale, float* work, hipStream_t stream);
 
+/* Backward of the batched forward with fp32 tensors (bsa_fwd with BSA_F32:
+ * its kernels round Q, K, V to bf16 at load), the same gradient as bsa_bwd
+ * (same pages and formulas): q, k, v, o and dout are rounded to bf16 (round
+ * to nearest even) into the workspace, bsa_bwd's kernels run on those copies
+ * with fp32 accumulation, and dq, dk, dv are written back as fp32 (the
+ * bf16 values widened exactly).  The gradient with respect to an fp32 input
+ * is taken as that with respect to its bf16 rounding.
+ *  q, o, dout, dq [B,Sq,H,D] and k, v, dk, dv [B,Sk,H_kv,D]: device fp32,
+ *    element strides as for bsa_bwd, 16-byte aligned rows.
+ *  lse, bs, mask_t, full_t, mask_mod, kv_valid, softmax_scale: as for bsa_bwd.
+ *  work: device scratch, 16-byte aligned, of
+ *    4*ceil((B*H*Sq + B*H_kv*ceil(Sk/block_kv))/4) + 2*(B*Sq*H*D + B*Sk*H_kv*D)
+ *    4-byte entries (bsa_bwd's workspace, then the bf16 copies of the eight
+ *    tensors), overwritten.
+ * Errors and determinism as bsa_bwd. */
+bsa_status bsa_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+                       const float* lse, const float* dout, float* dq, float* dk, float* dv,
+                       int32_t B, int32_t H, int32_t H_kv, int32_t Sq, int32_t Sk, int32_t D,
+                       const int64_t q_str[3], const int64_t k_str[3], const int64_t v_str[3],
+                       const int64_t o_str[3], const bsa_block_sparse* bs,
+                       const bsa_block_list* mask_t, const bsa_block_list* full_t,
+                       bsa_mask_mod mask_mod, const int32_t* kv_valid, float softmax_scale,
+                       float* work, hipStream_t stream);
+
 /* bsa_bwd without the `work` argument, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving or training
  * loops, harnesses that forbid hipMalloc.  The row dots (and, when they fit

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     assert names == sorted(["bsa_fwd", "bsa_varlen_fwd", "bsa_mask_to_index",
                             "bsa_varlen_mask_to_index", "bsa_varlen_offsets",
                             "bsa_expand_kv_blocks", "bsa_block_sparsity", "bsa_bitmask_to_index",
-                            "bsa_kv_major_lists", "bsa_bwd", "bsa_bwd_noalloc",
+                            "bsa_kv_major_lists", "bsa_bwd", "bsa_bwd_noalloc", "bsa_bwd_f32",
                             "bsa_varlen_bwd", "bsa_varlen_kv_major_lists", "bsa_status_str"])
     lib = bsa.load_library()
     for n in names:
@@ -100,3 +100,28 @@ def test_varlen_backward_argument_errors_on_the_host():
                                          None, None) == 1
     assert lib.bsa_varlen_kv_major_lists(None, None, 2, 1, None, None, None, 0, 0, 0, None, None,
                                          None, None) == 0
+
+
+def test_fp32_backward_argument_errors_on_the_host():
+    # Rejected before any device work: negative sizes, H not a multiple of
+    # H_kv, an unsupported head_dim, strides that break 16-byte rows; an
+    # empty problem is a no-op.
+    lib = bsa.load_library()
+    z = [None] * 9
+    good = (ctypes.c_int64 * 3)(1024, 64, 64)
+    odd = (ctypes.c_int64 * 3)(1024, 66, 66)
+    bs = bsa._BlockSparse(bsa._BlockList(), bsa._BlockList(), 64, 64, -1, -1)
+    lt = bsa._BlockList()
+    buf = ctypes.create_string_buffer(64 + 16)
+    p16 = (ctypes.addressof(buf) + 15) // 16 * 16  # host memory, never dereferenced
+
+    def call(B, H, Hkv, Sq, Sk, D, st=good, ptrs=None):
+        return lib.bsa_bwd_f32(*(ptrs or z), B, H, Hkv, Sq, Sk, D, st, st, st, st,
+                               ctypes.byref(bs), ctypes.byref(lt), ctypes.byref(lt), 0, None,
+                               0.1, ptrs[0] if ptrs else None, None)
+    assert call(-1, 2, 2, 8, 8, 64) == 1
+    assert call(1, 3, 2, 8, 8, 64) == 1
+    assert call(1, 2, 2, 8, 8, 80) == 2
+    assert call(0, 2, 2, 8, 8, 64) == 0
+    assert call(1, 2, 2, 8, 8, 64) == 1  # missing pointers
+    assert call(1, 2, 2, 8, 8, 64, odd, [p16] * 9) == 3

@@ -241,3 +241,65 @@ def test_varlen_bwd_rejects_short_valid_counts():
     with pytest.raises(ValueError):
         bsa.bsa_varlen_bwd(q, k, k, q, lse, q, m["cu_q"], m["cu_k"], m["cu_m"], m["cu_kv"],
                            m["offs"], m["tm"], m["tkv"], m["tn"], ml, fl, bq, bk, KVV, short)
+
+
+# ------------------------------------------ fp32 tensors (bsa_bwd_f32)
+@pytest.mark.parametrize("case", [
+    dict(mm=CAUSAL, Sq=300, Sk=300, D=128, bq=128, bk=64),
+    dict(mm=KVV, Sq=200, Sk=450, D=64, bq=64, bk=48),
+    dict(mm=LOCAL, Sq=260, Sk=260, D=192, bq=64, bk=128, window=(70, 0)),
+])
+def test_bwd_fp32_tensors(case):
+    # fp32 q, k, v, o, dout: the gradients are those of the bf16 path on the
+    # same tensors rounded to bf16, widened to fp32 (bit for bit), and within
+    # the 1 % bound of the float64 oracle on the rounded inputs.
+    seed = zlib.crc32(repr(sorted(case.items())).encode())
+    rng = np.random.default_rng(seed)
+    mm, Sq, Sk, D, bq, bk = case["mm"], case["Sq"], case["Sk"], case["D"], case["bq"], case["bk"]
+    window = case.get("window")
+    B, H, Hkv = 2, 4, 2
+    M, N = -(-Sq // bq), -(-Sk // bk)
+    q, k, v, do = (torch.from_numpy(rng.standard_normal(s, dtype=np.float32)).cuda()
+                   for s in ((B, Sq, H, D), (B, Sk, Hkv, D), (B, Sk, Hkv, D), (B, Sq, H, D)))
+    kvv = None
+    if mm in (CAUSAL, LOCAL):
+        f_c, p_c = oracle.block_sparsity(mm, Sq, Sk, bq, bk, window=window)
+        full = f_c.astype(bool)[None, None] & (rng.random((B, H, M, N)) < 0.7)
+        part = np.broadcast_to(p_c.astype(bool), (B, H, M, N)).copy()
+    else:
+        sel = rng.random((B, H, M, N)) < 0.5
+        split = rng.random((B, H, M, N)) < 0.5
+        full, part = sel & split, sel & ~split
+        kvv = rng.integers(0, bk + 1, N).astype(np.int32)
+    ml = _lists(part) if part.any() else None
+    fl = _lists(full) if full.any() else None
+    kvv_d = None if kvv is None else torch.from_numpy(kvv).cuda()
+    scale = 1 / math.sqrt(D)
+    o, lse = bsa.bsa_fwd(q, k, v, ml, fl, bq, bk, mm, kvv_d, scale, window=window)
+    assert o.dtype == torch.float32
+    dq, dk, dv = bsa.bsa_bwd(q, k, v, o, lse, do, ml, fl, bq, bk, mm, kvv_d, scale, window=window)
+    assert dq.dtype == dk.dtype == dv.dtype == torch.float32
+    r16 = [t.to(torch.bfloat16) for t in (q, k, v, o, do)]
+    g16 = bsa.bsa_bwd(*r16[:4], lse, r16[4], ml, fl, bq, bk, mm, kvv_d, scale, window=window)
+    torch.cuda.synchronize()
+    for name, g, h in zip(("dq", "dk", "dv"), (dq, dk, dv), g16):
+        assert torch.equal(g, h.float()), f"{name}: fp32 path differs from the bf16 path"
+    rq, rk, rv = oracle.blocksparse_attention_bwd(as_oracle(r16[0]), as_oracle(r16[1]),
+                                                  as_oracle(r16[2]), full, part, bq, bk, mm,
+                                                  scale, as_oracle(r16[4]), kv_valid=kvv,
+                                                  window=window)
+    for name, g, r in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        gg = g.double().cpu().numpy()
+        err, ref = float(np.abs(gg - r).max()), float(np.abs(r).max())
+        print(f"bwd fp32 {case} {name}: ratio {err / max(ref, 1e-6):.2e}")
+        assert err <= REL_TOL * max(ref, 1e-6), f"{name} {case}: err {err:.3e} vs max {ref:.3e}"
+
+
+def test_bwd_fp32_rejects_noalloc_and_mixed_dtypes():
+    q = torch.zeros((1, 64, 1, 64), dtype=torch.float32, device="cuda")
+    lse = torch.zeros((1, 1, 64), dtype=torch.float32, device="cuda")
+    fl = _lists(np.ones((1, 1, 1, 1), bool))
+    with pytest.raises(ValueError):
+        bsa.bsa_bwd(q, q, q, q, lse, q, None, fl, 64, 64, noalloc=True)
+    with pytest.raises(ValueError):
+        bsa.bsa_bwd(q, q, q, q, lse, q.to(torch.bfloat16), None, fl, 64, 64)
