@@ -658,6 +658,45 @@ def test_packed_routes(D, bq, bk, mm):
     check_o_lse(o, lse, O, L, f"packed routes D={D} ({bq},{bk}) mm={mm}")
 
 
+@pytest.mark.parametrize("D,bq,bk", [(128, 128, 16), (64, 64, 48), (192, 128, 17)])
+def test_packed_routes_long_lists_with_empty_entries(D, bq, bk):
+    # Lists far longer than the 64 entries fetched at a time, with entries
+    # that hold no visible key (valid count 0 under the valid-count
+    # mask_mod, and ids outside [0, N), which are skipped) spread over them,
+    # so packed items start, end and refetch the list around such entries.
+    rng = np.random.default_rng([41, D, bq, bk])
+    B, H, Sq, Sk = 1, 2, 2 * bq, 256 * bk - 7  # 256 KV blocks, the last one short
+    M, N = -(-Sq // bq), -(-Sk // bk)
+    q, k, v = (rng.standard_normal((B, S, H, D), dtype=np.float32) for S in (Sq, Sk, Sk))
+    part = rng.random((B, H, M, N)) < 0.6
+    full = (rng.random((B, H, M, N)) < 0.5) & ~part
+    kvv = rng.integers(1, bk + 1, N).astype(np.int32)
+    kvv[rng.random(N) < 0.35] = 0
+    w = workloads.BatchedWorkload("long_lists", q, k, v, full, part, bq, bk, KVV,
+                                  1 / math.sqrt(D), kvv)
+    # the lists with ids outside [0, N) inserted between the listed ones
+    def with_invalid(mask):
+        cnt = np.zeros((B, H, M), np.int32)
+        idx = np.full((B, H, M, N), -1, np.int32)
+        for b in range(B):
+            for h in range(H):
+                for i in range(M):
+                    ids = []
+                    for j in np.flatnonzero(mask[b, h, i]):
+                        if rng.random() < 0.2:
+                            ids.append(int(rng.choice([-1, -7, N, N + 3])))
+                        ids.append(int(j))
+                    assert len(ids) <= N  # a row holds at most N entries
+                    cnt[b, h, i] = len(ids)
+                    idx[b, h, i, :len(ids)] = ids
+        return torch.from_numpy(cnt).cuda(), torch.from_numpy(idx).cuda()
+    for lists in (None, (with_invalid(part), with_invalid(full))):
+        o, lse, qkv = run_batched(w, lists=lists)
+        torch.cuda.synchronize()
+        O, L = _oracle_batched(w, qkv)
+        check_o_lse(o, lse, O, L, f"long packed lists D={D} ({bq},{bk}) invalid={lists is not None}")
+
+
 def test_packed_routes_all_causal_runs():
     # 16-key blocks up to each Q block's diagonal, all in the causal mask list:
     # items made of four causal runs each
