@@ -143,6 +143,53 @@ def test_varlen_small_all_rows_ragged():
     check_o_lse(o, lse, O, L, "varlen small")
 
 
+@pytest.mark.parametrize("n_seq,tm", [(63, 128), (64, 128), (70, 128), (63, 256), (70, 64)])
+def test_varlen_many_sequences_every_row(n_seq, tm):
+    # The tile decode takes each workgroup's sequence from a per-lane lookup
+    # when there are fewer than 64 sequences and a scalar search otherwise;
+    # the work order is longest-first up to 64 sequences.  Every row of a
+    # packed batch of short sequences (empty ones and ones below a block
+    # included) against the oracle on both sides of those limits, for
+    # 128-, 256- and 64-row tiles.
+    rng = np.random.default_rng([51, n_seq, tm])
+    seqlens = [int(x) for x in rng.integers(0, 3 * tm, n_seq)]
+    seqlens[1] = 0
+    seqlens[2] = 1
+    H, D, bq, bk = 2, 64, tm, 64
+    w = workloads.varlen_packed(H=H, D=D, bs=bk, seed=[52, n_seq, tm], seqlens=seqlens)
+    # Q blocks of tm rows over the same KV blocks: rebuild the per-sequence masks
+    full, part = [], []
+    for sl in seqlens:
+        M, N = -(-sl // bq), -(-sl // bk)
+        ii = np.arange(M)[:, None] * bq
+        jj = np.arange(N)[None, :] * bk
+        diag = (jj < ii + bq) & (jj + bk > ii)  # KV blocks meeting the Q block's diagonal
+        below = (jj + bk <= ii) & (rng.random((H, M, N)) < 0.5)
+        part.append(np.broadcast_to(diag[None], (H, M, N)).copy())
+        full.append(below & ~diag[None])
+    cu, off, tmb, tn = bsa.bsa_varlen_offsets(seqlens, seqlens, bq, bk)
+    dev = lambda a: torch.tensor(a, dtype=torch.int32, device="cuda")
+    cu_q = dev([0] + list(np.cumsum(seqlens)))
+    mlist = tuple(torch.from_numpy(a).cuda() for a in
+                  oracle.pack_varlen_lists(part, seqlens, seqlens, bq, bk))
+    flist = tuple(torch.from_numpy(a).cuda() for a in
+                  oracle.pack_varlen_lists(full, seqlens, seqlens, bq, bk))
+    qd, kd, vd = (to_dev(x) for x in (w.q, w.k, w.v))
+    o, lse = bsa.bsa_varlen_fwd(qd, kd, vd, cu_q, cu_q, dev(cu), dev(off), tmb, tn, mlist, flist,
+                                bq, bk, CAUSAL, w.scale, validate=True)
+    torch.cuda.synchronize()
+    O, L = oracle.varlen_blocksparse_attention(as_oracle(qd), as_oracle(kd), as_oracle(vd),
+                                               seqlens, seqlens, full, part, bq, bk, CAUSAL,
+                                               w.scale)
+    what = f"varlen {n_seq} sequences, {tm}-row blocks"
+    if tm == 256:
+        # the 256-row kernel divides by the fp32 sum of P: rows of two or three
+        # keys (many here) take its documented bound
+        check_o_lse_fp32_normaliser(o, lse, O, L, float(np.abs(as_oracle(vd)).max()), what)
+    else:
+        check_o_lse(o, lse, O, L, what)
+
+
 def _video_lists(w):
     """Cube-level map -> 128-token tile lists + per-tile valid counts, on the GPU."""
     nc = len(w.cube_valid)
