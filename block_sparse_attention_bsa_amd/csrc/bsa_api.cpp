@@ -466,7 +466,8 @@ bsa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, 
                     const int64_t k_str[3], const int64_t v_str[3], const int64_t o_str[3],
                     const bsa_block_sparse* bs, const bsa_block_list* mask_t,
                     const bsa_block_list* full_t, bsa_mask_mod mask_mod, const int32_t* kv_valid,
-                    float softmax_scale, float* work, bool noalloc, hipStream_t stream) {
+                    float softmax_scale, float* work, bool noalloc, hipStream_t stream,
+                    bool check_only = false) {
   if (B < 0 || H <= 0 || H_kv <= 0 || Sq < 0 || Sk < 0 || H % H_kv != 0)
     return BSA_ERR_INVALID_ARGUMENT;
   if (mask_mod < BSA_MASK_NONE || mask_mod > BSA_MASK_LOCAL) return BSA_ERR_INVALID_ARGUMENT;
@@ -525,6 +526,7 @@ bsa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, 
   p.win_left = bs->window_left; p.win_right = bs->window_right;
   p.c = softmax_scale * kLog2e;
   p.scale = softmax_scale;
+  if (check_only) return BSA_OK;  // the arguments pass; nothing is launched
   if (noalloc && bsa::bwd_noalloc_scratch(&p.drow) != hipSuccess) return BSA_ERR_HIP;
   // the dK/dV launch order follows the row dots in the workspace (the static
   // array of the allocation-free entry point holds it when it fits)
@@ -585,6 +587,11 @@ bsa_status bsa_bwd_f32(const float* q, const float* k, const float* v, const flo
   uint16_t *k16 = dq16 + nq, *v16 = k16 + nk, *dk16 = v16 + nk, *dv16 = dk16 + nk;
   const int64_t sq16[3] = {(int64_t)Sq * H * D, (int64_t)H * D, D};
   const int64_t sk16[3] = {(int64_t)Sk * H_kv * D, (int64_t)H_kv * D, D};
+  // every check of the bf16 backward first, so that nothing runs on bad arguments
+  const bsa_status chk = bwd_impl(q16, k16, v16, o16, lse, do16, dq16, dk16, dv16, B, H, H_kv, Sq,
+                                  Sk, D, sq16, sk16, sk16, sq16, bs, mask_t, full_t, mask_mod,
+                                  kv_valid, softmax_scale, work, false, stream, true);
+  if (chk != BSA_OK) return chk;
   if (bsa::launch_cast_f32_bf16(q, q_str, B, Sq, H, D, q16, stream) != hipSuccess ||
       bsa::launch_cast_f32_bf16(o, o_str, B, Sq, H, D, o16, stream) != hipSuccess ||
       bsa::launch_cast_f32_bf16(dout, o_str, B, Sq, H, D, do16, stream) != hipSuccess ||

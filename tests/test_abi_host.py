@@ -125,3 +125,9 @@ def test_fp32_backward_argument_errors_on_the_host():
     assert call(0, 2, 2, 8, 8, 64) == 0
     assert call(1, 2, 2, 8, 8, 64) == 1  # missing pointers
     assert call(1, 2, 2, 8, 8, 64, odd, [p16] * 9) == 3
+    # a list with counts but no ids: rejected by the bf16 backward's checks,
+    # which run before the fp32 tensors are staged (nothing is launched)
+    bad = bsa._BlockList()
+    bad.cnt = p16
+    bs.mask = bad
+    assert call(1, 2, 2, 8, 8, 64, good, [p16] * 9) == 1
