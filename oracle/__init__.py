@@ -15,6 +15,6 @@ from .attention import (MASK_CAUSAL, MASK_KV_VALID_COUNT, MASK_LOCAL, MASK_NONE,
 from .metadata import (bitmask_to_index, bitmask_to_mask, cdiv,  # noqa: F401
                        expand_kv_blocks, index_to_mask, mask_to_index,
                        pack_varlen_lists, varlen_offsets)
-from .proxy import block_summaries, proxy_attention  # noqa: F401
+from .proxy import block_summaries, proxy_attention, proxy_attention_bwd  # noqa: F401
 from .backward import (blocksparse_attention_bwd, element_mask, kv_major_lists,  # noqa: F401
                        varlen_blocksparse_attention_bwd, varlen_kv_major_lists)

@@ -91,3 +91,55 @@ def proxy_attention(q, k, v, full, part, kbar, vsum, block_q: int, block_kv: int
         O[b, rows, h] = num / den[:, None]
         LSE[b, h, rows] = m[:, 0] + np.log(den)
     return O, LSE
+
+
+def proxy_attention_bwd(q, k, v, full, part, kbar, vsum, block_q: int, block_kv: int,
+                        scale: float, dout):
+    """Gradients of proxy_attention's O, for the upstream gradient dout
+    [B,Sq,H,D], with respect to q, k, v, kbar and vsum (float64).  The
+    forward's definition differentiated (the same pages; the backward is the
+    derivative of the forward): per query row, with P_j = e^{s_j} / den on
+    exact keys and Pbar_n = e^{sbar_n} / den on omitted blocks,
+
+        dv_j    += P_j dO                 dvsum_n += Pbar_n dO
+        dS_j     = P_j (dO.v_j - D)       dSbar_n  = Pbar_n (dO.vsum_n - c_n D)
+        dq       = scale (sum_j dS_j k_j + sum_n dSbar_n kbar_n)
+        dk_j    += scale dS_j q           dkbar_n += scale dSbar_n q
+
+    where D = dO.O and c_n is block n's token mass.  Rows are summed over the
+    Q heads that share a KV head.  Returns (dq, dk, dv, dkbar, dvsum)."""
+    q, k, v, kbar, vsum, dout = (np.asarray(x, np.float64) for x in (q, k, v, kbar, vsum, dout))
+    B, Sq, H, D = q.shape
+    _, Sk, Hkv, _ = k.shape
+    M, N = cdiv(Sq, block_q), cdiv(Sk, block_kv)
+    mass = np.array([min(block_kv, Sk - n * block_kv) for n in range(N)], np.float64)
+    O, LSE = proxy_attention(q, k, v, full, part, kbar, vsum, block_q, block_kv, scale)
+    dq = np.zeros_like(q)
+    dk, dv = np.zeros_like(k), np.zeros_like(v)
+    dkbar, dvsum = np.zeros_like(kbar), np.zeros_like(vsum)
+    for b in range(B):
+        for h in range(H):
+            hk = h // (H // Hkv)
+            for i in range(M):
+                rows = np.arange(i * block_q, min((i + 1) * block_q, Sq))
+                exact = np.asarray(full[b, h, i], bool) | np.asarray(part[b, h, i], bool)
+                cols = np.concatenate([np.arange(n * block_kv, min((n + 1) * block_kv, Sk))
+                                       for n in np.flatnonzero(exact)] + [np.zeros(0, np.int64)])
+                omitted = np.flatnonzero(~exact)
+                if cols.size + omitted.size == 0:
+                    continue
+                qr, g = q[b, rows, h], dout[b, rows, h]
+                lse = LSE[b, h, rows][:, None]
+                Dr = (g * O[b, rows, h]).sum(axis=1, keepdims=True)
+                kc, vc = k[b, cols, hk], v[b, cols, hk]
+                kb, vb = kbar[b, omitted, hk], vsum[b, omitted, hk]
+                P = np.exp(scale * qr @ kc.T - lse)
+                Pb = np.exp(scale * qr @ kb.T - lse)
+                dS = P * (g @ vc.T - Dr)
+                dSb = Pb * (g @ vb.T - mass[omitted][None, :] * Dr)
+                dq[b, rows, h] = scale * (dS @ kc + dSb @ kb)
+                dk[b, cols, hk] += scale * dS.T @ qr
+                dv[b, cols, hk] += P.T @ g
+                dkbar[b, omitted, hk] += scale * dSb.T @ qr
+                dvsum[b, omitted, hk] += Pb.T @ g
+    return dq, dk, dv, dkbar, dvsum

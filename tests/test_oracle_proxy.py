@@ -103,3 +103,101 @@ def test_all_selected_is_plain_attention():
     ref_o, ref_l = _sdpa(q[0], k[0], v[0], 0.5)
     np.testing.assert_allclose(O[0], ref_o, atol=1e-12)
     np.testing.assert_allclose(L[0], ref_l, atol=1e-12)
+
+
+# ------------------------------------------ backward
+def _rebuilt_autograd(q, k, v, kbar, vsum, full, part, bq, bk, scale, dout):
+    """Gradients by torch autograd (float64) of attention over keys rebuilt
+    token by token: per Q block, the exact blocks' tokens plus, for each
+    omitted block n, c_n copies of (kbar_n, vsum_n / c_n)."""
+    t = [torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v, kbar, vsum)]
+    tq, tk, tv, tkb, tvs = t
+    B, Sq, H, D = q.shape
+    Sk, Hkv = k.shape[1], k.shape[2]
+    M, N = -(-Sq // bq), -(-Sk // bk)
+    mass = [min(bk, Sk - n * bk) for n in range(N)]
+    loss = torch.zeros((), dtype=torch.float64)
+    g = torch.from_numpy(dout)
+    for b in range(B):
+        for h in range(H):
+            hk = h // (H // Hkv)
+            for i in range(M):
+                rows = slice(i * bq, min((i + 1) * bq, Sq))
+                keys, vals = [], []
+                for n in range(N):
+                    toks = slice(n * bk, min((n + 1) * bk, Sk))
+                    if full[b, h, i, n] or part[b, h, i, n]:
+                        keys.append(tk[b, toks, hk])
+                        vals.append(tv[b, toks, hk])
+                    else:
+                        keys.append(tkb[b, n, hk].expand(mass[n], D))
+                        vals.append((tvs[b, n, hk] / mass[n]).expand(mass[n], D))
+                K, V = torch.cat(keys), torch.cat(vals)
+                P = torch.softmax(scale * tq[b, rows, h] @ K.T, dim=-1)
+                loss = loss + (P @ V * g[b, rows, h]).sum()
+    loss.backward()
+    return [np.zeros(x.shape) if x.grad is None else x.grad.numpy() for x in t]
+
+
+@pytest.mark.parametrize("seed,Sq,Sk,bq,bk,density", [
+    (3, 70, 96, 32, 16, 0.3), (4, 50, 100, 16, 32, 0.5), (5, 33, 65, 32, 8, 0.0)])
+def test_backward_equals_autograd_over_rebuilt_tokens(seed, Sq, Sk, bq, bk, density):
+    B, H, Hkv, D = 2, 4, 2, 8
+    q, k, v, full, part = _inputs(seed, B, Sq, Sk, H, Hkv, D, bq, bk, density)
+    rng = np.random.default_rng(seed + 100)
+    N = -(-Sk // bk)
+    kbar = rng.standard_normal((B, N, Hkv, D))
+    vsum = rng.standard_normal((B, N, Hkv, D)) * 3
+    dout = rng.standard_normal(q.shape)
+    scale = 0.4
+    got = oracle.proxy_attention_bwd(q, k, v, full, part, kbar, vsum, bq, bk, scale, dout)
+    ref = _rebuilt_autograd(q, k, v, kbar, vsum, full, part, bq, bk, scale, dout)
+    for name, a, r in zip(("dq", "dk", "dv", "dkbar", "dvsum"), got, ref):
+        np.testing.assert_allclose(a, r, atol=1e-10, rtol=0, err_msg=name)
+
+
+def test_backward_all_selected_is_the_plain_backward():
+    B, Sq, Sk, H, Hkv, D, bq, bk = 1, 40, 48, 2, 1, 8, 16, 16
+    q, k, v, _, _ = _inputs(6, B, Sq, Sk, H, Hkv, D, bq, bk, 0.0)
+    M, N = -(-Sq // bq), -(-Sk // bk)
+    full = np.ones((B, H, M, N), bool)
+    part = np.zeros_like(full)
+    kbar, vsum = oracle.block_summaries(k, v, bk)
+    dout = np.random.default_rng(7).standard_normal(q.shape)
+    dq, dk, dv, dkb, dvs = oracle.proxy_attention_bwd(q, k, v, full, part, kbar, vsum, bq, bk,
+                                                      0.3, dout)
+    rq, rk, rv = oracle.blocksparse_attention_bwd(q, k, v, full, part, bq, bk, oracle.MASK_NONE,
+                                                  0.3, dout)
+    for a, r in ((dq, rq), (dk, rk), (dv, rv)):
+        np.testing.assert_allclose(a, r, atol=1e-12, rtol=0)
+    assert not dkb.any() and not dvs.any()
+
+
+def test_backward_block_constant_tokens_match_dense_attention():
+    """With identical tokens inside every KV block the proxy forward is plain
+    attention over all keys; then dq is the dense dq, and for every block the
+    dense gradient summed over its tokens equals the exact tokens' gradient
+    plus that of its summary (dk: kbar is the block's key; dv: vsum is c_n
+    times the block's value)."""
+    B, Sq, Sk, H, Hkv, D, bq, bk = 1, 60, 90, 2, 1, 8, 20, 16
+    q, _, _, full, part = _inputs(8, B, Sq, Sk, H, Hkv, D, bq, bk, 0.4)
+    rng = np.random.default_rng(9)
+    N = -(-Sk // bk)
+    kb, vb = rng.standard_normal((B, N, Hkv, D)), rng.standard_normal((B, N, Hkv, D))
+    owner = np.arange(Sk) // bk
+    k, v = kb[:, owner], vb[:, owner]
+    kbar, vsum = oracle.block_summaries(k, v, bk)
+    dout = rng.standard_normal(q.shape)
+    scale = 0.35
+    dq, dk, dv, dkb, dvs = oracle.proxy_attention_bwd(q, k, v, full, part, kbar, vsum, bq, bk,
+                                                      scale, dout)
+    allf = np.ones_like(full)
+    rq, rk, rv = oracle.blocksparse_attention_bwd(q, k, v, allf, np.zeros_like(allf), bq, bk,
+                                                  oracle.MASK_NONE, scale, dout)
+    np.testing.assert_allclose(dq, rq, atol=1e-11, rtol=0)
+    mass = np.array([min(bk, Sk - n * bk) for n in range(N)], np.float64)
+    for n in range(N):
+        toks = slice(n * bk, min((n + 1) * bk, Sk))
+        np.testing.assert_allclose(rk[:, toks].sum(1), dk[:, toks].sum(1) + dkb[:, n], atol=1e-11)
+        np.testing.assert_allclose(rv[:, toks].sum(1), dv[:, toks].sum(1) + mass[n] * dvs[:, n],
+                                   atol=1e-11)
