@@ -105,6 +105,9 @@ def load_library():
                                     P, P, P, P, P, P, P, ctypes.c_int, P, ctypes.c_float, P]
     lib.bsa_bwd_f32.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
                                 P, P, P, P, P, P, P, ctypes.c_int, P, ctypes.c_float, P, P]
+    lib.bsa_bwd_proxy_work_size.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32, P]
+    lib.bsa_bwd_proxy.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I32, I32, I32, I32, I32, I32,
+                                  P, P, P, P, P, ctypes.c_float, P, P]
     lib.bsa_kv_major_lists.argtypes = [P, P, I32, I32, I32, I32, P, P, P, P]
     lib.bsa_varlen_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I32, I32, I32, I32,
                                    P, P, P, P, P, I32, I32, I32, P, P, P, P, P, P, P,
@@ -119,7 +122,8 @@ def load_library():
     lib.bsa_status_str.argtypes = [ctypes.c_int]
     lib.bsa_status_str.restype = ctypes.c_char_p
     for fn in ("bsa_fwd", "bsa_varlen_fwd", "bsa_mask_to_index", "bsa_varlen_mask_to_index",
-               "bsa_bwd", "bsa_bwd_noalloc", "bsa_bwd_f32", "bsa_kv_major_lists",
+               "bsa_bwd", "bsa_bwd_noalloc", "bsa_bwd_f32", "bsa_bwd_proxy",
+               "bsa_bwd_proxy_work_size", "bsa_kv_major_lists",
                "bsa_bitmask_to_index",
                "bsa_varlen_bwd", "bsa_varlen_kv_major_lists",
                "bsa_varlen_offsets", "bsa_expand_kv_blocks", "bsa_block_sparsity"):
@@ -384,8 +388,11 @@ def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
             full_list: Optional[Tuple[torch.Tensor, torch.Tensor]],
             block_q: int, block_kv: int, mask_mod: int = MASK_NONE,
             kv_valid: Optional[torch.Tensor] = None, softmax_scale: Optional[float] = None,
-            window: Optional[Tuple[int, int]] = None, noalloc: bool = False):
-    """Backward of bsa_fwd (head_dim 64/96/128/192/256): returns (dq, dk, dv).
+            window: Optional[Tuple[int, int]] = None, noalloc: bool = False,
+            proxy: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """Backward of bsa_fwd (head_dim 64/96/128/192/256): returns (dq, dk, dv),
+    and with proxy=(k_mean, v_sum) (the forward's summaries, bf16, MASK_NONE)
+    (dq, dk, dv, dk_mean, dv_sum) through bsa_bwd_proxy.
     bf16 tensors call bsa_bwd; fp32 tensors (all five) call bsa_bwd_f32, which
     rounds them to bf16 in its workspace and returns fp32 gradients.  o and
     lse are the forward's outputs, dout the gradient of o; the lists, block
@@ -397,6 +404,8 @@ def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     f32 = q.dtype == torch.float32
     if f32 and noalloc:
         raise ValueError("noalloc is bf16 only")
+    if proxy is not None and (f32 or noalloc or mask_mod != MASK_NONE):
+        raise ValueError("the proxy route's backward is bf16, MASK_NONE, with a workspace")
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
         _dev(n, t, torch.float32 if f32 else torch.bfloat16)
         if t.dim() != 4 or t.stride(-1) != 1:
@@ -417,15 +426,42 @@ def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         cnt, idx = lst
         return (cnt.expand(B, H, M).contiguous(), idx.expand(B, H, M, N).contiguous())
     ml, fl = full_shape(mask_list), full_shape(full_list)
-    mt = bsa_kv_major_lists(ml) if ml is not None else None
-    ft = bsa_kv_major_lists(fl) if fl is not None else None
     bs = _BlockSparse(_block_list(ml, True, (B, H, M, N)), _block_list(fl, True, (B, H, M, N)),
                       int(block_q), int(block_kv), *_window(mask_mod, window))
-    lt_m = _block_list(mt, True, (B, H, N, M))
-    lt_f = _block_list(ft, True, (B, H, N, M))
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if dq.stride() != q.stride() or dk.stride() != k.stride() or dv.stride() != v.stride():
         raise ValueError("q, k and v must be dense (their gradients take their strides)")
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if proxy is not None:
+        for n, t in zip(("proxy k_mean", "proxy v_sum"), proxy):
+            _dev(n, t, torch.bfloat16)
+            if tuple(t.shape) != (B, N, Hkv, D) or t.stride(-1) != 1:
+                raise ValueError(f"{n} must be [B,N,Hkv,D]={(B, N, Hkv, D)} with a contiguous "
+                                 "last dimension")
+        bs.proxy_k, bs.proxy_v = proxy[0].data_ptr(), proxy[1].data_ptr()
+        bs.proxy_k_str = (ctypes.c_int64 * 3)(*proxy[0].stride()[:3])
+        bs.proxy_v_str = (ctypes.c_int64 * 3)(*proxy[1].stride()[:3])
+        dks, dvs = torch.empty_like(proxy[0]), torch.empty_like(proxy[1])
+        if dks.stride() != proxy[0].stride() or dvs.stride() != proxy[1].stride():
+            raise ValueError("the summaries must be dense (their gradients take their strides)")
+        nbytes = ctypes.c_int64()
+        _check("bsa_bwd_proxy_work_size",
+               lib.bsa_bwd_proxy_work_size(B, H, Hkv, Sq, Sk, D, int(block_q), int(block_kv),
+                                           ctypes.byref(nbytes)))
+        pwork = torch.empty(max(nbytes.value, 16), dtype=torch.uint8, device=q.device)
+        st = lib.bsa_bwd_proxy(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                               _ptr(dk), _ptr(dv), _ptr(dks), _ptr(dvs), B, H, Hkv, Sq, Sk, D,
+                               _i64([q.stride(0), q.stride(1), q.stride(2)]),
+                               _i64([k.stride(0), k.stride(1), k.stride(2)]),
+                               _i64([v.stride(0), v.stride(1), v.stride(2)]),
+                               _i64([o.stride(0), o.stride(1), o.stride(2)]),
+                               ctypes.byref(bs), scale, _ptr(pwork), _stream(q))
+        _check("bsa_bwd_proxy", st)
+        return dq, dk, dv, dks, dvs
+    mt = bsa_kv_major_lists(ml) if ml is not None else None
+    ft = bsa_kv_major_lists(fl) if fl is not None else None
+    lt_m = _block_list(mt, True, (B, H, N, M))
+    lt_f = _block_list(ft, True, (B, H, N, M))
     # row dots, then the dK/dV start order (fp32: then the bf16 copies)
     nwork = B * H * Sq + B * Hkv * N
     if f32:
@@ -437,7 +473,6 @@ def bsa_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
             raise ValueError(f"kv_valid must be a contiguous int32 tensor with {N} entries")
     elif mask_mod == MASK_KV_VALID_COUNT and mask_list is not None:
         raise ValueError("MASK_KV_VALID_COUNT needs kv_valid")
-    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
             _ptr(dv), B, H, Hkv, Sq, Sk, D, _i64([q.stride(0), q.stride(1), q.stride(2)]),
             _i64([k.stride(0), k.stride(1), k.stride(2)]),

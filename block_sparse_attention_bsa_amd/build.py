@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libbsa.so")
 
 ARCH = "gfx950"
 DEVICE_SOURCES = ["bsa_fwd.hip", "bsa_fwd_pp.hip", "bsa_fwd_staged.hip", "bsa_meta.hip",
-                  "bsa_bwd.hip"]
+                  "bsa_bwd.hip", "bsa_bwd_proxy.hip"]
 HOST_SOURCES = ["bsa_api.cpp"]
 # Packed fp32 VALU forms are kept out of the device code.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}"]

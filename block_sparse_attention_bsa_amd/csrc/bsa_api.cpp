@@ -609,6 +609,134 @@ bsa_status bsa_bwd_f32(const float* q, const float* k, const float* v, const flo
   return BSA_OK;
 }
 
+// Workspace of bsa_bwd_proxy: the extended K/V and their gradients, the
+// extended mask, lists, KV-major lists and valid counts, and the workspace
+// of the backward over them; regions 256-byte aligned.
+struct ProxyWork {
+  int64_t kx, vx, dkx, dvx, mask, cnt, idx, cnt_t, idx_t, tr, kvv, bwd, total;
+};
+
+ProxyWork proxy_work_layout(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+                            int64_t bq, int64_t bk) {
+  const int64_t N = cdiv64(Sk, bk), Nx = 2 * N, M = cdiv64(Sq, bq);
+  const int64_t xb = B * Nx * bk * Hkv * D * 2;
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  ProxyWork w{};
+  int64_t at = 0;
+  auto take = [&](int64_t bytes) { const int64_t o = at; at += up(bytes); return o; };
+  w.kx = take(xb); w.vx = take(xb); w.dkx = take(xb); w.dvx = take(xb);
+  w.mask = take(B * H * M * Nx);
+  w.cnt = take(B * H * M * 4); w.idx = take(B * H * M * Nx * 4);
+  w.cnt_t = take(B * H * Nx * 4); w.idx_t = take(B * H * Nx * M * 4); w.tr = take(B * H * Nx * M);
+  w.kvv = take(Nx * 4);
+  w.bwd = take((B * H * Sq + B * Hkv * Nx) * 4);
+  w.total = at;
+  return w;
+}
+
+bsa_status bsa_bwd_proxy_work_size(int32_t B, int32_t H, int32_t H_kv, int32_t Sq, int32_t Sk,
+                                   int32_t D, int32_t block_q, int32_t block_kv,
+                                   int64_t* bytes) {
+  if (!bytes || B < 0 || H <= 0 || H_kv <= 0 || Sq < 0 || Sk < 0 || D <= 0 || block_q <= 0 ||
+      block_kv <= 0)
+    return BSA_ERR_INVALID_ARGUMENT;
+  *bytes = proxy_work_layout(B, H, H_kv, Sq, Sk, D, block_q, block_kv).total;
+  return BSA_OK;
+}
+
+bsa_status bsa_bwd_proxy(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                         void* dproxy_k, void* dproxy_v, int32_t B, int32_t H, int32_t H_kv,
+                         int32_t Sq, int32_t Sk, int32_t D, const int64_t q_str[3],
+                         const int64_t k_str[3], const int64_t v_str[3], const int64_t o_str[3],
+                         const bsa_block_sparse* bs, float softmax_scale, void* work,
+                         hipStream_t stream) {
+  if (B < 0 || H <= 0 || H_kv <= 0 || Sq < 0 || Sk < 0 || H % H_kv != 0)
+    return BSA_ERR_INVALID_ARGUMENT;
+  if (!bs || !q_str || !k_str || !v_str || !o_str || !bs->proxy_k || !bs->proxy_v)
+    return BSA_ERR_INVALID_ARGUMENT;
+  if (bs->block_q <= 0 || bs->block_kv <= 0 || !list_ok(bs->mask) || !list_ok(bs->full))
+    return BSA_ERR_INVALID_ARGUMENT;
+  if (!(std::isfinite(softmax_scale) && softmax_scale > 0.f)) return BSA_ERR_INVALID_ARGUMENT;
+  if (!supported_head_dim(D)) return BSA_ERR_UNSUPPORTED;
+  if ((int64_t)B * H * (Sq + Sk) == 0) return BSA_OK;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !dproxy_k || !dproxy_v ||
+      !work)
+    return BSA_ERR_INVALID_ARGUMENT;
+  for (const void* ptr : {q, k, v, o, dout, (const void*)dq, (const void*)dk, (const void*)dv,
+                          (const void*)dproxy_k, (const void*)dproxy_v, bs->proxy_k, bs->proxy_v,
+                          (const void*)work})
+    if (!aligned16(ptr)) return BSA_ERR_MISALIGNED;
+  if (!strides_ok(q_str, 3, 2) || !strides_ok(k_str, 3, 2) || !strides_ok(v_str, 3, 2) ||
+      !strides_ok(o_str, 3, 2) || !strides_ok(bs->proxy_k_str, 3, 2) ||
+      !strides_ok(bs->proxy_v_str, 3, 2))
+    return BSA_ERR_MISALIGNED;
+  const int64_t N = cdiv64(Sk, bs->block_kv), M = cdiv64(Sq, bs->block_q);
+  const int64_t Sx = 2 * N * bs->block_kv;
+  if (Sx > std::numeric_limits<int32_t>::max() / 2 || 2 * N > std::numeric_limits<int32_t>::max())
+    return BSA_ERR_UNSUPPORTED;
+  const ProxyWork L = proxy_work_layout(B, H, H_kv, Sq, Sk, D, bs->block_q, bs->block_kv);
+  char* w = static_cast<char*>(work);
+  // the extended problem: keys and values, then c_n copies of each block's summaries
+  const int64_t sx[3] = {Sx * H_kv * D, (int64_t)H_kv * D, D};
+  bsa_block_sparse bsx{};
+  bsx.mask.cnt = reinterpret_cast<const int32_t*>(w + L.cnt);
+  bsx.mask.idx = reinterpret_cast<const int32_t*>(w + L.idx);
+  const int64_t cst[3] = {H * M, M, 1}, ist[4] = {H * M * 2 * N, M * 2 * N, 2 * N, 1};
+  for (int i = 0; i < 3; ++i) bsx.mask.cnt_stride[i] = cst[i];
+  for (int i = 0; i < 4; ++i) bsx.mask.idx_stride[i] = ist[i];
+  bsx.block_q = bs->block_q;
+  bsx.block_kv = bs->block_kv;
+  bsx.window_left = bsx.window_right = -1;
+  bsa_block_list mt{}, ft{};
+  mt.cnt = reinterpret_cast<const int32_t*>(w + L.cnt_t);
+  mt.idx = reinterpret_cast<const int32_t*>(w + L.idx_t);
+  const int64_t tcs[3] = {H * 2 * N, 2 * N, 1}, tis[4] = {H * 2 * N * M, 2 * N * M, M, 1};
+  for (int i = 0; i < 3; ++i) mt.cnt_stride[i] = tcs[i];
+  for (int i = 0; i < 4; ++i) mt.idx_stride[i] = tis[i];
+  const int32_t* kvvx = reinterpret_cast<const int32_t*>(w + L.kvv);
+  // every check of the backward over the extended problem before anything runs
+  bsa_status st = bwd_impl(q, w + L.kx, w + L.vx, o, lse, dout, dq, w + L.dkx, w + L.dvx, B, H,
+                           H_kv, Sq, (int32_t)Sx, D, q_str, sx, sx, o_str, &bsx, &mt, &ft,
+                           BSA_MASK_KV_VALID_COUNT, kvvx, softmax_scale,
+                           reinterpret_cast<float*>(w + L.bwd), false, stream, true);
+  if (st != BSA_OK) return st;
+  bsa::ProxyBwdParams pp{};
+  pp.k = static_cast<const uint16_t*>(k); pp.v = static_cast<const uint16_t*>(v);
+  pp.ks = static_cast<const uint16_t*>(bs->proxy_k); pp.vs = static_cast<const uint16_t*>(bs->proxy_v);
+  pp.k_sb = k_str[0]; pp.k_ss = k_str[1]; pp.k_sh = k_str[2];
+  pp.v_sb = v_str[0]; pp.v_ss = v_str[1]; pp.v_sh = v_str[2];
+  pp.ks_sb = bs->proxy_k_str[0]; pp.ks_sn = bs->proxy_k_str[1]; pp.ks_sh = bs->proxy_k_str[2];
+  pp.vs_sb = bs->proxy_v_str[0]; pp.vs_sn = bs->proxy_v_str[1]; pp.vs_sh = bs->proxy_v_str[2];
+  pp.kx = reinterpret_cast<uint16_t*>(w + L.kx); pp.vx = reinterpret_cast<uint16_t*>(w + L.vx);
+  pp.dkx = reinterpret_cast<const uint16_t*>(w + L.dkx);
+  pp.dvx = reinterpret_cast<const uint16_t*>(w + L.dvx);
+  pp.dk = static_cast<uint16_t*>(dk); pp.dv = static_cast<uint16_t*>(dv);
+  pp.dks = static_cast<uint16_t*>(dproxy_k); pp.dvs = static_cast<uint16_t*>(dproxy_v);
+  pp.maskx = reinterpret_cast<uint8_t*>(w + L.mask);
+  pp.kvvx = reinterpret_cast<int32_t*>(w + L.kvv);
+  pp.mcnt = bs->mask.cnt; pp.midx = bs->mask.idx; pp.fcnt = bs->full.cnt; pp.fidx = bs->full.idx;
+  for (int i = 0; i < 3; ++i) { pp.mc_s[i] = bs->mask.cnt_stride[i]; pp.fc_s[i] = bs->full.cnt_stride[i]; }
+  for (int i = 0; i < 4; ++i) { pp.mi_s[i] = bs->mask.idx_stride[i]; pp.fi_s[i] = bs->full.idx_stride[i]; }
+  pp.B = B; pp.H = H; pp.Hkv = H_kv; pp.M = (int32_t)M; pp.N = (int32_t)N;
+  pp.bk = bs->block_kv; pp.Sk = Sk; pp.D = D;
+  if (bsa::launch_proxy_bwd_prepare(pp, stream) != hipSuccess ||
+      bsa::launch_mask_to_index(pp.maskx, (int64_t)B * H * M, (int32_t)(2 * N),
+                                reinterpret_cast<int32_t*>(w + L.cnt),
+                                reinterpret_cast<int32_t*>(w + L.idx), stream) != hipSuccess ||
+      bsa::launch_kv_major_lists(reinterpret_cast<const int32_t*>(w + L.cnt),
+                                 reinterpret_cast<const int32_t*>(w + L.idx), B, H, (int32_t)M,
+                                 (int32_t)(2 * N), reinterpret_cast<uint8_t*>(w + L.tr),
+                                 reinterpret_cast<int32_t*>(w + L.cnt_t),
+                                 reinterpret_cast<int32_t*>(w + L.idx_t), stream) != hipSuccess)
+    return BSA_ERR_HIP;
+  st = bwd_impl(q, w + L.kx, w + L.vx, o, lse, dout, dq, w + L.dkx, w + L.dvx, B, H, H_kv, Sq,
+                (int32_t)Sx, D, q_str, sx, sx, o_str, &bsx, &mt, &ft, BSA_MASK_KV_VALID_COUNT,
+                kvvx, softmax_scale, reinterpret_cast<float*>(w + L.bwd), false, stream);
+  if (st != BSA_OK) return st;
+  return bsa::launch_proxy_bwd_gather(pp, stream) == hipSuccess ? BSA_OK : BSA_ERR_HIP;
+}
+
 bsa_status bsa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout, void* dq, void* dk, void* dv,
                            int32_t B, int32_t H, int32_t H_kv, int32_t Sq, int32_t Sk, int32_t D,

@@ -117,6 +117,27 @@ struct BwdParams {
 };
 // Rows the dK/dV launch order covers at most (beyond it: index order).
 constexpr int64_t kBwdOrderMaxItems = (int64_t)1 << 20;
+// Backward of the proxy route: the extended K/V (blocks 0..N-1 the keys and
+// values, N..2N-1 c_n copies of each block's summaries), its block mask and
+// valid counts, and the gradients read back out.  bf16 data as 16-bit
+// patterns; element strides; the extended arrays contiguous
+// [B, 2*N*bk, Hkv, D], the mask [B, H, M, 2N], the valid counts [2N].
+struct ProxyBwdParams {
+  const uint16_t *k, *v, *ks, *vs;
+  int64_t k_sb, k_ss, k_sh, v_sb, v_ss, v_sh;
+  int64_t ks_sb, ks_sn, ks_sh, vs_sb, vs_sn, vs_sh;
+  uint16_t *kx, *vx;
+  const uint16_t *dkx, *dvx;
+  uint16_t *dk, *dv, *dks, *dvs;
+  uint8_t* maskx;
+  int32_t* kvvx;
+  const int32_t *mcnt, *midx, *fcnt, *fidx;
+  int64_t mc_s[3], mi_s[4], fc_s[3], fi_s[4];
+  int32_t B, H, Hkv, M, N, bk, Sk, D;
+};
+hipError_t launch_proxy_bwd_prepare(const ProxyBwdParams& p, hipStream_t s);
+hipError_t launch_proxy_bwd_gather(const ProxyBwdParams& p, hipStream_t s);
+
 hipError_t launch_bwd(const BwdParams& p, int D, hipStream_t s);
 // fp32 [B,S,H,D] (element strides str, unit head_dim stride) <-> contiguous bf16
 // (bf16 as its 16-bit pattern)

@@ -259,6 +259,38 @@ bsa_status bsa_bwd_f32(const float* q, const float* k, const float* v, const flo
                        bsa_mask_mod mask_mod, const int32_t* kv_valid, float softmax_scale,
                        float* work, hipStream_t stream);
 
+/* Backward of the proxy-compensated forward (bsa_fwd with bs->proxy_k and
+ * proxy_v; the PrimTS page, "proxy-compensated block-sparse attention",
+ * flashinfer pull request 4872: description, proxy paragraph; the backward
+ * is that forward's derivative).  That forward is attention over keys rebuilt
+ * token by token: each Q block's listed blocks with their own tokens, every
+ * other block n as c_n copies of (proxy_k[n], proxy_v[n] / c_n), c_n its
+ * token count.  This call builds that extended KV sequence in the workspace
+ * (2N blocks: K and V, then the copies), runs bsa_bwd's kernels on it under
+ * the valid-count mask_mod, and reads out dq, dk, dv and the summaries'
+ * gradients: dproxy_k[n] = c_n times a copy's dK, dproxy_v[n] = a copy's dV.
+ * Cost: that of the backward over every listed block plus every omitted one
+ * at its full token count.
+ *  q, k, v, o, lse, dout, dq, dk, dv, strides: as for bsa_bwd (bf16).
+ *  bs: the forward's lists, block sizes and summaries (proxy_k, proxy_v
+ *    [B,N,H_kv,D] with strides proxy_*_str over {batch, block, head});
+ *    mask_mod NONE (the route has no element mask).
+ *  dproxy_k, dproxy_v: device bf16, the summaries' layout and strides.
+ *  work: device scratch, 16-byte aligned, of the size bsa_bwd_proxy_work_size
+ *    returns (the extended K/V and their gradients, its lists and their
+ *    KV-major transposes, and bsa_bwd's workspace), overwritten.
+ * Errors and determinism as bsa_bwd. */
+bsa_status bsa_bwd_proxy_work_size(int32_t B, int32_t H, int32_t H_kv, int32_t Sq, int32_t Sk,
+                                   int32_t D, int32_t block_q, int32_t block_kv,
+                                   int64_t* bytes);
+bsa_status bsa_bwd_proxy(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                         void* dproxy_k, void* dproxy_v, int32_t B, int32_t H, int32_t H_kv,
+                         int32_t Sq, int32_t Sk, int32_t D, const int64_t q_str[3],
+                         const int64_t k_str[3], const int64_t v_str[3], const int64_t o_str[3],
+                         const bsa_block_sparse* bs, float softmax_scale, void* work,
+                         hipStream_t stream);
+
 /* bsa_bwd without the `work` argument, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving or training
  * loops, harnesses that forbid hipMalloc.  The row dots (and, when they fit

@@ -26,6 +26,7 @@ def test_library_exports_every_declared_symbol():
                             "bsa_varlen_mask_to_index", "bsa_varlen_offsets",
                             "bsa_expand_kv_blocks", "bsa_block_sparsity", "bsa_bitmask_to_index",
                             "bsa_kv_major_lists", "bsa_bwd", "bsa_bwd_noalloc", "bsa_bwd_f32",
+                            "bsa_bwd_proxy", "bsa_bwd_proxy_work_size",
                             "bsa_varlen_bwd", "bsa_varlen_kv_major_lists", "bsa_status_str"])
     lib = bsa.load_library()
     for n in names:
@@ -131,3 +132,30 @@ def test_fp32_backward_argument_errors_on_the_host():
     bad.cnt = p16
     bs.mask = bad
     assert call(1, 2, 2, 8, 8, 64, good, [p16] * 9) == 1
+
+
+def test_proxy_backward_argument_errors_on_the_host():
+    # Rejected before any device work: bad sizes, no summaries, an
+    # unsupported head_dim, misaligned strides; the workspace size query.
+    lib = bsa.load_library()
+    z = [None] * 11
+    st = (ctypes.c_int64 * 3)(1024, 64, 64)
+    bs = bsa._BlockSparse(bsa._BlockList(), bsa._BlockList(), 64, 64, -1, -1)
+
+    def call(B, H, Hkv, D, ptrs=None):
+        return lib.bsa_bwd_proxy(*(ptrs or z), B, H, Hkv, 8, 8, D, st, st, st, st,
+                                 ctypes.byref(bs), 0.1, None, None)
+    assert call(-1, 2, 2, 64) == 1
+    assert call(1, 3, 2, 64) == 1
+    assert call(1, 2, 2, 64) == 1  # no summaries
+    buf = ctypes.create_string_buffer(64 + 16)
+    p16 = (ctypes.addressof(buf) + 15) // 16 * 16  # host memory, never dereferenced
+    bs.proxy_k = bs.proxy_v = p16
+    assert call(1, 2, 2, 80) == 2
+    assert call(1, 2, 2, 64) == 1  # missing tensors
+    nbytes = ctypes.c_int64()
+    assert lib.bsa_bwd_proxy_work_size(2, 4, 2, 300, 333, 128, 128, 48, ctypes.byref(nbytes)) == 0
+    N, M = 7, 3
+    xb = 2 * 2 * N * 48 * 2 * 128 * 2  # B * 2N*bk * Hkv * D * 2 bytes, four of them
+    assert nbytes.value >= 4 * xb + 2 * 4 * M * 2 * N * 4
+    assert lib.bsa_bwd_proxy_work_size(2, 4, 2, 300, 333, 128, 0, 48, ctypes.byref(nbytes)) == 1

@@ -127,3 +127,73 @@ def test_proxy_rejects_what_it_does_not_cover():
     with pytest.raises(ValueError):
         bsa.bsa_fwd(q, k, v, None, _lists(full), 64, 64, bsa.MASK_NONE, None, 0.1,
                     proxy=(ks[:, :-1], vs))
+
+
+# ------------------------------------------ backward (bsa_bwd_proxy)
+BWD_REL_TOL = 1e-2  # of each gradient's largest magnitude, as for bsa_bwd
+
+
+@pytest.mark.parametrize("case", [
+    dict(Sq=300, Sk=300, D=64, bq=64, bk=64, density=0.3),
+    dict(Sq=200, Sk=333, D=128, bq=128, bk=48, density=0.4),  # short last block (45 tokens)
+    dict(Sq=150, Sk=410, D=96, bq=64, bk=80, density=0.25),
+    dict(Sq=128, Sk=257, D=256, bq=64, bk=64, density=0.3),   # a last block of one token
+])
+def test_proxy_backward_matches_oracle(case):
+    # dq, dk, dv and both summaries' gradients against the float64 oracle on
+    # the same bf16 inputs, with the forward's O and LSE
+    seed = zlib.crc32(repr(sorted(case.items())).encode())
+    B, H, Hkv = 2, 4, 2
+    D, bq, bk = case["D"], case["bq"], case["bk"]
+    q, k, v, full, part, ks, vs = _case(seed, B, case["Sq"], case["Sk"], H, Hkv, D, bq, bk,
+                                        case["density"])
+    full[0, 0, 0] = part[0, 0, 0] = False  # a row of proxies only
+    full[1, 3, 1] = True                    # a row of exact blocks only
+    part[1, 3, 1] = False
+    scale = 1 / math.sqrt(D)
+    ml = _lists(part) if part.any() else None
+    fl = _lists(full) if full.any() else None
+    o, lse = bsa.bsa_fwd(q, k, v, ml, fl, bq, bk, bsa.MASK_NONE, None, scale, proxy=(ks, vs))
+    do = to_dev(np.random.default_rng(seed + 1).standard_normal(q.shape, dtype=np.float32))
+    grads = bsa.bsa_bwd(q, k, v, o, lse, do, ml, fl, bq, bk, bsa.MASK_NONE, None, scale,
+                        proxy=(ks, vs))
+    torch.cuda.synchronize()
+    refs = oracle.proxy_attention_bwd(as_oracle(q), as_oracle(k), as_oracle(v), full, part,
+                                      as_oracle(ks), as_oracle(vs), bq, bk, scale, as_oracle(do))
+    for name, g, r in zip(("dq", "dk", "dv", "dk_mean", "dv_sum"), grads, refs):
+        gg = as_oracle(g)
+        assert np.isfinite(gg).all(), f"{name}: NaN/inf"
+        err, ref = float(np.abs(gg - r).max()), float(np.abs(r).max())
+        print(f"proxy bwd {case} {name}: ratio {err / max(ref, 1e-6):.2e}")
+        assert err <= BWD_REL_TOL * max(ref, 1e-6), f"{name} {case}: err {err:.3e} vs {ref:.3e}"
+
+
+def test_proxy_backward_all_listed_is_the_plain_backward():
+    # every block listed: no proxy term, so the gradients are bsa_bwd's and
+    # the summaries' are zero
+    B, H, Hkv, D, bq, bk, Sq, Sk = 1, 2, 1, 64, 64, 64, 192, 200
+    q, k, v, full, part, ks, vs = _case(5, B, Sq, Sk, H, Hkv, D, bq, bk, 1.0)
+    scale = 1 / math.sqrt(D)
+    ml = _lists(part) if part.any() else None
+    fl = _lists(full) if full.any() else None
+    o, lse = bsa.bsa_fwd(q, k, v, ml, fl, bq, bk, bsa.MASK_NONE, None, scale, proxy=(ks, vs))
+    do = to_dev(np.random.default_rng(6).standard_normal(q.shape, dtype=np.float32))
+    dq, dk, dv, dks, dvs = bsa.bsa_bwd(q, k, v, o, lse, do, ml, fl, bq, bk, bsa.MASK_NONE, None,
+                                       scale, proxy=(ks, vs))
+    rq, rk, rv = bsa.bsa_bwd(q, k, v, o, lse, do, ml, fl, bq, bk, bsa.MASK_NONE, None, scale)
+    torch.cuda.synchronize()
+    assert not dks.any() and not dvs.any()
+    for g, r in ((dq, rq), (dk, rk), (dv, rv)):
+        gg, rr = as_oracle(g), as_oracle(r)
+        assert float(np.abs(gg - rr).max()) <= 1e-2 * float(np.abs(rr).max())
+
+
+def test_proxy_backward_rejects_what_it_does_not_cover():
+    q = torch.zeros((1, 64, 1, 64), dtype=torch.bfloat16, device="cuda")
+    lse = torch.zeros((1, 1, 64), dtype=torch.float32, device="cuda")
+    s = torch.zeros((1, 1, 1, 64), dtype=torch.bfloat16, device="cuda")
+    fl = _lists(np.ones((1, 1, 1, 1), bool))
+    with pytest.raises(ValueError):   # element masks are not part of the route
+        bsa.bsa_bwd(q, q, q, q, lse, q, fl, None, 64, 64, bsa.MASK_CAUSAL, proxy=(s, s))
+    with pytest.raises(ValueError):   # summaries of the wrong shape
+        bsa.bsa_bwd(q, q, q, q, lse, q, None, fl, 64, 64, proxy=(s[:, :, :, :32], s))
