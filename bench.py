@@ -567,6 +567,21 @@ def table(torch, np, bsa, workloads, oracle_s):
     emit(f"proxy workload, exact blocks only ({tag})", ms_e, fl, None, _MaxErr())
     emit(f"proxy-compensated ({tag}; TFLOP/s over exact-block FLOPs; "
          f"+{100 * (ms_p / ms_e - 1):.1f} % time over exact only)", ms_p, fl, cpu, err)
+    # their backward: the exact-only one, and the route's (over the extended KV sequence)
+    g = torch.randn_like(op)
+    run_be = lambda: bsa.bsa_bwd(q, k, v, oe, le, g, None, fl_p, w.block_q, bk, bsa.MASK_NONE,
+                                 None, w.scale)
+    run_bp = lambda: bsa.bsa_bwd(q, k, v, op, lp, g, None, fl_p, w.block_q, bk, bsa.MASK_NONE,
+                                 None, w.scale, proxy=(ks, vs))
+    run_be()
+    run_bp()
+    ms_be = _time_launches(torch, run_be, n=5)
+    ms_bp = _time_launches(torch, run_bp, n=5)
+    emit(f"backward, proxy workload, exact blocks only ({tag}; 10*d flops per listed cell)",
+         ms_be, 2.5 * fl, None, _MaxErr())
+    emit(f"backward, proxy-compensated ({tag}; over the exact blocks' 10*d flops; every omitted "
+         f"block at its full token count: {ms_bp / ms_be:.1f}x the exact-only time)", ms_bp,
+         2.5 * fl, None, _MaxErr())
     # varlen packed
     w = workloads.varlen_packed()
     H, bq, bk = w.q.shape[1], w.block_q, w.block_kv
