@@ -458,6 +458,23 @@ bsa_status bsa_mask_to_index(const uint8_t* mask, int32_t B, int32_t H, int32_t 
 
 namespace {
 
+// The proxy route's extra inputs to the backward kernels (bsa_bwd_proxy):
+// the bit sets of the summary positions each Q block takes ([B, H, M, w]
+// words), the gradient outputs of the keys and values (strides of the
+// caller's tensors, not of the extended K/V) and of the summaries, the
+// number of original KV blocks n, of full blocks nreg, the KV block gl of
+// the last block's summaries (-1 when that block is full), the original key
+// count sk and the last block's token count.
+struct ProxyBwd {
+  const uint64_t* keep;
+  void* dk;
+  void* dv;
+  void* dks;
+  void* dvs;
+  int64_t dk_str[3], dv_str[3], dks_str[3], dvs_str[3];
+  int32_t n, nreg, gl, w, sk, c_last;
+};
+
 // The backward behind bsa_bwd and bsa_bwd_noalloc.  work == nullptr with
 // noalloc: the row dots go to the library's static per-device array.
 bsa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -467,7 +484,7 @@ bsa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, 
                     const bsa_block_sparse* bs, const bsa_block_list* mask_t,
                     const bsa_block_list* full_t, bsa_mask_mod mask_mod, const int32_t* kv_valid,
                     float softmax_scale, float* work, bool noalloc, hipStream_t stream,
-                    bool check_only = false) {
+                    bool check_only = false, const ProxyBwd* px = nullptr) {
   if (B < 0 || H <= 0 || H_kv <= 0 || Sq < 0 || Sk < 0 || H % H_kv != 0)
     return BSA_ERR_INVALID_ARGUMENT;
   if (mask_mod < BSA_MASK_NONE || mask_mod > BSA_MASK_LOCAL) return BSA_ERR_INVALID_ARGUMENT;
@@ -526,6 +543,24 @@ bsa_status bwd_impl(const void* q, const void* k, const void* v, const void* o, 
   p.win_left = bs->window_left; p.win_right = bs->window_right;
   p.c = softmax_scale * kLog2e;
   p.scale = softmax_scale;
+  if (px) {  // the proxy route over the extended sequence (bsa_bwd_proxy)
+    p.dk_sb = px->dk_str[0]; p.dk_ss = px->dk_str[1]; p.dk_sh = px->dk_str[2];
+    p.dv_sb = px->dv_str[0]; p.dv_ss = px->dv_str[1]; p.dv_sh = px->dv_str[2];
+    p.px_keep = px->keep;
+    p.px_dks = px->dks;
+    p.px_dvs = px->dvs;
+    p.px_dks_sb = px->dks_str[0]; p.px_dks_sn = px->dks_str[1]; p.px_dks_sh = px->dks_str[2];
+    p.px_dvs_sb = px->dvs_str[0]; p.px_dvs_sn = px->dvs_str[1]; p.px_dvs_sh = px->dvs_str[2];
+    p.px_n = px->n;
+    p.px_nreg = px->nreg;
+    p.px_gl = px->gl;
+    p.px_w = px->w;
+    p.px_sk = px->sk;
+    p.px_k0 = px->n * bs->block_kv;
+    p.px_cl = px->c_last;
+    p.px_lw = std::log2((float)bs->block_kv);
+    p.px_lwl = std::log2((float)px->c_last);
+  }
   if (check_only) return BSA_OK;  // the arguments pass; nothing is launched
   if (noalloc && bsa::bwd_noalloc_scratch(&p.drow) != hipSuccess) return BSA_ERR_HIP;
   // the dK/dV launch order follows the row dots in the workspace (the static
@@ -609,27 +644,44 @@ bsa_status bsa_bwd_f32(const float* q, const float* k, const float* v, const flo
   return BSA_OK;
 }
 
-// Workspace of bsa_bwd_proxy: the extended K/V and their gradients, the
-// extended mask, lists, KV-major lists and valid counts, and the workspace
-// of the backward over them; regions 256-byte aligned.
+// Workspace of bsa_bwd_proxy: the extended K/V (N blocks of keys and values,
+// then Nc blocks of summary positions: one per full block, nreg of them, in
+// order, and the last block's, when shorter than block_kv, first in a block
+// of its own at position lastpos), the extended block mask, its Q-major and
+// KV-major lists, the bit sets of the summary positions each Q block takes,
+// and the backward's own entries; regions 256-byte aligned.
 struct ProxyWork {
-  int64_t kx, vx, dkx, dvx, mask, cnt, idx, cnt_t, idx_t, tr, kvv, bwd, total;
+  int64_t N, Nc, NX, W, nreg, lastpos, c_last;
+  int64_t kx, vx, mask, cnt, idx, cnt_t, idx_t, tr, keep, bwd, total;
 };
 
 ProxyWork proxy_work_layout(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
                             int64_t bq, int64_t bk) {
-  const int64_t N = cdiv64(Sk, bk), Nx = 2 * N, M = cdiv64(Sq, bq);
-  const int64_t xb = B * Nx * bk * Hkv * D * 2;
-  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
   ProxyWork w{};
+  w.N = cdiv64(Sk, bk);
+  w.c_last = w.N > 0 ? Sk - (w.N - 1) * bk : bk;
+  if (w.c_last == bk) {
+    w.nreg = w.N;
+    w.Nc = cdiv64(w.N, bk);
+    w.lastpos = -1;
+  } else {
+    w.nreg = w.N - 1;
+    w.lastpos = cdiv64(w.nreg, bk) * bk;
+    w.Nc = cdiv64(w.nreg, bk) + 1;
+  }
+  w.NX = w.N + w.Nc;
+  w.W = cdiv64(w.Nc * bk, 64);
+  const int64_t M = cdiv64(Sq, bq), NX = w.NX;
+  const int64_t xb = B * NX * bk * Hkv * D * 2;
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
   int64_t at = 0;
   auto take = [&](int64_t bytes) { const int64_t o = at; at += up(bytes); return o; };
-  w.kx = take(xb); w.vx = take(xb); w.dkx = take(xb); w.dvx = take(xb);
-  w.mask = take(B * H * M * Nx);
-  w.cnt = take(B * H * M * 4); w.idx = take(B * H * M * Nx * 4);
-  w.cnt_t = take(B * H * Nx * 4); w.idx_t = take(B * H * Nx * M * 4); w.tr = take(B * H * Nx * M);
-  w.kvv = take(Nx * 4);
-  w.bwd = take((B * H * Sq + B * Hkv * Nx) * 4);
+  w.kx = take(xb); w.vx = take(xb);
+  w.mask = take(B * H * M * NX);
+  w.cnt = take(B * H * M * 4); w.idx = take(B * H * M * NX * 4);
+  w.cnt_t = take(B * H * NX * 4); w.idx_t = take(B * H * NX * M * 4); w.tr = take(B * H * NX * M);
+  w.keep = take(B * H * M * w.W * 8);
+  w.bwd = take((B * H * Sq + B * Hkv * NX) * 4);
   w.total = at;
   return w;
 }
@@ -671,18 +723,18 @@ bsa_status bsa_bwd_proxy(const void* q, const void* k, const void* v, const void
       !strides_ok(o_str, 3, 2) || !strides_ok(bs->proxy_k_str, 3, 2) ||
       !strides_ok(bs->proxy_v_str, 3, 2))
     return BSA_ERR_MISALIGNED;
-  const int64_t N = cdiv64(Sk, bs->block_kv), M = cdiv64(Sq, bs->block_q);
-  const int64_t Sx = 2 * N * bs->block_kv;
-  if (Sx > std::numeric_limits<int32_t>::max() / 2 || 2 * N > std::numeric_limits<int32_t>::max())
-    return BSA_ERR_UNSUPPORTED;
   const ProxyWork L = proxy_work_layout(B, H, H_kv, Sq, Sk, D, bs->block_q, bs->block_kv);
+  const int64_t M = cdiv64(Sq, bs->block_q), NX = L.NX;
+  const int64_t Sx = NX * bs->block_kv;
+  if (Sx > std::numeric_limits<int32_t>::max() / 2 || NX > std::numeric_limits<int32_t>::max())
+    return BSA_ERR_UNSUPPORTED;
   char* w = static_cast<char*>(work);
-  // the extended problem: keys and values, then c_n copies of each block's summaries
+  // the extended problem: keys and values, then one summary key per block
   const int64_t sx[3] = {Sx * H_kv * D, (int64_t)H_kv * D, D};
   bsa_block_sparse bsx{};
   bsx.mask.cnt = reinterpret_cast<const int32_t*>(w + L.cnt);
   bsx.mask.idx = reinterpret_cast<const int32_t*>(w + L.idx);
-  const int64_t cst[3] = {H * M, M, 1}, ist[4] = {H * M * 2 * N, M * 2 * N, 2 * N, 1};
+  const int64_t cst[3] = {H * M, M, 1}, ist[4] = {H * M * NX, M * NX, NX, 1};
   for (int i = 0; i < 3; ++i) bsx.mask.cnt_stride[i] = cst[i];
   for (int i = 0; i < 4; ++i) bsx.mask.idx_stride[i] = ist[i];
   bsx.block_q = bs->block_q;
@@ -691,15 +743,27 @@ bsa_status bsa_bwd_proxy(const void* q, const void* k, const void* v, const void
   bsa_block_list mt{}, ft{};
   mt.cnt = reinterpret_cast<const int32_t*>(w + L.cnt_t);
   mt.idx = reinterpret_cast<const int32_t*>(w + L.idx_t);
-  const int64_t tcs[3] = {H * 2 * N, 2 * N, 1}, tis[4] = {H * 2 * N * M, 2 * N * M, M, 1};
+  const int64_t tcs[3] = {H * NX, NX, 1}, tis[4] = {H * NX * M, NX * M, M, 1};
   for (int i = 0; i < 3; ++i) mt.cnt_stride[i] = tcs[i];
   for (int i = 0; i < 4; ++i) mt.idx_stride[i] = tis[i];
-  const int32_t* kvvx = reinterpret_cast<const int32_t*>(w + L.kvv);
+  ProxyBwd px{};
+  px.keep = reinterpret_cast<const uint64_t*>(w + L.keep);
+  px.dk = dk; px.dv = dv; px.dks = dproxy_k; px.dvs = dproxy_v;
+  for (int i = 0; i < 3; ++i) {
+    px.dk_str[i] = k_str[i]; px.dv_str[i] = v_str[i];
+    px.dks_str[i] = bs->proxy_k_str[i]; px.dvs_str[i] = bs->proxy_v_str[i];
+  }
+  px.n = (int32_t)L.N;
+  px.nreg = (int32_t)L.nreg;
+  px.gl = L.lastpos >= 0 ? (int32_t)(NX - 1) : -1;
+  px.w = (int32_t)L.W;
+  px.sk = Sk;
+  px.c_last = (int32_t)L.c_last;
   // every check of the backward over the extended problem before anything runs
-  bsa_status st = bwd_impl(q, w + L.kx, w + L.vx, o, lse, dout, dq, w + L.dkx, w + L.dvx, B, H,
-                           H_kv, Sq, (int32_t)Sx, D, q_str, sx, sx, o_str, &bsx, &mt, &ft,
-                           BSA_MASK_KV_VALID_COUNT, kvvx, softmax_scale,
-                           reinterpret_cast<float*>(w + L.bwd), false, stream, true);
+  bsa_status st = bwd_impl(q, w + L.kx, w + L.vx, o, lse, dout, dq, dk, dv, B, H, H_kv, Sq,
+                           (int32_t)Sx, D, q_str, sx, sx, o_str, &bsx, &mt, &ft, BSA_MASK_NONE,
+                           nullptr, softmax_scale, reinterpret_cast<float*>(w + L.bwd), false,
+                           stream, true, &px);
   if (st != BSA_OK) return st;
   bsa::ProxyBwdParams pp{};
   pp.k = static_cast<const uint16_t*>(k); pp.v = static_cast<const uint16_t*>(v);
@@ -709,32 +773,28 @@ bsa_status bsa_bwd_proxy(const void* q, const void* k, const void* v, const void
   pp.ks_sb = bs->proxy_k_str[0]; pp.ks_sn = bs->proxy_k_str[1]; pp.ks_sh = bs->proxy_k_str[2];
   pp.vs_sb = bs->proxy_v_str[0]; pp.vs_sn = bs->proxy_v_str[1]; pp.vs_sh = bs->proxy_v_str[2];
   pp.kx = reinterpret_cast<uint16_t*>(w + L.kx); pp.vx = reinterpret_cast<uint16_t*>(w + L.vx);
-  pp.dkx = reinterpret_cast<const uint16_t*>(w + L.dkx);
-  pp.dvx = reinterpret_cast<const uint16_t*>(w + L.dvx);
-  pp.dk = static_cast<uint16_t*>(dk); pp.dv = static_cast<uint16_t*>(dv);
-  pp.dks = static_cast<uint16_t*>(dproxy_k); pp.dvs = static_cast<uint16_t*>(dproxy_v);
   pp.maskx = reinterpret_cast<uint8_t*>(w + L.mask);
-  pp.kvvx = reinterpret_cast<int32_t*>(w + L.kvv);
+  pp.keep = reinterpret_cast<uint64_t*>(w + L.keep);
   pp.mcnt = bs->mask.cnt; pp.midx = bs->mask.idx; pp.fcnt = bs->full.cnt; pp.fidx = bs->full.idx;
   for (int i = 0; i < 3; ++i) { pp.mc_s[i] = bs->mask.cnt_stride[i]; pp.fc_s[i] = bs->full.cnt_stride[i]; }
   for (int i = 0; i < 4; ++i) { pp.mi_s[i] = bs->mask.idx_stride[i]; pp.fi_s[i] = bs->full.idx_stride[i]; }
-  pp.B = B; pp.H = H; pp.Hkv = H_kv; pp.M = (int32_t)M; pp.N = (int32_t)N;
+  pp.B = B; pp.H = H; pp.Hkv = H_kv; pp.M = (int32_t)M; pp.N = (int32_t)L.N;
+  pp.Nc = (int32_t)L.Nc; pp.W = (int32_t)L.W;
   pp.bk = bs->block_kv; pp.Sk = Sk; pp.D = D;
+  pp.nreg = (int32_t)L.nreg; pp.lastpos = (int32_t)L.lastpos;
   if (bsa::launch_proxy_bwd_prepare(pp, stream) != hipSuccess ||
-      bsa::launch_mask_to_index(pp.maskx, (int64_t)B * H * M, (int32_t)(2 * N),
+      bsa::launch_mask_to_index(pp.maskx, (int64_t)B * H * M, (int32_t)NX,
                                 reinterpret_cast<int32_t*>(w + L.cnt),
                                 reinterpret_cast<int32_t*>(w + L.idx), stream) != hipSuccess ||
       bsa::launch_kv_major_lists(reinterpret_cast<const int32_t*>(w + L.cnt),
                                  reinterpret_cast<const int32_t*>(w + L.idx), B, H, (int32_t)M,
-                                 (int32_t)(2 * N), reinterpret_cast<uint8_t*>(w + L.tr),
+                                 (int32_t)NX, reinterpret_cast<uint8_t*>(w + L.tr),
                                  reinterpret_cast<int32_t*>(w + L.cnt_t),
                                  reinterpret_cast<int32_t*>(w + L.idx_t), stream) != hipSuccess)
     return BSA_ERR_HIP;
-  st = bwd_impl(q, w + L.kx, w + L.vx, o, lse, dout, dq, w + L.dkx, w + L.dvx, B, H, H_kv, Sq,
-                (int32_t)Sx, D, q_str, sx, sx, o_str, &bsx, &mt, &ft, BSA_MASK_KV_VALID_COUNT,
-                kvvx, softmax_scale, reinterpret_cast<float*>(w + L.bwd), false, stream);
-  if (st != BSA_OK) return st;
-  return bsa::launch_proxy_bwd_gather(pp, stream) == hipSuccess ? BSA_OK : BSA_ERR_HIP;
+  return bwd_impl(q, w + L.kx, w + L.vx, o, lse, dout, dq, dk, dv, B, H, H_kv, Sq, (int32_t)Sx, D,
+                  q_str, sx, sx, o_str, &bsx, &mt, &ft, BSA_MASK_NONE, nullptr, softmax_scale,
+                  reinterpret_cast<float*>(w + L.bwd), false, stream, false, &px);
 }
 
 bsa_status bsa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,

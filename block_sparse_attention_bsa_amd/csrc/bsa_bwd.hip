@@ -366,7 +366,11 @@ __device__ __forceinline__ float lse2_of(float lse) {
 // s_waitcnt vmcnt(0): this wave's vector-memory ops, DMA included, are done.
 __device__ __forceinline__ void wait_vmem0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <int D, int NW, bool VL>
+// PX: the proxy route (BwdParams, px_*): in a sub-tile of summary keys only
+// the summaries the Q block takes count, each with its block's log2 c_n
+// added to its exponent (one weight per sub-tile, taken off the LSE); kept
+// keys are tested as bits in every sub-tile of this instance.
+template <int D, int NW, bool VL, bool PX = false>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))  // two waves per SIMD up to d = 128
 void bwd_dq_kernel(const BwdParams p) {
@@ -465,6 +469,31 @@ void bwd_dq_kernel(const BwdParams p) {
       int klo = 0, khi = kBwdT - 1;
       if (list == 0) keys_kept(p, sv0.kvv, row, k0, j, klo, khi);
       khi = min(khi, nk - 1);
+      // proxy route: the lane's kept keys as bits (kb0 / kb1: keys of each
+      // half, bit 16*(reg >> 3) + (reg & 7) for accumulator reg), from the
+      // key range in a block of keys and from the Q block's bit set in a
+      // chunk of summaries, whose log-weight comes off the row's LSE
+      uint32_t kb0 = 0, kb1 = 0;
+      float l2e = lse2;
+      if constexpr (PX) {
+        uint64_t kb;
+        if (j < p.px_n) {
+          khi = min(khi, p.px_sk - k0 - 1);
+          kb = khi >= 63 ? ~0ull : khi < 0 ? 0ull : (1ull << (khi + 1)) - 1;
+        } else {
+          const int n0 = k0 - p.px_k0;  // summary position of the sub-tile's key 0
+          const uint64_t* wp = p.px_keep + ((int64_t)(b * p.H + h) * p.M + i) * p.px_w;
+          const int wi = n0 >> 6, sh = n0 & 63;
+          const uint64_t lo = wi < p.px_w ? wp[wi] : 0ull;
+          const uint64_t hi = (sh != 0 && wi + 1 < p.px_w) ? wp[wi + 1] : 0ull;
+          kb = (lo >> sh) | (sh != 0 ? hi << (64 - sh) : 0ull);
+          if (khi < 63) kb &= khi < 0 ? 0ull : (1ull << (khi + 1)) - 1;
+          l2e = lse2 - (j == p.px_gl ? p.px_lwl : p.px_lw);
+        }
+        const uint64_t lm = kb >> (8 * h32);
+        kb0 = (uint32_t)lm;
+        kb1 = (uint32_t)(lm >> 32);
+      }
       // per half (keys 32*hf ..): S^T and dP^T, then dS packed for the last
       // product; one half at a time keeps the registers of the other free
       uint32_t pk[2][8];
@@ -484,6 +513,7 @@ void bwd_dq_kernel(const BwdParams p) {
           sa = mfma32(*reinterpret_cast<const uint4*>(kr + c), qf[ks], sa);  // S^T
           da = mfma32(*reinterpret_cast<const uint4*>(vr + c), gf[ks], da);  // dP^T
         }
+        const uint32_t kbh = hf == 0 ? kb0 : kb1;
 #pragma unroll
         for (int x = 0; x < 8; ++x) {
           float v[2];
@@ -491,8 +521,9 @@ void bwd_dq_kernel(const BwdParams p) {
           for (int y = 0; y < 2; ++y) {
             const int reg = 2 * x + y;
             const int key = 16 * (reg >> 3) + 8 * h32 + (reg & 7) + 32 * hf;
-            const bool keep = key >= klo && key <= khi;
-            const float pr = keep ? __builtin_amdgcn_exp2f(fmaf(sa[reg], p.c, -lse2)) : 0.f;
+            const bool keep = PX ? ((kbh >> (16 * (reg >> 3) + (reg & 7))) & 1u) != 0
+                                 : key >= klo && key <= khi;
+            const float pr = keep ? __builtin_amdgcn_exp2f(fmaf(sa[reg], p.c, -l2e)) : 0.f;
             v[y] = pr * (da[reg] - drow);
           }
           pk[hf][x] = pack_bf16x2(v[0], v[1]);
@@ -525,7 +556,12 @@ void bwd_dq_kernel(const BwdParams p) {
 // accumulators, K and V fragments and the products' operands need more than
 // the 512 registers of a wave, so dV and dK run as two launches (S computed
 // in both) instead of one that spills.
-template <int D, int NQ, bool VL, int MODE>
+// PX: the proxy route (BwdParams, px_*): a workgroup of summary keys keeps,
+// per Q block, the rows of the Q blocks whose bit set holds its lane's
+// summary, takes its chunk's log2 c_n off the rows' staged LSE (adding it to
+// the exponent) and writes the summaries' gradients (dV over c_n);
+// workgroups of keys stop at px_sk.
+template <int D, int NQ, bool VL, int MODE, bool PX = false>
 __global__ __launch_bounds__(NQ * 64)
 __attribute__((amdgpu_waves_per_eu(D <= 64 ? 2 : 1)))
 void bwd_dkdv_kernel(const BwdParams p) {
@@ -555,10 +591,28 @@ void bwd_dkdv_kernel(const BwdParams p) {
   const int b = sv0.b;
   const int j = VL ? nrow - p.cu_n[b] : nrow;
   const int k0 = j * p.block_kv + s * TW;
-  const int kend = min((j + 1) * p.block_kv, sv0.Sk);
+  int kend = min((j + 1) * p.block_kv, sv0.Sk);
+  bool summ = false;  // proxy route: a workgroup of summary keys
+  if constexpr (PX) {
+    if (j < p.px_n)
+      kend = min(kend, p.px_sk);
+    else
+      summ = true;
+  }
   if (k0 >= kend) return;
   const int key = k0 + 32 * wq + l32;  // sequence-local
-  const bool kvalid = key < kend;
+  bool kvalid = key < kend;
+  int pu = 0, pn = 0;  // summary position of this lane's key, and its block
+  float lwk = 0.f;     // the workgroup's log2 c_n, taken off the staged LSE
+  if constexpr (PX) {
+    if (summ) {
+      pu = key - p.px_k0;
+      const bool last = j == p.px_gl;  // a chunk of its own: position = its first key
+      pn = last ? p.px_n - 1 : pu;
+      kvalid = kvalid && (last ? key == j * p.block_kv : pu < p.px_nreg);
+      lwk = last ? p.px_lwl : p.px_lw;
+    }
+  }
 
   const int64_t ktok = (int64_t)sv0.tk0 + key;
   const __bf16* krow = reinterpret_cast<const __bf16*>(p.k) + b * p.k_sb + ktok * p.k_ss + hk * p.k_sh;
@@ -566,6 +620,21 @@ void bwd_dkdv_kernel(const BwdParams p) {
   uint4 kf[DS], vf[DS];
   row_frags<D>(krow, kvalid, h32, kf);
   if (DO_DK) row_frags<D>(vrow, kvalid, h32, vf);
+
+  // where this lane's dK and dV rows go (set before the walk, so the walk
+  // keeps two addresses live rather than the tensors' bases and strides)
+  __bf16* kdst = reinterpret_cast<__bf16*>(p.dk) + b * p.dk_sb + ktok * p.dk_ss + hk * p.dk_sh;
+  __bf16* vdst = reinterpret_cast<__bf16*>(p.dv) + b * p.dv_sb + ktok * p.dv_ss + hk * p.dv_sh;
+  float vmul = 1.f;
+  if constexpr (PX) {
+    if (summ) {  // the summaries' gradients: d(mean key), d(summed value) = dV / c_n
+      kdst = reinterpret_cast<__bf16*>(p.px_dks) + b * p.px_dks_sb + (int64_t)pn * p.px_dks_sn +
+             hk * p.px_dks_sh;
+      vdst = reinterpret_cast<__bf16*>(p.px_dvs) + b * p.px_dvs_sb + (int64_t)pn * p.px_dvs_sn +
+             hk * p.px_dvs_sh;
+      vmul = 1.f / (float)(j == p.px_gl ? p.px_cl : p.block_kv);
+    }
+  }
 
   f32x16_t dv[DB], dk[DB];
 #pragma unroll
@@ -610,6 +679,15 @@ void bwd_dkdv_kernel(const BwdParams p) {
     W.blen = p.block_q;
     W.S = sv0.Sq;
     float l2n = 0.f, drn = 0.f;  // wave 0: its lane's row of the staged sub-tile
+    // proxy route: whether the staged (kwn) and the current (kwc) sub-tile's
+    // Q block takes this lane's summary; the lane's word of Q block 0 (the
+    // next Q block's is px_w words on)
+    uint32_t kwn = 1, kwc = 1;
+    const uint64_t* kwrow = nullptr;
+    if constexpr (PX) {
+      if (summ && kvalid)
+        kwrow = p.px_keep + ((int64_t)(b * p.H + h) * p.M) * p.px_w + (pu >> 6);
+    }
     // Q and dO rows (and the rows' LSE and row dots) of the walk's current
     // sub-tile into a stage
     auto issue = [&](int stage) {
@@ -618,8 +696,12 @@ void bwd_dkdv_kernel(const BwdParams p) {
       stage_tile<D, NQ>(qb0 + (int64_t)r0 * p.q_ss, p.q_ss, nr, ql, w, lane);
       stage_tile<D, NQ>(gb0 + (int64_t)r0 * p.do_ss, p.do_ss, nr, ql + T::BYTES, w, lane);
       if (w == 0) {
-        l2n = lane < nr ? lse2_of(p.lse[lbase + r0 + lane]) : __builtin_inff();
+        l2n = lane < nr ? lse2_of(p.lse[lbase + r0 + lane]) - lwk : __builtin_inff();
         drn = lane < nr ? p.drow[lbase + r0 + lane] : 0.f;
+      }
+      if constexpr (PX) {
+        if (summ)
+          kwn = kwrow ? (uint32_t)(kwrow[(int64_t)W.id * p.px_w] >> (pu & 63)) & 1u : 0u;
       }
     };
     auto put_rows = [&](int stage) {
@@ -635,6 +717,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
       issue(st);
       put_rows(st);
     }
+    kwc = kwn;
     wait_vmem0();
     __syncthreads();
     while (have) {
@@ -647,7 +730,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
         // kept rows of this sub-tile for this lane's key
         int rlo = 0, rhi = kBwdT - 1;
         if (list == 0) rows_kept(p, sv0.kvv, key, r0, j, rlo, rhi);
-        rhi = kvalid ? min(rhi, nr - 1) : -1;
+        rhi = kvalid && kwc ? min(rhi, nr - 1) : -1;
         // per half (rows 32*hf ..): S and dP, then P and dS packed for the
         // last products; one half at a time keeps the registers of the other
         // free
@@ -711,15 +794,14 @@ void bwd_dkdv_kernel(const BwdParams p) {
       wait_vmem0();
       __syncthreads();  // the next sub-tile has landed
       st = ST == 2 ? st ^ 1 : 0;
+      kwc = kwn;
       have = more;
     }
   }
 
   if (kvalid) {
-    __bf16* kdst = reinterpret_cast<__bf16*>(p.dk) + b * p.dk_sb + ktok * p.dk_ss + hk * p.dk_sh;
-    __bf16* vdst = reinterpret_cast<__bf16*>(p.dv) + b * p.dv_sb + ktok * p.dv_ss + hk * p.dv_sh;
     if (DO_DK) store_row<DB>(kdst, h32, dk, p.scale);
-    if (DO_DV) store_row<DB>(vdst, h32, dv, 1.f);
+    if (DO_DV) store_row<DB>(vdst, h32, dv, vmul);
   }
 }
 
@@ -770,7 +852,7 @@ __global__ __launch_bounds__(kOrderBuckets) void bwd_kv_order_kernel(const BwdPa
   for (int t = tid; t < n; t += kOrderBuckets) p.kv_order[atomicAdd(&hist[bucket(t)], 1)] = t;
 }
 
-template <int D, bool VL>
+template <int D, bool VL, bool PX = false>
 hipError_t launch_bwd_dv(const BwdParams& p, hipStream_t st) {
   // varlen: the row dots run over [H, total_q] as one sequence of Sq rows
   const int64_t rows = (VL ? 1 : (int64_t)p.B) * p.H * p.Sq;
@@ -790,9 +872,9 @@ hipError_t launch_bwd_dv(const BwdParams& p, hipStream_t st) {
   const int kthreads = nqk * 64;
   if (gq > 0) {
     if (nwq == 4)
-      hipLaunchKernelGGL((bwd_dq_kernel<D, 4, VL>), dim3((unsigned)gq), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, 4, VL, PX>), dim3((unsigned)gq), dim3(256), 0, st, p);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<D, 2, VL>), dim3((unsigned)gq), dim3(128), 0, st, p);
+      hipLaunchKernelGGL((bwd_dq_kernel<D, 2, VL, PX>), dim3((unsigned)gq), dim3(128), 0, st, p);
   }
   if (gk > 0 && p.kv_order) {
     const int64_t items = nb * (p.H / p.hrep) * p.N;
@@ -802,11 +884,11 @@ hipError_t launch_bwd_dv(const BwdParams& p, hipStream_t st) {
   auto dkdv = [&](auto mode) {
     constexpr int M = decltype(mode)::value;
     if (nqk == 4)
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, 4, VL, M>), dim3((unsigned)gk), dim3(kthreads), 0,
-                         st, p);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, 4, VL, M, PX>), dim3((unsigned)gk), dim3(kthreads),
+                         0, st, p);
     else
-      hipLaunchKernelGGL((bwd_dkdv_kernel<D, 2, VL, M>), dim3((unsigned)gk), dim3(kthreads), 0,
-                         st, p);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<D, 2, VL, M, PX>), dim3((unsigned)gk), dim3(kthreads),
+                         0, st, p);
   };
   if (gk > 0) {
     if constexpr (D >= 256) {
@@ -869,6 +951,7 @@ __global__ __launch_bounds__(256) void cast_bf16_f32_kernel(const __bf16* __rest
 
 template <int D>
 hipError_t launch_bwd_d(const BwdParams& p, hipStream_t st) {
+  if (p.px_keep) return launch_bwd_dv<D, false, true>(p, st);  // the proxy route (batched)
   return p.varlen ? launch_bwd_dv<D, true>(p, st) : launch_bwd_dv<D, false>(p, st);
 }
 

@@ -114,29 +114,50 @@ struct BwdParams {
   // dK/dV launch order (workspace, written by the launch): the KV-block
   // rows by decreasing KV-major list length, or nullptr for index order
   int32_t* kv_order;
+  // Proxy route (batched; the PX kernel instances run when px_keep is set).
+  // KV blocks 0 .. px_n-1 hold the keys and values (keys from px_sk on are
+  // masked); the blocks after them hold one summary key per original block
+  // (mean key, summed value / c_n; c_n the block's token count), whose
+  // softmax weight c_n enters as log2 c_n added to its exponent.  Summary
+  // position u (key px_k0 + u, px_k0 = px_n*block_kv) holds block u's
+  // summaries for u < px_nreg (full blocks, weight log2 block_kv = px_lw);
+  // a last block shorter than block_kv has a KV block of its own, px_gl,
+  // whose first key holds its summaries (weight px_lwl = log2 c_last; px_gl
+  // = -1 when there is none).  Q block i of (b, h) takes position u when bit
+  // u % 64 of word px_keep[((b*H + h)*M + i)*px_w + u/64] is set.  dK/dV of
+  // the keys go to dk/dv (rows < px_sk), those of the summaries to px_dks /
+  // px_dvs ([B, px_n, H_kv, D], element strides), dV divided by c_n.
+  const uint64_t* px_keep;
+  void* px_dks;
+  void* px_dvs;
+  int64_t px_dks_sb, px_dks_sn, px_dks_sh, px_dvs_sb, px_dvs_sn, px_dvs_sh;
+  int32_t px_n, px_nreg, px_gl, px_w, px_sk, px_k0, px_cl;
+  float px_lw, px_lwl;
 };
 // Rows the dK/dV launch order covers at most (beyond it: index order).
 constexpr int64_t kBwdOrderMaxItems = (int64_t)1 << 20;
-// Backward of the proxy route: the extended K/V (blocks 0..N-1 the keys and
-// values, N..2N-1 c_n copies of each block's summaries), its block mask and
-// valid counts, and the gradients read back out.  bf16 data as 16-bit
-// patterns; element strides; the extended arrays contiguous
-// [B, 2*N*bk, Hkv, D], the mask [B, H, M, 2N], the valid counts [2N].
+// Backward of the proxy route: the extended K/V, contiguous [B, (N + Nc)*bk,
+// Hkv, D]: rows t < N*bk the keys and values (zero past Sk), then summary
+// positions u = t - N*bk: block u's mean key and summed value / c_n for
+// u < nreg, the last block's at u = lastpos when it is shorter than bk
+// (lastpos = ceil(nreg / bk)*bk, its own chunk; else lastpos = -1), zero
+// elsewhere.  The extended block mask [B, H, M, N + Nc] marks block n < N
+// when the row lists it and block N + g when the row takes any summary
+// position of chunk g (positions g*bk .. g*bk + bk - 1); the positions a
+// row takes (blocks it does not list) are bits, [B, H, M, W] words of 64
+// (W = ceil(Nc*bk / 64)).  bf16 data as 16-bit patterns; element strides.
 struct ProxyBwdParams {
   const uint16_t *k, *v, *ks, *vs;
   int64_t k_sb, k_ss, k_sh, v_sb, v_ss, v_sh;
   int64_t ks_sb, ks_sn, ks_sh, vs_sb, vs_sn, vs_sh;
   uint16_t *kx, *vx;
-  const uint16_t *dkx, *dvx;
-  uint16_t *dk, *dv, *dks, *dvs;
   uint8_t* maskx;
-  int32_t* kvvx;
+  uint64_t* keep;
   const int32_t *mcnt, *midx, *fcnt, *fidx;
   int64_t mc_s[3], mi_s[4], fc_s[3], fi_s[4];
-  int32_t B, H, Hkv, M, N, bk, Sk, D;
+  int32_t B, H, Hkv, M, N, Nc, W, bk, Sk, D, nreg, lastpos;
 };
 hipError_t launch_proxy_bwd_prepare(const ProxyBwdParams& p, hipStream_t s);
-hipError_t launch_proxy_bwd_gather(const ProxyBwdParams& p, hipStream_t s);
 
 hipError_t launch_bwd(const BwdParams& p, int D, hipStream_t s);
 // fp32 [B,S,H,D] (element strides str, unit head_dim stride) <-> contiguous bf16
