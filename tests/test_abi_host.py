@@ -155,7 +155,9 @@ def test_proxy_backward_argument_errors_on_the_host():
     assert call(1, 2, 2, 64) == 1  # missing tensors
     nbytes = ctypes.c_int64()
     assert lib.bsa_bwd_proxy_work_size(2, 4, 2, 300, 333, 128, 128, 48, ctypes.byref(nbytes)) == 0
-    N, M = 7, 3
-    xb = 2 * 2 * N * 48 * 2 * 128 * 2  # B * 2N*bk * Hkv * D * 2 bytes, four of them
-    assert nbytes.value >= 4 * xb + 2 * 4 * M * 2 * N * 4
+    # Sk 333 = 6 full 48-key blocks and one of 45: the six summaries in one
+    # chunk, the partial block's in a chunk of its own, so 7 + 2 KV blocks
+    NX, M = 9, 3
+    xb = 2 * NX * 48 * 2 * 128 * 2  # B * NX*bk * Hkv * D * 2 bytes, K and V
+    assert nbytes.value >= 2 * xb + 2 * 4 * M * NX * 4
     assert lib.bsa_bwd_proxy_work_size(2, 4, 2, 300, 333, 128, 0, 48, ctypes.byref(nbytes)) == 1
