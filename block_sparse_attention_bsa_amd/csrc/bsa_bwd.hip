@@ -50,13 +50,22 @@ typedef __attribute__((address_space(3))) char lds_char;
 // side streams in sub-tiles of kBwdT positions.
 constexpr int kBwdT = 64;
 
+// Bits [max(lo, 0), min(hi, 63)] of a 64-bit mask (zero when empty).
+__device__ __forceinline__ uint64_t range_bits(int lo, int hi) {
+  lo = max(lo, 0);
+  hi = min(hi, 63);
+  if (hi < lo) return 0ull;
+  const uint64_t upto = hi >= 63 ? ~0ull : (1ull << (hi + 1)) - 1;
+  return upto & ~((1ull << lo) - 1);
+}
+
 __device__ __forceinline__ uint32_t word4(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
 // The positions [lo, hi] of a 64-position sub-tile that the element rule of
-// a mask-list block keeps for this lane, so the inner loops compare instead
-// of branching per element.  Keys (dQ: the lane owns sequence row `row`, the
+// a mask-list block keeps for this lane (the inner loops test them as bits,
+// range_bits, instead of branching per element).  Keys (dQ: the lane owns sequence row `row`, the
 // sub-tile holds keys k0 ..) or rows (dK/dV: the lane owns key `key`, the
 // sub-tile holds rows r0 ..) of KV block j.
 __device__ __forceinline__ void keys_kept(const BwdParams& p, const int32_t* kvv, int row, int k0,
@@ -469,13 +478,18 @@ void bwd_dq_kernel(const BwdParams p) {
       int klo = 0, khi = kBwdT - 1;
       if (list == 0) keys_kept(p, sv0.kvv, row, k0, j, klo, khi);
       khi = min(khi, nk - 1);
-      // proxy route: the lane's kept keys as bits (kb0 / kb1: keys of each
-      // half, bit 16*(reg >> 3) + (reg & 7) for accumulator reg), from the
-      // key range in a block of keys and from the Q block's bit set in a
-      // chunk of summaries, whose log-weight comes off the row's LSE
-      uint32_t kb0 = 0, kb1 = 0;
+      // the lane's kept keys as bits (kb0 / kb1: keys of each half, bit
+      // 16*(reg >> 3) + (reg & 7) for accumulator reg; one bit test per
+      // element is cheaper than the two compares of a range): from the key
+      // range, or on the proxy route in a chunk of summaries from the Q
+      // block's bit set, whose log-weight comes off the row's LSE
+      uint32_t kb0, kb1;
       float l2e = lse2;
-      if constexpr (PX) {
+      if constexpr (!PX) {
+        const uint64_t lm = range_bits(klo, khi) >> (8 * h32);
+        kb0 = (uint32_t)lm;
+        kb1 = (uint32_t)(lm >> 32);
+      } else {
         uint64_t kb;
         if (j < p.px_n) {
           khi = min(khi, p.px_sk - k0 - 1);
@@ -520,9 +534,7 @@ void bwd_dq_kernel(const BwdParams p) {
 #pragma unroll
           for (int y = 0; y < 2; ++y) {
             const int reg = 2 * x + y;
-            const int key = 16 * (reg >> 3) + 8 * h32 + (reg & 7) + 32 * hf;
-            const bool keep = PX ? ((kbh >> (16 * (reg >> 3) + (reg & 7))) & 1u) != 0
-                                 : key >= klo && key <= khi;
+            const bool keep = ((kbh >> (16 * (reg >> 3) + (reg & 7))) & 1u) != 0;
             const float pr = keep ? __builtin_amdgcn_exp2f(fmaf(sa[reg], p.c, -l2e)) : 0.f;
             v[y] = pr * (da[reg] - drow);
           }
@@ -731,6 +743,10 @@ void bwd_dkdv_kernel(const BwdParams p) {
         int rlo = 0, rhi = kBwdT - 1;
         if (list == 0) rows_kept(p, sv0.kvv, key, r0, j, rlo, rhi);
         rhi = kvalid && kwc ? min(rhi, nr - 1) : -1;
+        // as bits of the lane's rows (rb0 / rb1: rows of each half, bit
+        // 16*(reg >> 3) + (reg & 7) for accumulator reg)
+        const uint64_t rlm = range_bits(rlo, rhi) >> (8 * h32);
+        const uint32_t rb0 = (uint32_t)rlm, rb1 = (uint32_t)(rlm >> 32);
         // per half (rows 32*hf ..): S and dP, then P and dS packed for the
         // last products; one half at a time keeps the registers of the other
         // free
@@ -767,8 +783,8 @@ void bwd_dkdv_kernel(const BwdParams p) {
 #pragma unroll
             for (int y = 0; y < 2; ++y) {
               const int reg = 2 * x + y;
-              const int rl = 16 * (reg >> 3) + 8 * h32 + (reg & 7) + 32 * hf;
-              const bool keep = rl >= rlo && rl <= rhi;
+              const uint32_t rbh = hf == 0 ? rb0 : rb1;
+              const bool keep = ((rbh >> (16 * (reg >> 3) + (reg & 7))) & 1u) != 0;
               const int q4 = 2 * (reg >> 3) + ((reg & 7) >> 2), e4 = reg & 3;
               const float l2 = e4 == 0 ? l4[q4].x : e4 == 1 ? l4[q4].y : e4 == 2 ? l4[q4].z : l4[q4].w;
               const float dr = e4 == 0 ? d4[q4].x : e4 == 1 ? d4[q4].y : e4 == 2 ? d4[q4].z : d4[q4].w;
