@@ -385,7 +385,10 @@ __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))  // two waves per SIMD up
 void bwd_dq_kernel(const BwdParams p) {
   constexpr int TW = NW * 32;
   constexpr int DS = D / 16, DB = D / 32;
-  constexpr int ST = D <= 128 ? 2 : 1;  // LDS stages of (K, V) tiles
+  // LDS stages of (K, V) tiles: two for 4-wave workgroups up to d = 128; one
+  // for 2-wave ones, whose two stages (64 KiB at d = 128) would leave room
+  // for one wave per SIMD (one stage: two, and d128 64-row sweeps -4 %)
+  constexpr int ST = D <= 128 && NW == 4 ? 2 : 1;
   using T = BTile<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[ST * 2 * T::BYTES];
 
