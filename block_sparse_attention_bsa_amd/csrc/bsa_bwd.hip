@@ -50,24 +50,15 @@ typedef __attribute__((address_space(3))) char lds_char;
 // side streams in sub-tiles of kBwdT positions.
 constexpr int kBwdT = 64;
 
-// Bits [max(lo, 0), min(hi, 63)] of a 64-bit mask (zero when empty).
-__device__ __forceinline__ uint64_t range_bits(int lo, int hi) {
-  lo = max(lo, 0);
-  hi = min(hi, 63);
-  if (hi < lo) return 0ull;
-  const uint64_t upto = hi >= 63 ? ~0ull : (1ull << (hi + 1)) - 1;
-  return upto & ~((1ull << lo) - 1);
-}
-
 __device__ __forceinline__ uint32_t word4(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
 // The positions [lo, hi] of a 64-position sub-tile that the element rule of
 // a mask-list block keeps for this lane (the inner loops test them as bits,
-// range_bits, instead of branching per element).  Keys (dQ: the lane owns sequence row `row`, the
-// sub-tile holds keys k0 ..) or rows (dK/dV: the lane owns key `key`, the
-// sub-tile holds rows r0 ..) of KV block j.
+// key_bits, instead of branching per element).  Keys (dQ: the lane owns
+// sequence row `row`, the sub-tile holds keys k0 ..) or rows (dK/dV: the
+// lane owns key `key`, the sub-tile holds rows r0 ..) of KV block j.
 __device__ __forceinline__ void keys_kept(const BwdParams& p, const int32_t* kvv, int row, int k0,
                                           int j, int& lo, int& hi) {
   lo = 0;
@@ -505,7 +496,7 @@ void bwd_dq_kernel(const BwdParams p) {
       uint32_t kb0, kb1;
       float l2e = lse2;
       if constexpr (!PX) {
-        const uint64_t lm = range_bits(klo, khi) >> (8 * h32);
+        const uint64_t lm = key_bits(klo, khi) >> (8 * h32);
         kb0 = (uint32_t)lm;
         kb1 = (uint32_t)(lm >> 32);
       } else {
@@ -770,7 +761,7 @@ void bwd_dkdv_kernel(const BwdParams p) {
         rhi = kvalid && kwc ? min(rhi, nr - 1) : -1;
         // as bits of the lane's rows (rb0 / rb1: rows of each half, bit
         // 16*(reg >> 3) + (reg & 7) for accumulator reg)
-        const uint64_t rlm = range_bits(rlo, rhi) >> (8 * h32);
+        const uint64_t rlm = key_bits(rlo, rhi) >> (8 * h32);
         const uint32_t rb0 = (uint32_t)rlm, rb1 = (uint32_t)(rlm >> 32);
         // per half (rows 32*hf ..): S and dP, then P and dS packed for the
         // last products; one half at a time keeps the registers of the other

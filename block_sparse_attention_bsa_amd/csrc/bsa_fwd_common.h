@@ -478,6 +478,15 @@ __device__ __forceinline__ float half_swap_max(float x) {
   return fmaxf(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
 }
 
+// Bits [max(lo, 0), min(hi, 63)] of a 64-bit mask (zero when empty).
+__device__ __forceinline__ uint64_t key_bits(int lo, int hi) {
+  lo = max(lo, 0);
+  hi = min(hi, 63);
+  if (hi < lo) return 0ull;
+  const uint64_t upto = hi >= 63 ? ~0ull : (1ull << (hi + 1)) - 1;
+  return upto & ~((1ull << lo) - 1);
+}
+
 // Online-softmax step for one 64-key sub-tile.  s0/s1 hold S^T for keys
 // 0..31 / 32..63 of the sub-tile (raw dot products).  Applies the element
 // mask, updates the running max m (base-2 units of scale*s), the running sum
@@ -498,11 +507,11 @@ __device__ __forceinline__ void softmax_step(f32x16_t& s0, f32x16_t& s1, const I
                                              f32x16_t (&oacc)[DB], uint32_t (&pk0)[8],
                                              uint32_t (&pk1)[8]) {
   if (masked || it.nk < kKvTile) {
+    if constexpr (SEG) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = 16 * (r >> 3) + 8 * h32 + (r & 7);
-      bool keep0 = key < it.nk, keep1 = key + 32 < it.nk;
-      if constexpr (SEG) {
+      for (int r = 0; r < 16; ++r) {
+        const int key = 16 * (r >> 3) + 8 * h32 + (r & 7);
+        bool keep0 = key < it.nk, keep1 = key + 32 < it.nk;
         if (masked) {
           // run of item key k, its sequence key, and the causal test where
           // the run is marked (sums of steps: no select chains)
@@ -515,17 +524,27 @@ __device__ __forceinline__ void softmax_step(f32x16_t& s0, f32x16_t& s1, const I
           keep0 = keep0 && keep(key);
           keep1 = keep1 && keep(key + 32);
         }
-      } else if (masked) {
-        const int c0 = it.key0 + key, c1 = c0 + 32;
-        keep0 = keep0 && c0 <= mhi;
-        keep1 = keep1 && c1 <= mhi;
-        if constexpr (RANGE) {
-          keep0 = keep0 && c0 >= mlo;
-          keep1 = keep1 && c1 >= mlo;
-        }
+        if (!keep0) s0[r] = neg_inf();
+        if (!keep1) s1[r] = neg_inf();
       }
-      if (!keep0) s0[r] = neg_inf();
-      if (!keep1) s1[r] = neg_inf();
+    } else {
+      // the item's kept keys for this lane's row, [lo, hi], as bits of the
+      // lane's keys (one bit test per element instead of a chain of
+      // compares): bit 16*(r >> 3) + (r & 7) of the low (s0) and high (s1)
+      // words for accumulator r
+      int lo = 0, hi = it.nk - 1;
+      if (masked) {
+        hi = min(hi, mhi - it.key0);
+        if constexpr (RANGE) lo = max(lo, mlo - it.key0);
+      }
+      const uint64_t lm = key_bits(lo, hi) >> (8 * h32);
+      const uint32_t b0 = (uint32_t)lm, b1 = (uint32_t)(lm >> 32);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int bit = 16 * (r >> 3) + (r & 7);
+        if (((b0 >> bit) & 1u) == 0) s0[r] = neg_inf();
+        if (((b1 >> bit) & 1u) == 0) s1[r] = neg_inf();
+      }
     }
   }
   // row max: 32 values, a tree of 3-input maxes (v_max3_f32)
