@@ -487,6 +487,14 @@ __device__ __forceinline__ uint64_t key_bits(int lo, int hi) {
   return upto & ~((1ull << lo) - 1);
 }
 
+// x - base clamped to [-1, 64] (computed in 64 bits: x may be an unbounded
+// INT_MAX or a far negative window end, base negative): an item position
+// for key_bits.
+__device__ __forceinline__ int item_offset(int x, int base) {
+  const int64_t v = (int64_t)x - base;
+  return (int)(v < -1 ? -1 : v > kKvTile ? kKvTile : v);
+}
+
 // Online-softmax step for one 64-key sub-tile.  s0/s1 hold S^T for keys
 // 0..31 / 32..63 of the sub-tile (raw dot products).  Applies the element
 // mask, updates the running max m (base-2 units of scale*s), the running sum
@@ -507,37 +515,33 @@ __device__ __forceinline__ void softmax_step(f32x16_t& s0, f32x16_t& s1, const I
                                              f32x16_t (&oacc)[DB], uint32_t (&pk0)[8],
                                              uint32_t (&pk1)[8]) {
   if (masked || it.nk < kKvTile) {
+    // the item's kept keys for this lane's row as bits of the lane's keys
+    // (one bit test per element instead of a chain of compares): bit
+    // 16*(r >> 3) + (r & 7) of the low (s0) and high (s1) words for
+    // accumulator r
+    uint64_t kb;
     if constexpr (SEG) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 16 * (r >> 3) + 8 * h32 + (r & 7);
-        bool keep0 = key < it.nk, keep1 = key + 32 < it.nk;
-        if (masked) {
-          // run of item key k, its sequence key, and the causal test where
-          // the run is marked (sums of steps: no select chains)
-          auto keep = [&](int k) {
-            const int s = (int)(k >= it.e0) + (int)(k >= it.e1) + (int)(k >= it.e2);
-            const int ck = k + it.d0 + (it.d1 - it.d0) * (int)(k >= it.e0) +
-                           (it.d2 - it.d1) * (int)(k >= it.e1) + (it.d3 - it.d2) * (int)(k >= it.e2);
-            return ((it.is_mask >> s) & 1) == 0 || ck <= mhi;
-          };
-          keep0 = keep0 && keep(key);
-          keep1 = keep1 && keep(key + 32);
-        }
-        if (!keep0) s0[r] = neg_inf();
-        if (!keep1) s1[r] = neg_inf();
-      }
+      // runs [0, e0), [e0, e1), [e1, e2), [e2, nk): item key k of run s is
+      // sequence key k + d_s; a run marked causal keeps k + d_s <= mhi
+      auto run = [&](int a, int e, int d, int s) {
+        int last = e - 1;
+        if (masked && ((it.is_mask >> s) & 1)) last = min(last, item_offset(mhi, d));
+        return key_bits(a, last);
+      };
+      kb = run(0, min(it.e0, it.nk), it.d0, 0) | run(it.e0, min(it.e1, it.nk), it.d1, 1) |
+           run(it.e1, min(it.e2, it.nk), it.d2, 2) | run(it.e2, it.nk, it.d3, 3);
     } else {
-      // the item's kept keys for this lane's row, [lo, hi], as bits of the
-      // lane's keys (one bit test per element instead of a chain of
-      // compares): bit 16*(r >> 3) + (r & 7) of the low (s0) and high (s1)
-      // words for accumulator r
+      // [lo, hi]: within the visible count and, on a masked item, the row's
+      // key range
       int lo = 0, hi = it.nk - 1;
       if (masked) {
-        hi = min(hi, mhi - it.key0);
-        if constexpr (RANGE) lo = max(lo, mlo - it.key0);
+        hi = min(hi, item_offset(mhi, it.key0));
+        if constexpr (RANGE) lo = max(lo, item_offset(mlo, it.key0));
       }
-      const uint64_t lm = key_bits(lo, hi) >> (8 * h32);
+      kb = key_bits(lo, hi);
+    }
+    {
+      const uint64_t lm = kb >> (8 * h32);
       const uint32_t b0 = (uint32_t)lm, b1 = (uint32_t)(lm >> 32);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
