@@ -306,16 +306,16 @@ bsa_status bsa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   p.win_left = bs->window_left;
   p.win_right = bs->window_right;
   p.varlen = 0;
-  // Route packing where KV blocks leave at least a fifth of the 64-key
-  // items' MFMA slots empty (a packed item costs some VALU for its gathered
-  // addresses, which the 12.5 % of 112-key blocks does not repay: measured
-  // -4 % there, +18 % at 48 keys, 2.8x at 16): the 128/64/32-row bf16 kernel
-  // (no local mask, no proxies; not the 32-row tiles at head_dim >= 192,
-  // whose registers would spill) gathers K/V rows by 31-bit byte offsets
-  // from the sequence's first row
+  // Route packing where KV blocks are not a whole number of 64-key items
+  // (with the run masks tested as bits, even the 12.5 % of empty slots of
+  // 112-key blocks repays the gathered addresses: d128 sweep +0.5 %, d64
+  // +5 %, d192 +3.5 %, d256 +2.5 %; 48 keys +12 %, 16 keys 3x): the
+  // 128/64/32-row bf16 kernel (no local mask, no proxies; not the 32-row
+  // tiles at head_dim >= 192, whose registers would spill) gathers K/V rows
+  // by 31-bit byte offsets from the sequence's first row
   const int64_t lim = (int64_t)1 << 31;
   const int64_t bk_items = cdiv64(bs->block_kv, bsa::kKvTile) * bsa::kKvTile;
-  p.pack = 5 * (bk_items - bs->block_kv) >= bk_items && tile_m <= 128 &&
+  p.pack = bk_items > bs->block_kv && tile_m <= 128 &&
            !(tile_m == 32 && D >= 192) && dt == BSA_BF16 &&
            mask_mod != BSA_MASK_LOCAL && !proxy && (int64_t)Sk * k_str[1] * 2 < lim &&
            (int64_t)Sk * v_str[1] * 2 < lim;
