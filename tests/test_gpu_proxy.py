@@ -138,6 +138,12 @@ BWD_REL_TOL = 1e-2  # of each gradient's largest magnitude, as for bsa_bwd
     dict(Sq=200, Sk=333, D=128, bq=128, bk=48, density=0.4),  # short last block (45 tokens)
     dict(Sq=150, Sk=410, D=96, bq=64, bk=80, density=0.25),
     dict(Sq=128, Sk=257, D=256, bq=64, bk=64, density=0.3),   # a last block of one token
+    # full last blocks (no chunk of its own), 128-key blocks (two sub-tiles per chunk)
+    dict(Sq=256, Sk=512, D=128, bq=128, bk=128, density=0.3),
+    # 100 full 80-key blocks: the second chunk's positions 80.. straddle two 64-bit words
+    dict(Sq=192, Sk=8000, D=64, bq=64, bk=80, density=0.1),
+    # 16 full 16-key blocks fill their chunk exactly; the 5-token last one starts the next
+    dict(Sq=128, Sk=261, D=128, bq=64, bk=16, density=0.3),
 ])
 def test_proxy_backward_matches_oracle(case):
     # dq, dk, dv and both summaries' gradients against the float64 oracle on
