@@ -265,20 +265,26 @@ bsa_status bsa_bwd_f32(const float* q, const float* k, const float* v, const flo
  * is that forward's derivative).  That forward is attention over keys rebuilt
  * token by token: each Q block's listed blocks with their own tokens, every
  * other block n as c_n copies of (proxy_k[n], proxy_v[n] / c_n), c_n its
- * token count.  This call builds that extended KV sequence in the workspace
- * (2N blocks: K and V, then the copies), runs bsa_bwd's kernels on it under
- * the valid-count mask_mod, and reads out dq, dk, dv and the summaries'
- * gradients: dproxy_k[n] = c_n times a copy's dK, dproxy_v[n] = a copy's dV.
- * Cost: that of the backward over every listed block plus every omitted one
- * at its full token count.
+ * token count.  The c_n copies of a key are one key whose exponential is
+ * weighted by c_n, so this call builds an extended KV sequence in the
+ * workspace (the N blocks of K and V, then one key per block holding its
+ * summaries, the value divided by c_n, in chunks of block_kv; a last block
+ * shorter than block_kv in a chunk of its own), marks per Q block the chunks
+ * holding summaries it takes (the blocks it does not list) and those
+ * summaries as bits, and runs bsa_bwd's kernels on it with log2 c_n added to
+ * each summary's exponent.  dk, dv are the keys' and values' gradients;
+ * dproxy_k[n] is the summary key's dK (the sum over its copies) and
+ * dproxy_v[n] its dV over c_n.  Cost: that of the backward over every
+ * listed block plus one key per omitted block (on the page's workload,
+ * 84 of 512 blocks listed, 1.1-1.2 times the exact-only backward).
  *  q, k, v, o, lse, dout, dq, dk, dv, strides: as for bsa_bwd (bf16).
  *  bs: the forward's lists, block sizes and summaries (proxy_k, proxy_v
  *    [B,N,H_kv,D] with strides proxy_*_str over {batch, block, head});
  *    mask_mod NONE (the route has no element mask).
  *  dproxy_k, dproxy_v: device bf16, the summaries' layout and strides.
  *  work: device scratch, 16-byte aligned, of the size bsa_bwd_proxy_work_size
- *    returns (the extended K/V and their gradients, its lists and their
- *    KV-major transposes, and bsa_bwd's workspace), overwritten.
+ *    returns (the extended K/V, its block mask, lists and their KV-major
+ *    transposes, the bit sets, and bsa_bwd's workspace), overwritten.
  * Errors and determinism as bsa_bwd. */
 bsa_status bsa_bwd_proxy_work_size(int32_t B, int32_t H, int32_t H_kv, int32_t Sq, int32_t Sk,
                                    int32_t D, int32_t block_q, int32_t block_kv,
