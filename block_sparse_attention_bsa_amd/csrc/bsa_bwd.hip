@@ -320,6 +320,26 @@ __device__ __forceinline__ void tr_product(const unsigned char* t, const TrGeo<D
   }
 }
 
+// tr_product with the reads of one position step (every head-dim block) at a
+// time issued ahead of its MFMAs.
+template <int D>
+__device__ __forceinline__ void tr_product_steps(const unsigned char* t, const TrGeo<D>& g,
+                                                 const uint32_t (&pk0)[8],
+                                                 const uint32_t (&pk1)[8],
+                                                 f32x16_t (&acc)[D / 32]) {
+#pragma unroll
+  for (int ps = 0; ps < 4; ++ps) {
+    uint4 a[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) a[db] = g.op(t, ps, db);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint4 bop = p_operand(pk0, pk1, ps);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(a[db], bop, acc[db]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // acc (rows of head_dim per lane, the forward's output layout) * mul -> bf16 row.
 template <int DB>
 __device__ __forceinline__ void store_row(__bf16* dst, int h32, const f32x16_t (&acc)[DB],
@@ -592,7 +612,9 @@ void bwd_dkdv_kernel(const BwdParams p) {
   // first MFMA (a scheduling barrier keeps them there): left to itself the
   // compiler put each read just ahead of its MFMA with a wait between, and
   // with one wave per SIMD nothing hid that latency (d128 sweep backward
-  // 0.465 -> 0.424 ms).  Beyond d = 128 the operands would spill.
+  // 0.465 -> 0.424 ms).  Beyond d = 128 all of them would spill, and the
+  // reads go 4 k-steps (S, dP) or one position step (dV, dK) ahead (d192 /
+  // d256 sweep backward -8 / -6.5 %).
   constexpr bool PRE = D <= 128;
   constexpr int TW = NQ * 32;
   constexpr int DS = D / 16, DB = D / 32;
@@ -803,11 +825,23 @@ void bwd_dkdv_kernel(const BwdParams p) {
               if (DO_DK) da = mfma32(ga[ks], vf[ks], da);  // dP
             }
           } else {
+            // d > 128: the reads of 4 k-steps at a time ahead of their MFMAs
 #pragma unroll
-            for (int ks = 0; ks < DS; ++ks) {
-              const int c = ((2 * ks + h32) ^ asw) * 16;
-              sa = mfma32(*reinterpret_cast<const uint4*>(qr + c), kf[ks], sa);  // S
-              if (DO_DK) da = mfma32(*reinterpret_cast<const uint4*>(gr + c), vf[ks], da);  // dP
+            for (int k0 = 0; k0 < DS; k0 += 4) {
+              uint4 qa[4], ga[4];
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                const int c = ((2 * (k0 + u) + h32) ^ asw) * 16;
+                qa[u] = *reinterpret_cast<const uint4*>(qr + c);
+                if (DO_DK) ga[u] = *reinterpret_cast<const uint4*>(gr + c);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                sa = mfma32(qa[u], kf[k0 + u], sa);               // S
+                if (DO_DK) da = mfma32(ga[u], vf[k0 + u], da);  // dP
+              }
+              __builtin_amdgcn_sched_barrier(0);
             }
           }
 #pragma unroll
@@ -829,8 +863,13 @@ void bwd_dkdv_kernel(const BwdParams p) {
             if (DO_DK) pks[hf][x] = pack_bf16x2(w2[0], w2[1]);
           }
         }
-        if (DO_DV) tr_product<D, PRE>(gt, tg, pk[0], pk[1], dv);    // dV^T += dO^T P
-        if (DO_DK) tr_product<D, PRE>(qt, tg, pks[0], pks[1], dk);  // dK^T += Q^T dS
+        if constexpr (PRE) {
+          if (DO_DV) tr_product<D, true>(gt, tg, pk[0], pk[1], dv);    // dV^T += dO^T P
+          if (DO_DK) tr_product<D, true>(qt, tg, pks[0], pks[1], dk);  // dK^T += Q^T dS
+        } else {
+          if (DO_DV) tr_product_steps<D>(gt, tg, pk[0], pk[1], dv);
+          if (DO_DK) tr_product_steps<D>(qt, tg, pks[0], pks[1], dk);
+        }
       }
       if (ST == 2 && more) put_rows(st ^ 1);
       if (ST == 1) {
