@@ -551,11 +551,33 @@ void bwd_dq_kernel(const BwdParams p) {
         }
         const unsigned char* kr = kt + (arow + 32 * hf) * (D / 8) * 16;
         const unsigned char* vr = vt + (arow + 32 * hf) * (D / 8) * 16;
+        if constexpr (D > 128) {
+          // one wave per SIMD: the reads of 4 k-steps at a time ahead of their
+          // MFMAs
 #pragma unroll
-        for (int ks = 0; ks < DS; ++ks) {
-          const int c = ((2 * ks + h32) ^ asw) * 16;
-          sa = mfma32(*reinterpret_cast<const uint4*>(kr + c), qf[ks], sa);  // S^T
-          da = mfma32(*reinterpret_cast<const uint4*>(vr + c), gf[ks], da);  // dP^T
+          for (int k0 = 0; k0 < DS; k0 += 4) {
+            uint4 ka[4], va[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int c = ((2 * (k0 + u) + h32) ^ asw) * 16;
+              ka[u] = *reinterpret_cast<const uint4*>(kr + c);
+              va[u] = *reinterpret_cast<const uint4*>(vr + c);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              sa = mfma32(ka[u], qf[k0 + u], sa);  // S^T
+              da = mfma32(va[u], gf[k0 + u], da);  // dP^T
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < DS; ++ks) {
+            const int c = ((2 * ks + h32) ^ asw) * 16;
+            sa = mfma32(*reinterpret_cast<const uint4*>(kr + c), qf[ks], sa);  // S^T
+            da = mfma32(*reinterpret_cast<const uint4*>(vr + c), gf[ks], da);  // dP^T
+          }
         }
         const uint32_t kbh = hf == 0 ? kb0 : kb1;
 #pragma unroll
@@ -571,7 +593,10 @@ void bwd_dq_kernel(const BwdParams p) {
           pk[hf][x] = pack_bf16x2(v[0], v[1]);
         }
       }
-      tr_product<D>(kt, tg, pk[0], pk[1], acc);  // dQ^T += K^T dS^T
+      if constexpr (D > 128)
+        tr_product_steps<D>(kt, tg, pk[0], pk[1], acc);  // dQ^T += K^T dS^T
+      else
+        tr_product<D>(kt, tg, pk[0], pk[1], acc);
     }
     if (ST == 1) {
       __syncthreads();  // every wave is done with the stage
